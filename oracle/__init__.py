@@ -1,0 +1,355 @@
+"""CPU oracle for the indexer -> top-k -> sparse-attention forward path.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call or execute
+this package: only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU
+baseline leg use it. It shares no code, headers, tables or helpers with the HIP
+library, and it imports nothing from it.
+
+Every function is the plain definition of its step, written in numpy with float64
+arithmetic, one query row at a time, with no blocking, fusion or reordering beyond
+what the definition states. Library primitives (matmul, sort, exp) serve as steps.
+
+Sources (web pages on indexer-routed sparse attention in Megatron-LM):
+
+* [QSA] "Add trainable QSA sparse attention with a TileLang backend"
+  (Megatron-LM issue #7060).
+* [DSA] "Enable DSA CP/absorbed/THD paths with TileLang fused ops"
+  (Megatron-LM PR #3674).
+* [NOPE] "Support NoPE shapes and unaligned top-k in TileLang sparse MLA"
+  (Megatron-LM PR #7617), including the downstream GLM-5.3-Flash PR body quoted
+  on that page.
+
+Readings taken where the pages are silent (each is listed with its reason in the
+design notes):
+
+* score I[t,s] = sum_h w[t,h] * max(q[t,h,:].k[s,:], 0); one indexer key row per
+  token shared by all indexer heads; any score scaling is folded into w;
+* causal: key s is a candidate for query t iff seq_start(t) <= s <= t;
+* block score = max of the token scores I over the block's causal keys;
+* order: a before b iff val_a > val_b, or val_a == val_b and idx_a < idx_b;
+  -0.0 counts as +0.0;
+* selected slots are emitted in ascending index order, then -1 padding;
+* sparse attention over the slots of an index row: each slot counts once, -1
+  slots are skipped, a row with no valid slot gives zeros and lse = -inf;
+  natural-log lse.
+
+Parity status: every function below is pinned by CPU tests against brute force,
+library routines, hand-derived fixtures and invariants, except the two points the
+pages leave undefined: the indexer's "official score scaling" and the exact block
+statistic. For those two, "parity unpinned" holds: the oracle follows the readings
+above and nothing on the pages can confirm them.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+NEG_INF = np.float32(-np.inf)
+
+
+# ------------------------------------------------------------------------ helpers
+
+def _f64(x) -> np.ndarray:
+    """Host float64 copy of a numpy array or a (CPU/GPU, any dtype) torch tensor."""
+    if hasattr(x, "detach"):
+        x = x.detach().float().cpu().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _i64(x) -> np.ndarray:
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().numpy()
+    return np.asarray(x, dtype=np.int64)
+
+
+def seq_bounds(T: int, cu_seqlens=None):
+    """Per row t: (start, end) of the packed sequence holding t.
+
+    THD packing as used by [DSA] ("What does this PR do ?": packed THD with varlen
+    bounds): sequence j spans rows [cu[j], cu[j+1]); no cu_seqlens means one
+    sequence [0, T).
+    """
+    cu = np.array([0, T], dtype=np.int64) if cu_seqlens is None else _i64(cu_seqlens)
+    start = np.empty(T, dtype=np.int64)
+    end = np.empty(T, dtype=np.int64)
+    for j in range(len(cu) - 1):
+        start[cu[j]:cu[j + 1]] = cu[j]
+        end[cu[j]:cu[j + 1]] = cu[j + 1]
+    return start, end
+
+
+def _canon_zero(x: np.ndarray) -> np.ndarray:
+    """-0.0 -> +0.0 (ReLU times a negative weight gives -0.0; it must tie with +0.0)."""
+    x = np.array(x, dtype=np.float32, copy=True)
+    x[x == 0] = 0.0
+    return x
+
+
+# ------------------------------------------------------------------ O1: indexer
+
+def indexer_scores_row(q_t, k_keys, w_t) -> np.ndarray:
+    """Token scores of one query against a run of keys, fp32.
+
+    [QSA] "Describe the solution you'd like": a multi-head indexer whose ReLU scores
+    tie at zero; [DSA] file table: fused indexer forward. Definition:
+    I[s] = sum_h w[h] * max(sum_d q[h,d] k[s,d], 0), evaluated in float64 from the
+    stored values, then rounded once to fp32 (nearest even) with -0 -> +0.
+
+    q_t [H_I, D_I], k_keys [n, D_I], w_t [H_I] -> [n] float32.
+    """
+    q = _f64(q_t)
+    k = _f64(k_keys)
+    w = _f64(w_t)
+    z = k @ q.T                       # [n, H_I]: z[s,h] = q[h,:] . k[s,:]
+    relu = np.maximum(z, 0.0)
+    I = relu @ w                      # [n]: sum_h w[h] * relu[s,h]
+    return _canon_zero(I.astype(np.float32))
+
+
+def indexer_scores_dense(q_I, k_I, w, cu_seqlens=None, block_size: int = 1,
+                         rows=None, ld: int | None = None) -> np.ndarray:
+    """Causal score matrix: token scores (block_size 1) or block scores (block_size B).
+
+    Row t, column c: token mode -> key s = start(t) + c for c <= t - start(t);
+    block mode -> block c of t's sequence, the max of the token scores over the
+    block's causal keys [start + cB, min(start + cB + B - 1, t)] ([QSA] "Is your
+    feature request related to a problem?": exact block TopK over the
+    [sequence, sequence / block_size] scores). Columns outside the causal range are
+    -inf. Rounding commutes with max (round-to-nearest is monotone), so taking the
+    max of fp32 token scores equals rounding the max of the float64 ones.
+
+    ``rows`` restricts to a subset of query rows (returned in that order).
+    """
+    T = q_I.shape[0]
+    start, end = seq_bounds(T, cu_seqlens)
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    if ld is None:
+        Lmax = int((end - start).max())
+        ld = Lmax if block_size == 1 else -(-Lmax // block_size)
+    out = np.full((len(rows), ld), NEG_INF, dtype=np.float32)
+    kk = _f64(k_I)
+    for r, t in enumerate(rows):
+        s0 = int(start[t])
+        tok = indexer_scores_row(q_I[t], kk[s0:t + 1], w[t])
+        if block_size == 1:
+            out[r, :tok.size] = tok
+        else:
+            nb = -(-tok.size // block_size)
+            for b in range(nb):
+                out[r, b] = tok[b * block_size:(b + 1) * block_size].max()
+    return out
+
+
+# ------------------------------------------------------------------ O3: top-k
+
+def topk_select_row(vals, n_valid: int, k: int, index_base: int = 0,
+                    force_last: bool = False):
+    """Exact deterministic top-k of one row.
+
+    [QSA] "Describe the solution you'd like": selection keyed lexicographically on
+    (score, id) so that ReLU ties at zero resolve the same way every run; [NOPE]
+    "What does this PR do?": unused slots carry the -1 sentinel.
+
+    Candidates are columns 0..n_valid-1 of ``vals``. Order: higher score first,
+    equal scores -> smaller column first (-0.0 ties +0.0). Take the first min(k, n)
+    of a full sort. With ``force_last`` (block routing: the query's own block is
+    the last valid column) the last column is taken first and counts toward k; the
+    other k-1 come from the sort of the remaining columns. Output: the chosen
+    columns + index_base in ascending order, then -1; values in the same slots,
+    -inf on pads.
+    """
+    v = _canon_zero(np.asarray(vals, dtype=np.float32)[:n_valid]).astype(np.float64)
+    cols = np.arange(n_valid, dtype=np.int64)
+    chosen = []
+    if force_last and n_valid > 0 and k > 0:
+        chosen.append(n_valid - 1)
+        v, cols = v[:-1], cols[:-1]
+        k_rest = k - 1
+    else:
+        k_rest = k
+    order = np.lexsort((cols, -v))    # primary: -value ascending; secondary: column
+    chosen.extend(cols[order[:max(k_rest, 0)]].tolist())
+    chosen = np.sort(np.asarray(chosen, dtype=np.int64))
+    idx = np.full(k, -1, dtype=np.int32)
+    val = np.full(k, NEG_INF, dtype=np.float32)
+    idx[:chosen.size] = chosen + index_base
+    val[:chosen.size] = _canon_zero(np.asarray(vals, dtype=np.float32)[chosen])
+    return idx, val
+
+
+def topk_select_dense(scores, k: int, cu_seqlens=None, block_size: int = 1,
+                      force_own_block: bool = False, rows=None):
+    """Row-wise ``topk_select_row`` over a causal dense score matrix.
+
+    Token mode (block_size 1): row t has t - start + 1 valid columns and the
+    output indices are global key rows (column + start). Block mode: row t has
+    (t - start) // B + 1 valid blocks, the indices are block ids local to the
+    sequence, and ``force_own_block`` keeps the query's own (last) block.
+    Score row r belongs to query row ``rows[r]`` (default: r). Without
+    ``cu_seqlens`` every row is in one sequence starting at 0.
+    """
+    scores = np.asarray(scores)
+    rows = np.arange(scores.shape[0]) if rows is None else np.asarray(rows)
+    if cu_seqlens is None:
+        starts = np.zeros(len(rows), dtype=np.int64)
+    else:
+        cu = _i64(cu_seqlens)
+        start, _ = seq_bounds(int(cu[-1]), cu)
+        starts = start[rows]
+    idx = np.full((len(rows), k), -1, dtype=np.int32)
+    val = np.full((len(rows), k), NEG_INF, dtype=np.float32)
+    for r, t in enumerate(rows):
+        off = int(t - starts[r])
+        if block_size == 1:
+            n, base = off + 1, int(starts[r])
+        else:
+            n, base = off // block_size + 1, 0
+        idx[r], val[r] = topk_select_row(scores[r], n, k, base,
+                                         force_last=(block_size > 1 and force_own_block))
+    return idx, val
+
+
+def topk_select_candidates(cand_val, cand_idx, k: int):
+    """Top-k of an explicit candidate list (value, index) per row; -1 entries skipped.
+
+    Same order as ``topk_select_row``, with the candidate's own index in place of
+    its column. Output ascending by index, -1 padded.
+    """
+    cv = np.asarray(cand_val, dtype=np.float32)
+    ci = _i64(cand_idx)
+    T = cv.shape[0]
+    idx = np.full((T, k), -1, dtype=np.int32)
+    val = np.full((T, k), NEG_INF, dtype=np.float32)
+    for t in range(T):
+        keep = ci[t] >= 0
+        v = _canon_zero(cv[t][keep]).astype(np.float64)
+        ii = ci[t][keep]
+        order = np.lexsort((ii, -v))[:k]
+        sel = np.sort(ii[order])
+        idx[t, :sel.size] = sel
+        pos = {int(i): j for j, i in enumerate(ii)}
+        val[t, :sel.size] = [_canon_zero(cv[t][keep])[pos[int(i)]] for i in sel]
+    return idx, val
+
+
+# ------------------------------------------------------------- O4: sparse MLA
+
+def sparse_mla_row(q_t, kv, idx_t, scale: float, d_v: int = 512):
+    """Absorbed-MLA attention of one query row over its selected latent rows.
+
+    [DSA] file table: sparse-MLA forward; [NOPE] "What does this PR do?" and the
+    quoted GLM PR body ("Change"): q/k share the latent row, the value is the
+    first 512 channels of the same row, -1 slots are masked, the caller's softmax
+    scale is used as given. Definition, in float64 over valid slots j:
+      l[h,j] = scale * sum_c q[h,c] kv[idx_j, c]; m = max_j l; p = exp(l - m);
+      out[h,:] = sum_j p[h,j] kv[idx_j, :d_v] / sum_j p[h,j]; lse[h] = m + ln sum p.
+    No valid slot -> out = 0, lse = -inf. Each slot counts once (duplicates count
+    per slot).
+
+    q_t [H, d_qk], kv [S, d_qk], idx_t [k] -> out [H, d_v] float64, lse [H].
+    """
+    q = _f64(q_t)
+    idx = _i64(idx_t)
+    valid = idx[idx >= 0]
+    H = q.shape[0]
+    if valid.size == 0:
+        return np.zeros((H, d_v)), np.full(H, -np.inf)
+    rows = _f64(kv[valid.tolist()] if hasattr(kv, "detach") else kv[valid])
+    logits = scale * (q @ rows.T)                    # [H, n]
+    m = logits.max(axis=1, keepdims=True)
+    p = np.exp(logits - m)
+    Z = p.sum(axis=1, keepdims=True)
+    out = (p @ rows[:, :d_v]) / Z
+    lse = m[:, 0] + np.log(Z[:, 0])
+    return out, lse
+
+
+def sparse_mla(q, kv, idx, scale: float, d_v: int = 512, rows=None):
+    """``sparse_mla_row`` for every row (or a subset); returns float64 out, lse."""
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    kvh = _f64(kv)
+    idxh = _i64(idx)
+    H = q.shape[1]
+    out = np.zeros((len(rows), H, d_v))
+    lse = np.zeros((len(rows), H))
+    for r, t in enumerate(rows):
+        out[r], lse[r] = sparse_mla_row(q[t], kvh, idxh[t], scale, d_v)
+    return out, lse
+
+
+# -------------------------------------------------------- O5: block-sparse GQA
+
+def block_sparse_gqa_row(q_t, k, v, blk_t, t: int, seq_start: int,
+                         block_size: int, scale: float):
+    """Grouped-query attention of one query over its selected key blocks.
+
+    [QSA] "Describe the solution you'd like": sparse GQA attention over the blocks
+    chosen by the block TopK. Keys: every s with s <= t whose local block
+    (s - seq_start) // B is a slot of blk_t (slot -1 skipped; each slot counts
+    once). Head h reads kv head g = h // (Hq / Hkv). Per head, float64:
+      l[s] = scale * q[h,:].k[s,g,:]; out[h,:] = softmax(l) @ v[:, g, :];
+      lse[h] = log sum exp l. No key -> zeros and lse = -inf.
+
+    q_t [Hq, D], k [S, Hkv, D], v [S, Hkv, Dv] -> out [Hq, Dv], lse [Hq].
+    """
+    q = _f64(q_t)
+    Hq = q.shape[0]
+    Hkv = k.shape[1]
+    Dv = v.shape[2]
+    keys = []
+    for b in _i64(blk_t):
+        if b < 0:
+            continue
+        lo = seq_start + int(b) * block_size
+        hi = min(lo + block_size - 1, t)
+        keys.extend(range(lo, hi + 1))
+    out = np.zeros((Hq, Dv))
+    lse = np.full(Hq, -np.inf)
+    if not keys:
+        return out, lse
+    keys = np.asarray(keys, dtype=np.int64)
+    kk = _f64(k[keys])                                # [n, Hkv, D]
+    vv = _f64(v[keys])
+    group = Hq // Hkv
+    for h in range(Hq):
+        g = h // group
+        l = scale * (kk[:, g, :] @ q[h])
+        m = l.max()
+        p = np.exp(l - m)
+        Z = p.sum()
+        out[h] = (p @ vv[:, g, :]) / Z
+        lse[h] = m + np.log(Z)
+    return out, lse
+
+
+def block_sparse_gqa(q, k, v, blk, block_size: int, scale: float,
+                     cu_seqlens=None, rows=None):
+    """``block_sparse_gqa_row`` for every row (or a subset)."""
+    T = q.shape[0]
+    start, _ = seq_bounds(T, cu_seqlens)
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    kh, vh = _f64(k), _f64(v)
+    blkh = _i64(blk)
+    Hq, Dv = q.shape[1], v.shape[2]
+    out = np.zeros((len(rows), Hq, Dv))
+    lse = np.zeros((len(rows), Hq))
+    for r, t in enumerate(rows):
+        out[r], lse[r] = block_sparse_gqa_row(q[t], kh, vh, blkh[t], int(t), int(start[t]),
+                                              block_size, scale)
+    return out, lse
+
+
+# ------------------------------------------------------- composed: the path
+
+def indexer_topk(q_I, k_I, w, k: int, cu_seqlens=None, block_size: int = 1,
+                 force_own_block: bool = False, rows=None):
+    """Scores then selection, row by row (O1/O2 then O3)."""
+    T = q_I.shape[0]
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    idx = np.full((len(rows), k), -1, dtype=np.int32)
+    val = np.full((len(rows), k), NEG_INF, dtype=np.float32)
+    for r0 in range(0, len(rows), 64):
+        rr = rows[r0:r0 + 64]
+        sc = indexer_scores_dense(q_I, k_I, w, cu_seqlens, block_size, rows=rr)
+        i, v = topk_select_dense(sc, k, cu_seqlens, block_size, force_own_block, rows=rr)
+        idx[r0:r0 + len(rr)], val[r0:r0 + len(rr)] = i, v
+    return idx, val

@@ -1,0 +1,421 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each test checks an oracle function against one of: a hand-derived fixture under
+tests/golden/, a library routine the definition reduces to in a special case
+(torch scaled-dot-product attention in float64, numpy/torch matmul), brute force
+over Python tuples on tiny rows, or an invariant the mathematics fixes. The cases
+are chosen so that a dropped term, a wrong sign or index, or a transposed operand
+fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _none_to(x, v):
+    return np.array([[v if e is None else e for e in r] for r in x], dtype=np.float32)
+
+
+# ----------------------------------------------------------------- indexer (O1/O2)
+
+def test_indexer_golden_tokens_and_blocks():
+    g = _load("indexer_tiny.json")
+    q = np.array(g["q_I"], dtype=np.float32)
+    k = np.array(g["k_I"], dtype=np.float32)
+    w = np.array(g["w"], dtype=np.float32)
+    got = oracle.indexer_scores_dense(q, k, w)
+    np.testing.assert_array_equal(got, _none_to(g["scores"], -np.inf))
+    got_b = oracle.indexer_scores_dense(q, k, w, block_size=2)
+    np.testing.assert_array_equal(got_b, _none_to(g["block2"], -np.inf))
+
+
+def test_indexer_single_head_unit_weight_is_relu_matmul():
+    # H_I = 1, w = 1: the score is max(Q K^T, 0), a plain library matmul.
+    rng = np.random.default_rng(5)
+    T, D = 37, 16
+    q = rng.standard_normal((T, 1, D)).astype(np.float32)
+    k = rng.standard_normal((T, D)).astype(np.float32)
+    w = np.ones((T, 1), dtype=np.float32)
+    ref = torch.relu(torch.from_numpy(q[:, 0, :]).double() @ torch.from_numpy(k).double().T)
+    ref = ref.float().numpy()
+    got = oracle.indexer_scores_dense(q, k, w)
+    for t in range(T):
+        np.testing.assert_array_equal(got[t, :t + 1], np.where(ref[t, :t + 1] == 0, 0, ref[t, :t + 1]))
+        assert np.all(np.isneginf(got[t, t + 1:]))
+
+
+def test_indexer_integer_inputs_exact_and_invariants():
+    rng = np.random.default_rng(6)
+    T, H, D = 29, 5, 8
+    q = rng.integers(-3, 4, (T, H, D)).astype(np.float32)
+    k = rng.integers(-3, 4, (T, D)).astype(np.float32)
+    w = (rng.integers(-8, 9, (T, H)) / 4).astype(np.float32)
+    base = oracle.indexer_scores_dense(q, k, w)
+    # exact brute force with Python integers / fractions
+    for t in [0, 7, 28]:
+        for s in range(t + 1):
+            acc = 0.0
+            for h in range(H):
+                z = int(sum(int(q[t, h, d]) * int(k[s, d]) for d in range(D)))
+                acc += float(w[t, h]) * max(z, 0)
+            assert base[t, s] == np.float32(acc)
+    # permuting heads together with their weights leaves scores unchanged
+    perm = rng.permutation(H)
+    np.testing.assert_array_equal(oracle.indexer_scores_dense(q[:, perm], k, w[:, perm]), base)
+    # positive homogeneity in w and in k (powers of two keep it exact)
+    np.testing.assert_array_equal(oracle.indexer_scores_dense(q, k, 2 * w), 2 * base)
+    np.testing.assert_array_equal(oracle.indexer_scores_dense(q, 4 * k, w), 4 * base)
+    # a negative k flips which heads pass the ReLU: not homogeneous (guards a dropped ReLU)
+    neg = oracle.indexer_scores_dense(q, -k, w)
+    assert not np.array_equal(neg[np.isfinite(neg)], -base[np.isfinite(base)])
+
+
+def test_indexer_thd_rows_only_see_their_sequence():
+    rng = np.random.default_rng(7)
+    lengths = (5, 9, 3)
+    cu = workloads.cu_seqlens(lengths)
+    T = sum(lengths)
+    q = rng.standard_normal((T, 3, 4)).astype(np.float32)
+    k = rng.standard_normal((T, 4)).astype(np.float32)
+    w = rng.uniform(0, 1, (T, 3)).astype(np.float32)
+    got = oracle.indexer_scores_dense(q, k, w, cu_seqlens=cu)
+    for j in range(3):
+        a, b = cu[j], cu[j + 1]
+        alone = oracle.indexer_scores_dense(q[a:b], k[a:b], w[a:b], ld=got.shape[1])
+        np.testing.assert_array_equal(got[a:b], alone)
+
+
+def test_block_scores_are_blockwise_max_of_token_scores():
+    rng = np.random.default_rng(8)
+    T, B = 70, 8
+    q = rng.standard_normal((T, 2, 4)).astype(np.float32)
+    k = rng.standard_normal((T, 4)).astype(np.float32)
+    w = rng.standard_normal((T, 2)).astype(np.float32)
+    tok = oracle.indexer_scores_dense(q, k, w)
+    blk = oracle.indexer_scores_dense(q, k, w, block_size=B)
+    for t in range(T):
+        nb = t // B + 1
+        for b in range(nb):
+            lo, hi = b * B, min(b * B + B - 1, t)
+            assert blk[t, b] == max(tok[t, s] for s in range(lo, hi + 1))
+        assert np.all(np.isneginf(blk[t, nb:]))
+
+
+# ----------------------------------------------------------------------- top-k (O3)
+
+def test_topk_golden_ties():
+    g = _load("topk_ties.json")
+    row = np.array([-0.0 if v is None else v for v in g["row"]], dtype=np.float32)
+    assert np.signbit(row[3])
+    for c in g["cases"]:
+        idx, val = oracle.topk_select_row(row, c["n_valid"], c["k"], force_last=c["force_last"])
+        assert idx.tolist() == c["idx"], c["why"]
+        for j, i in enumerate(idx):
+            if i < 0:
+                assert np.isneginf(val[j])
+            else:
+                assert val[j] == row[i]
+                assert val[j] != 0 or not np.signbit(val[j])      # -0.0 reported as +0.0
+
+
+def _brute_topk(vals, n, k, base=0):
+    keyed = sorted(((-float(vals[c]) + 0.0, c) for c in range(n)))
+    pick = sorted(c for _, c in keyed[:k])
+    return [c + base for c in pick] + [-1] * (k - len(pick))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_matches_tuple_sort_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    for _ in range(40):
+        n = int(rng.integers(0, 60))
+        k = int(rng.integers(1, 70))
+        # few distinct values -> many ties, including signed zeros
+        vals = rng.choice(np.array([-1.0, -0.0, 0.0, 0.5, 2.0], dtype=np.float32), size=64)
+        base = int(rng.integers(0, 1000))
+        idx, _ = oracle.topk_select_row(vals, n, k, base)
+        assert idx.tolist() == _brute_topk(vals, n, k, base)
+
+
+def test_topk_invariants_random_rows():
+    rng = np.random.default_rng(9)
+    for _ in range(50):
+        n = int(rng.integers(1, 300))
+        k = int(rng.integers(1, 200))
+        vals = np.round(rng.standard_normal(n) * 2).astype(np.float32)  # heavy ties
+        idx, val = oracle.topk_select_row(vals, n, k)
+        sel = idx[idx >= 0]
+        assert sel.size == min(k, n)
+        assert np.all(np.diff(sel) > 0)                       # ascending, no duplicates
+        assert np.all(idx[sel.size:] == -1)
+        assert sel.min() >= 0 and sel.max() < n
+        uns = np.setdiff1d(np.arange(n), sel)
+        if uns.size:
+            assert vals[sel].min() >= vals[uns].max()
+            tau = vals[sel].min()
+            if np.any(vals[uns] == tau):                      # boundary tie: smaller wins
+                assert sel[vals[sel] == tau].max() < uns[vals[uns] == tau].min()
+
+
+def test_topk_special_cases():
+    z = np.zeros(100, dtype=np.float32)
+    idx, _ = oracle.topk_select_row(z, 100, 10)
+    assert idx.tolist() == list(range(10))                    # all-equal: k smallest indices
+    v = np.arange(50, dtype=np.float32)
+    idx, _ = oracle.topk_select_row(v, 50, 64)
+    assert idx.tolist() == list(range(50)) + [-1] * 14         # k >= valid: all valid
+    idx, _ = oracle.topk_select_row(v, 50, 3)
+    assert idx.tolist() == [47, 48, 49]
+
+
+def test_topk_union_of_tile_topks_equals_global():
+    # exactness of a per-tile partial top-k followed by a final top-k
+    rng = np.random.default_rng(10)
+    for _ in range(20):
+        n = int(rng.integers(100, 900))
+        k = int(rng.integers(1, 120))
+        vals = np.round(rng.standard_normal(n) * 3).astype(np.float32)
+        glob, _ = oracle.topk_select_row(vals, n, k)
+        tile = int(rng.integers(16, 200))
+        cv, ci = [], []
+        for a in range(0, n, tile):
+            i, v = oracle.topk_select_row(vals[a:], min(tile, n - a), k, index_base=a)
+            cv.extend(v[i >= 0].tolist())
+            ci.extend(i[i >= 0].tolist())
+        cv = np.array(cv, dtype=np.float32)[None]
+        ci = np.array(ci, dtype=np.int32)[None]
+        merged, _ = oracle.topk_select_candidates(cv, ci, k)
+        assert merged[0].tolist() == glob.tolist()
+
+
+def test_topk_dense_thd_and_block_mode():
+    lengths = (3, 5)
+    cu = workloads.cu_seqlens(lengths)
+    sc = np.full((8, 5), -np.inf, dtype=np.float32)
+    sc[0, :1] = [1]
+    sc[1, :2] = [0, 1]
+    sc[2, :3] = [2, 0, 1]
+    sc[3, :1] = [7]
+    sc[4, :2] = [1, 1]
+    sc[5, :3] = [0, 5, 0]
+    sc[6, :4] = [3, 3, 3, 3]
+    sc[7, :5] = [0, 1, 2, 3, 4]
+    idx, _ = oracle.topk_select_dense(sc, 2, cu_seqlens=cu)
+    assert idx.tolist() == [[0, -1], [0, 1], [0, 2], [3, -1], [3, 4], [3, 4], [3, 4], [6, 7]]
+    # block mode (B = 2), own block forced, ids local to the sequence
+    bs = np.full((8, 3), -np.inf, dtype=np.float32)
+    bs[7, :3] = [9, 1, 0]        # row 7 = offset 4 in seq 1 -> own block 2
+    idx, _ = oracle.topk_select_dense(bs, 2, cu_seqlens=cu, block_size=2,
+                                      force_own_block=True, rows=[7])
+    assert idx.tolist() == [[0, 2]]
+
+
+# ------------------------------------------------------------------ sparse MLA (O4)
+
+def test_mla_golden():
+    g = _load("attention_tiny.json")["mla"]
+    kv = np.array(g["kv"], dtype=np.float64)
+    for c in g["cases"]:
+        out, lse = oracle.sparse_mla_row(np.array(c["q"]), kv, np.array(c["idx"]), c["scale"], g["d_v"])
+        np.testing.assert_allclose(out, np.array(c["out"]), rtol=0, atol=1e-15)
+        if c["lse"][0] is None:
+            assert np.isneginf(lse[0])
+        else:
+            np.testing.assert_allclose(lse, c["lse"], rtol=1e-15)
+
+
+def _sdpa_masked(q, kv, mask, scale, d_v):
+    """torch's scaled-dot-product attention in float64 with a boolean key mask."""
+    qt = torch.from_numpy(q).double()[None]                  # [1, H, 1?]
+    return torch.nn.functional.scaled_dot_product_attention(
+        qt, torch.from_numpy(kv).double()[None, None],
+        torch.from_numpy(kv[:, :d_v]).double()[None, None],
+        attn_mask=torch.from_numpy(mask)[None, None], scale=scale)[0].numpy()
+
+
+def test_mla_matches_library_dense_masked_attention():
+    rng = np.random.default_rng(11)
+    S, H, dqk, dv, k = 40, 4, 24, 16, 9
+    kv = rng.standard_normal((S, dqk))
+    for t in [0, 5, 39]:
+        q = rng.standard_normal((H, dqk))
+        idx = np.full(k, -1)
+        n = min(k - 2, t + 1)
+        idx[rng.permutation(k)[:n]] = rng.permutation(t + 1)[:n]
+        out, lse = oracle.sparse_mla_row(q, kv, idx, 0.3, dv)
+        mask = np.zeros((1, S), dtype=bool)
+        mask[0, idx[idx >= 0]] = True
+        ref = _sdpa_masked(q[:, None, :], kv, mask, 0.3, dv)[:, 0, :]
+        np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+        logits = 0.3 * q @ kv[idx[idx >= 0]].T
+        np.testing.assert_allclose(lse, torch.logsumexp(torch.from_numpy(logits), 1).numpy(), rtol=1e-13)
+
+
+def test_mla_invariants():
+    rng = np.random.default_rng(12)
+    S, H = 30, 3
+    kv = rng.standard_normal((S, 576))
+    q = rng.standard_normal((H, 576))
+    idx = rng.permutation(S)[:12]
+    out, lse = oracle.sparse_mla_row(q, kv, idx, 1 / 24, 512)
+    # slot permutation and -1 insertion
+    o2, l2 = oracle.sparse_mla_row(q, kv, np.concatenate([[-1, -1], idx[::-1], [-1]]), 1 / 24, 512)
+    np.testing.assert_allclose(o2, out, atol=1e-12)
+    np.testing.assert_allclose(l2, lse, atol=1e-12)
+    # one valid slot: the output is that row's value channels exactly
+    o1, l1 = oracle.sparse_mla_row(q, kv, np.array([-1, 7, -1]), 1 / 24, 512)
+    np.testing.assert_array_equal(o1, np.broadcast_to(kv[7, :512], o1.shape))
+    np.testing.assert_allclose(l1, (q @ kv[7]) / 24, rtol=1e-13)
+    # all invalid
+    o0, l0 = oracle.sparse_mla_row(q, kv, np.full(5, -1), 1 / 24, 512)
+    assert np.all(o0 == 0) and np.all(np.isneginf(l0))
+    # the value is the first 512 channels: changing channels 512..575 of kv only
+    # moves the logits, so with q's RoPE slot zero the output is unchanged
+    qz = q.copy(); qz[:, 512:] = 0
+    kv2 = kv.copy(); kv2[:, 512:] = rng.standard_normal((S, 64))
+    np.testing.assert_array_equal(oracle.sparse_mla_row(qz, kv, idx, 0.1, 512)[0],
+                                  oracle.sparse_mla_row(qz, kv2, idx, 0.1, 512)[0])
+
+
+def test_mla_nope_512_equals_zero_padded_576():
+    rng = np.random.default_rng(13)
+    S, H = 50, 4
+    q512 = rng.standard_normal((S, H, 512)).astype(np.float32)
+    kv512 = rng.standard_normal((S, 512)).astype(np.float32)
+    q576 = np.pad(q512, ((0, 0), (0, 0), (0, 64)))
+    kv576 = np.pad(kv512, ((0, 0), (0, 64)))
+    idx = np.stack([np.where(np.arange(20) <= t, np.arange(20) * 2 % (t + 1), -1) for t in range(S)])
+    a, la = oracle.sparse_mla(q512, kv512, idx, 1 / math.sqrt(512), 512)
+    b, lb = oracle.sparse_mla(q576, kv576, idx, 1 / math.sqrt(512), 512)
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(la, lb)
+
+
+def test_mla_all_causal_keys_equals_causal_attention():
+    rng = np.random.default_rng(14)
+    S, H, d = 33, 2, 40
+    q = rng.standard_normal((S, H, d))
+    kv = rng.standard_normal((S, d))
+    idx = np.stack([np.where(np.arange(S) <= t, np.arange(S), -1) for t in range(S)])
+    out, _ = oracle.sparse_mla(q, kv, idx, 0.2, 32)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q).permute(1, 0, 2)[None],
+        torch.from_numpy(kv)[None, None].expand(1, H, S, d),
+        torch.from_numpy(kv[:, :32])[None, None].expand(1, H, S, 32),
+        is_causal=True, scale=0.2)[0].permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------- block-sparse GQA (O5)
+
+def test_gqa_golden():
+    g = _load("attention_tiny.json")["gqa"]
+    k = np.array(g["k"], dtype=np.float64)[:, None, :]
+    v = np.array(g["v"], dtype=np.float64)[:, None, :]
+    q = np.zeros((g["Hq"], g["D"]))
+    for c in g["cases"]:
+        out, _ = oracle.block_sparse_gqa_row(q, k, v, np.array(c["blk"]), c["t"], 0,
+                                             g["block_size"], 1.0)
+        np.testing.assert_allclose(out[:, 0], c["out"], atol=1e-15)
+
+
+def _gqa_sdpa(q, k, v, mask, scale):
+    Hq, Hkv = q.shape[1], k.shape[1]
+    rep = Hq // Hkv
+    kk = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(rep, 0)[None]
+    vv = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(rep, 0)[None]
+    qq = torch.from_numpy(q).permute(1, 0, 2)[None]
+    return torch.nn.functional.scaled_dot_product_attention(
+        qq, kk, vv, attn_mask=torch.from_numpy(mask)[None, None], scale=scale)[0].permute(1, 0, 2).numpy()
+
+
+def test_gqa_matches_library_with_block_mask_thd():
+    rng = np.random.default_rng(15)
+    lengths = (13, 20)
+    cu = workloads.cu_seqlens(lengths)
+    T, Hq, Hkv, D, Dv, B, nb = 33, 6, 2, 8, 5, 4, 3
+    q = rng.standard_normal((T, Hq, D))
+    k = rng.standard_normal((T, Hkv, D))
+    v = rng.standard_normal((T, Hkv, Dv))
+    start, _ = oracle.seq_bounds(T, cu)
+    blk = np.full((T, nb), -1)
+    mask = np.zeros((T, T), dtype=bool)
+    for t in range(T):
+        own = (t - start[t]) // B
+        choice = rng.permutation(own + 1)[:nb - 1].tolist()
+        row = sorted(set(choice + [own]))
+        blk[t, :len(row)] = row
+        for b in row:
+            for s in range(start[t] + b * B, min(start[t] + b * B + B - 1, t) + 1):
+                mask[t, s] = True
+    out, lse = oracle.block_sparse_gqa(q, k, v, blk, B, 0.35, cu_seqlens=cu)
+    ref = _gqa_sdpa(q, k, v, mask, 0.35)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_gqa_reductions():
+    rng = np.random.default_rng(16)
+    T, H, D, B = 24, 3, 6, 4
+    q = rng.standard_normal((T, H, D))
+    k = rng.standard_normal((T, H, D))
+    v = rng.standard_normal((T, H, D))
+    # Hq = Hkv with every block selected: dense causal attention
+    blk = np.stack([np.where(np.arange(T // B) <= t // B, np.arange(T // B), -1) for t in range(T)])
+    out, _ = oracle.block_sparse_gqa(q, k, v, blk, B, 0.5)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q).permute(1, 0, 2)[None], torch.from_numpy(k).permute(1, 0, 2)[None],
+        torch.from_numpy(v).permute(1, 0, 2)[None], is_causal=True, scale=0.5)[0].permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+    # B = 1 is token routing: same as a key mask from the token list
+    tok = np.stack([rng.permutation(t + 1)[:5].tolist() + [-1] * max(0, 5 - (t + 1)) for t in range(T)])
+    tok = tok[:, :5]
+    out1, _ = oracle.block_sparse_gqa(q, k, v, tok, 1, 0.5)
+    mask = np.zeros((T, T), dtype=bool)
+    for t in range(T):
+        mask[t, tok[t][tok[t] >= 0]] = True
+    np.testing.assert_allclose(out1, _gqa_sdpa(q, k, v, mask, 0.5), rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------- workloads / recipe
+
+def test_thd_lengths_recipe():
+    L = workloads.thd_lengths(4)
+    assert sorted(L) == [512, 595, 1171, 1198, 1445, 1699, 1912, 2141, 2667, 5005, 5235,
+                         6666, 7411, 8538, 9579, 9762]
+    assert sum(L) == 65536
+
+
+def test_integer_variant_is_exact_in_fp32():
+    for name in ["tiny_fp32", "nope_unaligned", "block_gqa"]:
+        wl = workloads.WORKLOADS[name]
+        x = workloads.indexer_inputs(wl, integer=True, T=min(wl.T, 2048))
+        assert workloads.exact_sum_bound(x["q_I"], x["k_I"], x["w"]) < 2 ** 24
+
+
+def test_generators_are_deterministic():
+    wl = workloads.WORKLOADS["nope_unaligned"]
+    a = workloads.indexer_inputs(wl, T=64)
+    b = workloads.indexer_inputs(wl, T=64)
+    for n in a:
+        assert torch.equal(a[n], b[n])
+    # the forced-negative key rows score exactly zero for every query
+    neg = (a["k_I"].float() <= 0).all(dim=1)
+    assert 0.15 < neg.float().mean().item() < 0.45
+    sc = oracle.indexer_scores_dense(a["q_I"], a["k_I"], a["w"])
+    for t in range(64):
+        s = np.nonzero(neg[:t + 1].numpy())[0]
+        assert np.all(sc[t, s] == 0)
