@@ -1,0 +1,208 @@
+/*
+ * sa.h -- C ABI of the indexer-routed sparse-attention forward path on AMD MI355X
+ * (gfx950). Four entry points, each a launch of hand-written HIP kernels on the
+ * caller's stream:
+ *
+ *   sa_indexer_scores        multi-head ReLU indexer (dense scores, or fused with an
+ *                            exact top-k so the score matrix is never stored)
+ *   sa_topk_select           exact, deterministic top-k of score rows
+ *   sa_sparse_mla_fwd        absorbed-MLA attention over selected latent rows
+ *   sa_block_sparse_gqa_fwd  grouped-query attention over selected key blocks
+ *
+ * Sources (web pages on indexer-routed sparse attention in Megatron-LM):
+ *   [QSA]  "Add trainable QSA sparse attention with a TileLang backend"
+ *          (Megatron-LM issue #7060)
+ *   [DSA]  "Enable DSA CP/absorbed/THD paths with TileLang fused ops"
+ *          (Megatron-LM PR #3674)
+ *   [NOPE] "Support NoPE shapes and unaligned top-k in TileLang sparse MLA"
+ *          (Megatron-LM PR #7617), with the downstream GLM-5.3-Flash PR body it quotes
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument except `stream` is a DEVICE pointer (hipMalloc'd or a
+ *     torch tensor's data). cu_seqlens included.
+ *   - The caller owns every buffer. The library never allocates, frees or
+ *     synchronises; each call only enqueues kernels on `stream` (a hipStream_t; NULL
+ *     means the default stream) and returns.
+ *   - Inputs are read only and are left byte-identical ([NOPE] "Validation": input
+ *     preservation). Outputs must not alias inputs or each other.
+ *   - Tensors are dense, row-major, with the shapes given; no strides.
+ *   - Packed variable-length (THD) layout ([DSA] "What does this PR do ?"): T rows are
+ *     num_seqs sequences back to back; cu_seqlens is int32 [num_seqs+1], cu[0] = 0,
+ *     cu[num_seqs] = T, non-decreasing; max_seqlen >= every cu[j+1]-cu[j]. Passing
+ *     cu_seqlens = NULL means one sequence [0, T) (num_seqs and max_seqlen ignored).
+ *     Causality is per sequence: key s is visible to query t iff start(t) <= s <= t.
+ *   - Errors: argument checks run on the host before any launch and return a status
+ *     without touching the stream ([QSA] "Additional context": fail fast on
+ *     unsupported combinations). SA_ERR_LAUNCH reports hipGetLastError after a launch.
+ *     Device-side contents (index values, cu_seqlens values) are NOT validated: an
+ *     index outside its documented range is undefined behaviour.
+ *   - Determinism: the same inputs give bitwise-identical outputs on every run,
+ *     independent of other work on the device ([NOPE] "Validation": forward bit-exact
+ *     replay). No call uses floating-point atomics.
+ *   - Thread safety: calls hold no global mutable state and may be issued from any
+ *     host thread.
+ */
+#ifndef SA_H
+#define SA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SA_ABI_VERSION 1
+
+typedef enum {
+  SA_OK = 0,
+  SA_ERR_NULL = 1,         /* a required pointer is NULL */
+  SA_ERR_SHAPE = 2,        /* a size is non-positive or inconsistent */
+  SA_ERR_DTYPE = 3,        /* unknown dtype code */
+  SA_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned */
+  SA_ERR_UNSUPPORTED = 5,  /* valid but unsupported combination (limits below) */
+  SA_ERR_LAUNCH = 6        /* a kernel launch failed */
+} sa_status;
+
+typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
+
+/* Human-readable name of a status code (static string). */
+const char* sa_status_string(int status);
+
+/* SA_ABI_VERSION of the built library. */
+int sa_abi_version(void);
+
+/*
+ * sa_indexer_scores -- ReLU-weighted multi-head indexer.
+ *
+ * [QSA] "Describe the solution you'd like" (trainable indexer, streaming runner with
+ * bounded memory, ReLU scores that tie at zero) and "Is your feature request related
+ * to a problem?" (never materialise the [sequence, sequence / block_size] scores);
+ * [DSA] file table (fused indexer forward). For query t and causal key s:
+ *
+ *     I[t,s] = sum_h w[t,h] * max( sum_d q_I[t,h,d] * k_I[s,d], 0 )
+ *
+ * accumulated in fp32 (bf16 products are exact in fp32). One k_I row per token is
+ * shared by all indexer heads; any score scaling must be folded into w by the caller.
+ * -0.0 results are stored as +0.0. With block_size B > 1 the row's score for block b
+ * of its sequence is max of I[t,s] over the block's causal keys
+ * s in [start + bB, min(start + bB + B - 1, t)].
+ *
+ * Inputs:
+ *   q_I  [T, H_I, D_I]  dtype        k_I [T, D_I] dtype       w [T, H_I] fp32
+ *   dtype  SA_F32 or SA_BF16 (q_I and k_I)
+ *   H_I in [1, 64] with 64 % H_I == 0; D_I in {64, 128}; block_size in {1} or a
+ *   multiple of 16 up to 256.
+ * Mode 1, dense (topk == 0): writes scores [T, ld] fp32; row t, column c holds the
+ *   score of key start(t)+c (token mode) or of local block c (block mode) for the
+ *   causal columns c < n(t), where n(t) = t-start(t)+1 (tokens) or
+ *   (t-start(t))/B + 1 (blocks). Columns >= n(t) are not written.
+ *   ld >= max_seqlen (tokens) or ceil(max_seqlen / B) (blocks); ld % 4 == 0.
+ *   out_idx/out_val must be NULL.
+ * Mode 2, fused selection (topk > 0): scores must be NULL. The kernel streams the
+ *   causal keys tile by tile and keeps, per row, an exact running top-k under the
+ *   order of sa_topk_select; the score matrix is never stored. Writes out_idx
+ *   [T, topk] int32 and, if out_val != NULL, out_val [T, topk] fp32, with exactly the
+ *   result sa_topk_select gives on the dense scores (same indices, same order).
+ *   Token mode: topk in [1, 2048]; block mode: topk in [1, 64].
+ *   force_own_block as in sa_topk_select (block mode only).
+ */
+sa_status sa_indexer_scores(const void* q_I, const void* k_I, const float* w, int dtype,
+                            int32_t T, const int32_t* cu_seqlens, int32_t num_seqs,
+                            int32_t max_seqlen, int32_t H_I, int32_t D_I, int32_t block_size,
+                            float* scores, int64_t ld,
+                            int32_t topk, int32_t force_own_block,
+                            int32_t* out_idx, float* out_val, void* stream);
+
+/*
+ * sa_topk_select -- exact, deterministic top-k of score rows.
+ *
+ * [QSA] "Describe the solution you'd like": exact selection keyed lexicographically
+ * on (score, id), so ties (ReLU zeros) resolve identically on every run and rank;
+ * [NOPE] "What does this PR do?": empty slots hold the -1 sentinel.
+ *
+ * Order: a precedes b iff score_a > score_b, or score_a == score_b and index_a <
+ * index_b (-0.0 equals +0.0). Row t keeps the first min(topk, n(t)) candidates in
+ * that order and writes them in ASCENDING index order to out_idx[t, 0..], then -1
+ * up to topk. out_val (nullable) receives the scores in the same slots (+0.0 for a
+ * zero score) and -inf on padding. NaN scores are not supported.
+ *
+ * Candidates of row t:
+ *   cand_idx == NULL (dense causal rows, as written by sa_indexer_scores mode 1):
+ *     columns c < n(t) of vals[t, :]; token mode (block_size 1) reports global key
+ *     rows start(t)+c; block mode (block_size B > 1) reports local block ids c, and
+ *     with force_own_block != 0 the query's own block (c = n(t)-1) is always kept and
+ *     counts toward topk.
+ *   cand_idx != NULL (explicit candidate lists): vals[t, c] with index cand_idx[t, c]
+ *     for every column c < ld whose cand_idx is >= 0; the valid indices of a row must
+ *     be strictly ascending left to right (-1 entries may sit anywhere). The layout
+ *     arguments are ignored; force_own_block must be 0.
+ * Sizes: ld % 4 == 0 (vals and cand_idx rows start 16-byte aligned), ld >= the
+ *   widest row, widest row <= 65536; topk in [1, 65536].
+ */
+sa_status sa_topk_select(const float* vals, const int32_t* cand_idx, int64_t ld,
+                         int32_t T, const int32_t* cu_seqlens, int32_t num_seqs,
+                         int32_t max_seqlen, int32_t block_size, int32_t topk,
+                         int32_t force_own_block, int32_t* out_idx, float* out_val,
+                         void* stream);
+
+/*
+ * sa_sparse_mla_fwd -- absorbed-MLA sparse attention forward.
+ *
+ * [DSA] file table (sparse-MLA forward kernel); [NOPE] "What does this PR do?" and
+ * the quoted GLM PR body, "Change": q and k share the 576-wide latent layout, the
+ * value is the first 512 channels of the same latent row, -1 slots are masked, the
+ * caller's softmax scale is used as given; a 512-wide (NoPE) q/kv is accepted
+ * directly (it equals the zero-padded 576 case). For query t and head h over the
+ * valid slots j (idx[t,j] >= 0):
+ *
+ *     l_j = scale * q[t,h,:] . kv[idx[t,j], :]          (d_qk channels)
+ *     out[t,h,:] = sum_j softmax(l)_j * kv[idx[t,j], 0:d_v]
+ *     lse[t,h]   = ln sum_j exp(l_j)
+ *
+ * fp32 softmax and accumulation; bf16 matrix products on MFMA for SA_BF16. A row
+ * with no valid slot gives out = 0 and lse = -inf. Each slot counts once (a repeated
+ * index counts twice). Slot order does not matter; topk need not be a multiple of
+ * anything.
+ *
+ * Inputs: q [T, H, d_qk], kv [S, d_qk] (dtype), idx [T, topk] int32 with values in
+ *   [0, S) or -1. Outputs: out [T, H, d_v] (dtype), lse [T, H] fp32 (nullable).
+ * Sizes: d_qk in {512, 576}; d_v == 512; H in [1, 128]; topk in [1, 4096] (bf16) or [1, 8192] (fp32); S >= 1.
+ *   SA_BF16 needs H % 16 == 0 or H < 16 (heads are processed in groups of 32;
+ *   partial groups are masked).
+ */
+sa_status sa_sparse_mla_fwd(const void* q, const void* kv, const int32_t* idx, int dtype,
+                            int32_t T, int32_t S, int32_t H, int32_t d_qk, int32_t d_v,
+                            int32_t topk, float scale, void* out, float* lse, void* stream);
+
+/*
+ * sa_block_sparse_gqa_fwd -- grouped-query attention over selected key blocks.
+ *
+ * [QSA] "Describe the solution you'd like": sparse GQA attention over the blocks
+ * chosen by the exact block TopK. For query t (sequence start c) and head h, the
+ * keys are every s <= t with local block (s - c) / block_size equal to a slot of
+ * blk[t, :] (slot -1 skipped; each slot counts once); head h reads kv head
+ * g = h / (Hq / Hkv):
+ *
+ *     out[t,h,:] = softmax_s(scale * q[t,h,:] . k[s,g,:]) @ v[s,g,:]
+ *     lse[t,h]   = ln sum_s exp(scale * q[t,h,:] . k[s,g,:])
+ *
+ * No key -> out = 0, lse = -inf.
+ * Inputs: q [T, Hq, D], k [T, Hkv, D], v [T, Hkv, Dv] (dtype), blk [T, nblk] int32
+ *   local block ids in [0, ceil(len/block_size)) or -1. Outputs: out [T, Hq, Dv]
+ *   (dtype), lse [T, Hq] fp32 (nullable).
+ * Sizes: D == Dv == 128 or 64; Hq % Hkv == 0; Hq / Hkv <= 16; block_size a multiple
+ *   of 16 up to 128; nblk >= 1.
+ */
+sa_status sa_block_sparse_gqa_fwd(const void* q, const void* k, const void* v,
+                                  const int32_t* blk, int dtype, int32_t T,
+                                  const int32_t* cu_seqlens, int32_t num_seqs,
+                                  int32_t max_seqlen, int32_t Hq, int32_t Hkv, int32_t D,
+                                  int32_t Dv, int32_t block_size, int32_t nblk, float scale,
+                                  void* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SA_H */

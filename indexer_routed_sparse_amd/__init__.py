@@ -1,0 +1,214 @@
+"""Python binding of libsa.so, the C ABI of the indexer-routed sparse-attention path.
+
+Argument marshalling only: each ``sa_*`` function checks that torch tensors have the
+expected dtype, shape, device and contiguity, passes their data pointers, sizes
+and the current HIP stream to the C function of the same name, and raises
+``SAError`` on a non-zero status. Every step of the computation runs in the HIP
+kernels of libsa.so; there is no other code path. Importing this package fails
+loudly if libsa.so is missing (build it with ``python -m
+indexer_routed_sparse_amd.build``).
+
+The convenience wrappers at the end (``indexer_topk``, ``sparse_mla`` ...) only
+allocate output tensors and call the ``sa_*`` functions.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "SAError", "SA_F32", "SA_BF16", "lib", "abi_version", "status_string",
+    "sa_indexer_scores", "sa_topk_select", "sa_sparse_mla_fwd", "sa_block_sparse_gqa_fwd",
+    "indexer_scores", "indexer_topk", "topk_select", "sparse_mla", "block_sparse_gqa",
+]
+
+SA_F32 = 0
+SA_BF16 = 1
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsa.so")
+
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        f"{_LIB_PATH} is missing: build the HIP library first "
+        "(python -m indexer_routed_sparse_amd.build)")
+lib = ctypes.CDLL(_LIB_PATH)
+
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+
+lib.sa_status_string.restype = ctypes.c_char_p
+lib.sa_status_string.argtypes = [ctypes.c_int]
+lib.sa_abi_version.restype = ctypes.c_int
+lib.sa_abi_version.argtypes = []
+lib.sa_indexer_scores.restype = ctypes.c_int
+lib.sa_indexer_scores.argtypes = [_p, _p, _p, ctypes.c_int, _i32, _p, _i32, _i32, _i32, _i32, _i32,
+                                  _p, _i64, _i32, _i32, _p, _p, _p]
+lib.sa_topk_select.restype = ctypes.c_int
+lib.sa_topk_select.argtypes = [_p, _p, _i64, _i32, _p, _i32, _i32, _i32, _i32, _i32, _p, _p, _p]
+lib.sa_sparse_mla_fwd.restype = ctypes.c_int
+lib.sa_sparse_mla_fwd.argtypes = [_p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _i32,
+                                  _f32, _p, _p, _p]
+lib.sa_block_sparse_gqa_fwd.restype = ctypes.c_int
+lib.sa_block_sparse_gqa_fwd.argtypes = [_p, _p, _p, _p, ctypes.c_int, _i32, _p, _i32, _i32, _i32,
+                                        _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p]
+
+
+class SAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def abi_version() -> int:
+    return lib.sa_abi_version()
+
+
+def status_string(status: int) -> str:
+    return lib.sa_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise SAError(status, where)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    if t.dtype == torch.bfloat16:
+        return SA_BF16
+    if t.dtype == torch.float32:
+        return SA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _layout(T, cu_seqlens, max_seqlen):
+    if cu_seqlens is None:
+        return None, 0, 0
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if max_seqlen is None:
+        raise ValueError("max_seqlen is required with cu_seqlens")
+    return cu_seqlens, cu_seqlens.numel() - 1, int(max_seqlen)
+
+
+# ------------------------------------------------------------------- C functions
+
+def sa_indexer_scores(q_I, k_I, w, *, cu_seqlens=None, max_seqlen=None, block_size=1,
+                      scores=None, topk=0, force_own_block=False, out_idx=None, out_val=None):
+    """sa_indexer_scores: dense scores (topk == 0) or fused exact top-k (topk > 0)."""
+    T, H_I, D_I = q_I.shape
+    cu, nseq, maxlen = _layout(T, cu_seqlens, max_seqlen)
+    if w.dtype != torch.float32:
+        raise TypeError("w must be float32")
+    ld = scores.shape[1] if scores is not None else 0
+    _check(lib.sa_indexer_scores(_ptr(q_I), _ptr(k_I), _ptr(w), _dtype_code(q_I), T, _ptr(cu), nseq,
+                                 maxlen, H_I, D_I, int(block_size), _ptr(scores), ld, int(topk),
+                                 int(bool(force_own_block)), _ptr(out_idx), _ptr(out_val),
+                                 _stream(q_I.device)), "sa_indexer_scores")
+
+
+def sa_topk_select(vals, out_idx, *, out_val=None, cand_idx=None, cu_seqlens=None, max_seqlen=None,
+                   block_size=1, force_own_block=False):
+    """sa_topk_select: exact top-k of each row of ``vals`` [T, ld] into ``out_idx`` [T, topk]."""
+    if vals.dtype != torch.float32 or out_idx.dtype != torch.int32:
+        raise TypeError("vals must be float32 and out_idx int32")
+    T, ld = vals.shape
+    topk = out_idx.shape[1]
+    cu, nseq, maxlen = _layout(T, cu_seqlens, max_seqlen)
+    _check(lib.sa_topk_select(_ptr(vals), _ptr(cand_idx), ld, T, _ptr(cu), nseq, maxlen,
+                              int(block_size), topk, int(bool(force_own_block)), _ptr(out_idx),
+                              _ptr(out_val), _stream(vals.device)), "sa_topk_select")
+
+
+def sa_sparse_mla_fwd(q, kv, idx, scale, out, lse=None):
+    """sa_sparse_mla_fwd: q [T,H,d_qk], kv [S,d_qk], idx [T,topk] -> out [T,H,d_v], lse [T,H]."""
+    T, H, d_qk = q.shape
+    S = kv.shape[0]
+    if idx.dtype != torch.int32:
+        raise TypeError("idx must be int32")
+    if kv.dtype != q.dtype or out.dtype != q.dtype:
+        raise TypeError("q, kv and out must share a dtype")
+    _check(lib.sa_sparse_mla_fwd(_ptr(q), _ptr(kv), _ptr(idx), _dtype_code(q), T, S, H, d_qk,
+                                 out.shape[2], idx.shape[1], float(scale), _ptr(out), _ptr(lse),
+                                 _stream(q.device)), "sa_sparse_mla_fwd")
+
+
+def sa_block_sparse_gqa_fwd(q, k, v, blk, scale, out, lse=None, *, block_size, cu_seqlens=None,
+                            max_seqlen=None):
+    """sa_block_sparse_gqa_fwd: q [T,Hq,D], k/v [T,Hkv,D], blk [T,nblk] -> out [T,Hq,Dv]."""
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    Dv = v.shape[2]
+    if blk.dtype != torch.int32:
+        raise TypeError("blk must be int32")
+    cu, nseq, maxlen = _layout(T, cu_seqlens, max_seqlen)
+    _check(lib.sa_block_sparse_gqa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(blk), _dtype_code(q), T,
+                                       _ptr(cu), nseq, maxlen, Hq, Hkv, D, Dv, int(block_size),
+                                       blk.shape[1], float(scale), _ptr(out), _ptr(lse),
+                                       _stream(q.device)), "sa_block_sparse_gqa_fwd")
+
+
+# ------------------------------------------------------- allocating conveniences
+
+def indexer_scores(q_I, k_I, w, *, cu_seqlens=None, max_seqlen=None, block_size=1, ld=None):
+    T = q_I.shape[0]
+    width = max_seqlen if cu_seqlens is not None else T
+    ncol = width if block_size == 1 else -(-width // block_size)
+    ld = ld or ((ncol + 3) // 4 * 4)
+    scores = torch.full((T, ld), float("-inf"), dtype=torch.float32, device=q_I.device)
+    sa_indexer_scores(q_I, k_I, w, cu_seqlens=cu_seqlens, max_seqlen=max_seqlen,
+                      block_size=block_size, scores=scores)
+    return scores
+
+
+def indexer_topk(q_I, k_I, w, topk, *, cu_seqlens=None, max_seqlen=None, block_size=1,
+                 force_own_block=False, with_values=False):
+    T = q_I.shape[0]
+    idx = torch.empty((T, topk), dtype=torch.int32, device=q_I.device)
+    val = torch.empty((T, topk), dtype=torch.float32, device=q_I.device) if with_values else None
+    sa_indexer_scores(q_I, k_I, w, cu_seqlens=cu_seqlens, max_seqlen=max_seqlen,
+                      block_size=block_size, topk=topk, force_own_block=force_own_block,
+                      out_idx=idx, out_val=val)
+    return (idx, val) if with_values else idx
+
+
+def topk_select(vals, topk, *, cand_idx=None, cu_seqlens=None, max_seqlen=None, block_size=1,
+                force_own_block=False, with_values=False):
+    T = vals.shape[0]
+    idx = torch.empty((T, topk), dtype=torch.int32, device=vals.device)
+    val = torch.empty((T, topk), dtype=torch.float32, device=vals.device) if with_values else None
+    sa_topk_select(vals, idx, out_val=val, cand_idx=cand_idx, cu_seqlens=cu_seqlens,
+                   max_seqlen=max_seqlen, block_size=block_size, force_own_block=force_own_block)
+    return (idx, val) if with_values else idx
+
+
+def sparse_mla(q, kv, idx, scale, d_v=512, with_lse=True):
+    T, H, _ = q.shape
+    out = torch.empty((T, H, d_v), dtype=q.dtype, device=q.device)
+    lse = torch.empty((T, H), dtype=torch.float32, device=q.device) if with_lse else None
+    sa_sparse_mla_fwd(q, kv, idx, scale, out, lse)
+    return (out, lse) if with_lse else out
+
+
+def block_sparse_gqa(q, k, v, blk, scale, *, block_size, cu_seqlens=None, max_seqlen=None,
+                     with_lse=True):
+    T, Hq, _ = q.shape
+    out = torch.empty((T, Hq, v.shape[2]), dtype=q.dtype, device=q.device)
+    lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device) if with_lse else None
+    sa_block_sparse_gqa_fwd(q, k, v, blk, scale, out, lse, block_size=block_size,
+                            cu_seqlens=cu_seqlens, max_seqlen=max_seqlen)
+    return (out, lse) if with_lse else out

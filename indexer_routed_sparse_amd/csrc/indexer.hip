@@ -1,0 +1,502 @@
+// Multi-head ReLU indexer, streamed over causal key tiles, with either a dense
+// score write or a fused exact top-k that never stores the score matrix.
+//
+// Operation ("Add trainable QSA sparse attention with a TileLang backend", sections
+// "Is your feature request related to a problem?" and "Describe the solution you'd
+// like": a trainable indexer with ReLU scores, a streaming runner with bounded
+// memory, exact block TopK without the [sequence, sequence / block] matrix; and
+// "Enable DSA CP/absorbed/THD paths with TileLang fused ops", file table: fused
+// indexer forward):  I[t,s] = sum_h w[t,h] * max(q[t,h,:] . k[s,:], 0).
+//
+// Layout of the work (gfx950):
+//   * a workgroup owns a run of consecutive query tokens of ONE sequence; its waves
+//     each own 64 (token, head) rows = 64 / H_I tokens, so every token's heads and
+//     its selection state belong to a single wave;
+//   * key tiles of 64 rows stream through LDS by 16-byte global_load_lds (double
+//     buffered, XOR-swizzled chunks for conflict-free operand reads);
+//   * scores of a tile come from MFMA (bf16 32x32x16, or fp32 32x32x2) with rows =
+//     (token, head) and columns = keys; the epilogue applies ReLU, the head weight
+//     and the head sum in registers (one cross-half lane add) and stages one fp32
+//     score per (token, key) in LDS;
+//   * dense mode writes the staged scores; fused mode appends the keys that beat
+//     the token's current k-th best key to an LDS candidate buffer (ballot/mbcnt
+//     compaction, ascending key order), and when the buffer is full the owning wave
+//     shrinks it back to exactly topk entries with a radix select (4 passes of 8-bit
+//     digits over order-preserving keys) and a stable in-place compaction. Because
+//     keys arrive in ascending index order, a later key equal to the k-th best can
+//     never enter (it loses the index tie-break), so a strict ">" filter is exact.
+#include "sa_common.h"
+#include "sa_kernels.h"
+
+namespace sa {
+namespace {
+
+constexpr int kKT = 64;       // keys per tile
+constexpr int kMaxWaves = 4;
+
+struct IdxArgs {
+  const void* q;
+  const void* k;
+  const float* w;
+  int T;
+  const int32_t* cu;
+  int nseq;
+  int B;                 // block size (1 = tokens)
+  int nwave;             // waves per workgroup
+  int chunks;            // token chunks per sequence (grid.x)
+  // dense
+  float* scores;
+  int64_t ld;
+  // fused
+  int topk;
+  int cap;               // candidate buffer entries per token
+  int force_own;
+  int32_t* out_idx;
+  float* out_val;
+};
+
+template <int CPR>
+SA_DEVICE int kswz(int r) {
+  if constexpr (CPR == 8) return (r >> 1) & 7;
+  else return r & 15;
+}
+
+SA_DEVICE void lds_dma16(uint32_t lds, const void* src) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(
+                   __builtin_amdgcn_readfirstlane(lds)),
+               "v"(src)
+               : "memory");
+}
+
+// ---- wave-level exact top-k shrink of a candidate buffer (keys, idx) of n entries,
+//      stored in ascending index order. Keeps the first `k` under (key desc, index
+//      asc) in place, in index order, and returns the smallest kept key.
+SA_DEVICE uint32_t wave_shrink(uint32_t* keys, int32_t* ids, int n, int k, uint32_t* hist) {
+  const int L = lane_id();
+  uint32_t prefix = 0, need = (uint32_t)k;
+  int mode = 2;            // 1: keep key >= thr; 2: keep key > thr + first `need` == thr
+  uint32_t thr = 0;
+#pragma unroll 1
+  for (int p = 0; p < 4; ++p) {
+    const int sh = 24 - 8 * p;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) hist[4 * L + r] = 0u;
+    __builtin_amdgcn_wave_barrier();
+    for (int e = L; e < n; e += kWave) {
+      const uint32_t kk = keys[e];
+      if (p == 0 || (kk >> (sh + 8)) == prefix) atomicAdd(&hist[(kk >> sh) & 255u], 1u);
+    }
+    __builtin_amdgcn_wave_barrier();
+    // lane L owns bins 255-4L .. 252-4L (descending)
+    uint32_t c[4], s = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) { c[r] = hist[255 - 4 * L - r]; s += c[r]; }
+    uint32_t run = wave_incl_scan(s) - s;
+    int found = -1;
+    uint32_t above_f = 0, cnt_f = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t above = run;
+      run += c[r];
+      if (above < need && run >= need) { found = 255 - 4 * L - r; above_f = above; cnt_f = c[r]; }
+    }
+    const uint64_t fb = ballot(found >= 0);
+    const int src = (int)__builtin_ctzll(fb);
+    const uint32_t d = (uint32_t)__shfl(found, src, kWave);
+    const uint32_t above = __shfl(above_f, src, kWave);
+    const uint32_t cnt = __shfl(cnt_f, src, kWave);
+    __builtin_amdgcn_wave_barrier();
+    prefix = (prefix << 8) | d;
+    need -= above;
+    if (cnt == need) { mode = 1; thr = prefix << sh; break; }
+    if (p == 3) thr = prefix;
+  }
+  // stable compaction, 64 entries per round; a round's reads precede its writes
+  int out = 0;
+  uint32_t eqseen = 0, kmin = 0xFFFFFFFFu;
+  for (int base = 0; base < n; base += kWave) {
+    const int e = base + L;
+    const bool in = e < n;
+    const uint32_t kk = in ? keys[e] : 0u;
+    const int32_t id = in ? ids[e] : 0;
+    const bool gt = in && (mode == 1 ? kk >= thr : kk > thr);
+    const bool eq = in && mode == 2 && kk == thr;
+    const uint64_t eb = ballot(eq);
+    const uint32_t er = eqseen + mbcnt(eb);
+    const bool take = gt || (eq && er < need);
+    const uint64_t tb = ballot(take);
+    const int pos = out + (int)mbcnt(tb);
+    __builtin_amdgcn_wave_barrier();
+    if (take) { keys[pos] = kk; ids[pos] = id; kmin = kmin < kk ? kmin : kk; }
+    out += __popcll(tb);
+    eqseen += (uint32_t)__popcll(eb);
+    __builtin_amdgcn_wave_barrier();
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = __shfl_xor(kmin, off, kWave);
+    kmin = kmin < o ? kmin : o;
+  }
+  return kmin;
+}
+
+// Appends the lanes with `take` set (ascending lane = ascending index) to a token
+// buffer, shrinking it first when it would overflow. `tau` is the filter (a key
+// must be > tau). Returns the new count; updates tau.
+SA_DEVICE int wave_append(uint32_t* keys, int32_t* ids, int n, int cap, int k, uint32_t* hist,
+                          uint32_t& tau, uint32_t kk, int32_t id, bool valid) {
+  bool take = valid && kk > tau;
+  uint64_t tb = ballot(take);
+  int cnt = __popcll(tb);
+  if (cnt == 0) return n;
+  if (n + cnt > cap) {
+    tau = wave_shrink(keys, ids, n, k, hist);
+    n = k;
+    take = valid && kk > tau;
+    tb = ballot(take);
+    cnt = __popcll(tb);
+  }
+  const int pos = n + (int)mbcnt(tb);
+  if (take) { keys[pos] = kk; ids[pos] = id; }
+  __builtin_amdgcn_wave_barrier();
+  return n + cnt;
+}
+
+template <bool BF16, int HI, int DI>
+__global__ __launch_bounds__(kMaxWaves * 64) void indexer_kernel(IdxArgs a) {
+  using elem_t = typename std::conditional<BF16, uint16_t, float>::type;
+  constexpr int ESZ = sizeof(elem_t);
+  constexpr int CPR = DI * ESZ / 16;          // 16-byte chunks per key row
+  constexpr int TILE_BYTES = kKT * CPR * 16;
+  constexpr int KSTEPS = BF16 ? DI / 16 : DI / 2;
+  constexpr int TW = 64 / HI;                 // tokens per wave
+  static_assert(64 % HI == 0 && HI >= 4, "heads");
+
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int nw = a.nwave;
+  const int QT = nw * TW;                     // tokens per workgroup
+  char* ktiles = lds;                                             // 2 tiles
+  float* stage = reinterpret_cast<float*>(lds + 2 * TILE_BYTES);  // [QT][64]
+  uint32_t* hist = reinterpret_cast<uint32_t*>(stage + QT * kKT); // [nw][256]
+  int* s_n = reinterpret_cast<int*>(hist + nw * 256);             // [QT]
+  uint32_t* s_tau = reinterpret_cast<uint32_t*>(s_n + QT);        // [QT]
+  float* s_bmax = reinterpret_cast<float*>(s_tau + QT);           // [QT]
+  float* s_own = s_bmax + QT;                                     // [QT]
+  uint32_t* bkeys = reinterpret_cast<uint32_t*>(s_own + QT);      // [QT][cap]
+  int32_t* bids = reinterpret_cast<int32_t*>(bkeys + (size_t)QT * a.cap);
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int L = tid & 63;
+  const int hl = L >> 5;
+  const bool fused = a.topk > 0;
+
+  // ---- token range of this workgroup
+  const int seq = blockIdx.y;
+  const int chunk = a.chunks - 1 - (int)blockIdx.x;   // longest rows first
+  const int cs = a.cu ? __ldg(a.cu + seq) : 0;
+  const int ce = a.cu ? __ldg(a.cu + seq + 1) : a.T;
+  const int t0 = cs + chunk * QT;
+  if (t0 >= ce) return;
+  const int t1 = min(t0 + QT, ce);
+  const int ntiles = (t1 - 1 - cs) / kKT + 1;
+
+  // ---- this wave's A operand (q rows) and head weights
+  const int wt0 = t0 + w * TW;               // first token of this wave
+  using aslice_t = typename std::conditional<BF16, bf16x8_t, float>::type;
+  aslice_t qa[2][KSTEPS];
+  float wr[2][16];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int r = 32 * mt + (L & 31);        // wave-local row
+    const int tok = wt0 + r / HI;
+    const int h = r % HI;
+    const bool ok = tok < t1;
+    const elem_t* qrow = reinterpret_cast<const elem_t*>(a.q) + ((int64_t)(ok ? tok : t0) * HI + h) * DI;
+#pragma unroll
+    for (int n = 0; n < KSTEPS; ++n) {
+      if constexpr (BF16) {
+        bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * n + 8 * hl);
+        qa[mt][n] = ok ? v : bf16x8_t{};
+      } else {
+        const float v = qrow[2 * n + hl];
+        qa[mt][n] = ok ? v : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int sg = 0; sg < 16; ++sg) {
+      const int rr = 32 * mt + 8 * (sg >> 2) + 4 * hl + (sg & 3);
+      const int tk = wt0 + rr / HI;
+      wr[mt][sg] = tk < t1 ? __ldg(a.w + (int64_t)tk * HI + rr % HI) : 0.0f;
+    }
+  }
+
+  // ---- per-token state
+  for (int i = tid; i < QT; i += nw * 64) {
+    s_n[i] = 0;
+    s_tau[i] = 0u;
+    s_bmax[i] = -__builtin_huge_valf();
+    s_own[i] = 0.0f;
+  }
+
+  // B operand offsets (K^T slices) inside a tile: row = 32*nt + (L&31)
+  int b_off[2][KSTEPS];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int r = 32 * nt + (L & 31);
+#pragma unroll
+    for (int n = 0; n < KSTEPS; ++n) {
+      if constexpr (BF16) {
+        const int c = 2 * n + hl;
+        b_off[nt][n] = (r * CPR + (c ^ kswz<CPR>(r))) * 16;
+      } else {
+        const int ch = 2 * n + hl;             // float index in the row
+        const int c = ch >> 2;
+        b_off[nt][n] = (r * CPR + (c ^ kswz<CPR>(r))) * 16 + (ch & 3) * 4;
+      }
+    }
+  }
+
+  auto gather = [&](int tile) {
+    const uint32_t base = (uint32_t)(uintptr_t)(SA_LDS char*)(ktiles + (tile & 1) * TILE_BYTES);
+    const int k0 = cs + tile * kKT;
+    for (int ii = w; ii < CPR; ii += nw) {   // CPR instructions of 64 chunks per tile
+      const int p = 64 * ii + L;
+      const int r = p / CPR;
+      const int c = (p % CPR) ^ kswz<CPR>(r);
+      const int row = min(k0 + r, a.T - 1);
+      lds_dma16(base + ii * 1024, reinterpret_cast<const char*>(a.k) + ((int64_t)row * DI) * ESZ + 16 * c);
+    }
+  };
+
+  gather(0);
+#pragma unroll 1
+  for (int tile = 0; tile < ntiles; ++tile) {
+    wait_vmcnt0();
+    __syncthreads();                      // tile resident; previous tile fully consumed
+    if (tile + 1 < ntiles) gather(tile + 1);
+    const char* tb = ktiles + (tile & 1) * TILE_BYTES;
+    const int k0 = cs + tile * kKT;
+
+    // ---- S = Q . K^T for 64 rows x 64 keys
+    floatx16_t S[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) S[mt][nt] = floatx16_t{};
+#pragma unroll
+    for (int n = 0; n < KSTEPS; ++n) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        if constexpr (BF16) {
+          const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(tb + b_off[nt][n]);
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+            S[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][n], b, S[mt][nt], 0, 0, 0);
+        } else {
+          const float b = *reinterpret_cast<const float*>(tb + b_off[nt][n]);
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+            S[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[mt][n], b, S[mt][nt], 0, 0, 0);
+        }
+      }
+    }
+
+    // ---- ReLU, head weight, head sum; stage one score per (token, key)
+    float* wst = stage + (w * TW) * kKT;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int key = 32 * nt + (L & 31);
+      if constexpr (HI >= 8) {
+        float acc[TW];
+#pragma unroll
+        for (int i = 0; i < TW; ++i) acc[i] = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int sg = 0; sg < 16; ++sg) {
+            const int tl = (32 * mt + 8 * (sg >> 2)) / HI;
+            acc[tl] = fmaf(wr[mt][sg], fmaxf(S[mt][nt][sg], 0.0f), acc[tl]);
+          }
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
+          const float v = acc[i] + __shfl_xor(acc[i], 32, kWave);
+          if (hl == 0) wst[i * kKT + key] = v;
+        }
+      } else {   // HI == 4: each token's 4 rows sit in one lane
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float v = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v = fmaf(wr[mt][4 * g + j], fmaxf(S[mt][nt][4 * g + j], 0.0f), v);
+            const int tl = 8 * mt + 2 * g + hl;
+            wst[tl * kKT + key] = v;
+          }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- per token of this wave: dense write, or fused selection
+#pragma unroll 1
+    for (int i = 0; i < TW; ++i) {
+      const int t = wt0 + i;
+      if (t >= t1) break;
+      if (k0 > t) continue;                 // no causal key of t in this tile
+      const int qi = w * TW + i;
+      float sc = wst[i * kKT + L];
+      if (sc == 0.0f) sc = 0.0f;             // -0 -> +0
+      const int kg = k0 + L;
+      const bool valid = kg <= t;            // kg >= cs always
+      const int off = kg - cs;
+      if (a.B == 1) {
+        if (!fused) {
+          if (valid) a.scores[(int64_t)t * a.ld + off] = sc;
+        } else {
+          uint32_t tau = s_tau[qi];
+          const int n = wave_append(bkeys + (size_t)qi * a.cap, bids + (size_t)qi * a.cap, s_n[qi],
+                                    a.cap, a.topk, hist + w * 256, tau, order_key(sc), kg, valid);
+          __builtin_amdgcn_wave_barrier();
+          if (L == 0) { s_n[qi] = n; s_tau[qi] = tau; }
+          __builtin_amdgcn_wave_barrier();
+        }
+      } else {
+        // block scores: max over the block's causal keys
+        const int B = a.B;
+        const int own = (t - cs) / B;
+        float m = valid ? sc : -__builtin_huge_valf();
+        bool emit;
+        int blk;
+        if (B <= kKT) {
+          for (int o = 1; o < B; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+          blk = off / B;
+          emit = (L % B == 0) && (k0 + L <= t);
+        } else {
+          m = wave_max(m);
+          m = fmaxf(m, s_bmax[qi]);
+          blk = (k0 - cs) / B;
+          const bool last_of_block = ((k0 - cs + kKT) % B == 0) || (k0 + kKT > t);
+          __builtin_amdgcn_wave_barrier();
+          if (L == 0) s_bmax[qi] = last_of_block ? -__builtin_huge_valf() : m;
+          __builtin_amdgcn_wave_barrier();
+          emit = last_of_block && L == 0;
+        }
+        if (!fused) {
+          if (emit) a.scores[(int64_t)t * a.ld + blk] = m;
+        } else {
+          uint32_t kk = order_key(m);
+          if (emit && a.force_own && blk == own) {
+            kk = 0xFFFFFFFFu;
+            s_own[qi] = m == 0.0f ? 0.0f : m;
+          }
+          uint32_t tau = s_tau[qi];
+          const int n = wave_append(bkeys + (size_t)qi * a.cap, bids + (size_t)qi * a.cap, s_n[qi],
+                                    a.cap, a.topk, hist + w * 256, tau, kk, blk, emit);
+          __builtin_amdgcn_wave_barrier();
+          if (L == 0) { s_n[qi] = n; s_tau[qi] = tau; }
+          __builtin_amdgcn_wave_barrier();
+        }
+      }
+    }
+  }
+
+  if (!fused) return;
+  // ---- final selection and output, per token of this wave
+#pragma unroll 1
+  for (int i = 0; i < TW; ++i) {
+    const int t = wt0 + i;
+    if (t >= t1) break;
+    const int qi = w * TW + i;
+    uint32_t* keys = bkeys + (size_t)qi * a.cap;
+    int32_t* ids = bids + (size_t)qi * a.cap;
+    int n = s_n[qi];
+    if (n > a.topk) { wave_shrink(keys, ids, n, a.topk, hist + w * 256); n = a.topk; }
+    const int own = a.B > 1 ? (t - cs) / a.B : -1;
+    int32_t* orow = a.out_idx + (int64_t)t * a.topk;
+    float* vrow = a.out_val ? a.out_val + (int64_t)t * a.topk : nullptr;
+    for (int j = L; j < a.topk; j += kWave) {
+      if (j < n) {
+        const int32_t id = ids[j];
+        orow[j] = id;
+        if (vrow) vrow[j] = (a.force_own && id == own) ? s_own[qi] : key_value(keys[j]);
+      } else {
+        orow[j] = -1;
+        if (vrow) vrow[j] = -__builtin_huge_valf();
+      }
+    }
+  }
+}
+
+template <bool BF16, int HI, int DI>
+hipError_t launch_hi(const IdxArgs& a0, int maxlen, hipStream_t st) {
+  IdxArgs a = a0;
+  const bool fused = a.topk > 0;
+  constexpr int CPR = DI * (BF16 ? 2 : 4) / 16;
+  constexpr int TILE_BYTES = kKT * CPR * 16;
+  constexpr int TW = 64 / HI;
+  auto lds_for = [&](int nw) {
+    const int QT = nw * TW;
+    size_t b = 2 * (size_t)TILE_BYTES + (size_t)QT * kKT * 4 + (size_t)nw * 256 * 4 + (size_t)QT * 16;
+    if (fused) b += (size_t)QT * a.cap * 8;
+    return b;
+  };
+  if (fused) {
+    const int extra = a.topk < 64 ? 64 : (a.topk > 1024 ? 1024 : a.topk);
+    a.cap = a.topk + extra;
+  }
+  int nw = kMaxWaves;
+  const size_t budget = 160 * 1024 - 256;
+  while (nw > 1 && lds_for(nw) > budget) nw >>= 1;
+  if (lds_for(nw) > budget) return hipErrorInvalidValue;
+  a.nwave = nw;
+  const int QT = nw * TW;
+  a.chunks = (maxlen + QT - 1) / QT;
+  const size_t shm = lds_for(nw);
+  hipError_t e = hipFuncSetAttribute((const void*)indexer_kernel<BF16, HI, DI>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((indexer_kernel<BF16, HI, DI>), dim3(a.chunks, a.nseq), dim3(nw * 64), shm, st, a);
+  return hipGetLastError();
+}
+
+template <bool BF16, int DI>
+hipError_t launch_di(const IdxArgs& a, int H_I, int maxlen, hipStream_t st) {
+  switch (H_I) {
+    case 4: return launch_hi<BF16, 4, DI>(a, maxlen, st);
+    case 8: return launch_hi<BF16, 8, DI>(a, maxlen, st);
+    case 16: return launch_hi<BF16, 16, DI>(a, maxlen, st);
+    case 32: return launch_hi<BF16, 32, DI>(a, maxlen, st);
+    default: return launch_hi<BF16, 64, DI>(a, maxlen, st);
+  }
+}
+
+hipError_t launch_any(const IdxArgs& a, bool bf16, int H_I, int D_I, int maxlen, hipStream_t st) {
+  if (bf16) return D_I == 64 ? launch_di<true, 64>(a, H_I, maxlen, st) : launch_di<true, 128>(a, H_I, maxlen, st);
+  return D_I == 64 ? launch_di<false, 64>(a, H_I, maxlen, st) : launch_di<false, 128>(a, H_I, maxlen, st);
+}
+
+}  // namespace
+
+hipError_t launch_indexer_dense(const void* q, const void* k, const float* w, bool bf16, int T,
+                                const int32_t* cu, int nseq, int maxlen, int H_I, int D_I,
+                                int block_size, float* scores, int64_t ld, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  IdxArgs a{};
+  a.q = q; a.k = k; a.w = w; a.T = T; a.cu = cu; a.nseq = cu ? nseq : 1; a.B = block_size;
+  a.scores = scores; a.ld = ld; a.topk = 0;
+  return launch_any(a, bf16, H_I, D_I, cu ? maxlen : T, st);
+}
+
+hipError_t launch_indexer_topk(const void* q, const void* k, const float* w, bool bf16, int T,
+                               const int32_t* cu, int nseq, int maxlen, int H_I, int D_I,
+                               int block_size, int topk, int force_own, int32_t* out_idx,
+                               float* out_val, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  IdxArgs a{};
+  a.q = q; a.k = k; a.w = w; a.T = T; a.cu = cu; a.nseq = cu ? nseq : 1; a.B = block_size;
+  a.topk = topk; a.force_own = force_own; a.out_idx = out_idx; a.out_val = out_val;
+  return launch_any(a, bf16, H_I, D_I, cu ? maxlen : T, st);
+}
+
+}  // namespace sa

@@ -1,0 +1,88 @@
+// Device helpers shared by the gfx950 kernels of the sparse-attention library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define SA_DEVICE __device__ __forceinline__
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+#define SA_LDS __attribute__((address_space(3)))
+
+namespace sa {
+
+constexpr int kWave = 64;
+
+SA_DEVICE int lane_id() { return __lane_id(); }
+
+// Number of set bits of `mask` below this lane (wave-wide exclusive prefix count).
+SA_DEVICE uint32_t mbcnt(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+SA_DEVICE uint64_t ballot(bool p) { return __ballot(p); }
+
+// Order-preserving map fp32 -> uint32 for finite values and +-inf: a > b as floats
+// iff key(a) > key(b) as unsigned. -0.0 is canonicalised to +0.0 first so the two
+// zeros tie. Every finite value maps above 0x007FFFFF, so 0 is free as "no value".
+SA_DEVICE uint32_t order_key(float f) {
+  if (f == 0.0f) f = 0.0f;
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+SA_DEVICE float key_value(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+SA_DEVICE uint16_t f2bf_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+SA_DEVICE float bf_bits2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// Packs two floats into one dword of two bf16 (low half = a).
+SA_DEVICE uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f2bf_bits(a) | ((uint32_t)f2bf_bits(b) << 16);
+}
+
+// Start row of the packed sequence that holds row t (cu: int32 [nseq+1], ascending).
+SA_DEVICE int seq_start_of(const int32_t* __restrict__ cu, int nseq, int t) {
+  int lo = 0, hi = nseq;  // invariant: cu[lo] <= t < cu[hi]
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (__ldg(cu + mid) <= t) lo = mid; else hi = mid;
+  }
+  return __ldg(cu + lo);
+}
+
+// Wave-wide inclusive scan of a 32-bit value.
+SA_DEVICE uint32_t wave_incl_scan(uint32_t x) {
+  const int l = lane_id();
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    uint32_t y = __shfl_up(x, off, kWave);
+    if (l >= off) x += y;
+  }
+  return x;
+}
+
+SA_DEVICE float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
+  return x;
+}
+
+SA_DEVICE void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+}  // namespace sa

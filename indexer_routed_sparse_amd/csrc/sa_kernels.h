@@ -1,0 +1,35 @@
+// Internal launch functions of the HIP kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+// topk_select.hip
+int topk_select_max_width();
+hipError_t launch_topk_select(const float* vals, const int32_t* cand, int64_t ld, int T,
+                              const int32_t* cu, int nseq, int width, int block_size, int topk,
+                              int force_own, int32_t* out_idx, float* out_val, hipStream_t st);
+
+// sparse_mla.hip
+hipError_t launch_sparse_mla(const void* q, const void* kv, const int32_t* idx, bool bf16, int T,
+                             int S, int H, int d_qk, int d_v, int topk, float scale, void* out,
+                             float* lse, hipStream_t st);
+
+// indexer.hip
+hipError_t launch_indexer_dense(const void* q, const void* k, const float* w, bool bf16, int T,
+                                const int32_t* cu, int nseq, int maxlen, int H_I, int D_I,
+                                int block_size, float* scores, int64_t ld, hipStream_t st);
+hipError_t launch_indexer_topk(const void* q, const void* k, const float* w, bool bf16, int T,
+                               const int32_t* cu, int nseq, int maxlen, int H_I, int D_I,
+                               int block_size, int topk, int force_own, int32_t* out_idx,
+                               float* out_val, hipStream_t st);
+
+// block_gqa.hip
+hipError_t launch_block_gqa(const void* q, const void* k, const void* v, const int32_t* blk,
+                            bool bf16, int T, const int32_t* cu, int nseq, int Hq, int Hkv, int D,
+                            int Dv, int block_size, int nblk, float scale, void* out, float* lse,
+                            hipStream_t st);
+
+}  // namespace sa

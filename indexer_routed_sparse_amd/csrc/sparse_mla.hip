@@ -1,0 +1,406 @@
+// Absorbed-MLA sparse attention forward over selected latent rows.
+//
+// Operation ("Support NoPE shapes and unaligned top-k in TileLang sparse MLA",
+// section "What does this PR do?", and the GLM-5.3-Flash PR body quoted there,
+// section "Change"): for query t and head h, softmax over the valid slots j of
+// scale * q[t,h,:] . kv[idx[t,j], :] (d_qk = 576 or 512 channels), weights applied
+// to kv[idx[t,j], 0:512]; -1 slots are masked; the caller's scale is used as given.
+//
+// bf16 kernel (gfx950), one workgroup per query token, NW waves of 32 heads each:
+//   * the token's q is held in registers as the B operand of S^T = K . Q^T
+//     (32x32x16 bf16 MFMA: rows = keys, columns = heads), loaded once;
+//   * the selected latent rows of a BK-key tile are gathered straight from HBM/L2
+//     into LDS with 16-byte global_load_lds (no register staging), double
+//     buffered: the gather of tile n+1 is in flight while tile n is computed;
+//   * the LDS tile is row-major with an XOR swizzle of the 16-byte chunks so that
+//     both the K reads (ds_read_b128) and the V reads are free of bank conflicts;
+//   * P = exp2(S - m) stays in registers: the S^T accumulator layout is already the
+//     A-operand layout of P . V up to a permutation of keys inside a tile, and V's
+//     B operand is read with the same key permutation through the gfx950 LDS
+//     transpose load (ds_read_b64_tr_b16) from the row-major tile;
+//   * online softmax with lazy rescaling: the running max only moves when a head's
+//     tile max exceeds it by more than 2^8, so the O rescale (a cross-lane shuffle
+//     of the factors) is rare;
+//   * fp32 accumulation throughout; no atomics, so results are bitwise
+//     reproducible.
+// A plain fp32 kernel serves fp32 inputs.
+#include "sa_common.h"
+#include "sa_kernels.h"
+
+namespace sa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// XOR swizzle of 16-byte chunk c in tile row R (bijective within aligned groups of
+// 8 (576-wide rows) or 16 (512-wide rows) chunks).
+template <int NCH>
+SA_DEVICE int chunk_swz(int R) {
+  if constexpr (NCH == 72) return (((R >> 1) & 1) << 2) | ((R >> 2) & 3);
+  else return ((R & 3) << 2) | ((R >> 2) & 3);
+}
+
+// 16-byte global -> LDS copy per lane: lane l writes LDS bytes [lds + 16 l, +16).
+// `lds` must be wave-uniform. The kernels using it set M0 only here.
+SA_DEVICE void lds_dma16(uint32_t lds, const void* src) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src)
+               : "memory");
+}
+
+constexpr int kBK = 32;        // keys per tile
+constexpr int kStages = 3;     // gather pipeline depth (tiles in flight + tile in use)
+
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most `vm` vector-memory
+// operations of this wave are outstanding and ignores the other counters.
+constexpr int waitcnt_vm(int vm) { return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+template <int DQK>
+constexpr int mla_tile_bytes() { return kBK * (DQK / 8) * 16; }
+
+template <int NW, int DQK>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+                            const int32_t* __restrict__ idx, int H, int topk, float scale_log2,
+                            uint16_t* __restrict__ out, float* __restrict__ lse) {
+  constexpr int NCH = DQK / 8;            // 16-byte chunks per latent row
+  constexpr int NK = DQK / 16;            // MFMA k-steps of S^T = K . Q^T
+  constexpr int NKL = 8;                  // k-steps whose q slices are kept in LDS
+  constexpr int NKR = NK - NKL;           // k-steps whose q slices are kept in VGPRs
+  constexpr int NDV = 512 / 32;           // 32-wide dv tiles of O
+  constexpr int TILE_BYTES = mla_tile_bytes<DQK>();
+  constexpr int NINSTR = kBK * NCH / 64;  // 1 KiB gather instructions per tile
+  constexpr int PER_WAVE = NINSTR / NW;   // gather instructions per wave per tile
+  constexpr int AGRP = (NCH == 72) ? 4 : 8;  // k-step classes of the A-read swizzle
+  static_assert(NINSTR % NW == 0, "gather split");
+  // fp32 P values stay below 2^16 times the reference; a larger tile max restarts
+  constexpr float kThr = 16.0f;
+
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  char* tiles = lds;                                           // kStages tiles
+  // q slices of the last NKL k-steps: [NKL][NW*64 lanes] x 16 bytes
+  char* s_q = lds + kStages * TILE_BYTES;
+  int32_t* s_idx = reinterpret_cast<int32_t*>(s_q + NKL * NW * 64 * 16);  // [topk]
+  __shared__ int s_restart;
+
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int L = tid & 63;
+  const int hl = L >> 5;        // lane half
+  const int head = 32 * w + (L & 31);
+  const bool head_ok = head < H;
+  const int ntiles = (topk + kBK - 1) / kBK;
+
+  // ---- stage the index row; q for this wave's 32 heads as B operand slices
+  {
+    const int32_t* __restrict__ irow = idx + (int64_t)t * topk;
+    for (int j = tid; j < ntiles * kBK; j += NW * 64) s_idx[j] = j < topk ? irow[j] : -1;
+  }
+  if (tid == 0) s_restart = 0;
+  bf16x8_t qv[NKR];
+  {
+    const uint16_t* qrow = q + ((int64_t)t * H + (head_ok ? head : 0)) * DQK + 8 * hl;
+#pragma unroll
+    for (int n = 0; n < NK; ++n) {
+      bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * n);
+      if (!head_ok) v = bf16x8_t{};
+      if (n < NKR) qv[n < NKR ? n : 0] = v;
+      else *reinterpret_cast<bf16x8_t*>(s_q + ((n - NKR) * NW * 64 + tid) * 16) = v;
+    }
+  }
+
+  // ---- per-lane LDS offsets
+  // A (K rows): row R = L&31, chunk 2n + hl; the swizzle depends on R&15 = L&15.
+  int a_off[AGRP];
+  {
+    const int R = L & 31;
+    const int f = chunk_swz<NCH>(R);
+#pragma unroll
+    for (int cls = 0; cls < AGRP; ++cls) a_off[cls] = (R * NCH + ((2 * cls + hl) ^ f)) * 16;
+  }
+  // V (transpose reads): lane L = 16g + s reads row 4(g/2) + s/4 (+16m + 8r) and
+  // columns 16(g%2) + 4(s%4) (+32nt), 8 bytes.
+  int v_off[2][4];      // [r][nt & 3]
+  {
+    const int g = L >> 4, s = L & 15;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int R = 8 * r + 4 * (g >> 1) + (s >> 2);
+      const int f = chunk_swz<NCH>(R);
+      const int col = 16 * (g & 1) + 4 * (s & 3);
+#pragma unroll
+      for (int nc = 0; nc < 4; ++nc) {
+        const int c = 4 * nc + (col >> 3);
+        v_off[r][nc] = (R * NCH + (c ^ f)) * 16 + (col & 7) * 2;
+      }
+    }
+  }
+  __syncthreads();
+
+  // Gather of one tile: instruction ii covers tile slots 64*ii + L (1 KiB of LDS).
+  // Issued through inline asm so that the compiler does not serialise later LDS
+  // reads behind it; completion is tracked by hand with s_waitcnt vmcnt.
+  auto gather = [&](int tile) {
+    const uint32_t base = (uint32_t)(uintptr_t)(SA_LDS char*)(tiles + (tile % kStages) * TILE_BYTES);
+    const int32_t* ir = s_idx + tile * kBK;
+    // The slot arithmetic is recomputed per tile on purpose: hoisted out of the
+    // tile loop it would pin 2*PER_WAVE registers for the whole kernel.
+    int zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int ii = w + NW * j;
+      const int p = 64 * ii + L + zero;
+      const int R = p / NCH;
+      const int c = (p - R * NCH) ^ chunk_swz<NCH>(R);
+      int row = ir[R];
+      row = row < 0 ? 0 : row;   // masked slot: any finite row keeps P*V finite
+      const uint16_t* src = kv + (int64_t)row * DQK + 8 * c;
+      lds_dma16(base + ii * 1024, src);
+    }
+  };
+
+  // O for dv tiles 0..NDV-3 lives in MFMA accumulators (AGPRs, 224 registers);
+  // the last two dv tiles are accumulated per key tile into a temporary and then
+  // added into O_tail (VGPRs). With the S tile and the temporary this keeps the
+  // accumulator file within its 256 registers.
+  constexpr int NOA = NDV - 2;             // dv tiles accumulated in AGPRs
+  floatx16_t O[NOA];
+  floatx16_t O_tail[NDV - NOA];            // the others, summed per key tile in VGPRs
+  float m_ref = -__builtin_huge_valf();   // softmax reference (log2 units), per head
+  float m_seen = -__builtin_huge_valf();
+  float l_run = 0.0f;
+
+#pragma unroll 1
+  for (;;) {   // one pass over the tiles; repeated only if a tile max outgrows m_ref
+#pragma unroll
+    for (int i = 0; i < NOA; ++i) O[i] = floatx16_t{};
+#pragma unroll
+    for (int i = 0; i < NDV - NOA; ++i) O_tail[i] = floatx16_t{};
+    l_run = 0.0f;
+    gather(0);
+    if (ntiles > 1) gather(1);
+#pragma unroll 1
+    for (int tile = 0; tile < ntiles; ++tile) {
+      if (tile + 1 < ntiles) __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER_WAVE));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      __syncthreads();               // tile resident in all waves' view
+      if (tile + 2 < ntiles) gather(tile + 2);   // its stage was last read in tile-1
+      const uint64_t vmask = ballot(L < kBK && s_idx[tile * kBK + (L & (kBK - 1))] >= 0);
+      const char* tb = tiles + (tile % kStages) * TILE_BYTES;
+
+      // ---- S^T = K . Q^T over d_qk; A slices prefetched two k-steps ahead
+      auto a_at = [&](int n) {
+        return *reinterpret_cast<const bf16x8_t*>(tb + a_off[n % AGRP] + (n / AGRP) * (AGRP * 32));
+      };
+      floatx16_t S = floatx16_t{};
+      {
+        bf16x8_t a0 = a_at(0), a1 = a_at(1);
+#pragma unroll
+        for (int n = 0; n < NK; ++n) {
+          bf16x8_t a2 = a1;
+          if (n + 2 < NK) a2 = a_at(n + 2);
+          const bf16x8_t b = n < NKR ? qv[n < NKR ? n : 0]
+                                     : *reinterpret_cast<const bf16x8_t*>(s_q + ((n - NKR) * NW * 64 + tid) * 16);
+          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, S, 0, 0, 0);
+          a0 = a1;
+          a1 = a2;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      // ---- masked logits (log2 units), tile max per head, reference update
+      float mx = -__builtin_huge_valf();
+#pragma unroll
+      for (int sg = 0; sg < 16; ++sg) {
+        const int key = 8 * (sg >> 2) + 4 * hl + (sg & 3);
+        const bool ok = (vmask >> key) & 1ull;
+        const float v = ok ? S[sg] * scale_log2 : -__builtin_huge_valf();
+        S[sg] = v;
+        mx = fmaxf(mx, v);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      m_seen = fmaxf(m_seen, mx);
+      if (m_ref == -__builtin_huge_valf()) m_ref = mx;   // first valid tile (O, l still 0)
+      if (mx > m_ref + kThr) s_restart = 1;               // seen by all after next barrier
+      const float m_use = (m_ref == -__builtin_huge_valf()) ? 0.0f : m_ref;
+
+      // ---- P (bf16) as A operands: half m -> slots 8m..8m+7 of S
+      bf16x8_t P[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = exp2f(S[8 * m + e] - m_use);
+          const float p1 = exp2f(S[8 * m + e + 1] - m_use);
+          l_run += p0 + p1;
+          pk[e >> 1] = pack_bf16x2(p0, p1);
+        }
+        P[m] = __builtin_bit_cast(bf16x8_t, pk);
+      }
+
+      // ---- O += P . V (V from the row-major tile through transpose reads),
+      //      B slices prefetched one step ahead
+      auto v_at = [&](int nt, int m) {
+        const int off = 16 * m * NCH * 16 + (nt >> 2) * 256;
+        const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(tb + off + v_off[0][nt & 3]));
+        const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(tb + off + v_off[1][nt & 3]));
+        const short __attribute__((ext_vector_type(8))) b8 = {lo[0], lo[1], lo[2], lo[3],
+                                                              hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8_t, b8);
+      };
+      {
+        bf16x8_t b0 = v_at(0, 0), b1 = v_at(0, 1);
+#pragma unroll
+        for (int st = 0; st < 2 * NDV; ++st) {
+          const int nt = st >> 1, m = st & 1;
+          bf16x8_t b2 = b1;
+          if (st + 2 < 2 * NDV) b2 = v_at((st + 2) >> 1, (st + 2) & 1);
+          if (nt < NOA) {
+            O[nt < NOA ? nt : 0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(P[m], b0, O[nt < NOA ? nt : 0], 0, 0, 0);
+          } else if (m == 0) {
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(P[0], b0, floatx16_t{}, 0, 0, 0);
+          } else {
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(P[1], b0, S, 0, 0, 0);
+            O_tail[nt >= NOA ? nt - NOA : 0] += S;
+          }
+          b0 = b1;
+          b1 = b2;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    // A tile max above m_ref + kThr anywhere in the pass: redo the pass with the
+    // largest max seen so far as the reference (all gathers have completed).
+    __syncthreads();
+    const bool restart = s_restart != 0;
+    __syncthreads();
+    if (!restart) break;
+    if (tid == 0) s_restart = 0;
+    m_ref = m_seen;
+  }
+
+  // ---- epilogue: normalise, write bf16 out and lse
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (lse && hl == 0 && head_ok) {
+    lse[(int64_t)t * H + head] =
+        l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : -__builtin_huge_valf();
+  }
+  uint16_t* __restrict__ orow = out + (int64_t)t * H * 512;
+#pragma unroll
+  for (int sg = 0; sg < 16; ++sg) {
+    const int hi = 8 * (sg >> 2) + 4 * hl + (sg & 3);
+    const float a = __shfl(inv, hi, 64);
+    const int hh = 32 * w + hi;
+    if (hh < H) {
+#pragma unroll
+      for (int nt = 0; nt < NDV; ++nt) {
+        const float o = nt < NOA ? O[nt < NOA ? nt : 0][sg] : O_tail[nt >= NOA ? nt - NOA : 0][sg];
+        orow[(int64_t)hh * 512 + 32 * nt + (L & 31)] = f2bf_bits(o * a);
+      }
+    }
+  }
+}
+
+// fp32 inputs: one workgroup per (token, head); plain FMA arithmetic, same definition.
+template <int NT>
+__global__ __launch_bounds__(NT) void sparse_mla_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ kv, const int32_t* __restrict__ idx,
+    int H, int d_qk, int d_v, int topk, float scale, float* __restrict__ out,
+    float* __restrict__ lse) {
+  extern __shared__ float sm[];          // [topk] probabilities, then [NT/64] reduce slots
+  float* red = sm + topk;
+  const int t = blockIdx.x / H, h = blockIdx.x % H;
+  const int tid = threadIdx.x, w = tid >> 6, L = tid & 63;
+  const float* qr = q + ((int64_t)t * H + h) * d_qk;
+  const int32_t* ir = idx + (int64_t)t * topk;
+  float mx = -__builtin_huge_valf();
+  for (int j = tid; j < topk; j += NT) {
+    const int r = ir[j];
+    float lg = -__builtin_huge_valf();
+    if (r >= 0) {
+      const float* kr = kv + (int64_t)r * d_qk;
+      float acc = 0.0f;
+      for (int c = 0; c < d_qk; ++c) acc = fmaf(qr[c], kr[c], acc);
+      lg = acc * scale;
+    }
+    sm[j] = lg;
+    mx = fmaxf(mx, lg);
+  }
+  mx = wave_max(mx);
+  if (L == 0) red[w] = mx;
+  __syncthreads();
+  mx = red[0];
+  for (int i = 1; i < NT / 64; ++i) mx = fmaxf(mx, red[i]);
+  __syncthreads();
+  float ps = 0.0f;
+  for (int j = tid; j < topk; j += NT) {
+    const float p = (mx == -__builtin_huge_valf()) ? 0.0f : expf(sm[j] - mx);
+    sm[j] = p;
+    ps += p;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ps += __shfl_xor(ps, off, 64);
+  if (L == 0) red[w] = ps;
+  __syncthreads();
+  float Z = 0.0f;
+  for (int i = 0; i < NT / 64; ++i) Z += red[i];
+  const float inv = Z > 0.0f ? 1.0f / Z : 0.0f;
+  for (int c = tid; c < d_v; c += NT) {
+    float acc = 0.0f;
+    for (int j = 0; j < topk; ++j) {
+      const int r = ir[j];
+      if (r >= 0) acc = fmaf(sm[j], kv[(int64_t)r * d_qk + c], acc);
+    }
+    out[((int64_t)t * H + h) * d_v + c] = acc * inv;
+  }
+  if (lse && tid == 0) lse[(int64_t)t * H + h] = Z > 0.0f ? mx + logf(Z) : -__builtin_huge_valf();
+}
+
+template <int NW, int DQK>
+hipError_t launch_bf16(const void* q, const void* kv, const int32_t* idx, int T, int H, int topk,
+                       float scale, void* out, float* lse, hipStream_t st) {
+  const int ntiles = (topk + kBK - 1) / kBK;
+  const size_t shm = (size_t)kStages * mla_tile_bytes<DQK>() + (size_t)8 * NW * 64 * 16 +
+                     (size_t)ntiles * kBK * 4;
+  hipError_t e = hipFuncSetAttribute((const void*)sparse_mla_bf16_kernel<NW, DQK>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((sparse_mla_bf16_kernel<NW, DQK>), dim3(T), dim3(NW * 64), shm, st,
+                     (const uint16_t*)q, (const uint16_t*)kv, idx, H, topk, scale * kLog2e,
+                     (uint16_t*)out, lse);
+  return hipGetLastError();
+}
+
+template <int DQK>
+hipError_t dispatch_bf16(const void* q, const void* kv, const int32_t* idx, int T, int H,
+                         int topk, float scale, void* out, float* lse, hipStream_t st) {
+  if (H <= 32) return launch_bf16<1, DQK>(q, kv, idx, T, H, topk, scale, out, lse, st);
+  if (H <= 64) return launch_bf16<2, DQK>(q, kv, idx, T, H, topk, scale, out, lse, st);
+  return launch_bf16<4, DQK>(q, kv, idx, T, H, topk, scale, out, lse, st);
+}
+
+}  // namespace
+
+hipError_t launch_sparse_mla(const void* q, const void* kv, const int32_t* idx, bool bf16, int T,
+                             int S, int H, int d_qk, int d_v, int topk, float scale, void* out,
+                             float* lse, hipStream_t st) {
+  (void)S;
+  if (T == 0) return hipSuccess;
+  if (bf16) {
+    if (d_qk == 576) return dispatch_bf16<576>(q, kv, idx, T, H, topk, scale, out, lse, st);
+    return dispatch_bf16<512>(q, kv, idx, T, H, topk, scale, out, lse, st);
+  }
+  constexpr int NT = 256;
+  const size_t shm = (size_t)(topk + NT / 64) * sizeof(float);
+  hipLaunchKernelGGL((sparse_mla_f32_kernel<NT>), dim3(T * H), dim3(NT), shm, st,
+                     (const float*)q, (const float*)kv, idx, H, d_qk, d_v, topk, scale,
+                     (float*)out, lse);
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -1,0 +1,374 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Indices are compared bit for bit: top-k selection is fed the oracle's own fp32
+scores, and the end-to-end indexer runs use integer-valued inputs whose scores are
+exact in fp32. Attention outputs are compared within max-abs 2e-2 + relative 1e-2
+(bf16) or 1e-5 (fp32 inputs), always on the same index tensor as the oracle. Small
+workloads are checked whole; the two full-size ones on sampled rows.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda")
+W = workloads.WORKLOADS
+
+
+@pytest.fixture(scope="module")
+def sa():
+    import indexer_routed_sparse_amd as m
+    return m
+
+
+def close(got, ref, atol, rtol, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(got), fin), f"{what}: finiteness differs"
+    bad = np.abs(got[fin] - ref[fin]) > atol + rtol * np.abs(ref[fin])
+    assert not bad.any(), f"{what}: {bad.sum()} elements out of tolerance, max err " \
+                          f"{np.abs(got[fin] - ref[fin]).max():.3g}"
+    assert np.array_equal(got[~fin], ref[~fin]), f"{what}: infinities differ"
+
+
+BF16_TOL = dict(atol=2e-2, rtol=1e-2)
+F32_TOL = dict(atol=1e-5, rtol=1e-5)
+
+
+def sample_rows(T, n, seed, lengths=None):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(T, size=min(n, T), replace=False).tolist())
+    rows |= {0, T - 1}
+    if lengths:
+        cu = workloads.cu_seqlens(lengths)
+        rows |= {int(c) for c in cu[:-1]} | {int(c) - 1 for c in cu[1:]}
+    return np.array(sorted(rows))
+
+
+def cu_dev(lengths):
+    return torch.from_numpy(workloads.cu_seqlens(lengths)).to(DEV)
+
+
+# ------------------------------------------------------------------------ top-k select
+
+@pytest.mark.parametrize("name,k,T", [("tiny_fp32", 64, None), ("nope_unaligned", 65, None),
+                                      ("nope_unaligned", 127, None), ("nope_unaligned", 2051, None)])
+def test_topk_select_on_oracle_scores(sa, name, k, T):
+    wl = W[name]
+    x = workloads.indexer_inputs(wl, T=T)
+    sc = oracle.indexer_scores_dense(x["q_I"], x["k_I"], x["w"])
+    ld = (sc.shape[1] + 3) // 4 * 4
+    scp = np.full((sc.shape[0], ld), -np.inf, dtype=np.float32)
+    scp[:, :sc.shape[1]] = sc
+    ref_i, ref_v = oracle.topk_select_dense(scp, k)
+    idx, val = sa.topk_select(torch.from_numpy(scp).to(DEV), k, with_values=True)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_i)
+    np.testing.assert_array_equal(val.cpu().numpy().view(np.uint32), ref_v.view(np.uint32))
+
+
+def test_topk_select_block_mode_forced_own(sa):
+    wl = W["block_gqa"]
+    T = 2048
+    x = workloads.indexer_inputs(wl, T=T)
+    sc = oracle.indexer_scores_dense(x["q_I"], x["k_I"], x["w"], block_size=64)
+    ref_i, ref_v = oracle.topk_select_dense(sc, 16, block_size=64, force_own_block=True)
+    idx, val = sa.topk_select(torch.from_numpy(sc).to(DEV), 16, block_size=64,
+                              force_own_block=True, with_values=True)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_i)
+    np.testing.assert_array_equal(val.cpu().numpy(), ref_v)
+
+
+def test_topk_select_thd_and_candidates(sa):
+    lengths = (300, 1, 77, 1000, 2)
+    T = sum(lengths)
+    wl = W["nope_unaligned"]
+    x = workloads.indexer_inputs(wl, T=T)
+    cu = workloads.cu_seqlens(lengths)
+    sc = oracle.indexer_scores_dense(x["q_I"], x["k_I"], x["w"], cu_seqlens=cu, ld=1000)
+    ref_i, _ = oracle.topk_select_dense(sc, 65, cu_seqlens=cu)
+    idx = sa.topk_select(torch.from_numpy(sc).to(DEV), 65, cu_seqlens=cu_dev(lengths), max_seqlen=1000)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_i)
+    # explicit candidate lists with -1 holes: same selection over the remaining ones
+    rng = np.random.default_rng(3)
+    cand = np.where(np.isfinite(sc), np.arange(1000)[None, :] + cu[:-1].repeat(lengths)[:, None], -1)
+    holes = rng.random(cand.shape) < 0.2
+    cand = np.where(holes, -1, cand).astype(np.int32)
+    ref_c, ref_cv = oracle.topk_select_candidates(np.where(cand >= 0, sc, -np.inf), cand, 65)
+    idx_c, val_c = sa.topk_select(torch.from_numpy(np.ascontiguousarray(sc)).to(DEV), 65,
+                                  cand_idx=torch.from_numpy(cand).to(DEV), with_values=True)
+    np.testing.assert_array_equal(idx_c.cpu().numpy(), ref_c)
+    np.testing.assert_array_equal(val_c.cpu().numpy(), ref_cv)
+
+
+@pytest.mark.parametrize("name", ["long_dsa", "thd_varlen"])
+def test_topk_select_full_size_sampled(sa, name):
+    wl = W[name]
+    T = wl.T
+    x = workloads.indexer_inputs(wl, device=DEV)
+    lengths = wl.lengths if len(wl.lengths) > 1 else None
+    rows = sample_rows(T, 10, 7, lengths)
+    cu = workloads.cu_seqlens(wl.lengths)
+    maxlen = max(wl.lengths)
+    sc = oracle.indexer_scores_dense(x["q_I"][rows].cpu() if False else x["q_I"].cpu(), x["k_I"].cpu(),
+                                     x["w"].cpu(), cu_seqlens=cu if lengths else None, rows=rows, ld=maxlen)
+    vals = torch.full((T, maxlen), float("-inf"), device=DEV)
+    vals[torch.from_numpy(rows).to(DEV)] = torch.from_numpy(sc).to(DEV)
+    kw = dict(cu_seqlens=cu_dev(wl.lengths), max_seqlen=maxlen) if lengths else {}
+    idx, val = sa.topk_select(vals, 2048, with_values=True, **kw)
+    ref_i, ref_v = oracle.topk_select_dense(sc, 2048, cu_seqlens=cu if lengths else None, rows=rows)
+    np.testing.assert_array_equal(idx.cpu().numpy()[rows], ref_i)
+    np.testing.assert_array_equal(val.cpu().numpy()[rows], ref_v)
+
+
+# ---------------------------------------------------------------------- indexer
+
+@pytest.mark.parametrize("name,T,B", [("tiny_fp32", None, 1), ("nope_unaligned", None, 1),
+                                      ("block_gqa", 1024, 1), ("block_gqa", 2048, 64)])
+def test_indexer_dense_integer_exact(sa, name, T, B):
+    wl = W[name]
+    x = workloads.indexer_inputs(wl, integer=True, T=T)
+    ref = oracle.indexer_scores_dense(x["q_I"], x["k_I"], x["w"], block_size=B)
+    got = sa.indexer_scores(x["q_I"].to(DEV), x["k_I"].to(DEV), x["w"].to(DEV), block_size=B)
+    got = got.cpu().numpy()[:, :ref.shape[1]]
+    np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("name,T", [("tiny_fp32", None), ("nope_unaligned", None), ("long_dsa", 1536)])
+def test_indexer_dense_normal_within_bound(sa, name, T):
+    # fp32 accumulation of bf16 products: |err| <= (D_I + H_I) * 2^-24 * B[t,s] with
+    # B[t,s] = sum_h |w| sum_d |q||k|; checked at 2e-5 * B.
+    wl = W[name]
+    x = workloads.indexer_inputs(wl, T=T)
+    ref = oracle.indexer_scores_dense(x["q_I"], x["k_I"], x["w"])
+    bound = oracle.indexer_scores_dense(x["q_I"].float().abs(), x["k_I"].float().abs(), x["w"].abs())
+    got = sa.indexer_scores(x["q_I"].to(DEV), x["k_I"].to(DEV), x["w"].to(DEV)).cpu().numpy()
+    got = got[:, :ref.shape[1]]
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(got), fin)
+    assert np.all(np.abs(got[fin] - ref[fin]) <= 2e-5 * bound[fin] + 1e-30)
+
+
+def test_indexer_dense_thd(sa):
+    lengths = (300, 5, 700, 64, 129)
+    T = sum(lengths)
+    wl = W["long_dsa"]
+    x = workloads.indexer_inputs(wl, integer=True, T=T)
+    cu = workloads.cu_seqlens(lengths)
+    for B in (1, 64):
+        ref = oracle.indexer_scores_dense(x["q_I"], x["k_I"], x["w"], cu_seqlens=cu, block_size=B)
+        got = sa.indexer_scores(x["q_I"].to(DEV), x["k_I"].to(DEV), x["w"].to(DEV), block_size=B,
+                                cu_seqlens=cu_dev(lengths), max_seqlen=700).cpu().numpy()
+        np.testing.assert_array_equal(got[:, :ref.shape[1]], ref)
+
+
+@pytest.mark.parametrize("name,k,T,B", [("tiny_fp32", 64, None, 1), ("nope_unaligned", 65, None, 1),
+                                        ("nope_unaligned", 127, None, 1), ("long_dsa", 2048, 3000, 1),
+                                        ("block_gqa", 16, 2048, 64)])
+def test_indexer_topk_fused_integer_exact(sa, name, k, T, B):
+    wl = W[name]
+    x = workloads.indexer_inputs(wl, integer=True, T=T)
+    ref_i, ref_v = oracle.indexer_topk(x["q_I"], x["k_I"], x["w"], k, block_size=B,
+                                       force_own_block=B > 1)
+    idx, val = sa.indexer_topk(x["q_I"].to(DEV), x["k_I"].to(DEV), x["w"].to(DEV), k,
+                               block_size=B, force_own_block=B > 1, with_values=True)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_i)
+    np.testing.assert_array_equal(val.cpu().numpy(), ref_v)
+
+
+@pytest.mark.parametrize("name", ["nope_unaligned", "block_gqa"])
+def test_indexer_fused_matches_dense_then_select(sa, name):
+    # On non-integer inputs both GPU paths compute the same fp32 scores, so the fused
+    # selection must equal sa_topk_select over the dense scores, bit for bit.
+    wl = W[name]
+    T = 1024 if name == "nope_unaligned" else 4096
+    B = wl.block_size
+    k = wl.topk[0]
+    x = {n: t.to(DEV) for n, t in workloads.indexer_inputs(wl, T=T).items()}
+    dense = sa.indexer_scores(x["q_I"], x["k_I"], x["w"], block_size=B)
+    i1, v1 = sa.topk_select(dense, k, block_size=B, force_own_block=B > 1, with_values=True)
+    i2, v2 = sa.indexer_topk(x["q_I"], x["k_I"], x["w"], k, block_size=B, force_own_block=B > 1,
+                             with_values=True)
+    assert torch.equal(i1, i2)
+    assert torch.equal(v1, v2)
+
+
+@pytest.mark.parametrize("name", ["long_dsa", "thd_varlen"])
+def test_indexer_topk_full_size_integer_sampled(sa, name):
+    wl = W[name]
+    T = wl.T
+    lengths = wl.lengths if len(wl.lengths) > 1 else None
+    x = workloads.indexer_inputs(wl, integer=True, device=DEV)
+    assert workloads.exact_sum_bound(x["q_I"][:2048], x["k_I"], x["w"][:2048]) < 2 ** 24
+    kw = dict(cu_seqlens=cu_dev(wl.lengths), max_seqlen=max(wl.lengths)) if lengths else {}
+    idx = sa.indexer_topk(x["q_I"], x["k_I"], x["w"], 2048, **kw).cpu().numpy()
+    rows = sample_rows(T, 8, 11, lengths)
+    cu = workloads.cu_seqlens(wl.lengths) if lengths else None
+    xc = {n: t.cpu() for n, t in x.items()}
+    ref_i, _ = oracle.indexer_topk(xc["q_I"], xc["k_I"], xc["w"], 2048, cu_seqlens=cu, rows=rows)
+    np.testing.assert_array_equal(idx[rows], ref_i)
+
+
+# ---------------------------------------------------------------------- sparse MLA
+
+def test_sparse_mla_tiny_fp32(sa):
+    wl = W["tiny_fp32"]
+    x = workloads.indexer_inputs(wl)
+    ref_idx, _ = oracle.indexer_topk(x["q_I"], x["k_I"], x["w"], 64)
+    m = workloads.mla_inputs(wl)
+    out, lse = sa.sparse_mla(m["q"].to(DEV), m["kv"].to(DEV), torch.from_numpy(ref_idx).to(DEV), wl.scale)
+    ro, rl = oracle.sparse_mla(m["q"], m["kv"], ref_idx, wl.scale)
+    close(out.cpu().numpy(), ro, **F32_TOL, what="out")
+    close(lse.cpu().numpy(), rl, **F32_TOL, what="lse")
+
+
+@pytest.mark.parametrize("k", [65, 127])
+def test_sparse_mla_nope_unaligned(sa, k):
+    wl = W["nope_unaligned"]
+    x = workloads.indexer_inputs(wl, integer=True)
+    ref_idx, _ = oracle.indexer_topk(x["q_I"], x["k_I"], x["w"], k)
+    for r in wl.invalid_rows:
+        ref_idx[r] = -1
+    m = workloads.mla_inputs(wl)
+    idx = torch.from_numpy(ref_idx).to(DEV)
+    o576, l576 = sa.sparse_mla(m["q"].to(DEV), m["kv"].to(DEV), idx, wl.scale)
+    o512, l512 = sa.sparse_mla(m["q512"].to(DEV), m["kv512"].to(DEV), idx, wl.scale)
+    # zero padding adds exact zeros to every logit: identical results
+    assert torch.equal(o576, o512) and torch.equal(l576, l512)
+    ro, rl = oracle.sparse_mla(m["q512"], m["kv512"], ref_idx, wl.scale)
+    close(o576.float().cpu().numpy(), ro, **BF16_TOL, what="out")
+    close(l576.cpu().numpy(), rl, **BF16_TOL, what="lse")
+    for r in wl.invalid_rows:
+        assert torch.all(o576[r] == 0) and torch.all(torch.isneginf(l576[r]))
+
+
+@pytest.mark.parametrize("H", [8, 16, 32, 64, 128])
+@pytest.mark.parametrize("k", [1, 64, 65, 127])
+@pytest.mark.parametrize("d_qk", [512, 576])
+def test_sparse_mla_shapes(sa, H, k, d_qk):
+    T, S = 40, 300
+    g = torch.Generator().manual_seed(H * 1000 + k * 10 + d_qk)
+    q = torch.randn((T, H, d_qk), generator=g).to(torch.bfloat16)
+    kv = torch.randn((S, d_qk), generator=g).to(torch.bfloat16)
+    idx = torch.randint(0, S, (T, k), generator=g, dtype=torch.int32)
+    idx[torch.rand((T, k), generator=g) < 0.1] = -1
+    idx[3] = -1                                  # an all-invalid row
+    scale = 1 / math.sqrt(d_qk)
+    out, lse = sa.sparse_mla(q.to(DEV), kv.to(DEV), idx.to(DEV), scale)
+    ro, rl = oracle.sparse_mla(q, kv, idx.numpy(), scale)
+    close(out.float().cpu().numpy(), ro, **BF16_TOL, what="out")
+    close(lse.cpu().numpy(), rl, **BF16_TOL, what="lse")
+
+
+def test_sparse_mla_large_logits_restart(sa):
+    # a later key whose logit exceeds the first tile's max by far: exercises the
+    # softmax reference restart
+    T, S, H, k = 4, 200, 32, 128
+    g = torch.Generator().manual_seed(5)
+    q = torch.randn((T, H, 576), generator=g)
+    kv = torch.randn((S, 576), generator=g) * 0.01
+    kv[150] = q[0, 0] * 0.5                     # one very aligned key for row 0, head 0
+    q, kv = q.to(torch.bfloat16), kv.to(torch.bfloat16)
+    idx = torch.arange(k, dtype=torch.int32)[None].repeat(T, 1) + 40
+    out, lse = sa.sparse_mla(q.to(DEV), kv.to(DEV), idx.to(DEV), 1.0)
+    ro, rl = oracle.sparse_mla(q, kv, idx.numpy(), 1.0)
+    close(out.float().cpu().numpy(), ro, **BF16_TOL, what="out")
+    close(lse.cpu().numpy(), rl, atol=2e-2, rtol=1e-3, what="lse")
+
+
+@pytest.mark.parametrize("name", ["long_dsa", "thd_varlen"])
+def test_sparse_mla_full_size_sampled(sa, name):
+    wl = W[name]
+    T = wl.T
+    lengths = wl.lengths if len(wl.lengths) > 1 else None
+    m = workloads.mla_inputs(wl, device=DEV)
+    idx = workloads.random_causal_index(T, 2048, wl.seed, lengths=wl.lengths, device=DEV)
+    out, lse = sa.sparse_mla(m["q"], m["kv"], idx, wl.scale)
+    rows = sample_rows(T, 12, 13, lengths)
+    rt = torch.from_numpy(rows).to(DEV)
+    ro, rl = oracle.sparse_mla(m["q"][rt].cpu(), m["kv"].cpu(), idx[rt].cpu().numpy(), wl.scale)
+    close(out[rt].float().cpu().numpy(), ro, **BF16_TOL, what="out")
+    close(lse[rt].cpu().numpy(), rl, **BF16_TOL, what="lse")
+
+
+# ------------------------------------------------------------------ block-sparse GQA
+
+def test_block_gqa_on_oracle_routes(sa):
+    wl = W["block_gqa"]
+    T = 2048
+    x = workloads.indexer_inputs(wl, T=T)
+    blk, _ = oracle.indexer_topk(x["q_I"], x["k_I"], x["w"], 16, block_size=64, force_own_block=True)
+    g = workloads.gqa_inputs(wl, T=T)
+    out, lse = sa.block_sparse_gqa(g["q"].to(DEV), g["k"].to(DEV), g["v"].to(DEV),
+                                   torch.from_numpy(blk).to(DEV), wl.scale, block_size=64)
+    rows = sample_rows(T, 200, 17)
+    ro, rl = oracle.block_sparse_gqa(g["q"], g["k"], g["v"], blk, 64, wl.scale, rows=rows)
+    close(out.float().cpu().numpy()[rows], ro, **BF16_TOL, what="out")
+    close(lse.cpu().numpy()[rows], rl, **BF16_TOL, what="lse")
+
+
+def test_block_gqa_full_size_thd_sampled(sa):
+    wl = W["block_gqa"]
+    lengths = (3000, 64, 5128)
+    T = sum(lengths)
+    g = workloads.gqa_inputs(wl, device=DEV)
+    blk = workloads.random_block_index(T, 16, 64, 9, lengths=lengths, device=DEV)
+    blk[100] = -1                                      # a row with no key
+    out, lse = sa.block_sparse_gqa(g["q"], g["k"], g["v"], blk, wl.scale, block_size=64,
+                                   cu_seqlens=cu_dev(lengths), max_seqlen=5128)
+    rows = sample_rows(T, 40, 19, lengths)
+    rows = np.union1d(rows, [100])
+    ro, rl = oracle.block_sparse_gqa(g["q"].cpu(), g["k"].cpu(), g["v"].cpu(), blk.cpu().numpy(), 64,
+                                     wl.scale, cu_seqlens=workloads.cu_seqlens(lengths), rows=rows)
+    close(out.float().cpu().numpy()[rows], ro, **BF16_TOL, what="out")
+    close(lse.cpu().numpy()[rows], rl, **BF16_TOL, what="lse")
+
+
+# ------------------------------------------------------------ determinism and inputs
+
+def test_replay_bitwise_and_inputs_preserved(sa):
+    wl = W["nope_unaligned"]
+    x = {n: t.to(DEV) for n, t in workloads.indexer_inputs(wl).items()}
+    m = {n: t.to(DEV) for n, t in workloads.mla_inputs(wl).items()}
+    gq = {n: t.to(DEV) for n, t in workloads.gqa_inputs(W["block_gqa"], T=1024).items()}
+    before = {n: t.clone() for n, t in {**x, **m, **gq}.items()}
+
+    def run():
+        idx, val = sa.indexer_topk(x["q_I"], x["k_I"], x["w"], 127, with_values=True)
+        dense = sa.indexer_scores(x["q_I"], x["k_I"], x["w"])
+        sel = sa.topk_select(dense, 127)
+        out, lse = sa.sparse_mla(m["q"], m["kv"], idx, wl.scale)
+        blk = sa.indexer_topk(x["q_I"], x["k_I"], x["w"], 16, block_size=64, force_own_block=True)
+        go, gl = sa.block_sparse_gqa(gq["q"], gq["k"], gq["v"], blk, 0.1, block_size=64)
+        return [idx, val, dense, sel, out, lse, blk, go, gl]
+
+    a = run()
+    b = run()
+    # third run under contention from another stream
+    side = torch.cuda.Stream()
+    big = torch.randn((4096, 4096), device=DEV)
+    with torch.cuda.stream(side):
+        for _ in range(8):
+            big = big @ big.T * 1e-3
+    c = run()
+    torch.cuda.synchronize()
+    for u, v, w_ in zip(a, b, c):
+        assert torch.equal(u, v) and torch.equal(u, w_)
+    for n, t in before.items():
+        assert torch.equal(t, {**x, **m, **gq}[n]), n
+
+
+def test_empty_inputs_are_noops(sa):
+    z = torch.empty((0, 16, 576), dtype=torch.bfloat16, device=DEV)
+    kv = torch.zeros((4, 576), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((0, 16, 512), dtype=torch.bfloat16, device=DEV)
+    sa.sa_sparse_mla_fwd(z, kv, torch.empty((0, 8), dtype=torch.int32, device=DEV), 1.0, out)
+    sa.sa_topk_select(torch.empty((0, 4), device=DEV), torch.empty((0, 2), dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()

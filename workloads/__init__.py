@@ -281,3 +281,41 @@ def random_index_rows(T, S, k, seed, lengths=None, device="cpu", frac_invalid=0.
         drop = torch.rand((T, k), generator=g) < frac_invalid
         idx[drop] = -1
     return idx.to(device)
+
+
+def random_causal_index(T, k, seed, lengths=None, device="cpu", frac_invalid=0.05):
+    """Random causal token indices [T,k] int32, vectorised (duplicates allowed).
+
+    Slot j of row t (sequence [c, c+L)) holds c + floor(u * (t - c + 1)), u ~ U(0,1),
+    i.e. a uniformly drawn causal key; a seeded fraction of slots is -1. Used to feed
+    attention kernels index rows at full size without any selection code.
+    """
+    lengths = lengths or (T,)
+    starts = torch.from_numpy(cu_seqlens(lengths)[:-1].astype(np.int64))
+    lens = torch.tensor(lengths, dtype=torch.int64)
+    seq_of = torch.repeat_interleave(torch.arange(len(lengths)), lens)
+    start = starts[seq_of].to(device)
+    t = torch.arange(T, device=device, dtype=torch.int64)
+    g = _gen(seed, 31, device)
+    u = torch.rand((T, k), generator=g, device=device, dtype=torch.float64)
+    idx = start[:, None] + torch.floor(u * (t - start + 1)[:, None].double()).long()
+    drop = torch.rand((T, k), generator=g, device=device) < frac_invalid
+    idx = torch.where(drop, torch.full_like(idx, -1), idx)
+    return idx.to(torch.int32).contiguous()
+
+
+def random_block_index(T, nblk, block_size, seed, lengths=None, device="cpu"):
+    """Random block routes [T,nblk] int32: the query's own block plus distinct earlier
+    blocks drawn at random, -1 padded when the row has fewer blocks. Local block ids."""
+    lengths = lengths or (T,)
+    g = _gen(seed, 32, "cpu")
+    out = torch.full((T, nblk), -1, dtype=torch.int32)
+    starts = cu_seqlens(lengths)
+    for j in range(len(lengths)):
+        c0, c1 = int(starts[j]), int(starts[j + 1])
+        for t in range(c0, c1):
+            own = (t - c0) // block_size
+            others = torch.randperm(own, generator=g)[:nblk - 1] if own > 0 else torch.empty(0, dtype=torch.long)
+            row = torch.cat([others, torch.tensor([own])]).sort().values
+            out[t, :row.numel()] = row.to(torch.int32)
+    return out.to(device)
