@@ -1,0 +1,280 @@
+"""Benchmark of the indexer -> top-k -> sparse-MLA forward path on one MI355X.
+
+A step is one pass of the hot path over the long-context workload (T = S = 32768, one
+sequence, bf16): the fused indexer with exact top-k (64 heads x 128, k = 2048) and
+absorbed sparse-MLA attention over the selected keys (128 heads, q/k 576, v 512).
+Inputs are synthetic (seeded normal draws on the device), resident in HBM before the
+timed region.
+
+Printed: ONE JSON line. `value` is the sparse-MLA forward throughput in TFLOP/s of
+algorithmic work (2 * (576 + 512) * 128 flop per valid slot); the line also carries
+the indexer->top-k rate in query tokens/s, the step time, the roofline of the
+dominant kernel (sparse MLA, MFMA-bound), the standalone top-k selection over a
+materialised 32768 x 32768 causal score matrix against the HBM roofline, the
+block-routed sparse GQA workload, and the CPU oracle timed on a bounded sample.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0               # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def _src_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "indexer_routed_sparse_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key, source_files, launches_per_unit=1):
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/traffic.json),
+    or None when missing or taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_digest") != _src_digest(*source_files):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream the library launches on)."""
+
+    def __init__(self):
+        self.s = torch.cuda.Event(enable_timing=True)
+        self.e = torch.cuda.Event(enable_timing=True)
+
+    def __enter__(self):
+        self.s.record()
+        return self
+
+    def __exit__(self, *a):
+        self.e.record()
+
+    def ms(self):
+        return self.s.elapsed_time(self.e)
+
+
+def cpu_baseline(wl, x, m, idx_gpu, n_rows=1024):
+    """Oracle (numpy float64) on a bounded sample of the same workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    T = wl.T
+    rows = np.linspace(T // 8, T - 1, n_rows).astype(np.int64)
+    xc = {n: t.cpu() for n, t in x.items()}
+    t0 = time.perf_counter()
+    ref_idx, _ = oracle.indexer_topk(xc["q_I"], xc["k_I"], xc["w"], 2048, rows=rows)
+    t1 = time.perf_counter()
+    rt = torch.from_numpy(rows).to(m["q"].device)
+    qs = m["q"][rt].cpu()
+    kv = m["kv"].cpu()
+    full_idx = np.full((T, 2048), -1, dtype=np.int32)
+    full_idx[rows] = ref_idx
+    t2 = time.perf_counter()
+    oracle.sparse_mla(qs, kv, ref_idx, wl.scale)
+    t3 = time.perf_counter()
+    slots = int((ref_idx >= 0).sum())
+    mla_flops = 2.0 * (576 + 512) * 128 * slots
+    return {
+        "value": mla_flops / (t3 - t2) / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{n_rows} query rows of long_dsa evenly spaced in [T/8, T): indexer + exact "
+                  f"top-k ({t1 - t0:.1f} s) and sparse MLA ({t3 - t2:.1f} s), numpy float64",
+        "indexer_topk_tokens_per_s": n_rows / (t1 - t0),
+        "path_tokens_per_s": n_rows / ((t1 - t0) + (t3 - t2)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the top-k select and GQA legs")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the sharding design is described in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import indexer_routed_sparse_amd as sa
+    import workloads
+
+    dev = torch.device("cuda:0")
+    wl = workloads.WORKLOADS["long_dsa"]
+    T, K, H = wl.T, 2048, wl.H
+    print(f"[bench] generating long_dsa inputs T={T}", file=sys.stderr, flush=True)
+    x = workloads.indexer_inputs(wl, device=dev)
+    m = workloads.mla_inputs(wl, device=dev)
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(timers=None):
+        if timers is None:
+            sa.sa_indexer_scores(x["q_I"], x["k_I"], x["w"], topk=K, out_idx=idx)
+            sa.sa_sparse_mla_fwd(m["q"], m["kv"], idx, wl.scale, out, lse)
+            return
+        with timers[0]:
+            sa.sa_indexer_scores(x["q_I"], x["k_I"], x["w"], topk=K, out_idx=idx)
+        with timers[1]:
+            sa.sa_sparse_mla_fwd(m["q"], m["kv"], idx, wl.scale, out, lse)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timers = [[Timer(), Timer()] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(timers[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_idx = float(np.mean([tm[0].ms() for tm in timers]))
+    t_mla = float(np.mean([tm[1].ms() for tm in timers]))
+
+    slots = int((idx >= 0).sum().item())
+    mla_flops = 2.0 * (576 + 512) * H * slots
+    idx_flops = 2.0 * wl.H_I * wl.D_I * (T * (T + 1) // 2)
+    mla_tflops = mla_flops / (t_mla * 1e-3) / 1e12
+    result = {
+        "metric": "sparse-MLA fwd TFLOP/s + indexer->top-k tokens/s @ S=32K, k=2048; % of roofline",
+        "value": round(mla_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "long_dsa", "T": T, "S": T, "topk": K, "mla_heads": H,
+                   "d_qk": 576, "d_v": 512, "indexer_heads": wl.H_I, "indexer_dim": wl.D_I,
+                   "step": "sa_indexer_scores(fused top-k) -> sa_sparse_mla_fwd"},
+        "indexer_topk_tokens_per_s": round(T / (t_idx * 1e-3), 1),
+        "indexer_tflops": round(idx_flops / (t_idx * 1e-3) / 1e12, 2),
+        "indexer_ms": round(t_idx, 3),
+        "sparse_mla_ms": round(t_mla, 3),
+        "valid_slots": slots,
+        "roofline": {
+            "kernel": "sparse_mla_bf16_kernel",
+            "bound": "mfma",
+            "achieved": round(mla_tflops, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(mla_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": _traffic("sparse_mla_long_dsa", ["sparse_mla.hip", "sa_common.h"]),
+        },
+        "roofline_indexer": {
+            "kernel": "indexer_kernel", "bound": "mfma",
+            "achieved": round(idx_flops / (t_idx * 1e-3) / 1e12, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(idx_flops / (t_idx * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        },
+    }
+
+    if not args.no_extras:
+        # ---- standalone exact top-k over a materialised causal score matrix (HBM-bound)
+        print("[bench] top-k select on materialised scores", file=sys.stderr, flush=True)
+        del out, lse
+        scores = torch.empty((T, T), dtype=torch.float32, device=dev)
+        sa.sa_indexer_scores(x["q_I"], x["k_I"], x["w"], scores=scores)
+        sel = torch.empty((T, K), dtype=torch.int32, device=dev)
+        for _ in range(2):
+            sa.sa_topk_select(scores, sel)
+        tms = []
+        for _ in range(max(3, args.steps)):
+            tm = Timer()
+            with tm:
+                sa.sa_topk_select(scores, sel)
+            tms.append(tm)
+        torch.cuda.synchronize()
+        t_sel = float(np.mean([tm.ms() for tm in tms]))
+        sel_bytes = 4.0 * (T * (T + 1) // 2) + 4.0 * T * K
+        gbs = sel_bytes / (t_sel * 1e-3) / 1e9
+        result["roofline_topk_select"] = {
+            "kernel": "topk_select_kernel", "bound": "hbm", "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "ms": round(t_sel, 4), "tokens_per_s": round(T / (t_sel * 1e-3), 1),
+            "traffic": _traffic("topk_select_long_dsa", ["topk_select.hip", "sa_common.h"]),
+        }
+        same = torch.equal(sel, idx)
+        result["roofline_topk_select"]["matches_fused_indexer"] = bool(same)
+        del scores, sel
+
+        # ---- block-routed sparse GQA workload (T = 8192)
+        print("[bench] block-routed GQA", file=sys.stderr, flush=True)
+        wq = workloads.WORKLOADS["block_gqa"]
+        xq = workloads.indexer_inputs(wq, device=dev)
+        gq = workloads.gqa_inputs(wq, device=dev)
+        blk = torch.empty((wq.T, 16), dtype=torch.int32, device=dev)
+        go = torch.empty((wq.T, wq.Hq, wq.Dv), dtype=torch.bfloat16, device=dev)
+        for _ in range(2):
+            sa.sa_indexer_scores(xq["q_I"], xq["k_I"], xq["w"], block_size=64, topk=16,
+                                 force_own_block=True, out_idx=blk)
+            sa.sa_block_sparse_gqa_fwd(gq["q"], gq["k"], gq["v"], blk, wq.scale, go, block_size=64)
+        ti, tg = Timer(), Timer()
+        with ti:
+            sa.sa_indexer_scores(xq["q_I"], xq["k_I"], xq["w"], block_size=64, topk=16,
+                                 force_own_block=True, out_idx=blk)
+        with tg:
+            sa.sa_block_sparse_gqa_fwd(gq["q"], gq["k"], gq["v"], blk, wq.scale, go, block_size=64)
+        torch.cuda.synchronize()
+        blk_np = blk.cpu().numpy()
+        t_idx_np = np.arange(wq.T)
+        attended = 0
+        for j in range(16):
+            b = blk_np[:, j]
+            ok = b >= 0
+            lo = b * 64
+            hi = np.minimum(lo + 63, t_idx_np)
+            attended += int(np.where(ok, np.maximum(hi - lo + 1, 0), 0).sum())
+        gqa_flops = 2.0 * (wq.D + wq.Dv) * wq.Hq * attended
+        result["block_gqa"] = {
+            "workload": "block_gqa", "T": wq.T, "indexer_block_topk_ms": round(ti.ms(), 3),
+            "gqa_ms": round(tg.ms(), 3), "attended_keys": attended,
+            "gqa_tflops": round(gqa_flops / (tg.ms() * 1e-3) / 1e12, 2),
+            "gqa_frac_mfma": round(gqa_flops / (tg.ms() * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        }
+
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline (bounded sample)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, x, m, idx)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

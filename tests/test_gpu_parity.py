@@ -117,9 +117,10 @@ def test_topk_select_full_size_sampled(sa, name):
     rows = sample_rows(T, 10, 7, lengths)
     cu = workloads.cu_seqlens(wl.lengths)
     maxlen = max(wl.lengths)
-    sc = oracle.indexer_scores_dense(x["q_I"][rows].cpu() if False else x["q_I"].cpu(), x["k_I"].cpu(),
-                                     x["w"].cpu(), cu_seqlens=cu if lengths else None, rows=rows, ld=maxlen)
-    vals = torch.full((T, maxlen), float("-inf"), device=DEV)
+    ld = (maxlen + 3) // 4 * 4
+    sc = oracle.indexer_scores_dense(x["q_I"].cpu(), x["k_I"].cpu(), x["w"].cpu(),
+                                     cu_seqlens=cu if lengths else None, rows=rows, ld=ld)
+    vals = torch.full((T, ld), float("-inf"), device=DEV)
     vals[torch.from_numpy(rows).to(DEV)] = torch.from_numpy(sc).to(DEV)
     kw = dict(cu_seqlens=cu_dev(wl.lengths), max_seqlen=maxlen) if lengths else {}
     idx, val = sa.topk_select(vals, 2048, with_values=True, **kw)
