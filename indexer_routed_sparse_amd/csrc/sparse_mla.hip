@@ -33,55 +33,66 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// XOR swizzle of 16-byte chunk c in tile row R (bijective within aligned groups of
-// 8 (576-wide rows) or 16 (512-wide rows) chunks).
-template <int NCH>
-SA_DEVICE int chunk_swz(int R) {
-  if constexpr (NCH == 72) return (((R >> 1) & 1) << 2) | ((R >> 2) & 3);
-  else return ((R & 3) << 2) | ((R >> 2) & 3);
-}
+// LDS tile of kBK = 32 gathered latent rows. The first 512 channels of each row
+// (64 chunks of 16 bytes) form the main region, row-major with a 1 KiB row stride;
+// the 64 RoPE channels (8 chunks) of all rows form a second region. Chunks are
+// XOR-swizzled so that the K reads (ds_read_b128, 16 rows per cycle) and the V
+// transpose reads (4 rows x 4 chunks per 32 lanes) hit distinct banks.
+SA_DEVICE int swz_main(int R) { return ((R & 3) << 2) | ((R >> 2) & 3); }
+SA_DEVICE int swz_rope(int R) { return (R >> 1) & 7; }
 
 // 16-byte global -> LDS copy per lane: lane l writes LDS bytes [lds + 16 l, +16).
-// `lds` must be wave-uniform. The kernels using it set M0 only here.
-SA_DEVICE void lds_dma16(uint32_t lds, const void* src) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src)
+// `lds` is wave-uniform. The address is a wave-uniform 64-bit base plus a per-lane
+// 32-bit byte offset. Issued through inline asm so that the compiler does not order
+// later LDS reads behind it; completion is tracked with s_waitcnt vmcnt. M0 is set
+// here and nowhere else in these kernels.
+SA_DEVICE void lds_dma16(uint32_t lds, const void* base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               ::"s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(base)
                : "memory");
 }
 
 constexpr int kBK = 32;        // keys per tile
-constexpr int kStages = 3;     // gather pipeline depth (tiles in flight + tile in use)
-
 
 // s_waitcnt immediate (gfx9 encoding) that waits until at most `vm` vector-memory
 // operations of this wave are outstanding and ignores the other counters.
 constexpr int waitcnt_vm(int vm) { return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
 template <int DQK>
-constexpr int mla_tile_bytes() { return kBK * (DQK / 8) * 16; }
+constexpr int mla_tile_bytes() { return kBK * 64 * 16 + (DQK == 576 ? kBK * 8 * 16 : 0); }
 
-template <int NW, int DQK>
+template <int NW, int DQK, int NST, int NKL>
+constexpr size_t mla_lds_bytes(int topk) {
+  return (size_t)NST * mla_tile_bytes<DQK>() + (size_t)NKL * NW * 64 * 16 +
+         (size_t)((topk + kBK - 1) / kBK) * kBK * 4;
+}
+
+// NW waves of 32 heads; NST gather stages; NKL k-steps of q held in LDS (the rest
+// in VGPRs).
+template <int NW, int DQK, int NST, int NKL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                             const int32_t* __restrict__ idx, int H, int topk, float scale_log2,
                             uint16_t* __restrict__ out, float* __restrict__ lse) {
-  constexpr int NCH = DQK / 8;            // 16-byte chunks per latent row
   constexpr int NK = DQK / 16;            // MFMA k-steps of S^T = K . Q^T
-  constexpr int NKL = 8;                  // k-steps whose q slices are kept in LDS
-  constexpr int NKR = NK - NKL;           // k-steps whose q slices are kept in VGPRs
+  constexpr int NKM = 32;                 // k-steps in the main region
+  constexpr int NKR = NK - NKL;           // k-steps whose q slices stay in VGPRs
   constexpr int NDV = 512 / 32;           // 32-wide dv tiles of O
+  constexpr bool ROPE = DQK == 576;
   constexpr int TILE_BYTES = mla_tile_bytes<DQK>();
-  constexpr int NINSTR = kBK * NCH / 64;  // 1 KiB gather instructions per tile
-  constexpr int PER_WAVE = NINSTR / NW;   // gather instructions per wave per tile
-  constexpr int AGRP = (NCH == 72) ? 4 : 8;  // k-step classes of the A-read swizzle
-  static_assert(NINSTR % NW == 0, "gather split");
+  constexpr int ROPE_OFF = kBK * 64 * 16;
+  constexpr int MAIN_PER_WAVE = kBK / NW;               // one DMA per row
+  constexpr int ROPE_PER_WAVE = ROPE ? 4 / NW + (4 % NW ? 1 : 0) : 0;
+  constexpr int DA = 4;                   // K-operand prefetch distance (k-steps)
+  constexpr int DV = 4;                   // V-operand prefetch distance (MFMAs)
+  static_assert(NW == 1 || NW == 2 || NW == 4, "waves");
   // fp32 P values stay below 2^16 times the reference; a larger tile max restarts
   constexpr float kThr = 16.0f;
 
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  char* tiles = lds;                                           // kStages tiles
-  // q slices of the last NKL k-steps: [NKL][NW*64 lanes] x 16 bytes
-  char* s_q = lds + kStages * TILE_BYTES;
-  int32_t* s_idx = reinterpret_cast<int32_t*>(s_q + NKL * NW * 64 * 16);  // [topk]
+  char* tiles = lds;                                           // NST tiles
+  char* s_q = lds + NST * TILE_BYTES;                          // [NKL][NW*64] x 16 B
+  int32_t* s_idx = reinterpret_cast<int32_t*>(s_q + NKL * NW * 64 * 16);  // [ntiles*32]
   __shared__ int s_restart;
 
   const int t = blockIdx.x;
@@ -93,13 +104,13 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
   const bool head_ok = head < H;
   const int ntiles = (topk + kBK - 1) / kBK;
 
-  // ---- stage the index row; q for this wave's 32 heads as B operand slices
+  // ---- stage the index row; q for this wave's 32 heads as B-operand slices
   {
     const int32_t* __restrict__ irow = idx + (int64_t)t * topk;
     for (int j = tid; j < ntiles * kBK; j += NW * 64) s_idx[j] = j < topk ? irow[j] : -1;
   }
   if (tid == 0) s_restart = 0;
-  bf16x8_t qv[NKR];
+  bf16x8_t qv[NKR > 0 ? NKR : 1];
   {
     const uint16_t* qrow = q + ((int64_t)t * H + (head_ok ? head : 0)) * DQK + 8 * hl;
 #pragma unroll
@@ -112,15 +123,19 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
   }
 
   // ---- per-lane LDS offsets
-  // A (K rows): row R = L&31, chunk 2n + hl; the swizzle depends on R&15 = L&15.
-  int a_off[AGRP];
+  // K reads (A operand): row R = L&31, chunk 2n + hl.
+  int a_off[8];
+  int a_rope[4];
   {
     const int R = L & 31;
-    const int f = chunk_swz<NCH>(R);
+    const int f = swz_main(R);
 #pragma unroll
-    for (int cls = 0; cls < AGRP; ++cls) a_off[cls] = (R * NCH + ((2 * cls + hl) ^ f)) * 16;
+    for (int cls = 0; cls < 8; ++cls) a_off[cls] = (R * 64 + ((2 * cls + hl) ^ f)) * 16;
+    const int gr = swz_rope(R);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a_rope[j] = ROPE_OFF + (R * 8 + ((2 * j + hl) ^ gr)) * 16;
   }
-  // V (transpose reads): lane L = 16g + s reads row 4(g/2) + s/4 (+16m + 8r) and
+  // V transpose reads: lane L = 16g + s reads row 4(g/2) + s/4 (+16m + 8r) and
   // columns 16(g%2) + 4(s%4) (+32nt), 8 bytes.
   int v_off[2][4];      // [r][nt & 3]
   {
@@ -128,37 +143,39 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int R = 8 * r + 4 * (g >> 1) + (s >> 2);
-      const int f = chunk_swz<NCH>(R);
+      const int f = swz_main(R);
       const int col = 16 * (g & 1) + 4 * (s & 3);
 #pragma unroll
       for (int nc = 0; nc < 4; ++nc) {
         const int c = 4 * nc + (col >> 3);
-        v_off[r][nc] = (R * NCH + (c ^ f)) * 16 + (col & 7) * 2;
+        v_off[r][nc] = (R * 64 + (c ^ f)) * 16 + (col & 7) * 2;
       }
     }
   }
   __syncthreads();
 
-  // Gather of one tile: instruction ii covers tile slots 64*ii + L (1 KiB of LDS).
-  // Issued through inline asm so that the compiler does not serialise later LDS
-  // reads behind it; completion is tracked by hand with s_waitcnt vmcnt.
   auto gather = [&](int tile) {
-    const uint32_t base = (uint32_t)(uintptr_t)(SA_LDS char*)(tiles + (tile % kStages) * TILE_BYTES);
+    const uint32_t base = (uint32_t)(uintptr_t)(SA_LDS char*)(tiles + (tile % NST) * TILE_BYTES);
     const int32_t* ir = s_idx + tile * kBK;
-    // The slot arithmetic is recomputed per tile on purpose: hoisted out of the
-    // tile loop it would pin 2*PER_WAVE registers for the whole kernel.
-    int zero;
-    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
 #pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) {
-      const int ii = w + NW * j;
-      const int p = 64 * ii + L + zero;
-      const int R = p / NCH;
-      const int c = (p - R * NCH) ^ chunk_swz<NCH>(R);
-      int row = ir[R];
+    for (int j = 0; j < MAIN_PER_WAVE; ++j) {
+      const int R = w + NW * j;                       // wave-uniform row
+      int row = __builtin_amdgcn_readfirstlane(ir[R]);
       row = row < 0 ? 0 : row;   // masked slot: any finite row keeps P*V finite
-      const uint16_t* src = kv + (int64_t)row * DQK + 8 * c;
-      lds_dma16(base + ii * 1024, src);
+      lds_dma16(base + R * 1024, kv + (int64_t)row * DQK, (uint32_t)((L ^ swz_main(R)) * 16));
+    }
+    if constexpr (ROPE) {
+#pragma unroll
+      for (int j = 0; j < ROPE_PER_WAVE; ++j) {
+        const int ii = w + NW * j;                    // rope instruction: rows 8ii..8ii+7
+        if (ii < 4) {
+          const int R = 8 * ii + (L >> 3);
+          int row = ir[R];
+          row = row < 0 ? 0 : row;
+          const int c = (L & 7) ^ swz_rope(R);
+          lds_dma16(base + ROPE_OFF + ii * 1024, kv, (uint32_t)(row * (DQK * 2) + 1024 + 16 * c));
+        }
+      }
     }
   };
 
@@ -168,7 +185,7 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
   // accumulator file within its 256 registers.
   constexpr int NOA = NDV - 2;             // dv tiles accumulated in AGPRs
   floatx16_t O[NOA];
-  floatx16_t O_tail[NDV - NOA];            // the others, summed per key tile in VGPRs
+  floatx16_t O_tail[NDV - NOA];
   float m_ref = -__builtin_huge_valf();   // softmax reference (log2 units), per head
   float m_seen = -__builtin_huge_valf();
   float l_run = 0.0f;
@@ -180,33 +197,41 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
     for (int i = 0; i < NDV - NOA; ++i) O_tail[i] = floatx16_t{};
     l_run = 0.0f;
-    gather(0);
-    if (ntiles > 1) gather(1);
+#pragma unroll
+    for (int p = 0; p < NST - 1; ++p)
+      if (p < ntiles) gather(p);
 #pragma unroll 1
     for (int tile = 0; tile < ntiles; ++tile) {
-      if (tile + 1 < ntiles) __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER_WAVE));
+      // wait for this tile's gather; the newer ones (up to NST-2) may stay in flight
+      const int newer = min(ntiles - 1 - tile, NST - 2);
+      if (newer >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * (MAIN_PER_WAVE + ROPE_PER_WAVE)));
+      else if (newer == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(MAIN_PER_WAVE + ROPE_PER_WAVE));
       else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       __syncthreads();               // tile resident in all waves' view
-      if (tile + 2 < ntiles) gather(tile + 2);   // its stage was last read in tile-1
+      if (tile + NST - 1 < ntiles) gather(tile + NST - 1);   // its stage was read in tile-1
       const uint64_t vmask = ballot(L < kBK && s_idx[tile * kBK + (L & (kBK - 1))] >= 0);
-      const char* tb = tiles + (tile % kStages) * TILE_BYTES;
+      const char* tb = tiles + (tile % NST) * TILE_BYTES;
 
-      // ---- S^T = K . Q^T over d_qk; A slices prefetched two k-steps ahead
+      // ---- S^T = K . Q^T over d_qk, K slices prefetched DA k-steps ahead
       auto a_at = [&](int n) {
-        return *reinterpret_cast<const bf16x8_t*>(tb + a_off[n % AGRP] + (n / AGRP) * (AGRP * 32));
+        const int off = n < NKM ? a_off[n & 7] + (n >> 3) * 256 : a_rope[(n - NKM) & 3];
+        return *reinterpret_cast<const bf16x8_t*>(tb + off);
+      };
+      auto q_at = [&](int n) {
+        return n < NKR ? qv[n < NKR ? n : 0]
+                       : *reinterpret_cast<const bf16x8_t*>(s_q + ((n - NKR) * NW * 64 + tid) * 16);
       };
       floatx16_t S = floatx16_t{};
       {
-        bf16x8_t a0 = a_at(0), a1 = a_at(1);
+        bf16x8_t ring[DA];
+#pragma unroll
+        for (int i = 0; i < DA; ++i) ring[i] = a_at(i);
 #pragma unroll
         for (int n = 0; n < NK; ++n) {
-          bf16x8_t a2 = a1;
-          if (n + 2 < NK) a2 = a_at(n + 2);
-          const bf16x8_t b = n < NKR ? qv[n < NKR ? n : 0]
-                                     : *reinterpret_cast<const bf16x8_t*>(s_q + ((n - NKR) * NW * 64 + tid) * 16);
-          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, S, 0, 0, 0);
-          a0 = a1;
-          a1 = a2;
+          const bf16x8_t a = ring[n % DA];
+          const bf16x8_t b = q_at(n);
+          if (n + DA < NK) ring[n % DA] = a_at(n + DA);
+          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, S, 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -224,7 +249,7 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       m_seen = fmaxf(m_seen, mx);
       if (m_ref == -__builtin_huge_valf()) m_ref = mx;   // first valid tile (O, l still 0)
-      if (mx > m_ref + kThr) s_restart = 1;               // seen by all after next barrier
+      if (mx > m_ref + kThr) s_restart = 1;               // seen by all after the pass
       const float m_use = (m_ref == -__builtin_huge_valf()) ? 0.0f : m_ref;
 
       // ---- P (bf16) as A operands: half m -> slots 8m..8m+7 of S
@@ -234,8 +259,8 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
         uint32_t pk[4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const float p0 = exp2f(S[8 * m + e] - m_use);
-          const float p1 = exp2f(S[8 * m + e + 1] - m_use);
+          const float p0 = __builtin_amdgcn_exp2f(S[8 * m + e] - m_use);
+          const float p1 = __builtin_amdgcn_exp2f(S[8 * m + e + 1] - m_use);
           l_run += p0 + p1;
           pk[e >> 1] = pack_bf16x2(p0, p1);
         }
@@ -243,9 +268,10 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
       }
 
       // ---- O += P . V (V from the row-major tile through transpose reads),
-      //      B slices prefetched one step ahead
-      auto v_at = [&](int nt, int m) {
-        const int off = 16 * m * NCH * 16 + (nt >> 2) * 256;
+      //      B slices prefetched DV MFMAs ahead
+      auto v_at = [&](int st) {
+        const int nt = st >> 1, m = st & 1;
+        const int off = m * (16 * 1024) + (nt >> 2) * 256;
         const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(tb + off + v_off[0][nt & 3]));
         const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(tb + off + v_off[1][nt & 3]));
         const short __attribute__((ext_vector_type(8))) b8 = {lo[0], lo[1], lo[2], lo[3],
@@ -253,22 +279,22 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
         return __builtin_bit_cast(bf16x8_t, b8);
       };
       {
-        bf16x8_t b0 = v_at(0, 0), b1 = v_at(0, 1);
+        bf16x8_t ring[DV];
+#pragma unroll
+        for (int i = 0; i < DV; ++i) ring[i] = v_at(i);
 #pragma unroll
         for (int st = 0; st < 2 * NDV; ++st) {
           const int nt = st >> 1, m = st & 1;
-          bf16x8_t b2 = b1;
-          if (st + 2 < 2 * NDV) b2 = v_at((st + 2) >> 1, (st + 2) & 1);
+          const bf16x8_t b = ring[st % DV];
+          if (st + DV < 2 * NDV) ring[st % DV] = v_at(st + DV);
           if (nt < NOA) {
-            O[nt < NOA ? nt : 0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(P[m], b0, O[nt < NOA ? nt : 0], 0, 0, 0);
+            O[nt < NOA ? nt : 0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(P[m], b, O[nt < NOA ? nt : 0], 0, 0, 0);
           } else if (m == 0) {
-            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(P[0], b0, floatx16_t{}, 0, 0, 0);
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(P[0], b, floatx16_t{}, 0, 0, 0);
           } else {
-            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(P[1], b0, S, 0, 0, 0);
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(P[1], b, S, 0, 0, 0);
             O_tail[nt >= NOA ? nt - NOA : 0] += S;
           }
-          b0 = b1;
-          b1 = b2;
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -361,18 +387,18 @@ __global__ __launch_bounds__(NT) void sparse_mla_f32_kernel(
   if (lse && tid == 0) lse[(int64_t)t * H + h] = Z > 0.0f ? mx + logf(Z) : -__builtin_huge_valf();
 }
 
+constexpr int kStages = 2;
+constexpr int kQInLds = 16;
+
 template <int NW, int DQK>
 hipError_t launch_bf16(const void* q, const void* kv, const int32_t* idx, int T, int H, int topk,
                        float scale, void* out, float* lse, hipStream_t st) {
-  const int ntiles = (topk + kBK - 1) / kBK;
-  const size_t shm = (size_t)kStages * mla_tile_bytes<DQK>() + (size_t)8 * NW * 64 * 16 +
-                     (size_t)ntiles * kBK * 4;
-  hipError_t e = hipFuncSetAttribute((const void*)sparse_mla_bf16_kernel<NW, DQK>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  const size_t shm = mla_lds_bytes<NW, DQK, kStages, kQInLds>(topk);
+  auto kern = sparse_mla_bf16_kernel<NW, DQK, kStages, kQInLds>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((sparse_mla_bf16_kernel<NW, DQK>), dim3(T), dim3(NW * 64), shm, st,
-                     (const uint16_t*)q, (const uint16_t*)kv, idx, H, topk, scale * kLog2e,
-                     (uint16_t*)out, lse);
+  hipLaunchKernelGGL(kern, dim3(T), dim3(NW * 64), shm, st, (const uint16_t*)q, (const uint16_t*)kv,
+                     idx, H, topk, scale * kLog2e, (uint16_t*)out, lse);
   return hipGetLastError();
 }
 
