@@ -157,10 +157,22 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
   auto gather = [&](int tile) {
     const uint32_t base = (uint32_t)(uintptr_t)(SA_LDS char*)(tiles + (tile % NST) * TILE_BYTES);
     const int32_t* ir = s_idx + tile * kBK;
+    // all row indices of this wave's DMAs first: one LDS round trip, not one per DMA
+    int rows[MAIN_PER_WAVE];
+    int rrows[ROPE_PER_WAVE > 0 ? ROPE_PER_WAVE : 1];
+#pragma unroll
+    for (int j = 0; j < MAIN_PER_WAVE; ++j) rows[j] = ir[w + NW * j];
+    if constexpr (ROPE) {
+#pragma unroll
+      for (int j = 0; j < ROPE_PER_WAVE; ++j) {
+        const int ii = w + NW * j;
+        rrows[j] = ii < 4 ? ir[8 * ii + (L >> 3)] : 0;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < MAIN_PER_WAVE; ++j) {
       const int R = w + NW * j;                       // wave-uniform row
-      int row = __builtin_amdgcn_readfirstlane(ir[R]);
+      int row = __builtin_amdgcn_readfirstlane(rows[j]);
       row = row < 0 ? 0 : row;   // masked slot: any finite row keeps P*V finite
       lds_dma16(base + R * 1024, kv + (int64_t)row * DQK, (uint32_t)((L ^ swz_main(R)) * 16));
     }
@@ -170,8 +182,7 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
         const int ii = w + NW * j;                    // rope instruction: rows 8ii..8ii+7
         if (ii < 4) {
           const int R = 8 * ii + (L >> 3);
-          int row = ir[R];
-          row = row < 0 ? 0 : row;
+          const int row = rrows[j] < 0 ? 0 : rrows[j];
           const int c = (L & 7) ^ swz_rope(R);
           lds_dma16(base + ROPE_OFF + ii * 1024, kv, (uint32_t)(row * (DQK * 2) + 1024 + 16 * c));
         }
