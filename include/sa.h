@@ -91,8 +91,8 @@ int sa_abi_version(void);
  * Inputs:
  *   q_I  [T, H_I, D_I]  dtype        k_I [T, D_I] dtype       w [T, H_I] fp32
  *   dtype  SA_F32 or SA_BF16 (q_I and k_I)
- *   H_I in [1, 64] with 64 % H_I == 0; D_I in {64, 128}; block_size in {1} or a
- *   multiple of 16 up to 256.
+ *   H_I in {4, 8, 16, 32, 64}; D_I in {64, 128}; block_size in {1, 16, 32, 64, 128,
+ *   256}; otherwise SA_ERR_UNSUPPORTED.
  * Mode 1, dense (topk == 0): writes scores [T, ld] fp32; row t, column c holds the
  *   score of key start(t)+c (token mode) or of local block c (block mode) for the
  *   causal columns c < n(t), where n(t) = t-start(t)+1 (tokens) or
@@ -139,6 +139,10 @@ sa_status sa_indexer_scores(const void* q_I, const void* k_I, const float* w, in
  *     arguments are ignored; force_own_block must be 0.
  * Sizes: ld % 4 == 0 (vals and cand_idx rows start 16-byte aligned), ld >= the
  *   widest row, widest row <= 65536; topk in [1, 65536].
+ * Launches: one or more kernels on `stream` (dense single-sequence rows are split by
+ *   width); a row that the fast pass cannot finish marks out_idx[t, 0] with INT32_MIN,
+ *   and a last kernel of the same call completes it, so after the call (in stream
+ *   order) every row holds its final result.
  */
 sa_status sa_topk_select(const float* vals, const int32_t* cand_idx, int64_t ld,
                          int32_t T, const int32_t* cu_seqlens, int32_t num_seqs,

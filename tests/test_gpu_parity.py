@@ -129,6 +129,86 @@ def test_topk_select_full_size_sampled(sa, name):
     np.testing.assert_array_equal(val.cpu().numpy()[rows], ref_v)
 
 
+def _cand_case(case, rng):
+    """(vals [T, ld] fp32, cand [T, ld] int32, topk) for one selection stress case.
+
+    Candidate ids are position + 1000 so that a position reported as an id shows.
+    """
+    def normal(T, ld):
+        return rng.standard_normal((T, ld)).astype(np.float32)
+    holes = None
+    if case == "normal_64k":
+        v, k = normal(3, 65536), 2048
+    elif case == "ties_64k":           # one value everywhere: selection is by index alone
+        v, k = np.ones((2, 65536), np.float32), 2048
+        v[0, 40000] = 2.0
+    elif case == "few_values":         # four distinct values: huge ties at the k-th
+        v, k = rng.integers(0, 4, (4, 20000)).astype(np.float32), 2048
+    elif case == "zeros_infs":         # -0/+0 tie, infinities, denormals
+        pool = np.array([-0.0, 0.0, -np.inf, np.inf, 1e-40, -1e-40, 1.0, -1.0], np.float32)
+        v, k = pool[rng.integers(0, pool.size, (4, 12288))], 3000
+    elif case == "big_topk":           # topk above the candidate buffer
+        v, k = normal(2, 40000), 8000
+    elif case == "holes":
+        v, k = normal(4, 30000), 2048
+        holes = rng.random(v.shape) < 0.9
+    elif case == "under_cap":          # more valid than k but fewer than the buffer
+        v, k = normal(4, 8192), 2048
+        holes = rng.random(v.shape) < 0.4
+    elif case == "trend":              # scores rising with position
+        v = (np.arange(32768)[None, :] * 1e-3 + rng.standard_normal((3, 32768))).astype(np.float32)
+        k = 2048
+    elif case == "clustered":          # one dense cluster around the k-th value
+        v = (100.0 + 1e-3 * rng.standard_normal((3, 32768))).astype(np.float32)
+        k = 2048
+    else:
+        raise ValueError(case)
+    cand = np.broadcast_to(np.arange(v.shape[1], dtype=np.int32) + 1000, v.shape).copy()
+    if holes is not None:
+        cand[holes] = -1
+    return v, cand, k
+
+
+@pytest.mark.parametrize("case", ["normal_64k", "ties_64k", "few_values", "zeros_infs", "big_topk",
+                                  "holes", "under_cap", "trend", "clustered"])
+def test_topk_select_candidate_stress(sa, case):
+    rng = np.random.default_rng(11)
+    v, cand, k = _cand_case(case, rng)
+    ref_i, ref_v = oracle.topk_select_candidates(np.where(cand >= 0, v, -np.inf), cand, k)
+    idx, val = sa.topk_select(torch.from_numpy(v).to(DEV), k, cand_idx=torch.from_numpy(cand).to(DEV),
+                              with_values=True)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_i)
+    np.testing.assert_array_equal(val.cpu().numpy().view(np.uint32), ref_v.view(np.uint32))
+
+
+@pytest.mark.parametrize("ld", [2044, 2048, 2052, 4096, 6144, 6148, 16388])
+def test_topk_select_row_width_edges(sa, ld):
+    rng = np.random.default_rng(ld)
+    v = rng.standard_normal((3, ld)).astype(np.float32)
+    cand = np.broadcast_to(np.arange(ld, dtype=np.int32), v.shape).copy()
+    for k in (1, 2048, ld - 1):
+        ref_i, ref_v = oracle.topk_select_candidates(v, cand, k)
+        idx, val = sa.topk_select(torch.from_numpy(v).to(DEV), k, cand_idx=torch.from_numpy(cand).to(DEV),
+                                  with_values=True)
+        np.testing.assert_array_equal(idx.cpu().numpy(), ref_i, err_msg=f"k={k}")
+        np.testing.assert_array_equal(val.cpu().numpy(), ref_v, err_msg=f"k={k}")
+
+
+def test_topk_select_wide_block_mode_forced_own(sa):
+    # block_size 2 over 14000 rows: rows up to 7000 blocks wide, above the candidate buffer
+    T, B, k = 14000, 2, 2048
+    n_cols = (T - 1) // B + 1
+    rng = np.random.default_rng(5)
+    vals = torch.from_numpy(rng.standard_normal((T, n_cols)).astype(np.float32)).to(DEV)
+    idx, val = sa.topk_select(vals, k, block_size=B, force_own_block=True, with_values=True)
+    rows = sample_rows(T, 40, 9)
+    rows = np.union1d(rows, [2 * 6144 - 1, 2 * 6144, 2 * 6145, 2 * 2048, 2 * 2049 + 1])
+    sc = vals.cpu().numpy()[rows]
+    ref_i, ref_v = oracle.topk_select_dense(sc, k, block_size=B, force_own_block=True, rows=rows)
+    np.testing.assert_array_equal(idx.cpu().numpy()[rows], ref_i)
+    np.testing.assert_array_equal(val.cpu().numpy()[rows], ref_v)
+
+
 # ---------------------------------------------------------------------- indexer
 
 @pytest.mark.parametrize("name,T,B", [("tiny_fp32", None, 1), ("nope_unaligned", None, 1),
