@@ -14,6 +14,8 @@ materialised 32768 x 32768 causal score matrix against the HBM roofline, the
 block-routed sparse GQA workload, and the CPU oracle timed on a bounded sample.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+       python bench.py --counters            (one launch per kernel, for rocprofv3 --pmc)
+       python bench.py --write-traffic FETCH_DIR WRITE_DIR   (counters -> profiles/traffic.json)
 """
 from __future__ import annotations
 
@@ -110,6 +112,106 @@ def cpu_baseline(wl, x, m, idx_gpu, n_rows=1024):
     }
 
 
+COPY_ELEMS = 1 << 26                 # 256 MiB of fp32: the counter calibration copy
+
+
+def counters_pass():
+    """One launch of each measured kernel at the bench workload, for rocprofv3 --pmc.
+
+    First a plain elementwise copy of COPY_ELEMS fp32 values (out = in * 1), whose
+    FETCH_SIZE / WRITE_SIZE readings calibrate the counters against known bytes; then
+    the fused indexer + sparse MLA step once, then the standalone top-k select over
+    the materialised causal score matrix once.
+    """
+    import indexer_routed_sparse_amd as sa
+    import workloads
+    dev = torch.device("cuda:0")
+    src = torch.empty(COPY_ELEMS, dtype=torch.float32, device=dev).uniform_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    print("[counters] calibration copy", file=sys.stderr, flush=True)
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    wl = workloads.WORKLOADS["long_dsa"]
+    T, K, H = wl.T, 2048, wl.H
+    x = workloads.indexer_inputs(wl, device=dev)
+    m = workloads.mla_inputs(wl, device=dev)
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    print("[counters] fused indexer top-k + sparse MLA", file=sys.stderr, flush=True)
+    sa.sa_indexer_scores(x["q_I"], x["k_I"], x["w"], topk=K, out_idx=idx)
+    sa.sa_sparse_mla_fwd(m["q"], m["kv"], idx, wl.scale, out, lse)
+    torch.cuda.synchronize()
+    del out, lse
+    scores = torch.empty((T, T), dtype=torch.float32, device=dev)
+    sa.sa_indexer_scores(x["q_I"], x["k_I"], x["w"], scores=scores)
+    sel = torch.empty((T, K), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    print("[counters] top-k select on materialised scores", file=sys.stderr, flush=True)
+    sa.sa_topk_select(scores, sel)
+    torch.cuda.synchronize()
+    print("[counters] done", file=sys.stderr, flush=True)
+
+
+def _read_counters(path):
+    """{dispatch id: (kernel name, {counter: summed value})} from a rocprofv3 csv dir."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {path}")
+    disp = {}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                d = int(r["Dispatch_Id"])
+                name, ctr = disp.setdefault(d, (r["Kernel_Name"], {}))
+                ctr[r["Counter_Name"]] = ctr.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return disp
+
+
+def write_traffic(fetch_dir, write_dir, command):
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by the calibration copy and
+    store HBM bytes per launch of the measured kernels in profiles/traffic.json."""
+    fetch, write = _read_counters(fetch_dir), _read_counters(write_dir)
+
+    def per_kernel(disp, counter, match):
+        vals = [c.get(counter, 0.0) for d, (n, c) in sorted(disp.items()) if match(n)]
+        return vals
+
+    is_copy = lambda n: "Mul" in n and "elementwise" in n
+    true_kib = COPY_ELEMS * 4 / 1024.0
+    f_cal = true_kib / per_kernel(fetch, "FETCH_SIZE", is_copy)[0]
+    w_cal = true_kib / per_kernel(write, "WRITE_SIZE", is_copy)[0]
+    rec = {"calibration": {"copy_bytes": COPY_ELEMS * 4, "fetch_factor": round(f_cal, 4),
+                           "write_factor": round(w_cal, 4)},
+           "command": command}
+    groups = {
+        "sparse_mla_long_dsa": (lambda n: "sparse_mla_bf16_kernel" in n, ["sparse_mla.hip", "sa_common.h"], 1),
+        "indexer_topk_long_dsa": (lambda n: "indexer_kernel" in n, ["indexer.hip", "sa_common.h"], None),
+        "topk_select_long_dsa": (lambda n: "topk_pivot_kernel" in n or "topk_retry_kernel" in n,
+                                 ["topk_select.hip", "sa_common.h"], None),
+    }
+    for key, (match, srcs, _) in groups.items():
+        fv = per_kernel(fetch, "FETCH_SIZE", match)
+        wv = per_kernel(write, "WRITE_SIZE", match)
+        if not fv:
+            continue
+        if key == "indexer_topk_long_dsa":   # the fused call is the first indexer dispatch
+            fv, wv = fv[:1], wv[:1]
+        fb = sum(fv) * f_cal * 1024.0
+        wb = sum(wv) * w_cal * 1024.0
+        rec[key] = {"dispatches_per_call": len(fv), "fetch_bytes": round(fb),
+                    "write_bytes": round(wb), "hbm_bytes_per_launch": round(fb + wb),
+                    "source_digest": _src_digest(*srcs)}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,7 +219,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the top-k select and GQA legs")
+    ap.add_argument("--counters", action="store_true",
+                    help="one launch per measured kernel plus a calibration copy (for rocprofv3 --pmc)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc csv outputs of --counters into profiles/traffic.json")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic, command=" ".join(sys.argv))
+        return
+    if args.counters:
+        counters_pass()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the sharding design is described in DESIGN.md).", file=sys.stderr)
