@@ -171,7 +171,10 @@ sa_status sa_topk_select(const float* vals, const int32_t* cand_idx, int64_t ld,
  *
  * Inputs: q [T, H, d_qk], kv [S, d_qk] (dtype), idx [T, topk] int32 with values in
  *   [0, S) or -1. Outputs: out [T, H, d_v] (dtype), lse [T, H] fp32 (nullable).
- * Sizes: d_qk in {512, 576}; d_v == 512; H in [1, 128]; topk in [1, 4096] (bf16) or [1, 8192] (fp32); S >= 1.
+ * Sizes: d_qk in {512, 576}; d_v == 512; H in [1, 128]; S >= 1; topk in [1, 8192] for
+ *   fp32 and [1, 4096] for bf16, except [1, 3968] for bf16 with H > 64 and d_qk = 576
+ *   (the index row shares the workgroup's LDS with the gather stages); larger values
+ *   return SA_ERR_UNSUPPORTED.
  *   SA_BF16 needs H % 16 == 0 or H < 16 (heads are processed in groups of 32;
  *   partial groups are masked).
  */

@@ -123,6 +123,7 @@ sa_status sa_sparse_mla_fwd(const void* q, const void* kv, const int32_t* idx, i
   if (dtype == SA_BF16 && H >= 16 && H % 16 != 0) return SA_ERR_UNSUPPORTED;
   // the index row is staged in LDS (bf16) / the probabilities are (fp32)
   if (topk > (dtype == SA_BF16 ? 4096 : 8192)) return SA_ERR_UNSUPPORTED;
+  if (dtype == SA_BF16 && !sa::sparse_mla_bf16_fits(H, d_qk, topk)) return SA_ERR_UNSUPPORTED;
   if (T == 0) return SA_OK;
   if (!q || !kv || !idx || !out) return SA_ERR_NULL;
   if (!aligned16(q) || !aligned16(kv) || !aligned16(out)) return SA_ERR_ALIGN;

@@ -11,6 +11,8 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 
 #define SA_LDS __attribute__((address_space(3)))
 
@@ -75,6 +77,13 @@ SA_DEVICE uint32_t wave_incl_scan(uint32_t x) {
     if (l >= off) x += y;
   }
   return x;
+}
+
+// The values of lane i mod 32 and lane i mod 32 + 32 of `x`, in every lane i (one
+// v_permlane32_swap, no LDS round trip): .x from the lower half, .y from the upper.
+SA_DEVICE float2_t lane_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return (float2_t){__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
 
 SA_DEVICE float wave_max(float x) {

@@ -13,6 +13,9 @@ hipError_t launch_topk_select(const float* vals, const int32_t* cand, int64_t ld
                               int force_own, int32_t* out_idx, float* out_val, hipStream_t st);
 
 // sparse_mla.hip
+// Whether the bf16 kernel's LDS (gather stages, q slices, P exchange, index row)
+// fits one workgroup for this head count, width and top-k.
+bool sparse_mla_bf16_fits(int H, int d_qk, int topk);
 hipError_t launch_sparse_mla(const void* q, const void* kv, const int32_t* idx, bool bf16, int T,
                              int S, int H, int d_qk, int d_v, int topk, float scale, void* out,
                              float* lse, hipStream_t st);

@@ -6,24 +6,31 @@
 // scale * q[t,h,:] . kv[idx[t,j], :] (d_qk = 576 or 512 channels), weights applied
 // to kv[idx[t,j], 0:512]; -1 slots are masked; the caller's scale is used as given.
 //
-// bf16 kernel (gfx950), one workgroup per query token, NW waves of 32 heads each:
-//   * the token's q is held in registers as the B operand of S^T = K . Q^T
-//     (32x32x16 bf16 MFMA: rows = keys, columns = heads), loaded once;
-//   * the selected latent rows of a BK-key tile are gathered straight from HBM/L2
+// bf16 kernel (gfx950), one workgroup per query token, NW = ceil(H / 32) waves:
+//   * logits: wave w computes S^T = K . Q^T for heads [32w, 32w+32) (32x32x16 bf16
+//     MFMA, rows = keys, columns = heads); the token's q slices are its B operands,
+//     loaded once and held in VGPRs and LDS;
+//   * the selected latent rows of a 32-key tile are gathered straight from HBM/L2
 //     into LDS with 16-byte global_load_lds (no register staging), double
 //     buffered: the gather of tile n+1 is in flight while tile n is computed;
 //   * the LDS tile is row-major with an XOR swizzle of the 16-byte chunks so that
 //     both the K reads (ds_read_b128) and the V reads are free of bank conflicts;
-//   * P = exp2(S - m) stays in registers: the S^T accumulator layout is already the
-//     A-operand layout of P . V up to a permutation of keys inside a tile, and V's
-//     B operand is read with the same key permutation through the gfx950 LDS
-//     transpose load (ds_read_b64_tr_b16) from the row-major tile;
-//   * online softmax with lazy rescaling: the running max only moves when a head's
-//     tile max exceeds it by more than 2^8, so the O rescale (a cross-lane shuffle
-//     of the factors) is rare;
+//   * P = exp2(S - m) is packed to bf16 in the A-operand layout of P . V: the S^T
+//     accumulator layout already is that layout up to a permutation of keys inside
+//     the tile. Each wave publishes its 32 heads' P in LDS;
+//   * values: wave w accumulates O for ALL heads over output channels
+//     [512w/NW, 512(w+1)/NW), so every V element is read from LDS once per tile (the
+//     gfx950 transposing read ds_read_b64_tr_b16, same key permutation as P) instead
+//     of once per wave; the transposing read is the slowest LDS path, and this
+//     split cuts its traffic by NW;
+//   * softmax with a fixed per-head reference: the first tile's max; a later tile
+//     max above it by more than 2^16 restarts the pass with the largest max seen, so
+//     O is never rescaled;
 //   * fp32 accumulation throughout; no atomics, so results are bitwise
 //     reproducible.
 // A plain fp32 kernel serves fp32 inputs.
+#include <type_traits>
+
 #include "sa_common.h"
 #include "sa_kernels.h"
 
@@ -64,11 +71,14 @@ constexpr int mla_tile_bytes() { return kBK * 64 * 16 + (DQK == 576 ? kBK * 8 * 
 template <int NW, int DQK, int NST, int NKL>
 constexpr size_t mla_lds_bytes(int topk) {
   return (size_t)NST * mla_tile_bytes<DQK>() + (size_t)NKL * NW * 64 * 16 +
-         (size_t)((topk + kBK - 1) / kBK) * kBK * 4;
+         (size_t)NW * 2 * 64 * 16 + (size_t)NW * 32 * 4 + (size_t)((topk + kBK - 1) / kBK) * kBK * 4;
 }
 
-// NW waves of 32 heads; NST gather stages; NKL k-steps of q held in LDS (the rest
-// in VGPRs).
+// NW waves. Wave w computes the logits and probabilities of heads [32w, 32w+32)
+// (S^T = K . Q^T, its q slices held as B operands: NKL k-steps in LDS, the rest in
+// VGPRs) and publishes its P tile in LDS; then every wave accumulates O for ALL
+// heads over its own 512/NW output channels, so each V element is read from LDS
+// by one wave only. NST gather stages.
 template <int NW, int DQK, int NST, int NKL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
@@ -77,22 +87,25 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
   constexpr int NK = DQK / 16;            // MFMA k-steps of S^T = K . Q^T
   constexpr int NKM = 32;                 // k-steps in the main region
   constexpr int NKR = NK - NKL;           // k-steps whose q slices stay in VGPRs
-  constexpr int NDV = 512 / 32;           // 32-wide dv tiles of O
+  constexpr int NDB = 16 / NW;            // 32-wide dv blocks owned by each wave
+  constexpr int NACC = NW * NDB;          // O accumulators per wave (always 16)
   constexpr bool ROPE = DQK == 576;
   constexpr int TILE_BYTES = mla_tile_bytes<DQK>();
   constexpr int ROPE_OFF = kBK * 64 * 16;
   constexpr int MAIN_PER_WAVE = kBK / NW;               // one DMA per row
   constexpr int ROPE_PER_WAVE = ROPE ? 4 / NW + (4 % NW ? 1 : 0) : 0;
   constexpr int DA = 4;                   // K-operand prefetch distance (k-steps)
-  constexpr int DV = 4;                   // V-operand prefetch distance (MFMAs)
   static_assert(NW == 1 || NW == 2 || NW == 4, "waves");
+  static_assert(NACC == 16, "accumulators");
   // fp32 P values stay below 2^16 times the reference; a larger tile max restarts
   constexpr float kThr = 16.0f;
 
   extern __shared__ __attribute__((aligned(16))) char lds[];
   char* tiles = lds;                                           // NST tiles
   char* s_q = lds + NST * TILE_BYTES;                          // [NKL][NW*64] x 16 B
-  int32_t* s_idx = reinterpret_cast<int32_t*>(s_q + NKL * NW * 64 * 16);  // [ntiles*32]
+  char* s_p = s_q + NKL * NW * 64 * 16;                        // [NW][2][64] x 16 B
+  float* s_inv = reinterpret_cast<float*>(s_p + NW * 2 * 64 * 16);       // [NW*32]
+  int32_t* s_idx = reinterpret_cast<int32_t*>(s_inv + NW * 32);          // [ntiles*32]
   __shared__ int s_restart;
 
   const int t = blockIdx.x;
@@ -154,49 +167,58 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
   }
   __syncthreads();
 
-  auto gather = [&](int tile) {
-    const uint32_t base = (uint32_t)(uintptr_t)(SA_LDS char*)(tiles + (tile % NST) * TILE_BYTES);
+  // Gather of one tile: this wave's MAIN_PER_WAVE row DMAs (1 KiB each: channels
+  // 0..511 of row R = w + NW j) and ROPE_PER_WAVE RoPE DMAs (channels 512..575 of
+  // 8 rows each). gather_rows() reads the row indices from LDS; gather_dma(j) issues
+  // DMA j. The DMAs of the next tile are spread over the logit MFMAs, so the wave
+  // never stalls on a burst of memory instructions.
+  constexpr int ND = MAIN_PER_WAVE + ROPE_PER_WAVE;
+  struct Rows { int main[MAIN_PER_WAVE]; int rope[ROPE_PER_WAVE > 0 ? ROPE_PER_WAVE : 1]; };
+  auto gather_rows = [&](int tile) {
+    Rows r;
     const int32_t* ir = s_idx + tile * kBK;
-    // all row indices of this wave's DMAs first: one LDS round trip, not one per DMA
-    int rows[MAIN_PER_WAVE];
-    int rrows[ROPE_PER_WAVE > 0 ? ROPE_PER_WAVE : 1];
 #pragma unroll
-    for (int j = 0; j < MAIN_PER_WAVE; ++j) rows[j] = ir[w + NW * j];
+    for (int j = 0; j < MAIN_PER_WAVE; ++j) r.main[j] = __builtin_amdgcn_readfirstlane(ir[w + NW * j]);
     if constexpr (ROPE) {
 #pragma unroll
       for (int j = 0; j < ROPE_PER_WAVE; ++j) {
         const int ii = w + NW * j;
-        rrows[j] = ii < 4 ? ir[8 * ii + (L >> 3)] : 0;
+        r.rope[j] = ii < 4 ? ir[8 * ii + (L >> 3)] : 0;
       }
     }
-#pragma unroll
-    for (int j = 0; j < MAIN_PER_WAVE; ++j) {
+    return r;
+  };
+  auto gather_dma = [&](int tile, const Rows& r, int j) {
+    const uint32_t base = (uint32_t)(uintptr_t)(SA_LDS char*)(tiles + (tile % NST) * TILE_BYTES);
+    if (j < MAIN_PER_WAVE) {
       const int R = w + NW * j;                       // wave-uniform row
-      int row = __builtin_amdgcn_readfirstlane(rows[j]);
+      int row = r.main[j < MAIN_PER_WAVE ? j : 0];
       row = row < 0 ? 0 : row;   // masked slot: any finite row keeps P*V finite
       lds_dma16(base + R * 1024, kv + (int64_t)row * DQK, (uint32_t)((L ^ swz_main(R)) * 16));
-    }
-    if constexpr (ROPE) {
-#pragma unroll
-      for (int j = 0; j < ROPE_PER_WAVE; ++j) {
-        const int ii = w + NW * j;                    // rope instruction: rows 8ii..8ii+7
-        if (ii < 4) {
-          const int R = 8 * ii + (L >> 3);
-          const int row = rrows[j] < 0 ? 0 : rrows[j];
-          const int c = (L & 7) ^ swz_rope(R);
-          lds_dma16(base + ROPE_OFF + ii * 1024, kv, (uint32_t)(row * (DQK * 2) + 1024 + 16 * c));
-        }
+    } else if constexpr (ROPE) {
+      const int jr = j - MAIN_PER_WAVE;
+      const int ii = w + NW * jr;                     // rope instruction: rows 8ii..8ii+7
+      if (ii < 4) {
+        const int R = 8 * ii + (L >> 3);
+        const int rr = r.rope[jr < ROPE_PER_WAVE ? jr : 0];
+        const int row = rr < 0 ? 0 : rr;
+        const int c = (L & 7) ^ swz_rope(R);
+        lds_dma16(base + ROPE_OFF + ii * 1024, kv, (uint32_t)(row * (DQK * 2) + 1024 + 16 * c));
       }
     }
   };
+  auto gather = [&](int tile) {
+    const Rows r = gather_rows(tile);
+#pragma unroll
+    for (int j = 0; j < ND; ++j) gather_dma(tile, r, j);
+  };
 
-  // O for dv tiles 0..NDV-3 lives in MFMA accumulators (AGPRs, 224 registers);
-  // the last two dv tiles are accumulated per key tile into a temporary and then
-  // added into O_tail (VGPRs). With the S tile and the temporary this keeps the
-  // accumulator file within its 256 registers.
-  constexpr int NOA = NDV - 2;             // dv tiles accumulated in AGPRs
-  floatx16_t O[NOA];
-  floatx16_t O_tail[NDV - NOA];
+  // O[hb * NDB + db]: heads [32hb, 32hb+32) x channels 32(NDB w + db) + [0, 32).
+  // With one wave, the last two accumulators are summed per key tile in a temporary
+  // (the S registers) and added into VGPRs, which keeps the 16 accumulators, S and
+  // the operands within the register file without spilling.
+  constexpr int NOA = NW == 1 ? NACC - 2 : NACC;
+  floatx16_t O[NACC];
   float m_ref = -__builtin_huge_valf();   // softmax reference (log2 units), per head
   float m_seen = -__builtin_huge_valf();
   float l_run = 0.0f;
@@ -204,9 +226,7 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll 1
   for (;;) {   // one pass over the tiles; repeated only if a tile max outgrows m_ref
 #pragma unroll
-    for (int i = 0; i < NOA; ++i) O[i] = floatx16_t{};
-#pragma unroll
-    for (int i = 0; i < NDV - NOA; ++i) O_tail[i] = floatx16_t{};
+    for (int i = 0; i < NACC; ++i) O[i] = floatx16_t{};
     l_run = 0.0f;
 #pragma unroll
     for (int p = 0; p < NST - 1; ++p)
@@ -218,9 +238,13 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
       if (newer >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * (MAIN_PER_WAVE + ROPE_PER_WAVE)));
       else if (newer == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(MAIN_PER_WAVE + ROPE_PER_WAVE));
       else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-      __syncthreads();               // tile resident in all waves' view
-      if (tile + NST - 1 < ntiles) gather(tile + NST - 1);   // its stage was read in tile-1
-      const uint64_t vmask = ballot(L < kBK && s_idx[tile * kBK + (L & (kBK - 1))] >= 0);
+      __syncthreads();               // tile resident in all waves' view; P of tile-1 consumed
+      // the next gather goes to the stage read in tile-1; its DMAs ride along the
+      // logit MFMAs below
+      const int gtile = tile + NST - 1;
+      const bool do_gather = gtile < ntiles;
+      const Rows grows = gather_rows(do_gather ? gtile : tile);
+      const int my_slot = s_idx[tile * kBK + (L & (kBK - 1))];   // consumed after S
       const char* tb = tiles + (tile % NST) * TILE_BYTES;
 
       // ---- S^T = K . Q^T over d_qk, K slices prefetched DA k-steps ahead
@@ -234,54 +258,90 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
       };
       floatx16_t S = floatx16_t{};
       {
-        bf16x8_t ring[DA];
+        // K slices and the LDS-held q slices are both read DA k-steps ahead of use
+        bf16x8_t ring[DA], qring[DA];
 #pragma unroll
-        for (int i = 0; i < DA; ++i) ring[i] = a_at(i);
+        for (int i = 0; i < DA; ++i) {
+          ring[i] = a_at(i);
+          if (i >= NKR) qring[i] = q_at(i);
+        }
 #pragma unroll
         for (int n = 0; n < NK; ++n) {
           const bf16x8_t a = ring[n % DA];
-          const bf16x8_t b = q_at(n);
-          if (n + DA < NK) ring[n % DA] = a_at(n + DA);
+          const bf16x8_t b = n < NKR ? qv[n < NKR ? n : 0] : qring[n % DA];
+          if (n + DA < NK) {
+            ring[n % DA] = a_at(n + DA);
+            if (n + DA >= NKR) qring[n % DA] = q_at(n + DA);
+          }
           S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, S, 0, 0, 0);
+#pragma unroll
+          for (int j = 0; j < ND; ++j)
+            if ((j * NK) / ND == n && do_gather) gather_dma(gtile, grows, j);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
 
-      // ---- masked logits (log2 units), tile max per head, reference update
-      float mx = -__builtin_huge_valf();
+      // ---- logits in log2 units, tile max per head, reference update, then P (bf16,
+      //      round to nearest even) in the A-operand layout of P . V (keys permuted
+      //      inside the tile: half m holds S slots 8m..8m+7), published for every
+      //      wave. A tile whose 32 slots are all valid (wave-uniform test) skips the
+      //      masking; scaling is monotone, so the max of the scaled logits is the
+      //      scaled max (or min, for a negative scale). Both variants are emitted
+      //      whole, so the compiler keeps a uniform branch instead of computing both.
+      const uint64_t vmask = ballot(L < kBK && my_slot >= 0);
+      auto softmax = [&](auto full_t) {
+        constexpr bool FULL = decltype(full_t)::value;
+        float mx;
+        uint32_t okbits = 0xFFFFu;          // bit sg: slot sg of this lane is valid
+        if constexpr (FULL) {
+          float hi = S[0], lo = S[0];
 #pragma unroll
-      for (int sg = 0; sg < 16; ++sg) {
-        const int key = 8 * (sg >> 2) + 4 * hl + (sg & 3);
-        const bool ok = (vmask >> key) & 1ull;
-        const float v = ok ? S[sg] * scale_log2 : -__builtin_huge_valf();
-        S[sg] = v;
-        mx = fmaxf(mx, v);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      m_seen = fmaxf(m_seen, mx);
-      if (m_ref == -__builtin_huge_valf()) m_ref = mx;   // first valid tile (O, l still 0)
-      if (mx > m_ref + kThr) s_restart = 1;               // seen by all after the pass
-      const float m_use = (m_ref == -__builtin_huge_valf()) ? 0.0f : m_ref;
-
-      // ---- P (bf16) as A operands: half m -> slots 8m..8m+7 of S
-      bf16x8_t P[2];
+          for (int sg = 1; sg < 15; sg += 2) {
+            hi = __builtin_elementwise_maximum(__builtin_elementwise_maximum(hi, S[sg]), S[sg + 1]);
+            lo = __builtin_elementwise_minimum(__builtin_elementwise_minimum(lo, S[sg]), S[sg + 1]);
+          }
+          hi = __builtin_elementwise_maximum(hi, S[15]);
+          lo = __builtin_elementwise_minimum(lo, S[15]);
+          mx = (scale_log2 >= 0.0f ? hi : lo) * scale_log2;
+        } else {
+          okbits = 0;
+          mx = -__builtin_huge_valf();
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        uint32_t pk[4];
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(S[8 * m + e] - m_use);
-          const float p1 = __builtin_amdgcn_exp2f(S[8 * m + e + 1] - m_use);
-          l_run += p0 + p1;
-          pk[e >> 1] = pack_bf16x2(p0, p1);
+          for (int sg = 0; sg < 16; ++sg) {
+            const int key = 8 * (sg >> 2) + 4 * hl + (sg & 3);
+            const bool ok = (vmask >> key) & 1ull;
+            okbits |= ok ? 1u << sg : 0u;
+            mx = __builtin_elementwise_maximum(mx, ok ? S[sg] * scale_log2 : -__builtin_huge_valf());
+          }
         }
-        P[m] = __builtin_bit_cast(bf16x8_t, pk);
-      }
-
-      // ---- O += P . V (V from the row-major tile through transpose reads),
-      //      B slices prefetched DV MFMAs ahead
-      auto v_at = [&](int st) {
-        const int nt = st >> 1, m = st & 1;
+        const float2_t mh = lane_halves(mx);
+        mx = __builtin_elementwise_maximum(mh.x, mh.y);
+        m_seen = __builtin_elementwise_maximum(m_seen, mx);
+        if (m_ref == -__builtin_huge_valf()) m_ref = mx;   // first valid tile (O, l still 0)
+        if (mx > m_ref + kThr) s_restart = 1;               // seen by all after the pass
+        const float m_use = (m_ref == -__builtin_huge_valf()) ? 0.0f : m_ref;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          float pf[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = fmaf(S[8 * m + e], scale_log2, -m_use);
+            pf[e] = __builtin_amdgcn_exp2f(FULL || ((okbits >> (8 * m + e)) & 1u) ? x : -__builtin_huge_valf());
+            l_run += pf[e];
+          }
+          bf16x2_t pk[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pk[e] = __builtin_convertvector((float2_t){pf[2 * e], pf[2 * e + 1]}, bf16x2_t);
+          *reinterpret_cast<bf16x8_t*>(s_p + ((w * 2 + m) * 64 + L) * 16) = __builtin_bit_cast(bf16x8_t, pk);
+        }
+      };
+      if ((uint32_t)vmask == 0xFFFFFFFFu) softmax(std::true_type{});
+      else softmax(std::false_type{});
+      // ---- O[hb][db] += P[hb] . V[:, dv block NDB w + db]; V's B operand is read
+      //      with the same key permutation through the LDS transpose read. The first
+      //      V operands do not depend on P and are read before the barrier.
+      auto v_at = [&](int m, int nt) {
         const int off = m * (16 * 1024) + (nt >> 2) * 256;
         const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(tb + off + v_off[0][nt & 3]));
         const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(tb + off + v_off[1][nt & 3]));
@@ -289,22 +349,35 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
                                                               hi[0], hi[1], hi[2], hi[3]};
         return __builtin_bit_cast(bf16x8_t, b8);
       };
+      constexpr int NB = 2 * NDB;          // B operands per tile, order (db, m)
+      constexpr int DV = NW == 1 ? 2 : 4;  // prefetch distance
+      bf16x8_t ring[DV];
+#pragma unroll
+      for (int i = 0; i < DV; ++i) ring[i] = v_at(i & 1, NDB * w + (i >> 1));
+      __syncthreads();               // every wave's P tile visible
+      bf16x8_t Pa[NW][2];
+#pragma unroll
+      for (int hb = 0; hb < NW; ++hb)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          Pa[hb][m] = *reinterpret_cast<const bf16x8_t*>(s_p + ((hb * 2 + m) * 64 + L) * 16);
       {
-        bf16x8_t ring[DV];
 #pragma unroll
-        for (int i = 0; i < DV; ++i) ring[i] = v_at(i);
-#pragma unroll
-        for (int st = 0; st < 2 * NDV; ++st) {
-          const int nt = st >> 1, m = st & 1;
+        for (int st = 0; st < NB; ++st) {
+          const int db = st >> 1, m = st & 1;
           const bf16x8_t b = ring[st % DV];
-          if (st + DV < 2 * NDV) ring[st % DV] = v_at(st + DV);
-          if (nt < NOA) {
-            O[nt < NOA ? nt : 0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(P[m], b, O[nt < NOA ? nt : 0], 0, 0, 0);
-          } else if (m == 0) {
-            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(P[0], b, floatx16_t{}, 0, 0, 0);
-          } else {
-            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(P[1], b, S, 0, 0, 0);
-            O_tail[nt >= NOA ? nt - NOA : 0] += S;
+          if (st + DV < NB) ring[st % DV] = v_at((st + DV) & 1, NDB * w + ((st + DV) >> 1));
+#pragma unroll
+          for (int hb = 0; hb < NW; ++hb) {
+            const int a = hb * NDB + db;
+            if (a < NOA) {
+              O[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Pa[hb][m], b, O[a], 0, 0, 0);
+            } else if (m == 0) {
+              S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Pa[hb][0], b, floatx16_t{}, 0, 0, 0);
+            } else {
+              S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Pa[hb][1], b, S, 0, 0, 0);
+              O[a] += S;
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -320,24 +393,26 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     m_ref = m_seen;
   }
 
-  // ---- epilogue: normalise, write bf16 out and lse
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  // ---- epilogue: per-head 1/l through LDS, normalise, write bf16 out and lse
+  const float2_t lh = lane_halves(l_run);
+  const float l_tot = lh.x + lh.y;
+  if (hl == 0) s_inv[head] = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (lse && hl == 0 && head_ok) {
     lse[(int64_t)t * H + head] =
         l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : -__builtin_huge_valf();
   }
+  __syncthreads();
   uint16_t* __restrict__ orow = out + (int64_t)t * H * 512;
 #pragma unroll
-  for (int sg = 0; sg < 16; ++sg) {
-    const int hi = 8 * (sg >> 2) + 4 * hl + (sg & 3);
-    const float a = __shfl(inv, hi, 64);
-    const int hh = 32 * w + hi;
-    if (hh < H) {
+  for (int hb = 0; hb < NW; ++hb) {
 #pragma unroll
-      for (int nt = 0; nt < NDV; ++nt) {
-        const float o = nt < NOA ? O[nt < NOA ? nt : 0][sg] : O_tail[nt >= NOA ? nt - NOA : 0][sg];
-        orow[(int64_t)hh * 512 + 32 * nt + (L & 31)] = f2bf_bits(o * a);
+    for (int sg = 0; sg < 16; ++sg) {
+      const int hh = 32 * hb + 8 * (sg >> 2) + 4 * hl + (sg & 3);
+      if (hh < H) {
+        const float a = s_inv[hh];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          orow[(int64_t)hh * 512 + 32 * (NDB * w + db) + (L & 31)] = f2bf_bits(O[hb * NDB + db][sg] * a);
       }
     }
   }
@@ -399,13 +474,26 @@ __global__ __launch_bounds__(NT) void sparse_mla_f32_kernel(
 }
 
 constexpr int kStages = 2;
-constexpr int kQInLds = 16;
+constexpr size_t kLdsLimit = 160 * 1024;
+
+// k-steps of q kept in LDS (the rest stay in VGPRs): one wave has LDS to spare and
+// keeps all of q there; two waves keep 20 k-steps there, four waves 16 (the most
+// that leaves two gather stages and a 2048-slot index row in 160 KiB).
+template <int NW, int DQK>
+constexpr int q_in_lds() { return NW == 1 ? DQK / 16 : (NW == 2 ? 20 : 16); }
+
+template <int NW, int DQK>
+size_t lds_bytes(int topk) { return mla_lds_bytes<NW, DQK, kStages, q_in_lds<NW, DQK>()>(topk); }
+
+int waves_for(int H) { return H <= 32 ? 1 : (H <= 64 ? 2 : 4); }
 
 template <int NW, int DQK>
 hipError_t launch_bf16(const void* q, const void* kv, const int32_t* idx, int T, int H, int topk,
                        float scale, void* out, float* lse, hipStream_t st) {
-  const size_t shm = mla_lds_bytes<NW, DQK, kStages, kQInLds>(topk);
-  auto kern = sparse_mla_bf16_kernel<NW, DQK, kStages, kQInLds>;
+  constexpr int NKL = q_in_lds<NW, DQK>();
+  const size_t shm = mla_lds_bytes<NW, DQK, kStages, NKL>(topk);
+  if (shm > kLdsLimit) return hipErrorInvalidValue;
+  auto kern = sparse_mla_bf16_kernel<NW, DQK, kStages, NKL>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(T), dim3(NW * 64), shm, st, (const uint16_t*)q, (const uint16_t*)kv,
@@ -416,12 +504,24 @@ hipError_t launch_bf16(const void* q, const void* kv, const int32_t* idx, int T,
 template <int DQK>
 hipError_t dispatch_bf16(const void* q, const void* kv, const int32_t* idx, int T, int H,
                          int topk, float scale, void* out, float* lse, hipStream_t st) {
-  if (H <= 32) return launch_bf16<1, DQK>(q, kv, idx, T, H, topk, scale, out, lse, st);
-  if (H <= 64) return launch_bf16<2, DQK>(q, kv, idx, T, H, topk, scale, out, lse, st);
-  return launch_bf16<4, DQK>(q, kv, idx, T, H, topk, scale, out, lse, st);
+  switch (waves_for(H)) {
+    case 1: return launch_bf16<1, DQK>(q, kv, idx, T, H, topk, scale, out, lse, st);
+    case 2: return launch_bf16<2, DQK>(q, kv, idx, T, H, topk, scale, out, lse, st);
+    default: return launch_bf16<4, DQK>(q, kv, idx, T, H, topk, scale, out, lse, st);
+  }
 }
 
 }  // namespace
+
+bool sparse_mla_bf16_fits(int H, int d_qk, int topk) {
+  size_t b;
+  switch (waves_for(H)) {
+    case 1: b = d_qk == 576 ? lds_bytes<1, 576>(topk) : lds_bytes<1, 512>(topk); break;
+    case 2: b = d_qk == 576 ? lds_bytes<2, 576>(topk) : lds_bytes<2, 512>(topk); break;
+    default: b = d_qk == 576 ? lds_bytes<4, 576>(topk) : lds_bytes<4, 512>(topk); break;
+  }
+  return b <= kLdsLimit;
+}
 
 hipError_t launch_sparse_mla(const void* q, const void* kv, const int32_t* idx, bool bf16, int T,
                              int S, int H, int d_qk, int d_v, int topk, float scale, void* out,
