@@ -187,8 +187,9 @@ sa_status sa_sparse_mla_fwd(const void* q, const void* kv, const int32_t* idx, i
  *
  * [QSA] "Describe the solution you'd like": sparse GQA attention over the blocks
  * chosen by the exact block TopK. For query t (sequence start c) and head h, the
- * keys are every s <= t with local block (s - c) / block_size equal to a slot of
- * blk[t, :] (slot -1 skipped; each slot counts once); head h reads kv head
+ * attended keys are the set of s <= t whose local block (s - c) / block_size appears
+ * among the slots of blk[t, :]; -1 slots and blocks past the query's own block add
+ * nothing, and a block listed twice contributes its keys once. Head h reads kv head
  * g = h / (Hq / Hkv):
  *
  *     out[t,h,:] = softmax_s(scale * q[t,h,:] . k[s,g,:]) @ v[s,g,:]
@@ -199,7 +200,7 @@ sa_status sa_sparse_mla_fwd(const void* q, const void* kv, const int32_t* idx, i
  *   local block ids in [0, ceil(len/block_size)) or -1. Outputs: out [T, Hq, Dv]
  *   (dtype), lse [T, Hq] fp32 (nullable).
  * Sizes: D == Dv == 128 or 64; Hq % Hkv == 0; Hq / Hkv <= 16; block_size a multiple
- *   of 16 up to 128; nblk >= 1.
+ *   of 16 up to 128; nblk in [1, 64].
  */
 sa_status sa_block_sparse_gqa_fwd(const void* q, const void* k, const void* v,
                                   const int32_t* blk, int dtype, int32_t T,

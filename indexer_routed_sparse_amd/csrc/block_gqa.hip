@@ -2,14 +2,30 @@
 //
 // Operation ("Add trainable QSA sparse attention with a TileLang backend", section
 // "Describe the solution you'd like": sparse GQA attention over the blocks picked by
-// the exact block TopK): query t attends to every causal key of the blocks listed in
-// blk[t, :] (local block ids of its sequence, -1 skipped); head h uses kv head
-// h / (Hq / Hkv).
+// the exact block TopK): query t attends to the set of causal keys s <= t whose local
+// block (s - start(t)) / B is listed in blk[t, :] (local block ids of its sequence;
+// -1 and blocks past the query's own are skipped; a block listed twice counts once);
+// head h uses kv head h / (Hq / Hkv).
 //
-// One workgroup per (token, kv head): the group's q rows stay in LDS, each selected
-// block's keys and values are staged in LDS as fp32, and an online softmax (running
-// max per head, exp2 domain) accumulates the output in registers. fp32 arithmetic
-// throughout, no atomics.
+// bf16 kernel (gfx950): one wave per (token, kv head), four independent waves per
+// workgroup. Routes differ from token to token, so the work is a gather: every wave
+// streams the keys and values of its own blocks, and the kernel is bound by the
+// L2/MALL -> CU bandwidth of those gathers, not by the matrix cores.
+//   * the wave's G <= 16 query heads are the 16 columns of 16x16x32 bf16 MFMAs:
+//     S^T = K . Q^T (rows = 16 keys), then O^T = V^T . P^T (rows = 16 value
+//     channels), so each lane owns one query head's softmax state and output column
+//     and every rescale is lane-local;
+//   * the route becomes a list of 32-key sub-tiles (one block = B/32 of them, the own
+//     block cut at the query); key and value rows of a sub-tile are loaded straight
+//     into VGPRs two sub-tiles ahead (no LDS on the load path), so many waves keep
+//     many gathers in flight;
+//   * K rows are the A operand as loaded; V rows are written to a per-wave LDS stage
+//     and read back transposed with ds_read_b64_tr_b16, in the key order of the S^T
+//     accumulator, which is P^T's operand layout;
+//   * online softmax in exp2 form, fp32 accumulation, no atomics.
+// fp32 inputs use a plain scalar kernel with the same definition.
+#include <type_traits>
+
 #include "sa_common.h"
 #include "sa_kernels.h"
 
@@ -18,25 +34,240 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kMaxRoute = 64;            // blocks per query row (API limit)
+constexpr int kWavesPerGroup = 4;
+
+typedef float floatx4v_t __attribute__((ext_vector_type(4)));
+
+// lanes (i mod 16) + 16 r, r = 0..3, hold the same query head: reductions over them
+SA_DEVICE float2_t lane_rows16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return (float2_t){__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+SA_DEVICE float head_max(float x) {
+  const float2_t a = lane_rows16(x);
+  const float y = __builtin_elementwise_maximum(a.x, a.y);
+  const float2_t b = lane_halves(y);
+  return __builtin_elementwise_maximum(b.x, b.y);
+}
+SA_DEVICE float head_sum(float x) {
+  const float2_t a = lane_rows16(x);
+  const float y = a.x + a.y;
+  const float2_t b = lane_halves(y);
+  return b.x + b.y;
+}
+
+// Per-wave LDS: value stage of one sub-tile (32 rows x D bf16, 16-byte chunks XOR-
+// swizzled by 2 (row mod 8) so that the transposed reads of 16 rows x 32 bytes spread
+// over the banks) and the wave's sub-tile list.
+template <int D>
+constexpr int stage_bytes() { return 32 * D * 2; }
+constexpr int kListMax = kMaxRoute * 4;  // sub-tiles per row: B <= 128 -> 4 per block
+template <int D>
+constexpr int wave_lds_bytes() { return stage_bytes<D>() + kListMax * 8; }
+
+template <int D>
+SA_DEVICE int vswz(int row) { return D == 128 ? 2 * (row & 7) : 2 * (row & 3); }
+
+template <int D>
+__global__ __launch_bounds__(kWavesPerGroup * 64) void block_gqa_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ blk, const int32_t* __restrict__ cu, int nseq, int T, int Hq,
+    int Hkv, int B, int nblk, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  constexpr int KS = D / 32;             // 32-wide k-steps of S^T
+  constexpr int CPR = D * 2 / 16;        // 16-byte chunks per row
+  constexpr int VL = 32 * CPR / 64;      // 16-byte value loads per lane per sub-tile
+  constexpr int NDT = D / 16;            // 16-row value-channel tiles of O^T
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int w = threadIdx.x >> 6;
+  const int L = threadIdx.x & 63;
+  const int unit = blockIdx.x * kWavesPerGroup + w;     // (token, kv head) pair
+  if ((int64_t)unit >= (int64_t)T * Hkv) return;       // whole wave leaves together
+  const int t = unit / Hkv;
+  const int g = unit - t * Hkv;
+  const int G = Hq / Hkv;
+  char* stage = lds + w * wave_lds_bytes<D>();
+  int2* list = reinterpret_cast<int2*>(stage + stage_bytes<D>());
+  const int c = cu ? seq_start_of(cu, nseq, t) : 0;
+  const int own = (t - c) / B;
+
+  // ---- route -> sub-tile list (s0, nkeys), in slot order; a repeated block is
+  //      skipped at its later slots
+  int nsub = 0;
+  for (int base = 0; base < nblk; base += 64) {
+    const int j = base + L;
+    const int b = j < nblk ? blk[(int64_t)t * nblk + j] : -1;
+    bool ok = b >= 0 && b <= own;
+    for (int i = 0; i < nblk; ++i) {                     // earlier slot with the same block?
+      if (i >= j) break;
+      ok = ok && blk[(int64_t)t * nblk + i] != b;
+    }
+    const int lo = c + b * B;
+    const int nk = ok ? min(B, t - lo + 1) : 0;
+    const int ns = (nk + 31) >> 5;
+    const uint32_t incl = wave_incl_scan((uint32_t)ns);
+    const int pos = nsub + (int)incl - ns;
+    for (int h = 0; h < ns; ++h) list[pos + h] = make_int2(lo + 32 * h, min(32, nk - 32 * h));
+    nsub += __shfl((int)incl, 63, 64);
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  // ---- q^T as B operands: column n = L & 15 (query head g*G + n), dims 32ks + 8(L>>4)
+  const int n = L & 15;
+  const int quad = L >> 4;
+  const bool head_ok = n < G;
+  bf16x8_t qb[KS];
+  {
+    const uint16_t* qr = q + ((int64_t)t * Hq + g * G + (head_ok ? n : 0)) * D + 8 * quad;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(qr + 32 * ks);
+      qb[ks] = head_ok ? x : bf16x8_t{};
+    }
+  }
+
+  // ---- loads of one sub-tile into registers
+  struct Tile {
+    bf16x8_t k[2][KS];     // A operands: key 16kt + (L&15), dims 32ks + 8(L>>4)
+    bf16x8_t v[VL];        // value rows: chunk p = 64 j + L is row p / CPR, chunk p % CPR
+  };
+  auto load = [&](int i, Tile& tl) {
+    const int2 e = list[i < nsub ? i : 0];
+    const int s0 = e.x, nk = e.y;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int r = 16 * kt + n;
+      const int key = r < nk ? s0 + r : s0;
+      const uint16_t* kr = k + ((int64_t)key * Hkv + g) * D + 8 * quad;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) tl.k[kt][ks] = *reinterpret_cast<const bf16x8_t*>(kr + 32 * ks);
+    }
+#pragma unroll
+    for (int j = 0; j < VL; ++j) {
+      const int p = 64 * j + L;
+      const int r = p / CPR;
+      const int key = r < nk ? s0 + r : s0;
+      tl.v[j] = *reinterpret_cast<const bf16x8_t*>(v + ((int64_t)key * Hkv + g) * D + 8 * (p % CPR));
+    }
+  };
+
+  floatx4v_t O[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i) O[i] = floatx4v_t{};
+  float m_run = -__builtin_huge_valf();   // log2 units, same in the 4 lanes of a head
+  float l_run = 0.0f;                     // this lane's keys only
+
+  Tile buf[2];
+  if (nsub > 0) load(0, buf[0]);
+  if (nsub > 1) load(1, buf[1]);
+
+  auto step = [&](int i, Tile& tl) {
+    const int nk = list[i].y;
+    // value rows -> LDS stage (row-major, swizzled chunks)
+#pragma unroll
+    for (int j = 0; j < VL; ++j) {
+      const int p = 64 * j + L;
+      const int r = p / CPR, ch = p % CPR;
+      *reinterpret_cast<bf16x8_t*>(stage + r * (CPR * 16) + ((ch ^ vswz<D>(r)) << 4)) = tl.v[j];
+    }
+    // S^T = K . Q^T, two 16-key tiles
+    floatx4v_t S[2] = {floatx4v_t{}, floatx4v_t{}};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl.k[kt][ks], qb[ks], S[kt], 0, 0, 0);
+    // masked logits in log2 units; this lane's keys are 16 kt + 4 quad + e
+    float mx = -__builtin_huge_valf();
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool ok = 16 * kt + 4 * quad + e < nk;
+        const float x = ok ? S[kt][e] * scale_log2 : -__builtin_huge_valf();
+        S[kt][e] = x;
+        mx = __builtin_elementwise_maximum(mx, x);
+      }
+    mx = head_max(mx);
+    const float m_new = __builtin_elementwise_maximum(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run = -inf
+    m_run = m_new;
+    if (ballot(alpha != 1.0f)) {
+#pragma unroll
+      for (int i = 0; i < NDT; ++i) O[i] *= alpha;
+    }
+    l_run *= alpha;
+    // P^T as the B operand: k slots 0..3 = keys 4 quad + e, 4..7 = keys 16 + 4 quad + e
+    float pf[8];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pf[4 * kt + e] = __builtin_amdgcn_exp2f(S[kt][e] - m_new);
+        l_run += pf[4 * kt + e];
+      }
+    bf16x2_t pk[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pk[e] = __builtin_convertvector((float2_t){pf[2 * e], pf[2 * e + 1]}, bf16x2_t);
+    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pk);
+    __builtin_amdgcn_wave_barrier();
+    // O^T += V^T . P^T; V^T's A operand read transposed from the stage
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      // lane (quad, n) reads row 4 quad + n/4 (+16 for the second key half), channels
+      // 16 dt + 4 (n & 3) .. +3: the transposed read hands it channel 16 dt + n of 4 keys
+      short4_t lo, hi;
+      {
+        const int row0 = 4 * quad + (n >> 2);
+        const int col = 16 * dt + 4 * (n & 3);
+        const int off0 = row0 * (CPR * 16) + (((col >> 3) ^ vswz<D>(row0)) << 4) + (col & 7) * 2;
+        const int row1 = row0 + 16;
+        const int off1 = row1 * (CPR * 16) + (((col >> 3) ^ vswz<D>(row1)) << 4) + (col & 7) * 2;
+        lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(stage + off0));
+        hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(stage + off1));
+      }
+      const short __attribute__((ext_vector_type(8))) a8 = {lo[0], lo[1], lo[2], lo[3],
+                                                            hi[0], hi[1], hi[2], hi[3]};
+      O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a8), pb, O[dt], 0, 0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+
+#pragma unroll 1
+  for (int i = 0; i < nsub; i += 2) {
+    step(i, buf[0]);
+    if (i + 2 < nsub) load(i + 2, buf[0]);
+    if (i + 1 < nsub) {
+      step(i + 1, buf[1]);
+      if (i + 3 < nsub) load(i + 3, buf[1]);
+    }
+  }
+
+  // ---- normalise and write: lane owns head n, channels 16 dt + 4 quad + e
+  const float l_tot = head_sum(l_run);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (head_ok) {
+    uint16_t* orow = out + ((int64_t)t * Hq + g * G + n) * D + 4 * quad;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      uint32_t pk0 = pack_bf16x2(O[dt][0] * inv, O[dt][1] * inv);
+      uint32_t pk1 = pack_bf16x2(O[dt][2] * inv, O[dt][3] * inv);
+      *reinterpret_cast<uint2*>(orow + 16 * dt) = make_uint2(pk0, pk1);
+    }
+    if (lse && quad == 0)
+      lse[(int64_t)t * Hq + g * G + n] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_huge_valf();
+  }
+}
+
+// fp32 inputs: one workgroup per (token, kv head); plain FMA arithmetic over the
+// deduplicated route, same definition.
 constexpr int kNT = 256;
 
-template <bool BF16>
-SA_DEVICE float ld_elem(const void* p, int64_t i) {
-  if constexpr (BF16) return bf_bits2f(reinterpret_cast<const uint16_t*>(p)[i]);
-  else return reinterpret_cast<const float*>(p)[i];
-}
-
-template <bool BF16>
-SA_DEVICE void st_elem(void* p, int64_t i, float v) {
-  if constexpr (BF16) reinterpret_cast<uint16_t*>(p)[i] = f2bf_bits(v);
-  else reinterpret_cast<float*>(p)[i] = v;
-}
-
-template <bool BF16, int D>
-__global__ __launch_bounds__(kNT) void block_gqa_kernel(
-    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+template <int D>
+__global__ __launch_bounds__(kNT) void block_gqa_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const int32_t* __restrict__ blk, const int32_t* __restrict__ cu, int nseq, int Hq, int Hkv,
-    int B, int nblk, float scale_log2, void* __restrict__ out, float* __restrict__ lse) {
+    int B, int nblk, float scale_log2, float* __restrict__ out, float* __restrict__ lse) {
   extern __shared__ float sm[];
   const int G = Hq / Hkv;                  // q heads per kv head (<= 16)
   float* sq = sm;                          // [G][D]   (pre-scaled q)
@@ -51,13 +282,13 @@ __global__ __launch_bounds__(kNT) void block_gqa_kernel(
   const int g = blockIdx.y;
   const int tid = threadIdx.x;
   const int start = cu ? seq_start_of(cu, nseq, t) : 0;
+  const int own = (t - start) / B;
 
   for (int i = tid; i < G * D; i += kNT) {
     const int h = i / D, d = i % D;
-    sq[i] = ld_elem<BF16>(q, ((int64_t)t * Hq + g * G + h) * D + d) * scale_log2;
+    sq[i] = q[((int64_t)t * Hq + g * G + h) * D + d] * scale_log2;
   }
   if (tid < 16) { sl[tid] = 0.0f; smx[tid] = -__builtin_huge_valf(); }
-  // each thread owns outputs (h, d) = i, i + kNT, ... of the G*D outputs
   constexpr int kPer = (16 * D + kNT - 1) / kNT;
   float acc[kPer];
 #pragma unroll
@@ -68,34 +299,35 @@ __global__ __launch_bounds__(kNT) void block_gqa_kernel(
 #pragma unroll 1
   for (int j = 0; j < nblk; ++j) {
     const int b = brow[j];
-    if (b < 0) continue;
+    if (b < 0 || b > own) continue;
+    bool dup = false;
+    for (int i = 0; i < j; ++i) dup = dup || brow[i] == b;
+    if (dup) continue;
     const int lo = start + b * B;
-    const int n = min(lo + B - 1, t) - lo + 1;   // causal keys in the block
-    if (n <= 0) continue;
-    for (int i = tid; i < n * D; i += kNT) {
+    const int nk = min(lo + B - 1, t) - lo + 1;   // causal keys in the block
+    for (int i = tid; i < nk * D; i += kNT) {
       const int s = i / D, d = i % D;
       const int64_t row = ((int64_t)(lo + s) * Hkv + g) * D + d;
-      sk[s * (D + 1) + d] = ld_elem<BF16>(k, row);
-      sv[s * D + d] = ld_elem<BF16>(v, row);
+      sk[s * (D + 1) + d] = k[row];
+      sv[s * D + d] = v[row];
     }
     __syncthreads();
-    for (int i = tid; i < G * n; i += kNT) {
-      const int h = i / n, s = i % n;
+    for (int i = tid; i < G * nk; i += kNT) {
+      const int h = i / nk, s = i % nk;
       float a = 0.0f;
       for (int d = 0; d < D; ++d) a = fmaf(sq[h * D + d], sk[s * (D + 1) + d], a);
       sp[h * B + s] = a;
     }
     __syncthreads();
-    // per head: new running max, probabilities, rescale factor (one wave per head)
     for (int h = tid >> 6; h < G; h += kNT / 64) {
       const int L = tid & 63;
       float m = -__builtin_huge_valf();
-      for (int s = L; s < n; s += 64) m = fmaxf(m, sp[h * B + s]);
+      for (int s = L; s < nk; s += 64) m = fmaxf(m, sp[h * B + s]);
       m = wave_max(m);
       const float m_old = smx[h];
       const float m_new = fmaxf(m_old, m);
       float ps = 0.0f;
-      for (int s = L; s < n; s += 64) {
+      for (int s = L; s < nk; s += 64) {
         const float p = exp2f(sp[h * B + s] - m_new);
         sp[h * B + s] = p;
         ps += p;
@@ -116,7 +348,7 @@ __global__ __launch_bounds__(kNT) void block_gqa_kernel(
       if (i < G * D) {
         const int h = i / D, d = i % D;
         float a = acc[r] * salpha[h];
-        for (int s = 0; s < n; ++s) a = fmaf(sp[h * B + s], sv[s * D + d], a);
+        for (int s = 0; s < nk; ++s) a = fmaf(sp[h * B + s], sv[s * D + d], a);
         acc[r] = a;
       }
     }
@@ -128,7 +360,7 @@ __global__ __launch_bounds__(kNT) void block_gqa_kernel(
     if (i < G * D) {
       const int h = i / D, d = i % D;
       const float l = sl[h];
-      st_elem<BF16>(out, ((int64_t)t * Hq + g * G + h) * D + d, l > 0.0f ? acc[r] / l : 0.0f);
+      out[((int64_t)t * Hq + g * G + h) * D + d] = l > 0.0f ? acc[r] / l : 0.0f;
     }
   }
   if (lse && tid < G) {
@@ -137,20 +369,36 @@ __global__ __launch_bounds__(kNT) void block_gqa_kernel(
   }
 }
 
-template <bool BF16, int D>
-hipError_t launch_d(const void* q, const void* k, const void* v, const int32_t* blk, int T,
-                    const int32_t* cu, int nseq, int Hq, int Hkv, int B, int nblk, float scale,
-                    void* out, float* lse, hipStream_t st) {
+template <int D>
+hipError_t launch_bf16(const void* q, const void* k, const void* v, const int32_t* blk, int T,
+                       const int32_t* cu, int nseq, int Hq, int Hkv, int B, int nblk, float scale,
+                       void* out, float* lse, hipStream_t st) {
+  const size_t shm = (size_t)kWavesPerGroup * wave_lds_bytes<D>();
+  const int64_t units = (int64_t)T * Hkv;
+  const int grid = (int)((units + kWavesPerGroup - 1) / kWavesPerGroup);
+  hipLaunchKernelGGL((block_gqa_bf16_kernel<D>), dim3(grid), dim3(kWavesPerGroup * 64), shm, st,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, blk, cu, nseq, T,
+                     Hq, Hkv, B, nblk, scale * kLog2e, (uint16_t*)out, lse);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_f32(const void* q, const void* k, const void* v, const int32_t* blk, int T,
+                      const int32_t* cu, int nseq, int Hq, int Hkv, int B, int nblk, float scale,
+                      void* out, float* lse, hipStream_t st) {
   const size_t shm = sizeof(float) * ((size_t)16 * D + (size_t)B * (D + 1) + (size_t)B * D + 16 * (size_t)B + 48);
-  hipError_t e = hipFuncSetAttribute((const void*)block_gqa_kernel<BF16, D>,
+  hipError_t e = hipFuncSetAttribute((const void*)block_gqa_f32_kernel<D>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((block_gqa_kernel<BF16, D>), dim3(T, Hkv), dim3(kNT), shm, st, q, k, v, blk, cu,
-                     nseq, Hq, Hkv, B, nblk, scale * kLog2e, out, lse);
+  hipLaunchKernelGGL((block_gqa_f32_kernel<D>), dim3(T, Hkv), dim3(kNT), shm, st, (const float*)q,
+                     (const float*)k, (const float*)v, blk, cu, nseq, Hq, Hkv, B, nblk,
+                     scale * kLog2e, (float*)out, lse);
   return hipGetLastError();
 }
 
 }  // namespace
+
+int block_gqa_max_route() { return kMaxRoute; }
 
 hipError_t launch_block_gqa(const void* q, const void* k, const void* v, const int32_t* blk,
                             bool bf16, int T, const int32_t* cu, int nseq, int Hq, int Hkv, int D,
@@ -158,12 +406,13 @@ hipError_t launch_block_gqa(const void* q, const void* k, const void* v, const i
                             hipStream_t st) {
   (void)Dv;
   if (T == 0) return hipSuccess;
+  const int ns = cu ? nseq : 1;
   if (bf16) {
-    if (D == 64) return launch_d<true, 64>(q, k, v, blk, T, cu, nseq, Hq, Hkv, block_size, nblk, scale, out, lse, st);
-    return launch_d<true, 128>(q, k, v, blk, T, cu, nseq, Hq, Hkv, block_size, nblk, scale, out, lse, st);
+    if (D == 64) return launch_bf16<64>(q, k, v, blk, T, cu, ns, Hq, Hkv, block_size, nblk, scale, out, lse, st);
+    return launch_bf16<128>(q, k, v, blk, T, cu, ns, Hq, Hkv, block_size, nblk, scale, out, lse, st);
   }
-  if (D == 64) return launch_d<false, 64>(q, k, v, blk, T, cu, nseq, Hq, Hkv, block_size, nblk, scale, out, lse, st);
-  return launch_d<false, 128>(q, k, v, blk, T, cu, nseq, Hq, Hkv, block_size, nblk, scale, out, lse, st);
+  if (D == 64) return launch_f32<64>(q, k, v, blk, T, cu, ns, Hq, Hkv, block_size, nblk, scale, out, lse, st);
+  return launch_f32<128>(q, k, v, blk, T, cu, ns, Hq, Hkv, block_size, nblk, scale, out, lse, st);
 }
 
 }  // namespace sa

@@ -145,6 +145,7 @@ sa_status sa_block_sparse_gqa_fwd(const void* q, const void* k, const void* v, c
   if (Hq / Hkv > 16) return SA_ERR_UNSUPPORTED;
   if (!((D == 128 && Dv == 128) || (D == 64 && Dv == 64))) return SA_ERR_UNSUPPORTED;
   if (block_size % 16 != 0 || block_size > 128) return SA_ERR_UNSUPPORTED;
+  if (nblk > sa::block_gqa_max_route()) return SA_ERR_UNSUPPORTED;
   if (T == 0) return SA_OK;
   if (!q || !k || !v || !blk || !out) return SA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SA_ERR_ALIGN;

@@ -31,7 +31,9 @@ design notes):
 * selected slots are emitted in ascending index order, then -1 padding;
 * sparse attention over the slots of an index row: each slot counts once, -1
   slots are skipped, a row with no valid slot gives zeros and lse = -inf;
-  natural-log lse.
+  natural-log lse;
+* block-routed attention attends to a set of keys: the causal keys of every block
+  that appears in the route (a block id listed twice contributes its keys once).
 
 Parity status: every function below is pinned by CPU tests against brute force,
 library routines, hand-derived fixtures and invariants, except the two points the
@@ -283,9 +285,10 @@ def block_sparse_gqa_row(q_t, k, v, blk_t, t: int, seq_start: int,
     """Grouped-query attention of one query over its selected key blocks.
 
     [QSA] "Describe the solution you'd like": sparse GQA attention over the blocks
-    chosen by the block TopK. Keys: every s with s <= t whose local block
-    (s - seq_start) // B is a slot of blk_t (slot -1 skipped; each slot counts
-    once). Head h reads kv head g = h // (Hq / Hkv). Per head, float64:
+    chosen by the block TopK. The attended keys form a set: every s with s <= t whose
+    local block (s - seq_start) // B appears among the slots of blk_t (slot -1
+    skipped; a block id listed twice contributes its keys once). Head h reads kv
+    head g = h // (Hq / Hkv). Per head, float64:
       l[s] = scale * q[h,:].k[s,g,:]; out[h,:] = softmax(l) @ v[:, g, :];
       lse[h] = log sum exp l. No key -> zeros and lse = -inf.
 
@@ -296,10 +299,8 @@ def block_sparse_gqa_row(q_t, k, v, blk_t, t: int, seq_start: int,
     Hkv = k.shape[1]
     Dv = v.shape[2]
     keys = []
-    for b in _i64(blk_t):
-        if b < 0:
-            continue
-        lo = seq_start + int(b) * block_size
+    for b in sorted(set(int(x) for x in _i64(blk_t) if x >= 0)):
+        lo = seq_start + b * block_size
         hi = min(lo + block_size - 1, t)
         keys.extend(range(lo, hi + 1))
     out = np.zeros((Hq, Dv))

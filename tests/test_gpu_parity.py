@@ -412,6 +412,41 @@ def test_block_gqa_full_size_thd_sampled(sa):
     close(lse.cpu().numpy()[rows], rl, **BF16_TOL, what="lse")
 
 
+@pytest.mark.parametrize("Hq,Hkv,D,B,dtype", [(32, 4, 128, 64, "bf16"), (8, 4, 128, 32, "bf16"),
+                                              (4, 4, 64, 16, "bf16"), (16, 1, 128, 128, "bf16"),
+                                              (12, 2, 64, 48, "bf16"), (8, 2, 64, 32, "f32")])
+def test_block_gqa_shapes_routes_with_repeats(sa, Hq, Hkv, D, B, dtype):
+    """Head-group sizes 1..16, D 64/128, block sizes 16..128, THD with a sequence shorter
+    than a block, and routes holding repeated blocks, blocks past the query's own and
+    -1 slots at random positions."""
+    lengths = (300, 7, 213)
+    T = sum(lengths)
+    gen = torch.Generator().manual_seed(Hq * 131 + D + B)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = torch.randn((T, Hq, D), generator=gen).to(tdt)
+    k = torch.randn((T, Hkv, D), generator=gen).to(tdt)
+    v = torch.randn((T, Hkv, D), generator=gen).to(tdt)
+    nblk = 6
+    blk = workloads.random_block_index(T, nblk, B, 23, lengths=lengths).clone()
+    starts = workloads.cu_seqlens(lengths)
+    for t in range(T):
+        c = int(starts[np.searchsorted(starts, t, side="right") - 1])
+        own = (t - c) // B
+        r = int(torch.randint(0, 4, (1,), generator=gen))
+        if r == 1 and blk[t, 0] >= 0:
+            blk[t, nblk - 1] = blk[t, 0]                  # repeated block
+        elif r == 2:
+            blk[t, nblk - 1] = own + 1                    # past the own block
+        elif r == 3:
+            blk[t, int(torch.randint(0, nblk, (1,), generator=gen))] = -1
+    out, lse = sa.block_sparse_gqa(q.to(DEV), k.to(DEV), v.to(DEV), blk.to(DEV), 0.3, block_size=B,
+                                   cu_seqlens=cu_dev(lengths), max_seqlen=max(lengths))
+    ro, rl = oracle.block_sparse_gqa(q, k, v, blk.numpy(), B, 0.3, cu_seqlens=starts)
+    tol = BF16_TOL if dtype == "bf16" else F32_TOL
+    close(out.float().cpu().numpy(), ro, **tol, what="out")
+    close(lse.cpu().numpy(), rl, **tol, what="lse")
+
+
 # ------------------------------------------------------------ determinism and inputs
 
 def test_replay_bitwise_and_inputs_preserved(sa):

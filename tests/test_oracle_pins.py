@@ -390,6 +390,28 @@ def test_gqa_reductions():
     np.testing.assert_allclose(out1, _gqa_sdpa(q, k, v, mask, 0.5), rtol=1e-12, atol=1e-12)
 
 
+def test_gqa_route_is_a_set():
+    """A block listed twice, or a block past the query's own, adds no key: the result
+    equals the library's masked attention over the set of routed causal keys."""
+    rng = np.random.default_rng(18)
+    T, Hq, Hkv, D, B = 40, 4, 2, 8, 8
+    q = rng.standard_normal((T, Hq, D))
+    k = rng.standard_normal((T, Hkv, D))
+    v = rng.standard_normal((T, Hkv, D))
+    blk = np.full((T, 6), -1, dtype=np.int64)
+    mask = np.zeros((T, T), dtype=bool)
+    for t in range(T):
+        own = t // B
+        picks = rng.integers(0, own + 1, size=3)
+        blk[t, :3] = picks
+        blk[t, 3] = picks[0]                  # repeated block
+        blk[t, 4] = own + 1                   # past the own block: no causal key
+        for b in set(picks.tolist()):
+            mask[t, b * B:min(b * B + B, t + 1)] = True
+    out, _ = oracle.block_sparse_gqa(q, k, v, blk, B, 0.7)
+    np.testing.assert_allclose(out, _gqa_sdpa(q, k, v, mask, 0.7), rtol=1e-12, atol=1e-12)
+
+
 # --------------------------------------------------------------- workloads / recipe
 
 def test_thd_lengths_recipe():
