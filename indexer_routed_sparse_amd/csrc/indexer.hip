@@ -428,6 +428,325 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer_kernel(IdxArgs a) {
   }
 }
 
+// ---- exact wave-level top-k of a candidate buffer, radix digits taken from the top
+//      of the occupied key range. keys[0..n) (order keys in [lo, hi]) and ids[0..n)
+//      are in ascending index order; keeps the first k under (key desc, index asc) in
+//      place, stable, and returns the smallest kept key. Each pass histograms the
+//      window that holds the k-th key into 256 buckets of width 2^shift, so it takes
+//      ceil(bits(hi - lo) / 8) passes at most, and ends early when the bucket of the
+//      k-th key is taken whole.
+SA_DEVICE uint32_t wave_select(uint32_t* keys, int32_t* ids, int n, int k, uint32_t* hist,
+                               uint32_t lo, uint32_t hi) {
+  const int L = lane_id();
+  uint32_t wlo = 0, whi = hi - lo;         // window (offsets from lo) holding the k-th key
+  uint32_t need = (uint32_t)k;             // keys still to take from the window
+  int mode = 1;                            // 1: keep >= thr; 2: keep > thr + first `need` == thr
+  uint32_t thr = lo;
+#pragma unroll 1
+  for (;;) {
+    const uint32_t span = whi - wlo;
+    const int shift = span >= 256u ? (32 - __builtin_clz(span)) - 8 : 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) hist[4 * L + r] = 0u;
+    __builtin_amdgcn_wave_barrier();
+    int e = L;
+#pragma unroll 1
+    for (; e + 192 < n; e += 256) {       // four independent reads in flight
+      uint32_t x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = keys[e + 64 * u] - lo;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (x[u] >= wlo && x[u] <= whi) atomicAdd(&hist[(x[u] - wlo) >> shift], 1u);
+    }
+#pragma unroll 1
+    for (; e < n; e += 64) {
+      const uint32_t x = keys[e] - lo;
+      if (x >= wlo && x <= whi) atomicAdd(&hist[(x - wlo) >> shift], 1u);
+    }
+    __builtin_amdgcn_wave_barrier();
+    // lane L owns buckets 255-4L .. 252-4L (descending)
+    uint32_t c[4], sum = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) { c[r] = hist[255 - 4 * L - r]; sum += c[r]; }
+    uint32_t run = wave_incl_scan(sum) - sum;
+    int found = -1;
+    uint32_t above_f = 0, cnt_f = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t above = run;
+      run += c[r];
+      if (above < need && run >= need) { found = 255 - 4 * L - r; above_f = above; cnt_f = c[r]; }
+    }
+    const int src = (int)__builtin_ctzll(ballot(found >= 0));
+    const uint32_t d = (uint32_t)__shfl(found, src, kWave);
+    const uint32_t above = __shfl(above_f, src, kWave);
+    const uint32_t cnt = __shfl(cnt_f, src, kWave);
+    __builtin_amdgcn_wave_barrier();
+    need -= above;
+    const uint32_t blo = wlo + (d << shift);
+    if (cnt == need) { mode = 1; thr = lo + blo; break; }      // bucket taken whole
+    if (shift == 0) { mode = 2; thr = lo + blo; break; }       // k-th key's exact value
+    wlo = blo;
+    whi = min(whi, blo + ((1u << shift) - 1u));
+  }
+  // stable compaction, 64 entries per round, four rounds per batch: a batch reads
+  // its 256 entries first, then writes only below its own start, so the reads of
+  // later batches never see a write
+  int out = 0;
+  uint32_t eqseen = 0, kmin = 0xFFFFFFFFu;
+#pragma unroll 1
+  for (int base = 0; base < n; base += 4 * kWave) {
+    uint32_t kk[4];
+    int32_t id[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = base + 64 * u + L;
+      kk[u] = e < n ? keys[e] : 0u;
+      id[u] = e < n ? ids[e] : 0;
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool in = base + 64 * u + L < n;
+      const bool gt = in && (mode == 1 ? kk[u] >= thr : kk[u] > thr);
+      const bool eq = in && mode == 2 && kk[u] == thr;
+      const uint64_t eb = ballot(eq);
+      const uint32_t er = eqseen + mbcnt(eb);
+      const bool take = gt || (eq && er < need);
+      const uint64_t tb = ballot(take);
+      const int pos = out + (int)mbcnt(tb);
+      if (take) { keys[pos] = kk[u]; ids[pos] = id[u]; kmin = kmin < kk[u] ? kmin : kk[u]; }
+      out += __popcll(tb);
+      eqseen += (uint32_t)__popcll(eb);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = __shfl_xor(kmin, off, kWave);
+    kmin = kmin < o ? kmin : o;
+  }
+  return kmin;
+}
+
+// Token scores with 64 indexer heads (bf16): one token per wave, so the 64 heads are
+// the 64 rows of the wave's MFMA tiles and a token's whole state stays in the wave.
+//   * key tiles of 64 rows stream through LDS (global_load_lds, double buffered); the
+//     K^T operand slices are read DA k-steps ahead of their MFMAs;
+//   * the ReLU, head weight and head sum run on the accumulators: each lane sums its
+//     32 (head, key) products, one lane-half swap completes the 64-head sum, and lane
+//     L ends up holding the score of key k0 + L, so no score goes through LDS;
+//   * dense mode stores the scores (one coalesced 256-byte row segment per tile);
+//     fused mode compares each lane's key with the running threshold held in a
+//     register and appends the winners, in index order, to the token's LDS candidate
+//     buffer; a full buffer is cut back to exactly k by wave_select, whose smallest
+//     kept key becomes the new threshold. Keys arrive in ascending index order, so a
+//     later key equal to a kept one never wins and the strict filter is exact.
+template <int DI>
+__global__ __launch_bounds__(kMaxWaves * 64) void indexer64_kernel(IdxArgs a) {
+  constexpr int CPR = DI * 2 / 16;            // 16-byte chunks per key row
+  constexpr int TILE_BYTES = kKT * CPR * 16;
+  constexpr int KSTEPS = DI / 16;
+  constexpr int DA = 4;                       // K^T operand prefetch distance (k-steps)
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  char* ktiles = lds;                                              // 2 tiles
+  uint32_t* hist = reinterpret_cast<uint32_t*>(lds + 2 * TILE_BYTES);   // [4][256]
+  uint32_t* bkeys = hist + kMaxWaves * 256;                         // [4][cap]
+  int32_t* bids = reinterpret_cast<int32_t*>(bkeys + (size_t)kMaxWaves * a.cap);
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int L = tid & 63;
+  const int hl = L >> 5;
+  const bool fused = a.topk > 0;
+
+  const int seq = blockIdx.y;
+  const int chunk = a.chunks - 1 - (int)blockIdx.x;   // longest rows first
+  const int cs = a.cu ? __ldg(a.cu + seq) : 0;
+  const int ce = a.cu ? __ldg(a.cu + seq + 1) : a.T;
+  const int t0 = cs + chunk * kMaxWaves;
+  if (t0 >= ce) return;
+  const int t1 = min(t0 + kMaxWaves, ce);
+  const int ntiles = (t1 - 1 - cs) / kKT + 1;
+  const int t = t0 + w;                                // this wave's token
+  const bool active = t < t1;
+  const int my_tiles = active ? (t - cs) / kKT + 1 : 0;
+
+  // A operands (q rows = heads) and head weights of this wave's token
+  bf16x8_t qa[2][KSTEPS];
+  float wr[2][16];
+  {
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + (int64_t)(active ? t : t0) * 64 * DI;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const uint16_t* qh = qrow + (32 * mt + (L & 31)) * DI + 8 * hl;
+#pragma unroll
+      for (int n = 0; n < KSTEPS; ++n) qa[mt][n] = *reinterpret_cast<const bf16x8_t*>(qh + 16 * n);
+#pragma unroll
+      for (int sg = 0; sg < 16; ++sg)
+        wr[mt][sg] = __ldg(a.w + (int64_t)(active ? t : t0) * 64 + 32 * mt + 8 * (sg >> 2) + 4 * hl + (sg & 3));
+    }
+  }
+  int b_off[2][KSTEPS];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int r = 32 * nt + (L & 31);
+#pragma unroll
+    for (int n = 0; n < KSTEPS; ++n) b_off[nt][n] = (r * CPR + ((2 * n + hl) ^ kswz<CPR>(r))) * 16;
+  }
+
+  auto gather = [&](int tile) {
+    const uint32_t base = (uint32_t)(uintptr_t)(SA_LDS char*)(ktiles + (tile & 1) * TILE_BYTES);
+    const int k0 = cs + tile * kKT;
+    for (int ii = w; ii < CPR; ii += kMaxWaves) {
+      const int p = 64 * ii + L;
+      const int r = p / CPR;
+      const int c = (p % CPR) ^ kswz<CPR>(r);
+      const int row = min(k0 + r, a.T - 1);
+      lds_dma16(base + ii * 1024, reinterpret_cast<const char*>(a.k) + ((int64_t)row * DI) * 2 + 16 * c);
+    }
+  };
+
+  uint32_t* keys = bkeys + (size_t)w * a.cap;
+  int32_t* ids = bids + (size_t)w * a.cap;
+  uint32_t* whist = hist + w * 256;
+  // Cut-backs are synchronised: a wave whose buffer has less than one tile of room
+  // left records the tile in s_req, and after the next barrier every wave holding
+  // more than k candidates cuts back at once, so no wave waits on another's cut-back.
+  __shared__ int s_req;
+  if (tid == 0) s_req = -1;
+  int n = 0;                       // candidates held
+  uint32_t tau = 0u;               // a key must exceed this to enter; every held key is
+                                   // >= tau (after a cut-back the smallest kept key == tau)
+  uint32_t kmax = 0u;              // largest key this lane appended
+
+  gather(0);
+#pragma unroll 1
+  for (int tile = 0; tile < ntiles; ++tile) {
+    wait_vmcnt0();
+    __syncthreads();                      // tile resident; previous tile fully consumed
+    if (tile + 1 < ntiles) gather(tile + 1);
+    auto cut_back = [&]() {
+      uint32_t hi = kmax;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) hi = max(hi, (uint32_t)__shfl_xor(hi, off, kWave));
+      tau = wave_select(keys, ids, n, a.topk, whist, tau, hi);
+      n = a.topk;
+    };
+    if (fused && s_req == tile - 1 && n > a.topk) cut_back();
+    if (tile >= my_tiles) continue;       // wave-uniform: no causal key of t left
+    const char* tb = ktiles + (tile & 1) * TILE_BYTES;
+    const int k0 = cs + tile * kKT;
+
+    floatx16_t S[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) S[mt][nt] = floatx16_t{};
+    {
+      bf16x8_t ring[DA][2];
+#pragma unroll
+      for (int i = 0; i < DA; ++i)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) ring[i][nt] = *reinterpret_cast<const bf16x8_t*>(tb + b_off[nt][i]);
+#pragma unroll
+      for (int kn = 0; kn < KSTEPS; ++kn) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const bf16x8_t b = ring[kn % DA][nt];
+          if (kn + DA < KSTEPS) ring[kn % DA][nt] = *reinterpret_cast<const bf16x8_t*>(tb + b_off[nt][kn + DA]);
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+            S[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][kn], b, S[mt][nt], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // ReLU, head weight, head sum; lane L gets the score of key k0 + L
+    float tot[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int sg = 0; sg < 16; ++sg) acc = fmaf(wr[mt][sg], fmaxf(S[mt][nt][sg], 0.0f), acc);
+      const float2_t h2 = lane_halves(acc);
+      tot[nt] = h2.x + h2.y;
+    }
+    float sc = hl ? tot[1] : tot[0];
+    if (sc == 0.0f) sc = 0.0f;             // -0 -> +0
+    const int kg = k0 + L;
+    const bool valid = kg <= t;            // kg >= cs always
+
+    if (!fused) {
+      if (valid) a.scores[(int64_t)t * a.ld + (kg - cs)] = sc;
+      continue;
+    }
+    const uint32_t kk = order_key(sc);
+    bool take = valid && kk > tau;
+    uint64_t tb2 = ballot(take);
+    if (tb2 == 0) continue;
+    int cnt = __popcll(tb2);
+    if (n + cnt > a.cap) {                // cannot happen after a requested cut-back
+      cut_back();
+      take = valid && kk > tau;
+      tb2 = ballot(take);
+      cnt = __popcll(tb2);
+    }
+    const int pos = n + (int)mbcnt(tb2);
+    if (take) { keys[pos] = kk; ids[pos] = kg; kmax = max(kmax, kk); }
+    n += cnt;
+    if (n > a.cap - kKT && L == 0) s_req = tile;
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  if (!fused || !active) return;
+  if (n > a.topk) {
+    uint32_t hi = kmax;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) hi = max(hi, (uint32_t)__shfl_xor(hi, off, kWave));
+    wave_select(keys, ids, n, a.topk, whist, tau, hi);
+    n = a.topk;
+  }
+  __builtin_amdgcn_wave_barrier();
+  int32_t* orow = a.out_idx + (int64_t)t * a.topk;
+  float* vrow = a.out_val ? a.out_val + (int64_t)t * a.topk : nullptr;
+  for (int j = L; j < a.topk; j += kWave) {
+    if (j < n) {
+      orow[j] = ids[j];
+      if (vrow) vrow[j] = key_value(keys[j]);
+    } else {
+      orow[j] = -1;
+      if (vrow) vrow[j] = -__builtin_huge_valf();
+    }
+  }
+}
+
+template <int DI>
+hipError_t launch_64(const IdxArgs& a0, int maxlen, hipStream_t st) {
+  IdxArgs a = a0;
+  constexpr int CPR = DI * 2 / 16;
+  constexpr int TILE_BYTES = kKT * CPR * 16;
+  const bool fused = a.topk > 0;
+  a.cap = 0;
+  if (fused) {
+    const int extra = a.topk < 64 ? 64 : (a.topk > 1024 ? 1024 : a.topk);
+    a.cap = a.topk + extra;
+  }
+  const size_t shm = 2 * (size_t)TILE_BYTES + (size_t)kMaxWaves * 256 * 4 + (size_t)kMaxWaves * a.cap * 8;
+  if (shm > 160 * 1024) return hipErrorInvalidValue;
+  a.nwave = kMaxWaves;
+  a.chunks = (maxlen + kMaxWaves - 1) / kMaxWaves;
+  hipError_t e = hipFuncSetAttribute((const void*)indexer64_kernel<DI>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((indexer64_kernel<DI>), dim3(a.chunks, a.nseq), dim3(kMaxWaves * 64), shm, st, a);
+  return hipGetLastError();
+}
+
 template <bool BF16, int HI, int DI>
 hipError_t launch_hi(const IdxArgs& a0, int maxlen, hipStream_t st) {
   IdxArgs a = a0;
@@ -472,6 +791,7 @@ hipError_t launch_di(const IdxArgs& a, int H_I, int maxlen, hipStream_t st) {
 }
 
 hipError_t launch_any(const IdxArgs& a, bool bf16, int H_I, int D_I, int maxlen, hipStream_t st) {
+  if (bf16 && H_I == 64 && a.B == 1) return D_I == 64 ? launch_64<64>(a, maxlen, st) : launch_64<128>(a, maxlen, st);
   if (bf16) return D_I == 64 ? launch_di<true, 64>(a, H_I, maxlen, st) : launch_di<true, 128>(a, H_I, maxlen, st);
   return D_I == 64 ? launch_di<false, 64>(a, H_I, maxlen, st) : launch_di<false, 128>(a, H_I, maxlen, st);
 }

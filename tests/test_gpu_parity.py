@@ -281,6 +281,24 @@ def test_indexer_fused_matches_dense_then_select(sa, name):
     assert torch.equal(v1, v2)
 
 
+@pytest.mark.parametrize("k", [1, 100, 777, 2048])
+@pytest.mark.parametrize("integer", [False, True])
+def test_indexer64_fused_matches_dense_then_select(sa, k, integer):
+    """64 indexer heads: the fused selection (many buffer cut-backs at small k, exact
+    ties on the integer grid) equals sa_topk_select over the dense scores, bit for bit,
+    on one sequence and on packed sequences."""
+    wl = W["long_dsa"]
+    for lengths in [(4096,), (1000, 3, 2048, 1045)]:
+        T = sum(lengths)
+        x = {n: t.to(DEV) for n, t in workloads.indexer_inputs(wl, integer=integer, T=T).items()}
+        kw = dict(cu_seqlens=cu_dev(lengths), max_seqlen=max(lengths)) if len(lengths) > 1 else {}
+        dense = sa.indexer_scores(x["q_I"], x["k_I"], x["w"], **kw)
+        i1, v1 = sa.topk_select(dense, k, with_values=True, **kw)
+        i2, v2 = sa.indexer_topk(x["q_I"], x["k_I"], x["w"], k, with_values=True, **kw)
+        assert torch.equal(i1, i2), f"lengths {lengths}"
+        assert torch.equal(v1, v2), f"lengths {lengths}"
+
+
 @pytest.mark.parametrize("name", ["long_dsa", "thd_varlen"])
 def test_indexer_topk_full_size_integer_sampled(sa, name):
     wl = W[name]
