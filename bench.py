@@ -191,7 +191,7 @@ def write_traffic(fetch_dir, write_dir, command):
            "command": command}
     groups = {
         "sparse_mla_long_dsa": (lambda n: "sparse_mla_bf16_kernel" in n, ["sparse_mla.hip", "sa_common.h"], 1),
-        "indexer_topk_long_dsa": (lambda n: "indexer_kernel" in n, ["indexer.hip", "sa_common.h"], None),
+        "indexer_topk_long_dsa": (lambda n: "indexer64_kernel" in n, ["indexer.hip", "sa_common.h"], None),
         "topk_select_long_dsa": (lambda n: "topk_pivot_kernel" in n or "topk_retry_kernel" in n,
                                  ["topk_select.hip", "sa_common.h"], None),
     }
@@ -309,7 +309,7 @@ def main():
             "traffic": _traffic("sparse_mla_long_dsa", ["sparse_mla.hip", "sa_common.h"]),
         },
         "roofline_indexer": {
-            "kernel": "indexer_kernel", "bound": "mfma",
+            "kernel": "indexer64_kernel", "bound": "mfma",
             "achieved": round(idx_flops / (t_idx * 1e-3) / 1e12, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(idx_flops / (t_idx * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),

@@ -68,6 +68,18 @@ SA_DEVICE void lds_dma16(uint32_t lds, const void* src) {
                : "memory");
 }
 
+// Same copy with a wave-uniform 64-bit base and a per-lane 32-bit byte offset.
+SA_DEVICE void lds_dma16_sv(uint32_t lds, const void* base, uint32_t voff) {
+  // readfirstlane returns a signed int: zero-extend each half before recombining
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint64_t sb = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(
+                   __builtin_amdgcn_readfirstlane(lds)),
+               "v"(voff), "s"(sb)
+               : "memory");
+}
+
 // ---- wave-level exact top-k shrink of a candidate buffer (keys, idx) of n entries,
 //      stored in ascending index order. Keeps the first `k` under (key desc, index
 //      asc) in place, in index order, and returns the smallest kept key.
@@ -530,6 +542,77 @@ SA_DEVICE uint32_t wave_select(uint32_t* keys, int32_t* ids, int n, int k, uint3
   return kmin;
 }
 
+// ---- one-pass cut-back of a candidate buffer: keys[0..n) (order keys in [lo, hi]),
+//      ids[0..n), ascending index order. Histograms [lo, hi] into 256 buckets, finds
+//      the lowest bucket b such that the buckets from b up hold at least k keys, and
+//      keeps (stably, in place) every key >= the lower edge of b. The kept set always
+//      contains the exact top-k, so the caller may raise its threshold to that edge
+//      minus one. Returns the number kept; if the top bucket alone holds more than
+//      `limit` keys (massive ties) nothing is dropped and n is returned.
+SA_DEVICE int wave_cut(uint32_t* keys, int32_t* ids, int n, int k, int limit, uint32_t* hist,
+                       uint32_t lo, uint32_t hi, uint32_t& edge) {
+  const int L = lane_id();
+  const uint32_t span = hi - lo;
+  const int shift = span >= 256u ? (32 - __builtin_clz(span)) - 8 : 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) hist[4 * L + r] = 0u;
+  __builtin_amdgcn_wave_barrier();
+  int e = L;
+#pragma unroll 1
+  for (; e + 448 < n; e += 512) {          // eight independent reads in flight
+    uint32_t x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = keys[e + 64 * u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) atomicAdd(&hist[(x[u] - lo) >> shift], 1u);
+  }
+#pragma unroll 1
+  for (; e < n; e += 64) atomicAdd(&hist[(keys[e] - lo) >> shift], 1u);
+  __builtin_amdgcn_wave_barrier();
+  uint32_t c[4], sum = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) { c[r] = hist[255 - 4 * L - r]; sum += c[r]; }
+  uint32_t run = wave_incl_scan(sum) - sum;
+  int found = -1;
+  uint32_t upto_f = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t above = run;
+    run += c[r];
+    if (above < (uint32_t)k && run >= (uint32_t)k) { found = 255 - 4 * L - r; upto_f = run; }
+  }
+  const int src = (int)__builtin_ctzll(ballot(found >= 0));
+  const uint32_t d = (uint32_t)__shfl(found, src, kWave);
+  const int kept = (int)__shfl(upto_f, src, kWave);
+  __builtin_amdgcn_wave_barrier();
+  if (kept > limit) { edge = lo; return n; }
+  edge = lo + (d << shift);
+  const uint32_t thr = edge;
+  int out = 0;
+#pragma unroll 1
+  for (int base = 0; base < n; base += 4 * kWave) {
+    uint32_t kk[4];
+    int32_t id[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = base + 64 * u + L;
+      kk[u] = i < n ? keys[i] : 0u;
+      id[u] = i < n ? ids[i] : 0;
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool take = base + 64 * u + L < n && kk[u] >= thr;
+      const uint64_t tb = ballot(take);
+      const int pos = out + (int)mbcnt(tb);
+      if (take) { keys[pos] = kk[u]; ids[pos] = id[u]; }
+      out += __popcll(tb);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  return out;
+}
+
 // Token scores with 64 indexer heads (bf16): one token per wave, so the 64 heads are
 // the 64 rows of the wave's MFMA tiles and a token's whole state stays in the wave.
 //   * key tiles of 64 rows stream through LDS (global_load_lds, double buffered); the
@@ -544,7 +627,8 @@ SA_DEVICE uint32_t wave_select(uint32_t* keys, int32_t* ids, int n, int k, uint3
 //     kept key becomes the new threshold. Keys arrive in ascending index order, so a
 //     later key equal to a kept one never wins and the strict filter is exact.
 template <int DI>
-__global__ __launch_bounds__(kMaxWaves * 64) void indexer64_kernel(IdxArgs a) {
+__global__ __launch_bounds__(kMaxWaves * 64) void indexer64_kernel(IdxArgs args) {
+  const IdxArgs a = args;   // local copy: lambdas capture it without a private-memory copy of the kernel argument
   constexpr int CPR = DI * 2 / 16;            // 16-byte chunks per key row
   constexpr int TILE_BYTES = kKT * CPR * 16;
   constexpr int KSTEPS = DI / 16;
@@ -596,15 +680,34 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer64_kernel(IdxArgs a) {
     for (int n = 0; n < KSTEPS; ++n) b_off[nt][n] = (r * CPR + ((2 * n + hl) ^ kswz<CPR>(r))) * 16;
   }
 
-  auto gather = [&](int tile) {
+  // Tile gather: CPR / 4 copies of 1 KiB per wave. Copy ii moves chunk p = 64 ii + L,
+  // i.e. row p / CPR, swizzled chunk; its byte offset inside the tile's rows is fixed,
+  // so a full tile needs only a scalar base per tile.
+  constexpr int NG = CPR / kMaxWaves;
+  uint32_t g_off[NG];
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    const int p = 64 * (w + kMaxWaves * j) + L;
+    const int r = p / CPR;
+    g_off[j] = (uint32_t)(r * DI * 2 + 16 * ((p % CPR) ^ kswz<CPR>(r)));
+  }
+  auto gather = [&](int tile) __attribute__((always_inline)) {
     const uint32_t base = (uint32_t)(uintptr_t)(SA_LDS char*)(ktiles + (tile & 1) * TILE_BYTES);
-    const int k0 = cs + tile * kKT;
-    for (int ii = w; ii < CPR; ii += kMaxWaves) {
-      const int p = 64 * ii + L;
-      const int r = p / CPR;
-      const int c = (p % CPR) ^ kswz<CPR>(r);
-      const int row = min(k0 + r, a.T - 1);
-      lds_dma16(base + ii * 1024, reinterpret_cast<const char*>(a.k) + ((int64_t)row * DI) * 2 + 16 * c);
+    const int k0 = __builtin_amdgcn_readfirstlane(cs + tile * kKT);
+    if (k0 + kKT <= a.T) {
+      const char* src = reinterpret_cast<const char*>(a.k) + (int64_t)k0 * DI * 2;
+#pragma unroll
+      for (int j = 0; j < NG; ++j) lds_dma16_sv(base + (w + kMaxWaves * j) * 1024, src, g_off[j]);
+    } else {                                // last tile of the key array: clamp rows
+#pragma unroll
+      for (int j = 0; j < NG; ++j) {
+        const int p = 64 * (w + kMaxWaves * j) + L;
+        const int r = p / CPR;
+        const int c = (p % CPR) ^ kswz<CPR>(r);
+        const int row = min(k0 + r, a.T - 1);
+        lds_dma16(base + (w + kMaxWaves * j) * 1024,
+                  reinterpret_cast<const char*>(a.k) + ((int64_t)row * DI) * 2 + 16 * c);
+      }
     }
   };
 
@@ -621,50 +724,32 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer64_kernel(IdxArgs a) {
                                    // >= tau (after a cut-back the smallest kept key == tau)
   uint32_t kmax = 0u;              // largest key this lane appended
 
-  gather(0);
-#pragma unroll 1
-  for (int tile = 0; tile < ntiles; ++tile) {
-    wait_vmcnt0();
-    __syncthreads();                      // tile resident; previous tile fully consumed
-    if (tile + 1 < ntiles) gather(tile + 1);
-    auto cut_back = [&]() {
-      uint32_t hi = kmax;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) hi = max(hi, (uint32_t)__shfl_xor(hi, off, kWave));
-      tau = wave_select(keys, ids, n, a.topk, whist, tau, hi);
-      n = a.topk;
-    };
-    if (fused && s_req == tile - 1 && n > a.topk) cut_back();
-    if (tile >= my_tiles) continue;       // wave-uniform: no causal key of t left
-    const char* tb = ktiles + (tile & 1) * TILE_BYTES;
-    const int k0 = cs + tile * kKT;
-
-    floatx16_t S[2][2];
+  // S = Q . K^T of one tile (rows = 64 heads, columns = 64 keys), K^T operand slices
+  // read DA k-steps ahead
+  auto mfma_tile = [&](const char* tb, floatx16_t (&S)[2][2]) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) S[mt][nt] = floatx16_t{};
-    {
-      bf16x8_t ring[DA][2];
+    bf16x8_t ring[DA][2];
 #pragma unroll
-      for (int i = 0; i < DA; ++i)
+    for (int i = 0; i < DA; ++i)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) ring[i][nt] = *reinterpret_cast<const bf16x8_t*>(tb + b_off[nt][i]);
+      for (int nt = 0; nt < 2; ++nt) ring[i][nt] = *reinterpret_cast<const bf16x8_t*>(tb + b_off[nt][i]);
 #pragma unroll
-      for (int kn = 0; kn < KSTEPS; ++kn) {
+    for (int kn = 0; kn < KSTEPS; ++kn) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const bf16x8_t b = ring[kn % DA][nt];
-          if (kn + DA < KSTEPS) ring[kn % DA][nt] = *reinterpret_cast<const bf16x8_t*>(tb + b_off[nt][kn + DA]);
+      for (int nt = 0; nt < 2; ++nt) {
+        const bf16x8_t b = ring[kn % DA][nt];
+        if (kn + DA < KSTEPS) ring[kn % DA][nt] = *reinterpret_cast<const bf16x8_t*>(tb + b_off[nt][kn + DA]);
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-            S[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][kn], b, S[mt][nt], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        for (int mt = 0; mt < 2; ++mt)
+          S[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][kn], b, S[mt][nt], 0, 0, 0);
       }
     }
-
-    // ReLU, head weight, head sum; lane L gets the score of key k0 + L
+  };
+  // ReLU, head weight, head sum; lane L gets the score of key k0 + L (+0.0 for -0.0)
+  auto epilogue = [&](const floatx16_t (&S)[2][2]) {
     float tot[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -672,23 +757,44 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer64_kernel(IdxArgs a) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int sg = 0; sg < 16; ++sg) acc = fmaf(wr[mt][sg], fmaxf(S[mt][nt][sg], 0.0f), acc);
+        for (int sg = 0; sg < 16; ++sg)
+          acc = fmaf(wr[mt][sg], __builtin_elementwise_maximum(S[mt][nt][sg], 0.0f), acc);
       const float2_t h2 = lane_halves(acc);
       tot[nt] = h2.x + h2.y;
     }
     float sc = hl ? tot[1] : tot[0];
-    if (sc == 0.0f) sc = 0.0f;             // -0 -> +0
-    const int kg = k0 + L;
+    return sc == 0.0f ? 0.0f : sc;
+  };
+  // Cut-back: one histogram pass keeps the buckets that hold the top k (a little more
+  // than k keys); only when ties leave the buffer nearly full is the exact select run.
+  auto cut_back = [&]() __attribute__((always_inline)) {
+    uint32_t hi = kmax;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) hi = max(hi, (uint32_t)__shfl_xor(hi, off, kWave));
+    // after a cut-back one more tile (kKT keys) must still fit: kept <= cap - kKT
+    const int limit = a.topk + (a.cap - a.topk - kKT) / 2;
+    uint32_t edge;
+    const int kept = wave_cut(keys, ids, n, a.topk, limit, whist, tau, hi, edge);
+    if (kept <= limit) {
+      n = kept;
+      tau = edge - 1u;                  // every held key is > edge - 1 = tau
+      if (edge == 0u) tau = 0u;
+    } else {
+      tau = wave_select(keys, ids, n, a.topk, whist, tau, hi);
+      n = a.topk;
+    }
+  };
+  auto select = [&](float sc, int tile) __attribute__((always_inline)) {
+    const int kg = cs + tile * kKT + L;
     const bool valid = kg <= t;            // kg >= cs always
-
     if (!fused) {
       if (valid) a.scores[(int64_t)t * a.ld + (kg - cs)] = sc;
-      continue;
+      return;
     }
     const uint32_t kk = order_key(sc);
     bool take = valid && kk > tau;
     uint64_t tb2 = ballot(take);
-    if (tb2 == 0) continue;
+    if (tb2 == 0) return;
     int cnt = __popcll(tb2);
     if (n + cnt > a.cap) {                // cannot happen after a requested cut-back
       cut_back();
@@ -701,6 +807,43 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer64_kernel(IdxArgs a) {
     n += cnt;
     if (n > a.cap - kKT && L == 0) s_req = tile;
     __builtin_amdgcn_wave_barrier();
+  };
+
+  // Software pipeline: iteration `tile` runs the MFMAs of tile+1 interleaved with the
+  // epilogue of tile (whose S is already in registers), then the selection of tile.
+  // Two iterations per loop trip, so the two S sets swap roles without copies.
+  auto iter = [&](int tile, const floatx16_t (&Scur)[2][2], floatx16_t (&Snext)[2][2]) {
+    wait_vmcnt0();
+    __syncthreads();                      // tile+1 resident; every wave is done with tile
+    if (tile + 2 < ntiles) gather(tile + 2);
+    if (fused && s_req == tile - 1 && n > a.topk) cut_back();
+    if (tile >= my_tiles) return;         // wave-uniform: no causal key of t left
+    float sc;
+    if (tile + 1 < my_tiles) {
+      mfma_tile(ktiles + ((tile + 1) & 1) * TILE_BYTES, Snext);
+      sc = epilogue(Scur);
+      // one MFMA, then a share of the epilogue's VALU work, 32 times
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
+      }
+    } else {
+      sc = epilogue(Scur);
+    }
+    select(sc, tile);
+  };
+  floatx16_t SA[2][2], SB[2][2];
+  gather(0);
+  wait_vmcnt0();
+  __syncthreads();                        // tile 0 resident, s_req initialised
+  if (ntiles > 1) gather(1);
+  if (my_tiles > 0) mfma_tile(ktiles, SA);
+#pragma unroll 1
+  for (int tile = 0; tile < ntiles; tile += 2) {
+    iter(tile, SA, SB);
+    if (tile + 1 < ntiles) iter(tile + 1, SB, SA);
   }
 
   if (!fused || !active) return;
@@ -732,8 +875,8 @@ hipError_t launch_64(const IdxArgs& a0, int maxlen, hipStream_t st) {
   constexpr int TILE_BYTES = kKT * CPR * 16;
   const bool fused = a.topk > 0;
   a.cap = 0;
-  if (fused) {
-    const int extra = a.topk < 64 ? 64 : (a.topk > 1024 ? 1024 : a.topk);
+  if (fused) {   // room above k: at least two tiles, so that a cut-back always frees a tile
+    const int extra = a.topk < 256 ? 256 : (a.topk > 1024 ? 1024 : a.topk);
     a.cap = a.topk + extra;
   }
   const size_t shm = 2 * (size_t)TILE_BYTES + (size_t)kMaxWaves * 256 * 4 + (size_t)kMaxWaves * a.cap * 8;
