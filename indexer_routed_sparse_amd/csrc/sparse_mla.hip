@@ -304,12 +304,16 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
           lo = __builtin_elementwise_minimum(lo, S[15]);
           mx = (scale_log2 >= 0.0f ? hi : lo) * scale_log2;
         } else {
+          // the volatile asm keeps the mask arithmetic inside this rarely taken branch
+          // (otherwise it is hoisted above the branch and paid by every full tile)
+          uint64_t vm = vmask;
+          asm volatile("" : "+s"(vm));
           okbits = 0;
           mx = -__builtin_huge_valf();
 #pragma unroll
           for (int sg = 0; sg < 16; ++sg) {
             const int key = 8 * (sg >> 2) + 4 * hl + (sg & 3);
-            const bool ok = (vmask >> key) & 1ull;
+            const bool ok = (vm >> key) & 1ull;
             okbits |= ok ? 1u << sg : 0u;
             mx = __builtin_elementwise_maximum(mx, ok ? S[sg] * scale_log2 : -__builtin_huge_valf());
           }
