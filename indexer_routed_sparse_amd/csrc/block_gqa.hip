@@ -39,24 +39,6 @@ constexpr int kWavesPerGroup = 4;
 
 typedef float floatx4v_t __attribute__((ext_vector_type(4)));
 
-// lanes (i mod 16) + 16 r, r = 0..3, hold the same query head: reductions over them
-SA_DEVICE float2_t lane_rows16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return (float2_t){__uint_as_float(r[0]), __uint_as_float(r[1])};
-}
-SA_DEVICE float head_max(float x) {
-  const float2_t a = lane_rows16(x);
-  const float y = __builtin_elementwise_maximum(a.x, a.y);
-  const float2_t b = lane_halves(y);
-  return __builtin_elementwise_maximum(b.x, b.y);
-}
-SA_DEVICE float head_sum(float x) {
-  const float2_t a = lane_rows16(x);
-  const float y = a.x + a.y;
-  const float2_t b = lane_halves(y);
-  return b.x + b.y;
-}
-
 // Per-wave LDS: value stage of one sub-tile (32 rows x D bf16, 16-byte chunks XOR-
 // swizzled by 2 (row mod 8) so that the transposed reads of 16 rows x 32 bytes spread
 // over the banks) and the wave's sub-tile list.
@@ -188,7 +170,7 @@ __global__ __launch_bounds__(kWavesPerGroup * 64) void block_gqa_bf16_kernel(
         S[kt][e] = x;
         mx = __builtin_elementwise_maximum(mx, x);
       }
-    mx = head_max(mx);
+    mx = quad_max(mx);
     const float m_new = __builtin_elementwise_maximum(m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run = -inf
     m_run = m_new;
@@ -244,7 +226,7 @@ __global__ __launch_bounds__(kWavesPerGroup * 64) void block_gqa_bf16_kernel(
   }
 
   // ---- normalise and write: lane owns head n, channels 16 dt + 4 quad + e
-  const float l_tot = head_sum(l_run);
+  const float l_tot = quad_sum(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (head_ok) {
     uint16_t* orow = out + ((int64_t)t * Hq + g * G + n) * D + 4 * quad;

@@ -86,6 +86,28 @@ SA_DEVICE float2_t lane_halves(float x) {
   return (float2_t){__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
 
+// The values of lanes i and i ^ 16 of `x` (one v_permlane16_swap): .x from the lane
+// whose bit 4 is clear, .y from the one whose bit 4 is set.
+SA_DEVICE float2_t lane_rows16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return (float2_t){__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
+// Max and sum over the four lanes (i mod 16) + 16 r, r = 0..3 (the lanes that share a
+// column of a 16x16 MFMA tile), in every one of them.
+SA_DEVICE float quad_max(float x) {
+  const float2_t a = lane_rows16(x);
+  const float y = __builtin_elementwise_maximum(a.x, a.y);
+  const float2_t b = lane_halves(y);
+  return __builtin_elementwise_maximum(b.x, b.y);
+}
+SA_DEVICE float quad_sum(float x) {
+  const float2_t a = lane_rows16(x);
+  const float y = a.x + a.y;
+  const float2_t b = lane_halves(y);
+  return b.x + b.y;
+}
+
 SA_DEVICE float wave_max(float x) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
