@@ -60,6 +60,28 @@ SA_DEVICE void lds_dma16(uint32_t lds, const void* base, uint32_t voff) {
 }
 
 constexpr int kBK = 32;        // keys per tile
+typedef int int4_t __attribute__((ext_vector_type(4)));
+
+// 32x32x16 bf16 MFMA with the accumulator in VGPRs. The compiler gives every MFMA
+// builtin an AGPR accumulator; the 256 AGPRs hold O here, and a builtin logit tile
+// would push one O tile out of them on every key tile (32 copies each way, and a wait
+// for the P . V MFMAs before the copy back). The caller keeps the MFMA-to-VALU wait
+// states: mfma32_last() ends with them (a VALU read of a 16-pass MFMA result needs 19
+// independent cycles).
+SA_DEVICE floatx16_t mfma32_first(bf16x8_t a, bf16x8_t b) {
+  floatx16_t c;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+  return c;
+}
+SA_DEVICE floatx16_t mfma32_acc(bf16x8_t a, bf16x8_t b, floatx16_t c) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  return c;
+}
+SA_DEVICE floatx16_t mfma32_last(bf16x8_t a, bf16x8_t b, floatx16_t c) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+v"(c) : "v"(a), "v"(b));
+  return c;
+}
 
 // s_waitcnt immediate (gfx9 encoding) that waits until at most `vm` vector-memory
 // operations of this wave are outstanding and ignores the other counters.
@@ -168,17 +190,22 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
   __syncthreads();
 
   // Gather of one tile: this wave's MAIN_PER_WAVE row DMAs (1 KiB each: channels
-  // 0..511 of row R = w + NW j) and ROPE_PER_WAVE RoPE DMAs (channels 512..575 of
-  // 8 rows each). gather_rows() reads the row indices from LDS; gather_dma(j) issues
-  // DMA j. The DMAs of the next tile are spread over the logit MFMAs, so the wave
+  // 0..511 of rows R = MAIN_PER_WAVE w + j, contiguous, so that their indices come in
+  // 16-byte LDS reads) and ROPE_PER_WAVE RoPE DMAs (channels 512..575 of 8 rows each).
+  // gather_rows() reads the row indices from LDS; gather_dma(j) issues DMA j. The DMAs of the next tile are spread over the logit MFMAs, so the wave
   // never stalls on a burst of memory instructions.
   constexpr int ND = MAIN_PER_WAVE + ROPE_PER_WAVE;
   struct Rows { int main[MAIN_PER_WAVE]; int rope[ROPE_PER_WAVE > 0 ? ROPE_PER_WAVE : 1]; };
   auto gather_rows = [&](int tile) {
     Rows r;
     const int32_t* ir = s_idx + tile * kBK;
+    const int4_t* ir4 = reinterpret_cast<const int4_t*>(ir + MAIN_PER_WAVE * w);
 #pragma unroll
-    for (int j = 0; j < MAIN_PER_WAVE; ++j) r.main[j] = __builtin_amdgcn_readfirstlane(ir[w + NW * j]);
+    for (int v = 0; v < MAIN_PER_WAVE / 4; ++v) {
+      const int4_t x = ir4[v];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r.main[4 * v + e] = __builtin_amdgcn_readfirstlane(x[e]);
+    }
     if constexpr (ROPE) {
 #pragma unroll
       for (int j = 0; j < ROPE_PER_WAVE; ++j) {
@@ -191,7 +218,7 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
   auto gather_dma = [&](int tile, const Rows& r, int j) {
     const uint32_t base = (uint32_t)(uintptr_t)(SA_LDS char*)(tiles + (tile % NST) * TILE_BYTES);
     if (j < MAIN_PER_WAVE) {
-      const int R = w + NW * j;                       // wave-uniform row
+      const int R = MAIN_PER_WAVE * w + j;            // wave-uniform row
       int row = r.main[j < MAIN_PER_WAVE ? j : 0];
       row = row < 0 ? 0 : row;   // masked slot: any finite row keeps P*V finite
       lds_dma16(base + R * 1024, kv + (int64_t)row * DQK, (uint32_t)((L ^ swz_main(R)) * 16));
@@ -215,8 +242,8 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 
   // O[hb * NDB + db]: heads [32hb, 32hb+32) x channels 32(NDB w + db) + [0, 32).
   // With one wave, the last two accumulators are summed per key tile in a temporary
-  // (the S registers) and added into VGPRs, which keeps the 16 accumulators, S and
-  // the operands within the register file without spilling.
+  // and added into VGPRs, which keeps the 16 accumulators, S and the operands within
+  // the register file without spilling.
   constexpr int NOA = NW == 1 ? NACC - 2 : NACC;
   floatx16_t O[NACC];
   float m_ref = -__builtin_huge_valf();   // softmax reference (log2 units), per head
@@ -243,7 +270,7 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
       // logit MFMAs below
       const int gtile = tile + NST - 1;
       const bool do_gather = gtile < ntiles;
-      const Rows grows = gather_rows(do_gather ? gtile : tile);
+      Rows grows;   // read after the first logit MFMA is issued (first DMA at k-step 2)
       const int my_slot = s_idx[tile * kBK + (L & (kBK - 1))];   // consumed after S
       const char* tb = tiles + (tile % NST) * TILE_BYTES;
 
@@ -256,7 +283,7 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
         return n < NKR ? qv[n < NKR ? n : 0]
                        : *reinterpret_cast<const bf16x8_t*>(s_q + ((n - NKR) * NW * 64 + tid) * 16);
       };
-      floatx16_t S = floatx16_t{};
+      floatx16_t S;
       {
         // K slices and the LDS-held q slices are both read DA k-steps ahead of use
         bf16x8_t ring[DA], qring[DA];
@@ -273,10 +300,15 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
             ring[n % DA] = a_at(n + DA);
             if (n + DA >= NKR) qring[n % DA] = q_at(n + DA);
           }
-          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, S, 0, 0, 0);
+          if (n == 0) S = mfma32_first(a, b);
+          else if (n == NK - 1) S = mfma32_last(a, b, S);
+          else S = mfma32_acc(a, b, S);
+          if (n == 0) grows = gather_rows(do_gather ? gtile : tile);
+          // the next gather's DMAs, spread over the k-steps from k-step 2 on (the row
+          // indices read at the top of the tile have arrived by then)
 #pragma unroll
           for (int j = 0; j < ND; ++j)
-            if ((j * NK) / ND == n && do_gather) gather_dma(gtile, grows, j);
+            if (2 + (j * (NK - 2)) / ND == n && do_gather) gather_dma(gtile, grows, j);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -360,6 +392,7 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
       for (int i = 0; i < DV; ++i) ring[i] = v_at(i & 1, NDB * w + (i >> 1));
       __syncthreads();               // every wave's P tile visible
       bf16x8_t Pa[NW][2];
+      floatx16_t T;   // one-wave kernel: per-tile partial of the last two accumulators
 #pragma unroll
       for (int hb = 0; hb < NW; ++hb)
 #pragma unroll
@@ -377,10 +410,10 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
             if (a < NOA) {
               O[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Pa[hb][m], b, O[a], 0, 0, 0);
             } else if (m == 0) {
-              S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Pa[hb][0], b, floatx16_t{}, 0, 0, 0);
+              T = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Pa[hb][0], b, floatx16_t{}, 0, 0, 0);
             } else {
-              S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Pa[hb][1], b, S, 0, 0, 0);
-              O[a] += S;
+              T = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Pa[hb][1], b, T, 0, 0, 0);
+              O[a] += T;
             }
           }
           __builtin_amdgcn_sched_barrier(0);
