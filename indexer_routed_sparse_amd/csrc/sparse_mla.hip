@@ -255,6 +255,7 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
     for (int i = 0; i < NACC; ++i) O[i] = floatx16_t{};
     l_run = 0.0f;
+    bool grow = false;   // a tile max above m_ref + kThr (kept in a register: no branch)
 #pragma unroll
     for (int p = 0; p < NST - 1; ++p)
       if (p < ntiles) gather(p);
@@ -354,7 +355,7 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
         mx = __builtin_elementwise_maximum(mh.x, mh.y);
         m_seen = __builtin_elementwise_maximum(m_seen, mx);
         if (m_ref == -__builtin_huge_valf()) m_ref = mx;   // first valid tile (O, l still 0)
-        if (mx > m_ref + kThr) s_restart = 1;               // seen by all after the pass
+        grow |= mx > m_ref + kThr;                          // published after the pass
         const float m_use = (m_ref == -__builtin_huge_valf()) ? 0.0f : m_ref;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
@@ -363,8 +364,9 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
           for (int e = 0; e < 8; ++e) {
             const float x = fmaf(S[8 * m + e], scale_log2, -m_use);
             pf[e] = __builtin_amdgcn_exp2f(FULL || ((okbits >> (8 * m + e)) & 1u) ? x : -__builtin_huge_valf());
-            l_run += pf[e];
           }
+          // pairwise, so that the sum is not one dependent chain
+          l_run += ((pf[0] + pf[1]) + (pf[2] + pf[3])) + ((pf[4] + pf[5]) + (pf[6] + pf[7]));
           bf16x2_t pk[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -422,6 +424,7 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     }
     // A tile max above m_ref + kThr anywhere in the pass: redo the pass with the
     // largest max seen so far as the reference (all gathers have completed).
+    if (grow) s_restart = 1;
     __syncthreads();
     const bool restart = s_restart != 0;
     __syncthreads();
