@@ -60,6 +60,7 @@ SA_DEVICE void lds_dma16(uint32_t lds, const void* base, uint32_t voff) {
 }
 
 constexpr int kBK = 32;        // keys per tile
+SA_DEVICE int uniform_i(int x) { return __builtin_amdgcn_readfirstlane(x); }
 typedef int int4_t __attribute__((ext_vector_type(4)));
 
 // 32x32x16 bf16 MFMA with the accumulator in VGPRs. The compiler gives every MFMA
@@ -137,12 +138,22 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
   const int hl = L >> 5;        // lane half
   const int head = 32 * w + (L & 31);
   const bool head_ok = head < H;
-  const int ntiles = (topk + kBK - 1) / kBK;
+  const int ntiles_all = (topk + kBK - 1) / kBK;
+  __shared__ int s_wlast[NW];
 
-  // ---- stage the index row; q for this wave's 32 heads as B-operand slices
+  // ---- stage the index row (and find its last valid slot); q for this wave's 32
+  //      heads as B-operand slices
   {
     const int32_t* __restrict__ irow = idx + (int64_t)t * topk;
-    for (int j = tid; j < ntiles * kBK; j += NW * 64) s_idx[j] = j < topk ? irow[j] : -1;
+    int last = 0;
+    for (int j = tid; j < ntiles_all * kBK; j += NW * 64) {
+      const int32_t v = j < topk ? irow[j] : -1;
+      s_idx[j] = v;
+      last = v >= 0 ? j + 1 : last;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) last = max(last, __shfl_xor(last, off, 64));
+    if (L == 0) s_wlast[w] = last;
   }
   if (tid == 0) s_restart = 0;
   bf16x8_t qv[NKR > 0 ? NKR : 1];
@@ -188,6 +199,15 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     }
   }
   __syncthreads();
+  // Tiles after the last valid slot hold only masked slots: they change neither O nor
+  // l, and are not visited (a row without a valid slot visits none).
+  int ntiles = 0;
+  {
+    int last = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) last = max(last, s_wlast[i]);
+    ntiles = (int)uniform_i((last + kBK - 1) / kBK);
+  }
 
   // Gather of one tile: this wave's MAIN_PER_WAVE row DMAs (1 KiB each: channels
   // 0..511 of rows R = MAIN_PER_WAVE w + j, contiguous, so that their indices come in

@@ -369,7 +369,7 @@ def test_sparse_mla_shapes(sa, H, k, d_qk):
 @pytest.mark.parametrize("H", [32, 128])
 def test_sparse_mla_large_logits_restart(sa, H):
     # a later key whose logit exceeds the first tile's max by far: exercises the
-    # softmax reference restart (H = 128 runs the eight-wave kernel)
+    # softmax reference restart (H = 128 runs the four-wave kernel)
     T, S, k = 4, 200, 128
     g = torch.Generator().manual_seed(5)
     q = torch.randn((T, H, 576), generator=g)
@@ -381,6 +381,26 @@ def test_sparse_mla_large_logits_restart(sa, H):
     ro, rl = oracle.sparse_mla(q, kv, idx.numpy(), 1.0)
     close(out.float().cpu().numpy(), ro, **BF16_TOL, what="out")
     close(lse.cpu().numpy(), rl, atol=2e-2, rtol=1e-3, what="lse")
+
+
+@pytest.mark.parametrize("H", [16, 64, 128])
+def test_sparse_mla_trailing_masked_tiles(sa, H):
+    # index rows whose valid slots end early (ragged -1 tails ending inside, at and past
+    # the 32-slot tile edges), a whole masked tile between valid ones, and an empty row:
+    # trailing all-masked tiles are skipped, inner masked tiles are visited
+    T, S, k = 8, 300, 160
+    g = torch.Generator().manual_seed(11)
+    q = torch.randn((T, H, 576), generator=g).to(torch.bfloat16)
+    kv = torch.randn((S, 576), generator=g).to(torch.bfloat16)
+    idx = torch.randint(0, S, (T, k), generator=g, dtype=torch.int32)
+    for t, n in enumerate([160, 159, 129, 128, 97, 33, 1, 0]):
+        idx[t, n:] = -1
+    idx[0, 32:64] = -1
+    scale = 576 ** -0.5
+    out, lse = sa.sparse_mla(q.to(DEV), kv.to(DEV), idx.to(DEV), scale)
+    ro, rl = oracle.sparse_mla(q, kv, idx.numpy(), scale)
+    close(out.float().cpu().numpy(), ro, **BF16_TOL, what="out")
+    close(lse.cpu().numpy(), rl, **BF16_TOL, what="lse")
 
 
 @pytest.mark.parametrize("name", ["long_dsa", "thd_varlen"])
