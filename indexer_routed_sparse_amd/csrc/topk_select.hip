@@ -153,8 +153,11 @@ SA_DEVICE bool take_eq(uint32_t k, const Cut& c) { return c.mode == 2 && k == c.
 // thread once every thread has entered. Digits are taken over the exact key range
 // of the nonzero keys.
 template <int N, class S>
+SA_DEVICE Cut radix_select_in(const uint32_t (&x)[N], int R, uint32_t k, S& sm, uint32_t lo, uint32_t hi);
+
+template <int N, class S>
 SA_DEVICE Cut radix_select(const uint32_t (&x)[N], int R, uint32_t k, S& sm) {
-  constexpr int kNT = S::kNT, kNW = S::kNW, kPT = S::kPT;
+  constexpr int kNW = S::kNW;
   const int tid = threadIdx.x, w = (int)uniform((uint32_t)tid / kWave), l = lane_id();
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
@@ -178,7 +181,15 @@ SA_DEVICE Cut radix_select(const uint32_t (&x)[N], int R, uint32_t k, S& sm) {
     lo = (uint32_t)__builtin_amdgcn_readlane((int)rl, kNW - 1);
     hi = (uint32_t)__builtin_amdgcn_readlane((int)rh, kNW - 1);
   }
-  // every key in use lies in [lo, hi]; invalid slots hold 0 < lo
+  return radix_select_in<N>(x, R, k, sm, lo, hi);
+}
+
+// The select proper, given bounds: every nonzero key in use lies in [lo, hi] (lo > 0;
+// invalid slots hold 0 < lo). The bounds may be loose: they only set the digit width.
+template <int N, class S>
+SA_DEVICE Cut radix_select_in(const uint32_t (&x)[N], int R, uint32_t k, S& sm, uint32_t lo, uint32_t hi) {
+  constexpr int kNT = S::kNT, kNW = S::kNW, kPT = S::kPT;
+  const int tid = threadIdx.x, w = (int)uniform((uint32_t)tid / kWave), l = lane_id();
   int s = bit_width(hi - lo) - kDigit;
   s = s > 0 ? s : 0;
   uint32_t need = k;
@@ -472,6 +483,20 @@ SA_DEVICE void select_row(int t, const RowArgs& a, S& sm) {
           __syncthreads();
           pf = pivot_search(std::false_type{}, z, nvalid);
         }
+        // The row's largest key bounds the candidates for the radix select from above
+        // (the pivot bounds them from below), so the select needs no range pass: each
+        // wave's maximum (a DPP reduction) rides the count's barrier. fmaxf skips the NaNs
+        // of excluded slots; +1 covers a -0.0 maximum beside a +0.0 key.
+        {
+          float vmax = -__builtin_huge_valf();
+#pragma unroll
+          for (int c = 0; c < CH; ++c)
+            if (c < m)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) vmax = fmaxf(vmax, v[4 * c + j]);
+          const uint32_t kx = dpp_max_to_last(key_or_zero(vmax));
+          if (l == kWave - 1) sm.red[7][w] = kx == 0xFFFFFFFFu ? kx : kx + 1u;
+        }
         // A pivot that keeps fewer than k keys or more than the buffer holds is searched again
         // with a wider or narrower margin.
 #pragma unroll 1
@@ -532,7 +557,16 @@ SA_DEVICE void select_row(int t, const RowArgs& a, S& sm) {
             }
           }
         }
-        const Cut c2 = radix_select<kPer>(ck, R, (uint32_t)k1, sm);
+        uint32_t rlo, rhi;
+        {
+          const uint32_t kp = order_key(pf);   // every candidate is >= pf
+          rlo = kp > 0u ? kp : 1u;
+          const uint32_t rh = row_scan16(l < kNW ? sm.red[7][l] : 0u, 0u,
+                                         [](uint32_t a, uint32_t b) { return max(a, b); });
+          rhi = (uint32_t)__builtin_amdgcn_readlane((int)rh, kNW - 1);
+          rhi = rhi > rlo ? rhi : rlo;
+        }
+        const Cut c2 = radix_select_in<kPer>(ck, R, (uint32_t)k1, sm, rlo, rhi);
         // ranks: block-wide exclusive count of (greater, equal) in position order
         uint32_t ng = 0, ne = 0;
 #pragma unroll
