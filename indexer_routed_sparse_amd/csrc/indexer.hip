@@ -875,9 +875,13 @@ hipError_t launch_64(const IdxArgs& a0, int maxlen, hipStream_t st) {
   constexpr int TILE_BYTES = kKT * CPR * 16;
   const bool fused = a.topk > 0;
   a.cap = 0;
-  if (fused) {   // room above k: at least two tiles, so that a cut-back always frees a tile
+  if (fused) {
+    // room above k: at least two tiles, so that a cut-back always frees a tile, and as
+    // much more as the LDS holds (each cut-back then frees more room: fewer of them)
+    const size_t fixed = 2 * (size_t)TILE_BYTES + (size_t)kMaxWaves * 256 * 4 + 256;   // + static LDS
+    const int fit = (int)((160 * 1024 - fixed) / ((size_t)kMaxWaves * 8));
     const int extra = a.topk < 256 ? 256 : (a.topk > 1024 ? 1024 : a.topk);
-    a.cap = a.topk + extra;
+    a.cap = max(a.topk + extra, min(fit, 2 * a.topk + 2 * kKT));
   }
   const size_t shm = 2 * (size_t)TILE_BYTES + (size_t)kMaxWaves * 256 * 4 + (size_t)kMaxWaves * a.cap * 8;
   if (shm > 160 * 1024) return hipErrorInvalidValue;
