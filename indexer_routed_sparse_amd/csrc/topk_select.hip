@@ -713,7 +713,11 @@ template <int CH, int NT, bool CAND>
 hipError_t launch_rows_as(const RowArgs& a, int r0, int r1, hipStream_t st) {
   RowArgs b = a;
   b.row0 = r0;
-  if (a.topk > cap_of(NT, CH))
+  // Rows wider than k but at most 2k wide keep most of their keys as candidates: a radix
+  // select over the registers-held row costs less than sampling, pivoting and compacting
+  // them (rows up to k wide take every key, which the pivot kernel does without a select).
+  constexpr int64_t kSpanRow = (int64_t)(NT / kWave) * kSpan * CH;
+  if (a.topk > cap_of(NT, CH) || (kSpanRow > (int64_t)a.topk && kSpanRow <= 2 * (int64_t)a.topk))
     hipLaunchKernelGGL((topk_full_kernel<CH, NT, CAND>), dim3(r1 - r0), dim3(NT), 0, st, b);
   else
     hipLaunchKernelGGL((topk_pivot_kernel<CH, NT, CAND>), dim3(r1 - r0), dim3(NT), 0, st, b);
