@@ -158,6 +158,9 @@ def _cand_case(case, rng):
     elif case == "trend":              # scores rising with position
         v = (np.arange(32768)[None, :] * 1e-3 + rng.standard_normal((3, 32768))).astype(np.float32)
         k = 2048
+    elif case == "dup_bins":           # quarter steps: each radix bin holds a few repeated values
+        v = (1000.0 + 0.25 * rng.integers(0, 3000, (4, 20000))).astype(np.float32)
+        k = 2048
     elif case == "clustered":          # one dense cluster around the k-th value
         v = (100.0 + 1e-3 * rng.standard_normal((3, 32768))).astype(np.float32)
         k = 2048
@@ -170,7 +173,7 @@ def _cand_case(case, rng):
 
 
 @pytest.mark.parametrize("case", ["normal_64k", "ties_64k", "few_values", "zeros_infs", "big_topk",
-                                  "holes", "under_cap", "trend", "clustered"])
+                                  "holes", "under_cap", "trend", "clustered", "dup_bins"])
 def test_topk_select_candidate_stress(sa, case):
     rng = np.random.default_rng(11)
     v, cand, k = _cand_case(case, rng)
