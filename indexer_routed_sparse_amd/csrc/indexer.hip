@@ -25,6 +25,8 @@
 //     digits over order-preserving keys) and a stable in-place compaction. Because
 //     keys arrive in ascending index order, a later key equal to the k-th best can
 //     never enter (it loses the index tie-break), so a strict ">" filter is exact.
+#include <type_traits>
+
 #include "sa_common.h"
 #include "sa_kernels.h"
 
@@ -83,6 +85,20 @@ SA_DEVICE void lds_dma16_sv(uint32_t lds, const void* base, uint32_t voff) {
 // ---- wave-level exact top-k shrink of a candidate buffer (keys, idx) of n entries,
 //      stored in ascending index order. Keeps the first `k` under (key desc, index
 //      asc) in place, in index order, and returns the smallest kept key.
+// 32x32x16 bf16 MFMA with the A operand in AGPRs and the accumulator in VGPRs (the
+// builtin would put the accumulator in AGPRs, and every epilogue read would need a
+// copy). A VALU read of the result needs 19 wait states after the MFMA; the caller
+// provides them.
+SA_DEVICE floatx16_t idx_mfma_first(bf16x8_t a, bf16x8_t b) {
+  floatx16_t c;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "a"(a), "v"(b));
+  return c;
+}
+SA_DEVICE floatx16_t idx_mfma_acc(bf16x8_t a, bf16x8_t b, floatx16_t c) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "a"(a), "v"(b));
+  return c;
+}
+
 SA_DEVICE uint32_t wave_shrink(uint32_t* keys, int32_t* ids, int n, int k, uint32_t* hist) {
   const int L = lane_id();
   uint32_t prefix = 0, need = (uint32_t)k;
@@ -724,45 +740,77 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer64_kernel(IdxArgs args)
                                    // >= tau (after a cut-back the smallest kept key == tau)
   uint32_t kmax = 0u;              // largest key this lane appended
 
-  // S = Q . K^T of one tile (rows = 64 heads, columns = 64 keys), K^T operand slices
-  // read DA k-steps ahead
-  auto mfma_tile = [&](const char* tb, floatx16_t (&S)[2][2]) {
+  // S = Q . K^T of one tile in two key halves, S0 = keys 0..31 and S1 = keys 32..63,
+  // each as two 32x32 blocks of heads (mt). The accumulators live in VGPRs (inline-asm
+  // MFMAs) so that the epilogue reads them without copies; the q slices are the A
+  // operands, held in AGPRs. K^T operand slices are read DA k-steps ahead, over the
+  // 2 x KSTEPS slices of a tile in order (half nt, k-step kn: slice KSTEPS nt + kn).
+  constexpr int NSL = 2 * KSTEPS;
+  constexpr int VPP = 32 / KSTEPS;            // epilogue values per k-step
+  floatx16_t S0[2], S1[2];
+  bf16x8_t ring[DA];
+  auto slice_load = [&](const char* tb, int i) __attribute__((always_inline)) {
+    ring[i % DA] = *reinterpret_cast<const bf16x8_t*>(tb + b_off[i / KSTEPS][i % KSTEPS]);
+  };
+  auto tile_start = [&](const char* tb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int i = 0; i < DA; ++i) slice_load(tb, i);
+  };
+  // ReLU, head weight, head sum of one key half: each lane sums its 32 (head, key)
+  // products in (mt, sg) order; one lane-half swap completes the 64-head sum.
+  auto epi_part = [&](const floatx16_t (&S)[2], int j, float acc) __attribute__((always_inline)) {
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) S[mt][nt] = floatx16_t{};
-    bf16x8_t ring[DA][2];
-#pragma unroll
-    for (int i = 0; i < DA; ++i)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) ring[i][nt] = *reinterpret_cast<const bf16x8_t*>(tb + b_off[nt][i]);
+    for (int u = 0; u < VPP; ++u) {
+      const int v = VPP * j + u, mt = v >> 4, sg = v & 15;
+      acc = fmaf(wr[mt][sg], __builtin_elementwise_maximum(S[mt][sg], 0.0f), acc);
+    }
+    return acc;
+  };
+  auto epi_end = [&](float acc) __attribute__((always_inline)) {
+    const float2_t h2 = lane_halves(acc);
+    return h2.x + h2.y;
+  };
+  // The MFMAs of key half nt of the tile at tb into Sd; with EPI, the epilogue of Se
+  // rides along, one slice per k-step. Se's last MFMA was issued before this call:
+  // the leading s_nops give a VALU read of its result the wait states it needs.
+  auto half = [&](auto epi_t, const char* tb, int nt, floatx16_t (&Sd)[2], const floatx16_t (&Se)[2])
+      __attribute__((always_inline)) -> float {
+    constexpr bool EPI = decltype(epi_t)::value;
+    float acc = 0.0f;
+    // The empty asm statements keep the epilogue where it is written: Se passes through
+    // one here (so its ReLUs are not hoisted into a common block before the caller's
+    // branch), and each k-step's partial sum through another (so its slice is not
+    // sunk past the later MFMAs).
+    floatx16_t E[2] = {Se[0], Se[1]};
+    if constexpr (EPI) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(E[0]), "+v"(E[1]));
 #pragma unroll
     for (int kn = 0; kn < KSTEPS; ++kn) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const bf16x8_t b = ring[kn % DA][nt];
-        if (kn + DA < KSTEPS) ring[kn % DA][nt] = *reinterpret_cast<const bf16x8_t*>(tb + b_off[nt][kn + DA]);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-          S[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][kn], b, S[mt][nt], 0, 0, 0);
-      }
-    }
-  };
-  // ReLU, head weight, head sum; lane L gets the score of key k0 + L (+0.0 for -0.0)
-  auto epilogue = [&](const floatx16_t (&S)[2][2]) {
-    float tot[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      float acc = 0.0f;
+      const int i = KSTEPS * nt + kn;
+      const bf16x8_t b = ring[i % DA];
+      if (i + DA < NSL) slice_load(tb, i + DA);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int sg = 0; sg < 16; ++sg)
-          acc = fmaf(wr[mt][sg], __builtin_elementwise_maximum(S[mt][nt][sg], 0.0f), acc);
-      const float2_t h2 = lane_halves(acc);
-      tot[nt] = h2.x + h2.y;
+        Sd[mt] = kn == 0 ? idx_mfma_first(qa[mt][0], b) : idx_mfma_acc(qa[mt][kn], b, Sd[mt]);
+      if constexpr (EPI) {
+        acc = epi_part(E, kn, acc);
+        asm volatile("" : "+v"(acc));
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    float sc = hl ? tot[1] : tot[0];
+    return EPI ? epi_end(acc) : 0.0f;
+  };
+  // epilogue of one half without MFMAs (the wave's last tile)
+  auto epi_only = [&](const floatx16_t (&Se)[2]) __attribute__((always_inline)) -> float {
+    floatx16_t E[2] = {Se[0], Se[1]};
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(E[0]), "+v"(E[1]));
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < KSTEPS; ++j) acc = epi_part(E, j, acc);
+    return epi_end(acc);
+  };
+  // lane L's score of key k0 + L (+0.0 for -0.0): keys 0..31 from tot0, 32..63 from tot1
+  auto score_of = [&](float tot0, float tot1) __attribute__((always_inline)) {
+    const float sc = hl ? tot1 : tot0;
     return sc == 0.0f ? 0.0f : sc;
   };
   // Cut-back: one histogram pass keeps the buckets that hold the top k (a little more
@@ -809,41 +857,35 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer64_kernel(IdxArgs args)
     __builtin_amdgcn_wave_barrier();
   };
 
-  // Software pipeline: iteration `tile` runs the MFMAs of tile+1 interleaved with the
-  // epilogue of tile (whose S is already in registers), then the selection of tile.
-  // Two iterations per loop trip, so the two S sets swap roles without copies.
-  auto iter = [&](int tile, const floatx16_t (&Scur)[2][2], floatx16_t (&Snext)[2][2]) {
-    wait_vmcnt0();
-    __syncthreads();                      // tile+1 resident; every wave is done with tile
-    if (tile + 2 < ntiles) gather(tile + 2);
-    if (fused && s_req == tile - 1 && n > a.topk) cut_back();
-    if (tile >= my_tiles) return;         // wave-uniform: no causal key of t left
-    float sc;
-    if (tile + 1 < my_tiles) {
-      mfma_tile(ktiles + ((tile + 1) & 1) * TILE_BYTES, Snext);
-      sc = epilogue(Scur);
-      // one MFMA, then a share of the epilogue's VALU work, 32 times
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
-      }
-    } else {
-      sc = epilogue(Scur);
-    }
-    select(sc, tile);
-  };
-  floatx16_t SA[2][2], SB[2][2];
+  // Software pipeline over key halves: iteration `tile` runs the first half's MFMAs of
+  // tile+1 with the epilogue of tile's second half, selects tile, then runs the second
+  // half's MFMAs of tile+1 with the epilogue of its first half (kept in tot0).
+  float tot0 = 0.0f;
   gather(0);
   wait_vmcnt0();
   __syncthreads();                        // tile 0 resident, s_req initialised
   if (ntiles > 1) gather(1);
-  if (my_tiles > 0) mfma_tile(ktiles, SA);
+  if (my_tiles > 0) {
+    tile_start(ktiles);
+    half(std::false_type{}, ktiles, 0, S0, S1);
+    tot0 = half(std::true_type{}, ktiles, 1, S1, S0);
+  }
 #pragma unroll 1
-  for (int tile = 0; tile < ntiles; tile += 2) {
-    iter(tile, SA, SB);
-    if (tile + 1 < ntiles) iter(tile + 1, SB, SA);
+  for (int tile = 0; tile < ntiles; ++tile) {
+    wait_vmcnt0();
+    __syncthreads();                      // tile+1 resident; every wave is done with tile
+    if (tile + 2 < ntiles) gather(tile + 2);
+    if (fused && s_req == tile - 1 && n > a.topk) cut_back();
+    if (tile >= my_tiles) continue;       // wave-uniform: no causal key of t left
+    if (tile + 1 < my_tiles) {
+      const char* tb = ktiles + ((tile + 1) & 1) * TILE_BYTES;
+      tile_start(tb);
+      const float tot1 = half(std::true_type{}, tb, 0, S0, S1);
+      select(score_of(tot0, tot1), tile);
+      tot0 = half(std::true_type{}, tb, 1, S1, S0);
+    } else {
+      select(score_of(tot0, epi_only(S1)), tile);
+    }
   }
 
   if (!fused || !active) return;

@@ -225,6 +225,26 @@ def test_indexer_dense_integer_exact(sa, name, T, B):
     np.testing.assert_array_equal(got, ref)
 
 
+def test_indexer64_head_dim_64(sa):
+    """64 indexer heads of dimension 64 (the 64-head kernel's other instantiation): dense
+    scores equal the oracle on the integer grid, and the fused selection equals the
+    select over those scores, bit for bit, with a ragged last tile."""
+    import dataclasses
+    wl = dataclasses.replace(W["long_dsa"], D_I=64)
+    T = 1000
+    x = workloads.indexer_inputs(wl, integer=True, T=T)
+    assert x["q_I"].shape == (T, 64, 64)
+    ref = oracle.indexer_scores_dense(x["q_I"], x["k_I"], x["w"])
+    xd = {n: t.to(DEV) for n, t in x.items()}
+    dense = sa.indexer_scores(xd["q_I"], xd["k_I"], xd["w"])
+    np.testing.assert_array_equal(dense.cpu().numpy()[:, :ref.shape[1]], ref)
+    for k in (100, 513):
+        i1, v1 = sa.topk_select(dense, k, with_values=True)
+        i2, v2 = sa.indexer_topk(xd["q_I"], xd["k_I"], xd["w"], k, with_values=True)
+        assert torch.equal(i1, i2), f"k={k}"
+        assert torch.equal(v1, v2), f"k={k}"
+
+
 @pytest.mark.parametrize("name,T", [("tiny_fp32", None), ("nope_unaligned", None), ("long_dsa", 1536)])
 def test_indexer_dense_normal_within_bound(sa, name, T):
     # fp32 accumulation of bf16 products: |err| <= (D_I + H_I) * 2^-24 * B[t,s] with
