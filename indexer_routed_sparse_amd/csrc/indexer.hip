@@ -82,9 +82,6 @@ SA_DEVICE void lds_dma16_sv(uint32_t lds, const void* base, uint32_t voff) {
                : "memory");
 }
 
-// ---- wave-level exact top-k shrink of a candidate buffer (keys, idx) of n entries,
-//      stored in ascending index order. Keeps the first `k` under (key desc, index
-//      asc) in place, in index order, and returns the smallest kept key.
 // 32x32x16 bf16 MFMA with the A operand in AGPRs and the accumulator in VGPRs (the
 // builtin would put the accumulator in AGPRs, and every epilogue read would need a
 // copy). A VALU read of the result needs 19 wait states after the MFMA; the caller
@@ -99,6 +96,9 @@ SA_DEVICE floatx16_t idx_mfma_acc(bf16x8_t a, bf16x8_t b, floatx16_t c) {
   return c;
 }
 
+// ---- wave-level exact top-k shrink of a candidate buffer (keys, idx) of n entries,
+//      stored in ascending index order. Keeps the first `k` under (key desc, index
+//      asc) in place, in index order, and returns the smallest kept key.
 SA_DEVICE uint32_t wave_shrink(uint32_t* keys, int32_t* ids, int n, int k, uint32_t* hist) {
   const int L = lane_id();
   uint32_t prefix = 0, need = (uint32_t)k;
@@ -642,7 +642,7 @@ SA_DEVICE int wave_cut(uint32_t* keys, int32_t* ids, int n, int k, int limit, ui
 //     buffer; a full buffer is cut back to exactly k by wave_select, whose smallest
 //     kept key becomes the new threshold. Keys arrive in ascending index order, so a
 //     later key equal to a kept one never wins and the strict filter is exact.
-template <int DI>
+template <int DI, bool SPREAD>
 __global__ __launch_bounds__(kMaxWaves * 64) void indexer64_kernel(IdxArgs args) {
   const IdxArgs a = args;   // local copy: lambdas capture it without a private-memory copy of the kernel argument
   constexpr int CPR = DI * 2 / 16;            // 16-byte chunks per key row
@@ -707,6 +707,21 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer64_kernel(IdxArgs args)
     const int r = p / CPR;
     g_off[j] = (uint32_t)(r * DI * 2 + 16 * ((p % CPR) ^ kswz<CPR>(r)));
   }
+  auto gather_one = [&](int tile, int j) __attribute__((always_inline)) {
+    const uint32_t base = (uint32_t)(uintptr_t)(SA_LDS char*)(ktiles + (tile & 1) * TILE_BYTES);
+    const int k0 = __builtin_amdgcn_readfirstlane(cs + tile * kKT);
+    if (k0 + kKT <= a.T) {
+      const char* src = reinterpret_cast<const char*>(a.k) + (int64_t)k0 * DI * 2;
+      lds_dma16_sv(base + (w + kMaxWaves * j) * 1024, src, g_off[j]);
+    } else {                                // last tile of the key array: clamp rows
+      const int p = 64 * (w + kMaxWaves * j) + L;
+      const int r = p / CPR;
+      const int c = (p % CPR) ^ kswz<CPR>(r);
+      const int row = min(k0 + r, a.T - 1);
+      lds_dma16(base + (w + kMaxWaves * j) * 1024,
+                reinterpret_cast<const char*>(a.k) + ((int64_t)row * DI) * 2 + 16 * c);
+    }
+  };
   auto gather = [&](int tile) __attribute__((always_inline)) {
     const uint32_t base = (uint32_t)(uintptr_t)(SA_LDS char*)(ktiles + (tile & 1) * TILE_BYTES);
     const int k0 = __builtin_amdgcn_readfirstlane(cs + tile * kKT);
@@ -714,16 +729,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer64_kernel(IdxArgs args)
       const char* src = reinterpret_cast<const char*>(a.k) + (int64_t)k0 * DI * 2;
 #pragma unroll
       for (int j = 0; j < NG; ++j) lds_dma16_sv(base + (w + kMaxWaves * j) * 1024, src, g_off[j]);
-    } else {                                // last tile of the key array: clamp rows
+    } else {
 #pragma unroll
-      for (int j = 0; j < NG; ++j) {
-        const int p = 64 * (w + kMaxWaves * j) + L;
-        const int r = p / CPR;
-        const int c = (p % CPR) ^ kswz<CPR>(r);
-        const int row = min(k0 + r, a.T - 1);
-        lds_dma16(base + (w + kMaxWaves * j) * 1024,
-                  reinterpret_cast<const char*>(a.k) + ((int64_t)row * DI) * 2 + 16 * c);
-      }
+      for (int j = 0; j < NG; ++j) gather_one(tile, j);
     }
   };
 
@@ -773,8 +781,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer64_kernel(IdxArgs args)
   // The MFMAs of key half nt of the tile at tb into Sd; with EPI, the epilogue of Se
   // rides along, one slice per k-step. Se's last MFMA was issued before this call:
   // the leading s_nops give a VALU read of its result the wait states it needs.
-  auto half = [&](auto epi_t, const char* tb, int nt, floatx16_t (&Sd)[2], const floatx16_t (&Se)[2])
-      __attribute__((always_inline)) -> float {
+  auto half = [&](auto epi_t, const char* tb, int nt, floatx16_t (&Sd)[2], const floatx16_t (&Se)[2],
+                  int gtile = -1) __attribute__((always_inline)) -> float {
     constexpr bool EPI = decltype(epi_t)::value;
     float acc = 0.0f;
     // The empty asm statements keep the epilogue where it is written: Se passes through
@@ -795,6 +803,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer64_kernel(IdxArgs args)
         acc = epi_part(E, kn, acc);
         asm volatile("" : "+v"(acc));
       }
+      // a tile gather's DMAs, one per k-step from the first: each DMA's issue then
+      // overlaps the MFMAs instead of stalling the wave before them, and the copy
+      // still starts early in the tile
+      if (gtile >= 0 && kn < NG) gather_one(gtile, kn);
       __builtin_amdgcn_sched_barrier(0);
     }
     return EPI ? epi_end(acc) : 0.0f;
@@ -874,13 +886,19 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer64_kernel(IdxArgs args)
   for (int tile = 0; tile < ntiles; ++tile) {
     wait_vmcnt0();
     __syncthreads();                      // tile+1 resident; every wave is done with tile
-    if (tile + 2 < ntiles) gather(tile + 2);
+    // The gather of tile+2 refills the buffer every wave finished reading before the
+    // barrier. With SPREAD (the dense launch) a wave with MFMAs to issue spreads its
+    // DMAs over the first half, which measured faster there; the fused launch issues
+    // them at once, before a possible cut-back (spreading them measured slower there).
+    const int gt = tile + 2 < ntiles ? tile + 2 : -1;
+    const bool spread = SPREAD && tile + 1 < my_tiles;
+    if (gt >= 0 && !spread) gather(gt);
     if (fused && s_req == tile - 1 && n > a.topk) cut_back();
     if (tile >= my_tiles) continue;       // wave-uniform: no causal key of t left
     if (tile + 1 < my_tiles) {
       const char* tb = ktiles + ((tile + 1) & 1) * TILE_BYTES;
       tile_start(tb);
-      const float tot1 = half(std::true_type{}, tb, 0, S0, S1);
+      const float tot1 = half(std::true_type{}, tb, 0, S0, S1, SPREAD ? gt : -1);
       select(score_of(tot0, tot1), tile);
       tot0 = half(std::true_type{}, tb, 1, S1, S0);
     } else {
@@ -929,10 +947,13 @@ hipError_t launch_64(const IdxArgs& a0, int maxlen, hipStream_t st) {
   if (shm > 160 * 1024) return hipErrorInvalidValue;
   a.nwave = kMaxWaves;
   a.chunks = (maxlen + kMaxWaves - 1) / kMaxWaves;
-  hipError_t e = hipFuncSetAttribute((const void*)indexer64_kernel<DI>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  const void* kern = fused ? (const void*)indexer64_kernel<DI, false> : (const void*)indexer64_kernel<DI, true>;
+  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((indexer64_kernel<DI>), dim3(a.chunks, a.nseq), dim3(kMaxWaves * 64), shm, st, a);
+  if (fused)
+    hipLaunchKernelGGL((indexer64_kernel<DI, false>), dim3(a.chunks, a.nseq), dim3(kMaxWaves * 64), shm, st, a);
+  else
+    hipLaunchKernelGGL((indexer64_kernel<DI, true>), dim3(a.chunks, a.nseq), dim3(kMaxWaves * 64), shm, st, a);
   return hipGetLastError();
 }
 
