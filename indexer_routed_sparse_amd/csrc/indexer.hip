@@ -559,31 +559,41 @@ SA_DEVICE uint32_t wave_select(uint32_t* keys, int32_t* ids, int n, int k, uint3
 }
 
 // ---- one-pass cut-back of a candidate buffer: keys[0..n) (order keys in [lo, hi]),
-//      ids[0..n), ascending index order. Histograms [lo, hi] into 256 buckets, finds
+//      ids[0..n), ascending index order, in a buffer of `cap` entries (cap a multiple
+//      of 4, both arrays 16-byte aligned). Histograms [lo, hi] into 256 buckets, finds
 //      the lowest bucket b such that the buckets from b up hold at least k keys, and
 //      keeps (stably, in place) every key >= the lower edge of b. The kept set always
 //      contains the exact top-k, so the caller may raise its threshold to that edge
-//      minus one. Returns the number kept; if the top bucket alone holds more than
+//      minus one. Returns the number kept; if the buckets from b up hold more than
 //      `limit` keys (massive ties) nothing is dropped and n is returned.
-SA_DEVICE int wave_cut(uint32_t* keys, int32_t* ids, int n, int k, int limit, uint32_t* hist,
+//      Lane L takes entries 4L..4L+3 of each 256-entry batch with 16-byte reads (reads
+//      past n are clamped into the buffer and masked), the loops run on a wave-uniform
+//      count, and the compaction places each kept entry by ballot counts.
+SA_DEVICE int wave_cut(uint32_t* keys, int32_t* ids, int n, int cap, int k, int limit, uint32_t* hist,
                        uint32_t lo, uint32_t hi, uint32_t& edge) {
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
   const int L = lane_id();
+  n = __builtin_amdgcn_readfirstlane(n);
   const uint32_t span = hi - lo;
   const int shift = span >= 256u ? (32 - __builtin_clz(span)) - 8 : 0;
 #pragma unroll
   for (int r = 0; r < 4; ++r) hist[4 * L + r] = 0u;
   __builtin_amdgcn_wave_barrier();
-  int e = L;
 #pragma unroll 1
-  for (; e + 448 < n; e += 512) {          // eight independent reads in flight
-    uint32_t x[8];
+  for (int base = 0; base < n; base += 512) {   // two batches of reads in flight
+    u32x4_t x[2];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) x[u] = keys[e + 64 * u];
+    for (int u = 0; u < 2; ++u)
+      x[u] = *reinterpret_cast<const u32x4_t*>(keys + min(base + 256 * u + 4 * L, cap - 4));
 #pragma unroll
-    for (int u = 0; u < 8; ++u) atomicAdd(&hist[(x[u] - lo) >> shift], 1u);
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {     // masked entries add 0 to bucket 0: no branch
+        const bool in = base + 256 * u + 4 * L + j < n;
+        atomicAdd(&hist[in ? (x[u][j] - lo) >> shift : 0u], in ? 1u : 0u);
+      }
   }
-#pragma unroll 1
-  for (; e < n; e += 64) atomicAdd(&hist[(keys[e] - lo) >> shift], 1u);
   __builtin_amdgcn_wave_barrier();
   uint32_t c[4], sum = 0;
 #pragma unroll
@@ -604,26 +614,31 @@ SA_DEVICE int wave_cut(uint32_t* keys, int32_t* ids, int n, int k, int limit, ui
   if (kept > limit) { edge = lo; return n; }
   edge = lo + (d << shift);
   const uint32_t thr = edge;
+  // A batch's reads all land before its writes, and every write goes at or below its
+  // own source, below the next batch's reads.
   int out = 0;
 #pragma unroll 1
   for (int base = 0; base < n; base += 4 * kWave) {
-    uint32_t kk[4];
-    int32_t id[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = base + 64 * u + L;
-      kk[u] = i < n ? keys[i] : 0u;
-      id[u] = i < n ? ids[i] : 0;
-    }
+    const int e = min(base + 4 * L, cap - 4);
+    const u32x4_t kk = *reinterpret_cast<const u32x4_t*>(keys + e);
+    const i32x4_t id = *reinterpret_cast<const i32x4_t*>(ids + e);
     __builtin_amdgcn_wave_barrier();
+    bool take[4];
+    uint32_t below = 0, cnt = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const bool take = base + 64 * u + L < n && kk[u] >= thr;
-      const uint64_t tb = ballot(take);
-      const int pos = out + (int)mbcnt(tb);
-      if (take) { keys[pos] = kk[u]; ids[pos] = id[u]; }
-      out += __popcll(tb);
+    for (int j = 0; j < 4; ++j) {
+      take[j] = base + 4 * L + j < n && kk[j] >= thr;
+      const uint64_t tb = ballot(take[j]);
+      below += mbcnt(tb);                 // kept entries of the lower lanes, slot j
+      cnt += (uint32_t)__popcll(tb);
     }
+    int pos = out + (int)below;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (take[j]) { keys[pos] = kk[j]; ids[pos] = id[j]; }
+      pos += take[j] ? 1 : 0;
+    }
+    out += (int)cnt;
     __builtin_amdgcn_wave_barrier();
   }
   return out;
@@ -834,7 +849,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer64_kernel(IdxArgs args)
     // after a cut-back one more tile (kKT keys) must still fit: kept <= cap - kKT
     const int limit = a.topk + (a.cap - a.topk - kKT) / 2;
     uint32_t edge;
-    const int kept = wave_cut(keys, ids, n, a.topk, limit, whist, tau, hi, edge);
+    const int kept = wave_cut(keys, ids, n, a.cap, a.topk, limit, whist, tau, hi, edge);
     if (kept <= limit) {
       n = kept;
       tau = edge - 1u;                  // every held key is > edge - 1 = tau
@@ -942,6 +957,7 @@ hipError_t launch_64(const IdxArgs& a0, int maxlen, hipStream_t st) {
     const int fit = (int)((160 * 1024 - fixed) / ((size_t)kMaxWaves * 8));
     const int extra = a.topk < 256 ? 256 : (a.topk > 1024 ? 1024 : a.topk);
     a.cap = max(a.topk + extra, min(fit, 2 * a.topk + 2 * kKT));
+    a.cap &= ~63;                         // 16-byte aligned buffers for the cut-back's reads
   }
   const size_t shm = 2 * (size_t)TILE_BYTES + (size_t)kMaxWaves * 256 * 4 + (size_t)kMaxWaves * a.cap * 8;
   if (shm > 160 * 1024) return hipErrorInvalidValue;
