@@ -654,9 +654,13 @@ SA_DEVICE int wave_cut(uint32_t* keys, int32_t* ids, int n, int cap, int k, int 
 //   * dense mode stores the scores (one coalesced 256-byte row segment per tile);
 //     fused mode compares each lane's key with the running threshold held in a
 //     register and appends the winners, in index order, to the token's LDS candidate
-//     buffer; a full buffer is cut back to exactly k by wave_select, whose smallest
-//     kept key becomes the new threshold. Keys arrive in ascending index order, so a
-//     later key equal to a kept one never wins and the strict filter is exact.
+//     buffer; a nearly full buffer is cut back by wave_cut (one histogram pass keeps
+//     the buckets that hold the top k, and the kept edge becomes the new threshold),
+//     or by the exact wave_select when ties defeat the histogram; the exact select also
+//     finishes the row. Keys arrive in ascending index order, so a later key equal to
+//     a kept one never wins and the strict filter is exact.
+// SPREAD (the dense launch): a wave spreads its share of the next gather over the
+// first key half's MFMAs instead of issuing it right after the barrier.
 template <int DI, bool SPREAD>
 __global__ __launch_bounds__(kMaxWaves * 64) void indexer64_kernel(IdxArgs args) {
   const IdxArgs a = args;   // local copy: lambdas capture it without a private-memory copy of the kernel argument
