@@ -102,7 +102,7 @@ constexpr size_t mla_lds_bytes(int topk) {
 // VGPRs) and publishes its P tile in LDS; then every wave accumulates O for ALL
 // heads over its own 512/NW output channels, so each V element is read from LDS
 // by one wave only. NST gather stages.
-template <int NW, int DQK, int NST, int NKL>
+template <int NW, int DQK, int NST, int NKL, bool NEG>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                             const int32_t* __restrict__ idx, int H, int topk, float scale_log2,
@@ -347,15 +347,15 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
         float mx;
         uint32_t okbits = 0xFFFFu;          // bit sg: slot sg of this lane is valid
         if constexpr (FULL) {
-          float hi = S[0], lo = S[0];
+          // NEG (a negative scale, chosen at launch): the largest scaled logit is the
+          // smallest raw one
+          float e = S[0];
 #pragma unroll
-          for (int sg = 1; sg < 15; sg += 2) {
-            hi = __builtin_elementwise_maximum(__builtin_elementwise_maximum(hi, S[sg]), S[sg + 1]);
-            lo = __builtin_elementwise_minimum(__builtin_elementwise_minimum(lo, S[sg]), S[sg + 1]);
-          }
-          hi = __builtin_elementwise_maximum(hi, S[15]);
-          lo = __builtin_elementwise_minimum(lo, S[15]);
-          mx = (scale_log2 >= 0.0f ? hi : lo) * scale_log2;
+          for (int sg = 1; sg < 15; sg += 2)
+            e = NEG ? __builtin_elementwise_minimum(__builtin_elementwise_minimum(e, S[sg]), S[sg + 1])
+                    : __builtin_elementwise_maximum(__builtin_elementwise_maximum(e, S[sg]), S[sg + 1]);
+          e = NEG ? __builtin_elementwise_minimum(e, S[15]) : __builtin_elementwise_maximum(e, S[15]);
+          mx = e * scale_log2;
         } else {
           // the volatile asm keeps the mask arithmetic inside this rarely taken branch
           // (otherwise it is hoisted above the branch and paid by every full tile)
@@ -553,7 +553,8 @@ hipError_t launch_bf16(const void* q, const void* kv, const int32_t* idx, int T,
   constexpr int NKL = q_in_lds<NW, DQK>();
   const size_t shm = mla_lds_bytes<NW, DQK, kStages, NKL>(topk);
   if (shm > kLdsLimit) return hipErrorInvalidValue;
-  auto kern = sparse_mla_bf16_kernel<NW, DQK, kStages, NKL>;
+  auto kern = scale < 0.0f ? sparse_mla_bf16_kernel<NW, DQK, kStages, NKL, true>
+                           : sparse_mla_bf16_kernel<NW, DQK, kStages, NKL, false>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(T), dim3(NW * 64), shm, st, (const uint16_t*)q, (const uint16_t*)kv,

@@ -426,6 +426,24 @@ def test_sparse_mla_trailing_masked_tiles(sa, H):
     close(lse.cpu().numpy(), rl, **BF16_TOL, what="lse")
 
 
+@pytest.mark.parametrize("H", [16, 128])
+def test_sparse_mla_negative_scale(sa, H):
+    # the caller's scale is used as given, sign included: with a negative scale the
+    # largest logit comes from the smallest raw product (full and masked tiles)
+    T, S, k = 6, 400, 96
+    g = torch.Generator().manual_seed(5)
+    q = torch.randn((T, H, 576), generator=g).to(torch.bfloat16)
+    kv = torch.randn((S, 576), generator=g).to(torch.bfloat16)
+    idx = torch.randint(0, S, (T, k), generator=g, dtype=torch.int32)
+    idx[1, 40:] = -1
+    idx[2, 5::3] = -1
+    scale = -(576 ** -0.5)
+    out, lse = sa.sparse_mla(q.to(DEV), kv.to(DEV), idx.to(DEV), scale)
+    ro, rl = oracle.sparse_mla(q, kv, idx.numpy(), scale)
+    close(out.float().cpu().numpy(), ro, **BF16_TOL, what="out")
+    close(lse.cpu().numpy(), rl, **BF16_TOL, what="lse")
+
+
 @pytest.mark.parametrize("name", ["long_dsa", "thd_varlen"])
 def test_sparse_mla_full_size_sampled(sa, name):
     wl = W[name]
