@@ -348,7 +348,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer_kernel(IdxArgs a) {
           }
 #pragma unroll
         for (int i = 0; i < TW; ++i) {
-          const float v = acc[i] + __shfl_xor(acc[i], 32, kWave);
+          const float2_t h = lane_halves(acc[i]);   // own + the other lane half's
+          const float v = h.x + h.y;
           if (hl == 0) wst[i * kKT + key] = v;
         }
       } else {   // HI == 4: each token's 4 rows sit in one lane
@@ -397,7 +398,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer_kernel(IdxArgs a) {
         bool emit;
         int blk;
         if (B <= kKT) {
-          for (int o = 1; o < B; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+          m = group_max(m, B);
           blk = off / B;
           emit = (L % B == 0) && (k0 + L <= t);
         } else {

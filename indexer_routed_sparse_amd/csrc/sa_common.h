@@ -108,11 +108,27 @@ SA_DEVICE float quad_sum(float x) {
   return b.x + b.y;
 }
 
-SA_DEVICE float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
+// x from another lane through one DPP move (CTRL a constant dpp_ctrl code).
+template <int CTRL>
+SA_DEVICE float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Max over the aligned groups of B lanes (B a power of two, 1..64), in every lane of
+// each group: two quad permutes, the half-row and row mirrors, then the 16- and
+// 32-lane swaps. Each step pairs every lane with one of the other half of its group,
+// so no value goes through LDS.
+SA_DEVICE float group_max(float x, int B) {
+  if (B >= 2) x = fmaxf(x, dpp_f32<0xB1>(x));    // quad_perm [1,0,3,2]
+  if (B >= 4) x = fmaxf(x, dpp_f32<0x4E>(x));    // quad_perm [2,3,0,1]
+  if (B >= 8) x = fmaxf(x, dpp_f32<0x141>(x));   // row_half_mirror
+  if (B >= 16) x = fmaxf(x, dpp_f32<0x140>(x));  // row_mirror
+  if (B >= 32) { const float2_t r = lane_rows16(x); x = fmaxf(r.x, r.y); }
+  if (B >= 64) { const float2_t h = lane_halves(x); x = fmaxf(h.x, h.y); }
   return x;
 }
+
+SA_DEVICE float wave_max(float x) { return group_max(x, kWave); }
 
 SA_DEVICE void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
