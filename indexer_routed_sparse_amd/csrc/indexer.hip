@@ -130,9 +130,9 @@ SA_DEVICE uint32_t wave_shrink(uint32_t* keys, int32_t* ids, int n, int k, uint3
     }
     const uint64_t fb = ballot(found >= 0);
     const int src = (int)__builtin_ctzll(fb);
-    const uint32_t d = (uint32_t)__shfl(found, src, kWave);
-    const uint32_t above = __shfl(above_f, src, kWave);
-    const uint32_t cnt = __shfl(cnt_f, src, kWave);
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane(found, src);
+    const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)above_f, src);
+    const uint32_t cnt = (uint32_t)__builtin_amdgcn_readlane((int)cnt_f, src);
     __builtin_amdgcn_wave_barrier();
     prefix = (prefix << 8) | d;
     need -= above;
@@ -508,9 +508,9 @@ SA_DEVICE uint32_t wave_select(uint32_t* keys, int32_t* ids, int n, int k, uint3
       if (above < need && run >= need) { found = 255 - 4 * L - r; above_f = above; cnt_f = c[r]; }
     }
     const int src = (int)__builtin_ctzll(ballot(found >= 0));
-    const uint32_t d = (uint32_t)__shfl(found, src, kWave);
-    const uint32_t above = __shfl(above_f, src, kWave);
-    const uint32_t cnt = __shfl(cnt_f, src, kWave);
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane(found, src);
+    const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)above_f, src);
+    const uint32_t cnt = (uint32_t)__builtin_amdgcn_readlane((int)cnt_f, src);
     __builtin_amdgcn_wave_barrier();
     need -= above;
     const uint32_t blo = wlo + (d << shift);
@@ -609,8 +609,8 @@ SA_DEVICE int wave_cut(uint32_t* keys, int32_t* ids, int n, int cap, int k, int 
     if (above < (uint32_t)k && run >= (uint32_t)k) { found = 255 - 4 * L - r; upto_f = run; }
   }
   const int src = (int)__builtin_ctzll(ballot(found >= 0));
-  const uint32_t d = (uint32_t)__shfl(found, src, kWave);
-  const int kept = (int)__shfl(upto_f, src, kWave);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane(found, src);
+  const int kept = __builtin_amdgcn_readlane((int)upto_f, src);
   __builtin_amdgcn_wave_barrier();
   if (kept > limit) { edge = lo; return n; }
   edge = lo + (d << shift);

@@ -68,14 +68,16 @@ SA_DEVICE int seq_start_of(const int32_t* __restrict__ cu, int nseq, int t) {
   return __ldg(cu + lo);
 }
 
-// Wave-wide inclusive scan of a 32-bit value.
+// Wave-wide inclusive scan of a 32-bit value: shifts by 1, 2, 4 and 8 inside each row
+// of 16 lanes, then row 0's last lane into row 1 (and 2's into 3), then lane 31 into
+// rows 2 and 3 (DPP row shifts and row broadcasts; out-of-row sources read 0).
 SA_DEVICE uint32_t wave_incl_scan(uint32_t x) {
-  const int l = lane_id();
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    uint32_t y = __shfl_up(x, off, kWave);
-    if (l >= off) x += y;
-  }
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return x;
 }
 
