@@ -312,12 +312,23 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer_kernel(IdxArgs a) {
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) S[mt][nt] = floatx16_t{};
+    // bf16: the K^T slices are read DA k-steps ahead of their MFMAs (read just before
+    // each MFMA pair, every k-step waited out a whole LDS latency)
+    constexpr int DA = 4;
+    bf16x8_t ring[BF16 ? DA : 1][2];
+    if constexpr (BF16) {
+#pragma unroll
+      for (int i = 0; i < DA; ++i)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) ring[i][nt] = *reinterpret_cast<const bf16x8_t*>(tb + b_off[nt][i]);
+    }
 #pragma unroll
     for (int n = 0; n < KSTEPS; ++n) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         if constexpr (BF16) {
-          const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(tb + b_off[nt][n]);
+          const bf16x8_t b = ring[n % DA][nt];
+          if (n + DA < KSTEPS) ring[n % DA][nt] = *reinterpret_cast<const bf16x8_t*>(tb + b_off[nt][n + DA]);
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt)
             S[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][n], b, S[mt][nt], 0, 0, 0);
@@ -328,6 +339,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer_kernel(IdxArgs a) {
             S[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[mt][n], b, S[mt][nt], 0, 0, 0);
         }
       }
+      if constexpr (BF16) __builtin_amdgcn_sched_barrier(0);   // keep each k-step's read-ahead in place
     }
 
     // ---- ReLU, head weight, head sum; stage one score per (token, key)
