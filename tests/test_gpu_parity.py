@@ -260,6 +260,31 @@ def test_indexer_dense_normal_within_bound(sa, name, T):
     assert np.all(np.abs(got[fin] - ref[fin]) <= 2e-5 * bound[fin] + 1e-30)
 
 
+@pytest.mark.parametrize("B", [16, 32, 128, 256])
+def test_indexer_block_sizes_integer_exact(sa, B):
+    """Block mode at every other supported block size (the block max runs over a lane
+    group of B lanes up to 64, and across key tiles above): dense block scores equal
+    the oracle on the integer grid, and the fused top-k with the own block forced equals
+    the oracle's, on one sequence and on packed sequences with ragged lengths."""
+    wl = W["block_gqa"]
+    for lengths in [(1000,), (300, 7, 520, 129)]:
+        T = sum(lengths)
+        x = workloads.indexer_inputs(wl, integer=True, T=T)
+        cu = workloads.cu_seqlens(lengths) if len(lengths) > 1 else None
+        kw = dict(cu_seqlens=cu_dev(lengths), max_seqlen=max(lengths)) if cu is not None else {}
+        ref = oracle.indexer_scores_dense(x["q_I"], x["k_I"], x["w"], cu_seqlens=cu, block_size=B)
+        got = sa.indexer_scores(x["q_I"].to(DEV), x["k_I"].to(DEV), x["w"].to(DEV), block_size=B,
+                                **kw).cpu().numpy()
+        np.testing.assert_array_equal(got[:, :ref.shape[1]], ref, err_msg=f"lengths {lengths}")
+        k = 5
+        ref_i, ref_v = oracle.indexer_topk(x["q_I"], x["k_I"], x["w"], k, cu_seqlens=cu, block_size=B,
+                                           force_own_block=True)
+        idx, val = sa.indexer_topk(x["q_I"].to(DEV), x["k_I"].to(DEV), x["w"].to(DEV), k, block_size=B,
+                                   force_own_block=True, with_values=True, **kw)
+        np.testing.assert_array_equal(idx.cpu().numpy(), ref_i, err_msg=f"lengths {lengths}")
+        np.testing.assert_array_equal(val.cpu().numpy(), ref_v, err_msg=f"lengths {lengths}")
+
+
 def test_indexer_dense_thd(sa):
     lengths = (300, 5, 700, 64, 129)
     T = sum(lengths)
