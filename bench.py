@@ -84,6 +84,7 @@ def cpu_baseline(wl, x, m, idx_gpu, n_rows=1024):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count()
+    host = _host_cpu()
     T = wl.T
     rows = np.linspace(T // 8, T - 1, n_rows).astype(np.int64)
     xc = {n: t.cpu() for n, t in x.items()}
@@ -109,7 +110,29 @@ def cpu_baseline(wl, x, m, idx_gpu, n_rows=1024):
                   f"top-k ({t1 - t0:.1f} s) and sparse MLA ({t3 - t2:.1f} s), numpy float64",
         "indexer_topk_tokens_per_s": n_rows / (t1 - t0),
         "path_tokens_per_s": n_rows / ((t1 - t0) + (t3 - t2)),
+        "host_cores": host["cores"],
+        "host_cpus_usable": host["usable"],
+        "host_cpu_model": host["model"],
     }
+
+
+def _host_cpu():
+    """Logical CPU count, the CPUs this process may run on, and the CPU model name
+    (from /proc/cpuinfo, the source lscpu reads)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cores": os.cpu_count(), "usable": usable, "model": model}
 
 
 COPY_ELEMS = 1 << 26                 # 256 MiB of fp32: the counter calibration copy
@@ -271,8 +294,9 @@ def main():
         step(timers[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_idx = float(np.mean([tm[0].ms() for tm in timers]))
-    t_mla = float(np.mean([tm[1].ms() for tm in timers]))
+    # per-kernel times: median over the timed steps (robust to a stray slow step)
+    t_idx = float(np.median([tm[0].ms() for tm in timers]))
+    t_mla = float(np.median([tm[1].ms() for tm in timers]))
 
     slots = int((idx >= 0).sum().item())
     mla_flops = 2.0 * (576 + 512) * H * slots
@@ -332,7 +356,7 @@ def main():
                 sa.sa_topk_select(scores, sel)
             tms.append(tm)
         torch.cuda.synchronize()
-        t_sel = float(np.mean([tm.ms() for tm in tms]))
+        t_sel = float(np.median([tm.ms() for tm in tms]))
         sel_bytes = 4.0 * (T * (T + 1) // 2) + 4.0 * T * K
         gbs = sel_bytes / (t_sel * 1e-3) / 1e9
         result["roofline_topk_select"] = {

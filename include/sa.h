@@ -176,7 +176,7 @@ sa_status sa_topk_select(const float* vals, const int32_t* cand_idx, int64_t ld,
  *   (the index row shares the workgroup's LDS with the gather stages); larger values
  *   return SA_ERR_UNSUPPORTED.
  *   SA_BF16 needs H % 16 == 0 or H < 16 (heads are processed in groups of 32;
- *   partial groups are masked).
+ *   partial groups are masked), and kv of at most 2^31 - 1 bytes (S * d_qk * 2).
  */
 sa_status sa_sparse_mla_fwd(const void* q, const void* kv, const int32_t* idx, int dtype,
                             int32_t T, int32_t S, int32_t H, int32_t d_qk, int32_t d_v,

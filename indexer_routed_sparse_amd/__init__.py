@@ -1,9 +1,10 @@
 """Python binding of libsa.so, the C ABI of the indexer-routed sparse-attention path.
 
-Argument marshalling only: each ``sa_*`` function checks that torch tensors have the
-expected dtype, shape, device and contiguity, passes their data pointers, sizes
-and the current HIP stream to the C function of the same name, and raises
-``SAError`` on a non-zero status. Every step of the computation runs in the HIP
+Argument marshalling only: each ``sa_*`` function checks that every torch tensor
+lives on the same HIP device as the first input, is contiguous and has the dtype and
+full shape the C function expects, passes the data pointers, sizes and that device's
+current stream to the C function of the same name, and raises ``SAError`` on a
+non-zero status. Every step of the computation runs in the HIP
 kernels of libsa.so; there is no other code path. Importing this package fails
 loudly if libsa.so is missing (build it with ``python -m
 indexer_routed_sparse_amd.build``).
@@ -78,8 +79,6 @@ def _check(status: int, where: str):
 def _ptr(t):
     if t is None:
         return None
-    if not t.is_contiguous():
-        raise ValueError("tensors must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -95,11 +94,41 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def _layout(T, cu_seqlens, max_seqlen):
+def _need(t, name, device, dtype=None, shape=None, optional=False):
+    """Check that ``t`` is a contiguous device tensor on ``device`` with the given dtype
+    and shape (None entries of ``shape`` match any size). The kernels trust these
+    facts: a host tensor or an undersized output would be read or written out of
+    bounds on the device."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda" or t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(s is not None and int(a) != int(s)
+                                        for a, s in zip(t.shape, shape)):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _device_of(t, name):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    return t.device
+
+
+def _layout(T, cu_seqlens, max_seqlen, device):
     if cu_seqlens is None:
         return None, 0, 0
-    if cu_seqlens.dtype != torch.int32:
-        raise TypeError("cu_seqlens must be int32")
+    _need(cu_seqlens, "cu_seqlens", device, torch.int32, (None,))
+    if cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens needs at least two entries")
     if max_seqlen is None:
         raise ValueError("max_seqlen is required with cu_seqlens")
     return cu_seqlens, cu_seqlens.numel() - 1, int(max_seqlen)
@@ -110,56 +139,82 @@ def _layout(T, cu_seqlens, max_seqlen):
 def sa_indexer_scores(q_I, k_I, w, *, cu_seqlens=None, max_seqlen=None, block_size=1,
                       scores=None, topk=0, force_own_block=False, out_idx=None, out_val=None):
     """sa_indexer_scores: dense scores (topk == 0) or fused exact top-k (topk > 0)."""
+    dev = _device_of(q_I, "q_I")
+    if q_I.dim() != 3:
+        raise ValueError("q_I must be [T, H_I, D_I]")
     T, H_I, D_I = q_I.shape
-    cu, nseq, maxlen = _layout(T, cu_seqlens, max_seqlen)
-    if w.dtype != torch.float32:
-        raise TypeError("w must be float32")
-    ld = scores.shape[1] if scores is not None else 0
+    _need(q_I, "q_I", dev)
+    _need(k_I, "k_I", dev, q_I.dtype, (T, D_I))
+    _need(w, "w", dev, torch.float32, (T, H_I))
+    cu, nseq, maxlen = _layout(T, cu_seqlens, max_seqlen, dev)
+    if topk == 0:
+        _need(scores, "scores", dev, torch.float32, (T, None))
+        ld = scores.shape[1]
+    else:
+        if scores is not None:
+            raise ValueError("scores must be None with topk > 0")
+        ld = 0
+        _need(out_idx, "out_idx", dev, torch.int32, (T, topk))
+        _need(out_val, "out_val", dev, torch.float32, (T, topk), optional=True)
     _check(lib.sa_indexer_scores(_ptr(q_I), _ptr(k_I), _ptr(w), _dtype_code(q_I), T, _ptr(cu), nseq,
                                  maxlen, H_I, D_I, int(block_size), _ptr(scores), ld, int(topk),
                                  int(bool(force_own_block)), _ptr(out_idx), _ptr(out_val),
-                                 _stream(q_I.device)), "sa_indexer_scores")
+                                 _stream(dev)), "sa_indexer_scores")
 
 
 def sa_topk_select(vals, out_idx, *, out_val=None, cand_idx=None, cu_seqlens=None, max_seqlen=None,
                    block_size=1, force_own_block=False):
     """sa_topk_select: exact top-k of each row of ``vals`` [T, ld] into ``out_idx`` [T, topk]."""
-    if vals.dtype != torch.float32 or out_idx.dtype != torch.int32:
-        raise TypeError("vals must be float32 and out_idx int32")
+    dev = _device_of(vals, "vals")
+    _need(vals, "vals", dev, torch.float32, (None, None))
     T, ld = vals.shape
+    _need(out_idx, "out_idx", dev, torch.int32, (T, None))
     topk = out_idx.shape[1]
-    cu, nseq, maxlen = _layout(T, cu_seqlens, max_seqlen)
+    _need(out_val, "out_val", dev, torch.float32, (T, topk), optional=True)
+    _need(cand_idx, "cand_idx", dev, torch.int32, (T, ld), optional=True)
+    cu, nseq, maxlen = _layout(T, cu_seqlens, max_seqlen, dev)
     _check(lib.sa_topk_select(_ptr(vals), _ptr(cand_idx), ld, T, _ptr(cu), nseq, maxlen,
                               int(block_size), topk, int(bool(force_own_block)), _ptr(out_idx),
-                              _ptr(out_val), _stream(vals.device)), "sa_topk_select")
+                              _ptr(out_val), _stream(dev)), "sa_topk_select")
 
 
 def sa_sparse_mla_fwd(q, kv, idx, scale, out, lse=None):
     """sa_sparse_mla_fwd: q [T,H,d_qk], kv [S,d_qk], idx [T,topk] -> out [T,H,d_v], lse [T,H]."""
+    dev = _device_of(q, "q")
+    if q.dim() != 3:
+        raise ValueError("q must be [T, H, d_qk]")
     T, H, d_qk = q.shape
+    _need(q, "q", dev)
+    _need(kv, "kv", dev, q.dtype, (None, d_qk))
     S = kv.shape[0]
-    if idx.dtype != torch.int32:
-        raise TypeError("idx must be int32")
-    if kv.dtype != q.dtype or out.dtype != q.dtype:
-        raise TypeError("q, kv and out must share a dtype")
+    _need(idx, "idx", dev, torch.int32, (T, None))
+    _need(out, "out", dev, q.dtype, (T, H, None))
+    _need(lse, "lse", dev, torch.float32, (T, H), optional=True)
     _check(lib.sa_sparse_mla_fwd(_ptr(q), _ptr(kv), _ptr(idx), _dtype_code(q), T, S, H, d_qk,
                                  out.shape[2], idx.shape[1], float(scale), _ptr(out), _ptr(lse),
-                                 _stream(q.device)), "sa_sparse_mla_fwd")
+                                 _stream(dev)), "sa_sparse_mla_fwd")
 
 
 def sa_block_sparse_gqa_fwd(q, k, v, blk, scale, out, lse=None, *, block_size, cu_seqlens=None,
                             max_seqlen=None):
     """sa_block_sparse_gqa_fwd: q [T,Hq,D], k/v [T,Hkv,D], blk [T,nblk] -> out [T,Hq,Dv]."""
+    dev = _device_of(q, "q")
+    if q.dim() != 3:
+        raise ValueError("q must be [T, Hq, D]")
     T, Hq, D = q.shape
+    _need(q, "q", dev)
+    _need(k, "k", dev, q.dtype, (T, None, D))
     Hkv = k.shape[1]
+    _need(v, "v", dev, q.dtype, (T, Hkv, None))
     Dv = v.shape[2]
-    if blk.dtype != torch.int32:
-        raise TypeError("blk must be int32")
-    cu, nseq, maxlen = _layout(T, cu_seqlens, max_seqlen)
+    _need(blk, "blk", dev, torch.int32, (T, None))
+    _need(out, "out", dev, q.dtype, (T, Hq, Dv))
+    _need(lse, "lse", dev, torch.float32, (T, Hq), optional=True)
+    cu, nseq, maxlen = _layout(T, cu_seqlens, max_seqlen, dev)
     _check(lib.sa_block_sparse_gqa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(blk), _dtype_code(q), T,
                                        _ptr(cu), nseq, maxlen, Hq, Hkv, D, Dv, int(block_size),
                                        blk.shape[1], float(scale), _ptr(out), _ptr(lse),
-                                       _stream(q.device)), "sa_block_sparse_gqa_fwd")
+                                       _stream(dev)), "sa_block_sparse_gqa_fwd")
 
 
 # ------------------------------------------------------- allocating conveniences

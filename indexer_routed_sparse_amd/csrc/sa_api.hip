@@ -124,6 +124,9 @@ sa_status sa_sparse_mla_fwd(const void* q, const void* kv, const int32_t* idx, i
   // the index row is staged in LDS (bf16) / the probabilities are (fp32)
   if (topk > (dtype == SA_BF16 ? 4096 : 8192)) return SA_ERR_UNSUPPORTED;
   if (dtype == SA_BF16 && !sa::sparse_mla_bf16_fits(H, d_qk, topk)) return SA_ERR_UNSUPPORTED;
+  // the bf16 kernel addresses the RoPE channels of gathered rows with 32-bit byte
+  // offsets from the start of kv
+  if (dtype == SA_BF16 && (int64_t)S * d_qk * 2 > (int64_t)INT32_MAX) return SA_ERR_UNSUPPORTED;
   if (T == 0) return SA_OK;
   if (!q || !kv || !idx || !out) return SA_ERR_NULL;
   if (!aligned16(q) || !aligned16(kv) || !aligned16(out)) return SA_ERR_ALIGN;

@@ -58,6 +58,7 @@ MIS = P(0x10004)
     ((FAKE, FAKE, FAKE, 1, 4, 4, 256, 576, 512, 8, 1.0, FAKE, None), 5),  # H > 128
     ((FAKE, FAKE, FAKE, 1, 4, 4, 24, 576, 512, 8, 1.0, FAKE, None), 5),   # H % 16
     ((FAKE, FAKE, FAKE, 1, 4, 0, 16, 576, 512, 8, 1.0, FAKE, None), 2),   # S
+    ((FAKE, FAKE, FAKE, 1, 4, 1 << 21, 16, 576, 512, 8, 1.0, FAKE, None), 5),  # kv > 2 GiB
     ((FAKE, FAKE, FAKE, 1, 4, 4, 16, 576, 512, 0, 1.0, FAKE, None), 2),   # topk
     ((None, FAKE, FAKE, 1, 4, 4, 16, 576, 512, 8, 1.0, FAKE, None), 1),   # null q
     ((FAKE, FAKE, FAKE, 1, 4, 4, 16, 576, 512, 8, 1.0, None, None), 1),   # null out

@@ -312,6 +312,79 @@ def test_indexer_topk_fused_integer_exact(sa, name, k, T, B):
     np.testing.assert_array_equal(val.cpu().numpy(), ref_v)
 
 
+@pytest.mark.parametrize("lengths", [(8192,), (3000, 64, 5128)])
+def test_block_routed_path_full_size_against_oracle(sa, lengths):
+    """The block-routed workload at its stated size (8192 tokens, 16 indexer heads x 128,
+    64-key blocks, top 16 blocks with the query's own block forced) on the integer grid:
+    the fused block top-k equals the oracle bit for bit (ids and values) on sampled rows,
+    among them the last 64 rows, whose candidate blocks (128 on one sequence, 81 in the
+    last packed sequence) overflow the 80-entry candidate buffer so that it is cut back
+    mid-stream; then sparse GQA over those GPU
+    routes equals the oracle's attention on the same rows."""
+    wl = W["block_gqa"]
+    T = sum(lengths)
+    assert T == wl.T
+    x = workloads.indexer_inputs(wl, integer=True)
+    assert workloads.exact_sum_bound(x["q_I"], x["k_I"], x["w"]) < 2 ** 24
+    multi = len(lengths) > 1
+    cu = workloads.cu_seqlens(lengths) if multi else None
+    kw = dict(cu_seqlens=cu_dev(lengths), max_seqlen=max(lengths)) if multi else {}
+    xd = {n: t.to(DEV) for n, t in x.items()}
+    blk, val = sa.indexer_topk(xd["q_I"], xd["k_I"], xd["w"], 16, block_size=64,
+                               force_own_block=True, with_values=True, **kw)
+    rows = sample_rows(T, 64, 29, lengths if multi else None)
+    rows = np.union1d(rows, np.arange(T - 64, T))
+    ref_i, ref_v = oracle.indexer_topk(x["q_I"], x["k_I"], x["w"], 16, cu_seqlens=cu, block_size=64,
+                                       force_own_block=True, rows=rows)
+    np.testing.assert_array_equal(blk.cpu().numpy()[rows], ref_i)
+    np.testing.assert_array_equal(val.cpu().numpy()[rows], ref_v)
+    g = workloads.gqa_inputs(wl, device=DEV)
+    out, lse = sa.block_sparse_gqa(g["q"], g["k"], g["v"], blk, wl.scale, block_size=64, **kw)
+    ro, rl = oracle.block_sparse_gqa(g["q"].cpu(), g["k"].cpu(), g["v"].cpu(), blk.cpu().numpy(), 64,
+                                     wl.scale, cu_seqlens=cu, rows=rows)
+    close(out.float().cpu().numpy()[rows], ro, **BF16_TOL, what="out")
+    close(lse.cpu().numpy()[rows], rl, **BF16_TOL, what="lse")
+
+
+@pytest.mark.parametrize("B,k", [(16, 5), (32, 1), (16, 64)])
+def test_block_topk_buffer_cutback_against_oracle(sa, B, k):
+    """Block routes with more candidate blocks than the buffer holds (2048 tokens of
+    16-key blocks: 128 blocks against a 69-entry buffer at k = 5), so the fused block
+    top-k cuts its buffer back mid-stream; every row equals the oracle bit for bit."""
+    wl = W["block_gqa"]
+    T = 2048
+    x = workloads.indexer_inputs(wl, integer=True, T=T)
+    ref_i, ref_v = oracle.indexer_topk(x["q_I"], x["k_I"], x["w"], k, block_size=B,
+                                       force_own_block=True)
+    idx, val = sa.indexer_topk(x["q_I"].to(DEV), x["k_I"].to(DEV), x["w"].to(DEV), k, block_size=B,
+                               force_own_block=True, with_values=True)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_i)
+    np.testing.assert_array_equal(val.cpu().numpy(), ref_v)
+
+
+@pytest.mark.parametrize("k", [1, 100, 777, 2048])
+def test_indexer64_fused_small_k_against_oracle(sa, k):
+    """64 indexer heads on the integer grid, one sequence of 4096 tokens and packed
+    sequences: the fused selection (many buffer cut-backs at small k, exact ties at
+    zero) equals the oracle bit for bit on sampled rows, among them each sequence's
+    first and last rows and the last 32 rows."""
+    wl = W["long_dsa"]
+    for lengths in [(4096,), (1000, 3, 2048, 1045)]:
+        T = sum(lengths)
+        multi = len(lengths) > 1
+        x = workloads.indexer_inputs(wl, integer=True, T=T)
+        kw = dict(cu_seqlens=cu_dev(lengths), max_seqlen=max(lengths)) if multi else {}
+        idx, val = sa.indexer_topk(x["q_I"].to(DEV), x["k_I"].to(DEV), x["w"].to(DEV), k,
+                                   with_values=True, **kw)
+        rows = np.union1d(sample_rows(T, 24, 31 + k, lengths if multi else None),
+                          np.arange(T - 32, T))
+        ref_i, ref_v = oracle.indexer_topk(x["q_I"], x["k_I"], x["w"], k,
+                                           cu_seqlens=workloads.cu_seqlens(lengths) if multi else None,
+                                           rows=rows)
+        np.testing.assert_array_equal(idx.cpu().numpy()[rows], ref_i, err_msg=f"lengths {lengths}")
+        np.testing.assert_array_equal(val.cpu().numpy()[rows], ref_v, err_msg=f"lengths {lengths}")
+
+
 @pytest.mark.parametrize("name", ["nope_unaligned", "block_gqa"])
 def test_indexer_fused_matches_dense_then_select(sa, name):
     # On non-integer inputs both GPU paths compute the same fp32 scores, so the fused
@@ -407,6 +480,28 @@ def test_sparse_mla_shapes(sa, H, k, d_qk):
     idx = torch.randint(0, S, (T, k), generator=g, dtype=torch.int32)
     idx[torch.rand((T, k), generator=g) < 0.1] = -1
     idx[3] = -1                                  # an all-invalid row
+    scale = 1 / math.sqrt(d_qk)
+    out, lse = sa.sparse_mla(q.to(DEV), kv.to(DEV), idx.to(DEV), scale)
+    ro, rl = oracle.sparse_mla(q, kv, idx.numpy(), scale)
+    close(out.float().cpu().numpy(), ro, **BF16_TOL, what="out")
+    close(lse.cpu().numpy(), rl, **BF16_TOL, what="lse")
+
+
+@pytest.mark.parametrize("H", [16, 64, 128])
+@pytest.mark.parametrize("d_qk", [512, 576])
+def test_sparse_mla_glm_width_2051(sa, H, d_qk):
+    """Top-k width 2048 + 3 (the GLM k-pool width: a query's incomplete tail pool
+    appended), 512 and 576 wide: a ragged last 32-slot tile of three slots, -1 slots
+    spread through the row, a row that ends inside the tail and an all-invalid row."""
+    T, S, k = 24, 5000, 2051
+    g = torch.Generator().manual_seed(2051 + H + d_qk)
+    q = torch.randn((T, H, d_qk), generator=g).to(torch.bfloat16)
+    kv = torch.randn((S, d_qk), generator=g).to(torch.bfloat16)
+    idx = torch.randint(0, S, (T, k), generator=g, dtype=torch.int32)
+    idx[torch.rand((T, k), generator=g) < 0.05] = -1
+    idx[5, 2049:] = -1
+    idx[6, 2050] = -1
+    idx[7] = -1
     scale = 1 / math.sqrt(d_qk)
     out, lse = sa.sparse_mla(q.to(DEV), kv.to(DEV), idx.to(DEV), scale)
     ro, rl = oracle.sparse_mla(q, kv, idx.numpy(), scale)

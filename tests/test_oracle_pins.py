@@ -219,9 +219,91 @@ def test_topk_dense_thd_and_block_mode():
     # block mode (B = 2), own block forced, ids local to the sequence
     bs = np.full((8, 3), -np.inf, dtype=np.float32)
     bs[7, :3] = [9, 1, 0]        # row 7 = offset 4 in seq 1 -> own block 2
-    idx, _ = oracle.topk_select_dense(bs, 2, cu_seqlens=cu, block_size=2,
+    idx, _ = oracle.topk_select_dense(bs[[7]], 2, cu_seqlens=cu, block_size=2,
                                       force_own_block=True, rows=[7])
     assert idx.tolist() == [[0, 2]]
+    # score row r belongs to query row rows[r]: a different best block must show
+    bs[7, :3] = [0, 9, 1]
+    idx, _ = oracle.topk_select_dense(bs[[7]], 2, cu_seqlens=cu, block_size=2,
+                                      force_own_block=True, rows=[7])
+    assert idx.tolist() == [[1, 2]]
+    # the full matrix without rows= gives the same row 7
+    full, _ = oracle.topk_select_dense(bs, 2, cu_seqlens=cu, block_size=2, force_own_block=True)
+    assert full[7].tolist() == [1, 2]
+
+
+def _brute_indexer_topk(q, k, w, K, lengths, B, force_own, rows):
+    """From-scratch top-k of the indexer scores with exact rational arithmetic.
+
+    Scores: Fractions of the stored values, sum over heads of w * max(q.k, 0). Block
+    mode takes the max over the block's causal keys. Ranking: a Python sort of
+    (-score, id) tuples; the own block first when forced. Returns ids, values, and the
+    score lists per row (global key ids in token mode, local block ids in block mode).
+    """
+    from fractions import Fraction as F
+    starts = np.concatenate([[0], np.cumsum(lengths)])
+    ids_out, vals_out, score_rows = [], [], []
+    for t in rows:
+        j = int(np.searchsorted(starts, t, side="right") - 1)
+        c = int(starts[j])
+        tok = []
+        for s in range(c, t + 1):
+            acc = F(0)
+            for h in range(q.shape[1]):
+                z = sum(F(float(q[t, h, d])) * F(float(k[s, d])) for d in range(q.shape[2]))
+                acc += F(float(w[t, h])) * max(z, F(0))
+            tok.append(acc)
+        if B == 1:
+            cands = [(sc, c + i) for i, sc in enumerate(tok)]
+        else:
+            cands = [(max(tok[b * B:(b + 1) * B]), b) for b in range((t - c) // B + 1)]
+        score_rows.append(cands)
+        chosen = []
+        rest = cands
+        if force_own:
+            chosen = [cands[-1]]
+            rest = cands[:-1]
+        chosen += sorted(rest, key=lambda e: (-e[0], e[1]))[:K - len(chosen)]
+        chosen.sort(key=lambda e: e[1])
+        ids_out.append([i for _, i in chosen] + [-1] * (K - len(chosen)))
+        vals_out.append([np.float32(float(v)) for v, _ in chosen] + [np.float32(-np.inf)] * (K - len(chosen)))
+    return np.array(ids_out), np.array(vals_out, dtype=np.float32), score_rows
+
+
+@pytest.mark.parametrize("B,K,force_own", [(1, 5, False), (1, 1, False), (4, 3, True),
+                                           (4, 3, False), (3, 1, True)])
+def test_indexer_topk_and_row_subsets_match_brute_force_thd(B, K, force_own):
+    """oracle.indexer_topk (and indexer_scores_dense with rows=) on packed sequences,
+    against exact rational scores and a tuple sort; rows given out of order, so a
+    wrong row slice, start offset or sequence boundary shows."""
+    rng = np.random.default_rng(20 + B * 7 + K)
+    lengths = (7, 1, 13, 20)
+    T = sum(lengths)
+    cu = workloads.cu_seqlens(lengths)
+    q = (rng.integers(-4, 5, (T, 3, 4)) * 0.5).astype(np.float32)
+    k = (rng.integers(-4, 5, (T, 4)) * 0.5).astype(np.float32)
+    w = (rng.integers(-64, 65, (T, 3)) / 64).astype(np.float32)
+    rows = np.array([40, 0, 7, 8, 21, 6, 33, 20, 9, 28, 1])
+    ref_i, ref_v, ref_rows = _brute_indexer_topk(q, k, w, K, lengths, B, force_own, rows)
+    got_i, got_v = oracle.indexer_topk(q, k, w, K, cu_seqlens=cu, block_size=B,
+                                       force_own_block=force_own, rows=rows)
+    np.testing.assert_array_equal(got_i, ref_i)
+    np.testing.assert_array_equal(got_v, ref_v)
+    # dense scores of a row subset: same as the brute-force scores, column by column
+    sub = oracle.indexer_scores_dense(q, k, w, cu_seqlens=cu, block_size=B, rows=rows)
+    full = oracle.indexer_scores_dense(q, k, w, cu_seqlens=cu, block_size=B)
+    np.testing.assert_array_equal(sub, full[rows])
+    for r, cands in enumerate(ref_rows):
+        vals = [np.float32(float(v)) for v, _ in cands]
+        np.testing.assert_array_equal(sub[r, :len(vals)], np.array(vals, dtype=np.float32))
+        assert np.all(np.isneginf(sub[r, len(vals):]))
+    # the oracle's chunking of rows (64 at a time) is invisible: more than 64 rows
+    many = np.concatenate([np.arange(T)[::-1], np.arange(T)])
+    gi, _ = oracle.indexer_topk(q, k, w, K, cu_seqlens=cu, block_size=B,
+                                force_own_block=force_own, rows=many)
+    ai, _ = oracle.indexer_topk(q, k, w, K, cu_seqlens=cu, block_size=B,
+                                force_own_block=force_own)
+    np.testing.assert_array_equal(gi, ai[many])
 
 
 # ------------------------------------------------------------------ sparse MLA (O4)
