@@ -10,7 +10,9 @@
 // bf16 kernel (gfx950): one wave per (token, kv head), four independent waves per
 // workgroup. Routes differ from token to token, so the work is a gather: every wave
 // streams the keys and values of its own blocks, and the kernel is bound by the
-// L2/MALL -> CU bandwidth of those gathers, not by the matrix cores.
+// L2/MALL -> CU bandwidth of those gathers, not by the matrix cores. When Hkv
+// divides 8, the workgroups of each XCD serve a single kv head, so an XCD's L2
+// caches the keys and values of one head instead of all of them.
 //   * the wave's G <= 16 query heads are the 16 columns of 16x16x32 bf16 MFMAs:
 //     S^T = K . Q^T (rows = 16 keys), then O^T = V^T . P^T (rows = 16 value
 //     channels), so each lane owns one query head's softmax state and output column
@@ -55,7 +57,8 @@ template <int D>
 __global__ __launch_bounds__(kWavesPerGroup * 64) void block_gqa_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ blk, const int32_t* __restrict__ cu, int nseq, int T, int Hq,
-    int Hkv, int B, int nblk, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    int Hkv, int B, int nblk, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
+    int by_xcd) {
   constexpr int KS = D / 32;             // 32-wide k-steps of S^T
   constexpr int CPR = D * 2 / 16;        // 16-byte chunks per row
   constexpr int VL = 32 * CPR / 64;      // 16-byte value loads per lane per sub-tile
@@ -63,10 +66,21 @@ __global__ __launch_bounds__(kWavesPerGroup * 64) void block_gqa_bf16_kernel(
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int w = threadIdx.x >> 6;
   const int L = threadIdx.x & 63;
-  const int unit = blockIdx.x * kWavesPerGroup + w;     // (token, kv head) pair
-  if ((int64_t)unit >= (int64_t)T * Hkv) return;       // whole wave leaves together
-  const int t = unit / Hkv;
-  const int g = unit - t * Hkv;
+  int t, g;
+  if (by_xcd) {
+    // Workgroups are dealt to the 8 XCDs in turn (workgroup b runs on XCD b mod 8).
+    // Each XCD serves one kv head (8 / Hkv XCDs per head), so its L2 holds the keys
+    // and values of that head only; a workgroup takes 4 consecutive tokens.
+    const int b = blockIdx.x, xcd = b & 7, nx = 8 / Hkv;
+    g = xcd % Hkv;
+    t = ((b >> 3) * nx + xcd / Hkv) * kWavesPerGroup + w;
+    if (t >= T) return;                                // whole wave leaves together
+  } else {
+    const int unit = blockIdx.x * kWavesPerGroup + w;   // (token, kv head) pair
+    if ((int64_t)unit >= (int64_t)T * Hkv) return;
+    t = unit / Hkv;
+    g = unit - t * Hkv;
+  }
   const int G = Hq / Hkv;
   char* stage = lds + w * wave_lds_bytes<D>();
   int2* list = reinterpret_cast<int2*>(stage + stage_bytes<D>());
@@ -356,11 +370,19 @@ hipError_t launch_bf16(const void* q, const void* k, const void* v, const int32_
                        const int32_t* cu, int nseq, int Hq, int Hkv, int B, int nblk, float scale,
                        void* out, float* lse, hipStream_t st) {
   const size_t shm = (size_t)kWavesPerGroup * wave_lds_bytes<D>();
-  const int64_t units = (int64_t)T * Hkv;
-  const int grid = (int)((units + kWavesPerGroup - 1) / kWavesPerGroup);
-  hipLaunchKernelGGL((block_gqa_bf16_kernel<D>), dim3(grid), dim3(kWavesPerGroup * 64), shm, st,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, blk, cu, nseq, T,
-                     Hq, Hkv, B, nblk, scale * kLog2e, (uint16_t*)out, lse);
+  const int by_xcd = 8 % Hkv == 0;
+  int64_t grid;
+  if (by_xcd) {
+    const int64_t groups = ((int64_t)T + kWavesPerGroup - 1) / kWavesPerGroup;
+    const int nx = 8 / Hkv;
+    grid = (groups + nx - 1) / nx * 8;
+  } else {
+    grid = ((int64_t)T * Hkv + kWavesPerGroup - 1) / kWavesPerGroup;
+  }
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((block_gqa_bf16_kernel<D>), dim3((unsigned)grid), dim3(kWavesPerGroup * 64), shm,
+                     st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, blk, cu, nseq, T,
+                     Hq, Hkv, B, nblk, scale * kLog2e, (uint16_t*)out, lse, by_xcd);
   return hipGetLastError();
 }
 
