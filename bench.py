@@ -163,9 +163,10 @@ def counters_pass():
     idx = torch.empty((T, K), dtype=torch.int32, device=dev)
     out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = sa.indexer_workspace(x["q_I"], K)
     torch.cuda.synchronize()
     print("[counters] fused indexer top-k + sparse MLA", file=sys.stderr, flush=True)
-    sa.sa_indexer_scores(x["q_I"], x["k_I"], x["w"], topk=K, out_idx=idx)
+    sa.sa_indexer_scores(x["q_I"], x["k_I"], x["w"], topk=K, out_idx=idx, ws=ws)
     sa.sa_sparse_mla_fwd(m["q"], m["kv"], idx, wl.scale, out, lse)
     torch.cuda.synchronize()
     del out, lse
@@ -270,15 +271,16 @@ def main():
     idx = torch.empty((T, K), dtype=torch.int32, device=dev)
     out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = sa.indexer_workspace(x["q_I"], K)      # two-pass selection workspace
     torch.cuda.synchronize()
 
     def step(timers=None):
         if timers is None:
-            sa.sa_indexer_scores(x["q_I"], x["k_I"], x["w"], topk=K, out_idx=idx)
+            sa.sa_indexer_scores(x["q_I"], x["k_I"], x["w"], topk=K, out_idx=idx, ws=ws)
             sa.sa_sparse_mla_fwd(m["q"], m["kv"], idx, wl.scale, out, lse)
             return
         with timers[0]:
-            sa.sa_indexer_scores(x["q_I"], x["k_I"], x["w"], topk=K, out_idx=idx)
+            sa.sa_indexer_scores(x["q_I"], x["k_I"], x["w"], topk=K, out_idx=idx, ws=ws)
         with timers[1]:
             sa.sa_sparse_mla_fwd(m["q"], m["kv"], idx, wl.scale, out, lse)
 

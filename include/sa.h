@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 1
+#define SA_ABI_VERSION 2
 
 typedef enum {
   SA_OK = 0,
@@ -61,7 +61,8 @@ typedef enum {
   SA_ERR_DTYPE = 3,        /* unknown dtype code */
   SA_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned */
   SA_ERR_UNSUPPORTED = 5,  /* valid but unsupported combination (limits below) */
-  SA_ERR_LAUNCH = 6        /* a kernel launch failed */
+  SA_ERR_LAUNCH = 6,       /* a kernel launch failed */
+  SA_ERR_WORKSPACE = 7     /* the workspace is smaller than the call needs */
 } sa_status;
 
 typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
@@ -99,20 +100,47 @@ int sa_abi_version(void);
  *   (t-start(t))/B + 1 (blocks). Columns >= n(t) are not written.
  *   ld >= max_seqlen (tokens) or ceil(max_seqlen / B) (blocks); ld % 4 == 0.
  *   out_idx/out_val must be NULL.
- * Mode 2, fused selection (topk > 0): scores must be NULL. The kernel streams the
- *   causal keys tile by tile and keeps, per row, an exact running top-k under the
- *   order of sa_topk_select; the score matrix is never stored. Writes out_idx
- *   [T, topk] int32 and, if out_val != NULL, out_val [T, topk] fp32, with exactly the
- *   result sa_topk_select gives on the dense scores (same indices, same order).
- *   Token mode: topk in [1, 2048]; block mode: topk in [1, 64].
- *   force_own_block as in sa_topk_select (block mode only).
+ * Mode 2, fused selection (topk > 0): scores must be NULL. The causal keys stream
+ *   tile by tile and each tile's scores are filtered on the fly; the score matrix is
+ *   never stored. Writes out_idx [T, topk] int32 and, if out_val != NULL, out_val
+ *   [T, topk] fp32, with exactly the result sa_topk_select gives on the dense scores
+ *   (same indices, same order). Token mode: topk in [1, 2048]; block mode: topk in
+ *   [1, 64]. force_own_block as in sa_topk_select (block mode only).
+ *   Two ways to run it (same results, bit for bit):
+ *   - ws == NULL: one pass; each row keeps an exact running top-k in on-chip
+ *     memory ([QSA] "Describe the solution you'd like": streaming runner with
+ *     bounded memory).
+ *   - ws != NULL with ws_bytes >= sa_indexer_workspace_bytes(...): when that size is
+ *     non-zero (bf16, 64 indexer heads, token mode), two passes ([DSA] file table: the
+ *     fused top-k's cached scratch buffers): the first appends, per row, the keys
+ *     at or above a pivot drawn from a sample of the row's scores to the row's slice
+ *     of the workspace (a per-tile partial selection; a few thousand entries per
+ *     row), then the exact selection of sa_topk_select finishes each row; a row
+ *     whose pivot kept fewer than topk keys is redone by the one-pass kernel. The
+ *     workspace holds [T, cap] fp32 scores, [T, cap] int32 key ids and [T] int32
+ *     counts; its contents on return are unspecified, and two calls in flight must
+ *     not share one. A smaller ws_bytes returns SA_ERR_WORKSPACE; ws must be 16-byte
+ *     aligned. When the size is zero, ws is ignored.
  */
 sa_status sa_indexer_scores(const void* q_I, const void* k_I, const float* w, int dtype,
                             int32_t T, const int32_t* cu_seqlens, int32_t num_seqs,
                             int32_t max_seqlen, int32_t H_I, int32_t D_I, int32_t block_size,
                             float* scores, int64_t ld,
                             int32_t topk, int32_t force_own_block,
-                            int32_t* out_idx, float* out_val, void* stream);
+                            int32_t* out_idx, float* out_val, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/*
+ * sa_indexer_workspace_bytes -- workspace size for sa_indexer_scores mode 2.
+ *
+ * Bytes that the two-pass fused selection needs for these arguments (T, the widest
+ * sequence max_seqlen -- T for one sequence --, dtype, H_I, D_I, block_size, topk);
+ * 0 when the call runs in one pass (dense mode, block mode, fp32, or H_I != 64).
+ * For T = 32768 one-sequence rows at topk = 2048 it is about 1.3 GB. Host-only; no
+ * device access.
+ */
+size_t sa_indexer_workspace_bytes(int dtype, int32_t T, int32_t max_seqlen, int32_t H_I,
+                                  int32_t D_I, int32_t block_size, int32_t topk);
 
 /*
  * sa_topk_select -- exact, deterministic top-k of score rows.

@@ -21,7 +21,7 @@ import torch
 
 __all__ = [
     "SAError", "SA_F32", "SA_BF16", "lib", "abi_version", "status_string",
-    "sa_indexer_scores", "sa_topk_select", "sa_sparse_mla_fwd", "sa_block_sparse_gqa_fwd",
+    "sa_indexer_workspace_bytes", "indexer_workspace", "sa_indexer_scores", "sa_topk_select", "sa_sparse_mla_fwd", "sa_block_sparse_gqa_fwd",
     "indexer_scores", "indexer_topk", "topk_select", "sparse_mla", "block_sparse_gqa",
 ]
 
@@ -46,7 +46,9 @@ lib.sa_abi_version.restype = ctypes.c_int
 lib.sa_abi_version.argtypes = []
 lib.sa_indexer_scores.restype = ctypes.c_int
 lib.sa_indexer_scores.argtypes = [_p, _p, _p, ctypes.c_int, _i32, _p, _i32, _i32, _i32, _i32, _i32,
-                                  _p, _i64, _i32, _i32, _p, _p, _p]
+                                  _p, _i64, _i32, _i32, _p, _p, _p, ctypes.c_size_t, _p]
+lib.sa_indexer_workspace_bytes.restype = ctypes.c_size_t
+lib.sa_indexer_workspace_bytes.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _i32]
 lib.sa_topk_select.restype = ctypes.c_int
 lib.sa_topk_select.argtypes = [_p, _p, _i64, _i32, _p, _i32, _i32, _i32, _i32, _i32, _p, _p, _p]
 lib.sa_sparse_mla_fwd.restype = ctypes.c_int
@@ -136,9 +138,20 @@ def _layout(T, cu_seqlens, max_seqlen, device):
 
 # ------------------------------------------------------------------- C functions
 
+def sa_indexer_workspace_bytes(dtype, T, max_seqlen, H_I, D_I, block_size, topk) -> int:
+    """sa_indexer_workspace_bytes: workspace bytes of a fused selection (0: one pass)."""
+    code = SA_BF16 if dtype in (torch.bfloat16, SA_BF16) else SA_F32
+    return int(lib.sa_indexer_workspace_bytes(code, int(T), int(max_seqlen), int(H_I), int(D_I),
+                                              int(block_size), int(topk)))
+
+
 def sa_indexer_scores(q_I, k_I, w, *, cu_seqlens=None, max_seqlen=None, block_size=1,
-                      scores=None, topk=0, force_own_block=False, out_idx=None, out_val=None):
-    """sa_indexer_scores: dense scores (topk == 0) or fused exact top-k (topk > 0)."""
+                      scores=None, topk=0, force_own_block=False, out_idx=None, out_val=None,
+                      ws=None):
+    """sa_indexer_scores: dense scores (topk == 0) or fused exact top-k (topk > 0).
+
+    ``ws`` (optional) is a uint8 device tensor used as the workspace of the two-pass
+    selection; its size is checked by the library."""
     dev = _device_of(q_I, "q_I")
     if q_I.dim() != 3:
         raise ValueError("q_I must be [T, H_I, D_I]")
@@ -156,10 +169,12 @@ def sa_indexer_scores(q_I, k_I, w, *, cu_seqlens=None, max_seqlen=None, block_si
         ld = 0
         _need(out_idx, "out_idx", dev, torch.int32, (T, topk))
         _need(out_val, "out_val", dev, torch.float32, (T, topk), optional=True)
+    _need(ws, "ws", dev, torch.uint8, (None,), optional=True)
+    ws_bytes = ws.numel() if ws is not None else 0
     _check(lib.sa_indexer_scores(_ptr(q_I), _ptr(k_I), _ptr(w), _dtype_code(q_I), T, _ptr(cu), nseq,
                                  maxlen, H_I, D_I, int(block_size), _ptr(scores), ld, int(topk),
                                  int(bool(force_own_block)), _ptr(out_idx), _ptr(out_val),
-                                 _stream(dev)), "sa_indexer_scores")
+                                 _ptr(ws), ws_bytes, _stream(dev)), "sa_indexer_scores")
 
 
 def sa_topk_select(vals, out_idx, *, out_val=None, cand_idx=None, cu_seqlens=None, max_seqlen=None,
@@ -230,14 +245,29 @@ def indexer_scores(q_I, k_I, w, *, cu_seqlens=None, max_seqlen=None, block_size=
     return scores
 
 
+def indexer_workspace(q_I, topk, *, max_seqlen=None, block_size=1):
+    """A workspace tensor for a fused selection over q_I (None when it runs in one pass)."""
+    T, H_I, D_I = q_I.shape
+    n = sa_indexer_workspace_bytes(q_I.dtype, T, max_seqlen or T, H_I, D_I, block_size, topk)
+    return torch.empty(n, dtype=torch.uint8, device=q_I.device) if n else None
+
+
 def indexer_topk(q_I, k_I, w, topk, *, cu_seqlens=None, max_seqlen=None, block_size=1,
-                 force_own_block=False, with_values=False):
+                 force_own_block=False, with_values=False, workspace=True):
+    """Fused exact top-k; ``workspace`` True allocates the two-pass workspace when the
+    call can use one, False runs the one-pass kernel, a tensor is used as given."""
     T = q_I.shape[0]
     idx = torch.empty((T, topk), dtype=torch.int32, device=q_I.device)
     val = torch.empty((T, topk), dtype=torch.float32, device=q_I.device) if with_values else None
+    ws = workspace
+    if workspace is True:
+        ws = indexer_workspace(q_I, topk, max_seqlen=max_seqlen if cu_seqlens is not None else None,
+                               block_size=block_size)
+    elif workspace is False:
+        ws = None
     sa_indexer_scores(q_I, k_I, w, cu_seqlens=cu_seqlens, max_seqlen=max_seqlen,
                       block_size=block_size, topk=topk, force_own_block=force_own_block,
-                      out_idx=idx, out_val=val)
+                      out_idx=idx, out_val=val, ws=ws)
     return (idx, val) if with_values else idx
 
 

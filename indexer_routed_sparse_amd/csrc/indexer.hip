@@ -25,6 +25,8 @@
 //     digits over order-preserving keys) and a stable in-place compaction. Because
 //     keys arrive in ascending index order, a later key equal to the k-th best can
 //     never enter (it loses the index tie-break), so a strict ">" filter is exact.
+#include <algorithm>
+#include <cmath>
 #include <type_traits>
 
 #include "sa_common.h"
@@ -55,7 +57,19 @@ struct IdxArgs {
   int force_own;
   int32_t* out_idx;
   float* out_val;
+  // two-pass selection through a workspace (64 heads): candidate rows [T, ws_cap]
+  // (score, key id) and the number each row holds (-1: left to the exact kernel)
+  float* ws_val;
+  int32_t* ws_idx;
+  int32_t* ws_cnt;
+  int ws_cap;
 };
+
+// Launch modes of the 64-head kernel.
+constexpr int kDense = 0;    // write the scores
+constexpr int kFused = 1;    // exact running top-k in LDS candidate buffers
+constexpr int kAppend = 2;   // keys above a sampled pivot appended to the workspace
+constexpr int kSample = 1024;   // pivot sample size (16 key tiles)
 
 template <int CPR>
 SA_DEVICE int kswz(int r) {
@@ -672,11 +686,22 @@ SA_DEVICE int wave_cut(uint32_t* keys, int32_t* ids, int n, int cap, int k, int 
 //     or by the exact wave_select when ties defeat the histogram; the exact select also
 //     finishes the row. Keys arrive in ascending index order, so a later key equal to
 //     a kept one never wins and the strict filter is exact.
-// SPREAD (the dense launch): a wave spreads its share of the next gather over the
-// first key half's MFMAs instead of issuing it right after the barrier.
-template <int DI, bool SPREAD>
+// MODE kAppend (first pass of the two-pass selection): before the stream, the
+// workgroup scores a sample of kSample evenly spaced causal keys; each wave bisects
+// its token's sample for a pivot that about k plus four standard deviations of the
+// sample rank reach, then appends every key at or above it, in index order, to the
+// token's workspace row and records how many it appended. A row whose count falls
+// below k (or overflows the row) is marked -1 and redone by the kFused launch, so
+// the pivot never decides a result; sa_topk_select finishes the other rows.
+// With ws_cnt set, a kFused launch only runs the workgroups holding a marked row.
+// SPREAD (the dense and append launches): a wave spreads its share of the next
+// gather over the first key half's MFMAs instead of issuing it right after the
+// barrier.
+template <int DI, int MODE>
 __global__ __launch_bounds__(kMaxWaves * 64) void indexer64_kernel(IdxArgs args) {
   const IdxArgs a = args;   // local copy: lambdas capture it without a private-memory copy of the kernel argument
+  constexpr bool SPREAD = MODE != kFused;
+  constexpr bool APPEND = MODE == kAppend;
   constexpr int CPR = DI * 2 / 16;            // 16-byte chunks per key row
   constexpr int TILE_BYTES = kKT * CPR * 16;
   constexpr int KSTEPS = DI / 16;
@@ -691,7 +716,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer64_kernel(IdxArgs args)
   const int w = tid >> 6;
   const int L = tid & 63;
   const int hl = L >> 5;
-  const bool fused = a.topk > 0;
+  const bool fused = MODE == kFused;
 
   const int seq = blockIdx.y;
   const int chunk = a.chunks - 1 - (int)blockIdx.x;   // longest rows first
@@ -700,6 +725,13 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer64_kernel(IdxArgs args)
   const int t0 = cs + chunk * kMaxWaves;
   if (t0 >= ce) return;
   const int t1 = min(t0 + kMaxWaves, ce);
+  if constexpr (MODE == kFused) {
+    if (a.ws_cnt) {                                    // redo only marked rows (uniform test)
+      bool marked = false;
+      for (int i = t0; i < t1; ++i) marked = marked || __ldg(a.ws_cnt + i) < 0;
+      if (!marked) return;
+    }
+  }
   const int ntiles = (t1 - 1 - cs) / kKT + 1;
   const int t = t0 + w;                                // this wave's token
   const bool active = t < t1;
@@ -879,6 +911,18 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer64_kernel(IdxArgs args)
   auto select = [&](float sc, int tile) __attribute__((always_inline)) {
     const int kg = cs + tile * kKT + L;
     const bool valid = kg <= t;            // kg >= cs always
+    if constexpr (APPEND) {
+      const bool take = valid && order_key(sc) > tau;
+      const uint64_t tb2 = ballot(take);
+      if (tb2 == 0) return;
+      const int pos = n + (int)mbcnt(tb2);
+      if (take && pos < a.ws_cap) {
+        a.ws_val[(int64_t)t * a.ws_cap + pos] = sc;
+        a.ws_idx[(int64_t)t * a.ws_cap + pos] = kg;
+      }
+      n += __popcll(tb2);
+      return;
+    }
     if (!fused) {
       if (valid) a.scores[(int64_t)t * a.ld + (kg - cs)] = sc;
       return;
@@ -900,6 +944,59 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer64_kernel(IdxArgs args)
     if (n > a.cap - kKT && L == 0) s_req = tile;
     __builtin_amdgcn_wave_barrier();
   };
+
+  if constexpr (APPEND) {
+    // ---- pivot from a sample of the workgroup's causal keys (when some token of the
+    //      workgroup has more keys than its workspace row holds): sample key j of
+    //      kSample is cs + j * n0 / kSample, n0 = keys of the first token, so every
+    //      sample key is causal for all four tokens
+    if (t1 - cs > a.ws_cap) {
+      const int n0 = t0 - cs + 1;
+      auto sgather = [&](int st) __attribute__((always_inline)) {
+        const uint32_t base = (uint32_t)(uintptr_t)(SA_LDS char*)(ktiles + (st & 1) * TILE_BYTES);
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+          const int p = 64 * (w + kMaxWaves * j) + L;
+          const int r = p / CPR;
+          const int c = (p % CPR) ^ kswz<CPR>(r);
+          const int key = cs + (int)(((int64_t)(st * kKT + r) * n0) / kSample);
+          lds_dma16(base + (w + kMaxWaves * j) * 1024,
+                    reinterpret_cast<const char*>(a.k) + (int64_t)key * DI * 2 + 16 * c);
+        }
+      };
+      constexpr int NS = kSample / kKT;
+      uint32_t xs[NS];
+      sgather(0);
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        wait_vmcnt0();
+        __syncthreads();                  // sample tile st resident; tile st-1 read by all
+        if (st + 1 < NS) sgather(st + 1);
+        const char* tb = ktiles + (st & 1) * TILE_BYTES;
+        tile_start(tb);
+        half(std::false_type{}, tb, 0, S0, S1);
+        const float s0 = half(std::true_type{}, tb, 1, S1, S0);
+        xs[st] = order_key(score_of(s0, epi_only(S1)));
+      }
+      __syncthreads();                    // every wave is done with the sample tiles
+      const int nt = t - cs + 1;
+      if (active && nt > a.ws_cap) {
+        // the k-th key's expected sample rank r0, aimed at r0 + 4.3 sqrt(r0) + 1
+        const float r0 = (float)kSample * (float)a.topk / (float)nt;
+        const uint32_t target = (uint32_t)(r0 + 4.3f * __builtin_sqrtf(r0)) + 1u;
+        uint32_t P = 0u;                  // largest key that `target` sample keys reach
+#pragma unroll 1
+        for (int b = 31; b >= 0; --b) {
+          const uint32_t cnd = P | (1u << b);
+          uint32_t cnt = 0;
+#pragma unroll
+          for (int i = 0; i < NS; ++i) cnt += (uint32_t)__popcll(ballot(xs[i] >= cnd));
+          if (cnt >= target) P = cnd;
+        }
+        tau = P > 0u ? P - 1u : 0u;       // append keys >= P
+      }
+    }
+  }
 
   // Software pipeline over key halves: iteration `tile` runs the first half's MFMAs of
   // tile+1 with the epilogue of tile's second half, selects tile, then runs the second
@@ -938,6 +1035,13 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer64_kernel(IdxArgs args)
     }
   }
 
+  if constexpr (APPEND) {
+    if (active && L == 0) {
+      const int nv = t - cs + 1;
+      a.ws_cnt[t] = n <= a.ws_cap && (n >= a.topk || n == nv) ? n : -1;
+    }
+    return;
+  }
   if (!fused || !active) return;
   if (n > a.topk) {
     uint32_t hi = kmax;
@@ -960,14 +1064,16 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer64_kernel(IdxArgs args)
   }
 }
 
+// 64-head launches. Dense (topk == 0), fused with LDS candidate buffers, or the
+// append pass of the two-pass selection (a.ws_val set).
 template <int DI>
 hipError_t launch_64(const IdxArgs& a0, int maxlen, hipStream_t st) {
   IdxArgs a = a0;
   constexpr int CPR = DI * 2 / 16;
   constexpr int TILE_BYTES = kKT * CPR * 16;
-  const bool fused = a.topk > 0;
+  const int mode = a.topk == 0 ? kDense : a.ws_val ? kAppend : kFused;
   a.cap = 0;
-  if (fused) {
+  if (mode == kFused) {
     // room above k: at least two tiles, so that a cut-back always frees a tile, and as
     // much more as the LDS holds (each cut-back then frees more room: fewer of them)
     const size_t fixed = 2 * (size_t)TILE_BYTES + (size_t)kMaxWaves * 256 * 4 + 256;   // + static LDS
@@ -976,17 +1082,24 @@ hipError_t launch_64(const IdxArgs& a0, int maxlen, hipStream_t st) {
     a.cap = max(a.topk + extra, min(fit, 2 * a.topk + 2 * kKT));
     a.cap &= ~63;                         // 16-byte aligned buffers for the cut-back's reads
   }
-  const size_t shm = 2 * (size_t)TILE_BYTES + (size_t)kMaxWaves * 256 * 4 + (size_t)kMaxWaves * a.cap * 8;
+  const size_t shm = mode == kAppend
+                         ? 2 * (size_t)TILE_BYTES
+                         : 2 * (size_t)TILE_BYTES + (size_t)kMaxWaves * 256 * 4 + (size_t)kMaxWaves * a.cap * 8;
   if (shm > 160 * 1024) return hipErrorInvalidValue;
   a.nwave = kMaxWaves;
   a.chunks = (maxlen + kMaxWaves - 1) / kMaxWaves;
-  const void* kern = fused ? (const void*)indexer64_kernel<DI, false> : (const void*)indexer64_kernel<DI, true>;
+  const void* kern = mode == kDense   ? (const void*)indexer64_kernel<DI, kDense>
+                     : mode == kFused ? (const void*)indexer64_kernel<DI, kFused>
+                                      : (const void*)indexer64_kernel<DI, kAppend>;
   hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
-  if (fused)
-    hipLaunchKernelGGL((indexer64_kernel<DI, false>), dim3(a.chunks, a.nseq), dim3(kMaxWaves * 64), shm, st, a);
+  const dim3 grid(a.chunks, a.nseq), block(kMaxWaves * 64);
+  if (mode == kDense)
+    hipLaunchKernelGGL((indexer64_kernel<DI, kDense>), grid, block, shm, st, a);
+  else if (mode == kFused)
+    hipLaunchKernelGGL((indexer64_kernel<DI, kFused>), grid, block, shm, st, a);
   else
-    hipLaunchKernelGGL((indexer64_kernel<DI, true>), dim3(a.chunks, a.nseq), dim3(kMaxWaves * 64), shm, st, a);
+    hipLaunchKernelGGL((indexer64_kernel<DI, kAppend>), grid, block, shm, st, a);
   return hipGetLastError();
 }
 
@@ -1051,15 +1164,59 @@ hipError_t launch_indexer_dense(const void* q, const void* k, const float* w, bo
   return launch_any(a, bf16, H_I, D_I, cu ? maxlen : T, st);
 }
 
+bool indexer_two_pass(bool bf16, int H_I, int block_size, int topk) {
+  return bf16 && H_I == 64 && block_size == 1 && topk > 0;
+}
+
+// Entries per workspace row: the keys of a whole row when every row fits, else enough
+// for the pivot's count with margin. Sample key j of kSample stands for maxlen /
+// kSample keys; the pivot aims at r0 + 4.3 sqrt(r0) + 1 sample keys (r0 = kSample k /
+// maxlen), and the row holds the count that the sample reaches with that many keys
+// 4.3 standard deviations below its mean: c = maxlen / kSample * (z/2 + sqrt(z^2/4 +
+// target))^2. Rounded up to 64 entries.
+int indexer_ws_cap(int topk, int maxlen) {
+  const double z = 4.3;
+  const double r0 = (double)kSample * topk / (double)maxlen;
+  const double target = r0 + z * std::sqrt(r0) + 2.0;
+  const double root = z / 2 + std::sqrt(z * z / 4 + target);
+  int64_t cap = (int64_t)std::ceil((double)maxlen / kSample * root * root) + 64;
+  cap = std::max<int64_t>(cap, topk);
+  cap = std::min<int64_t>(cap, maxlen);
+  return (int)((cap + 63) / 64 * 64);
+}
+
+size_t indexer_ws_bytes(bool bf16, int T, int maxlen, int H_I, int block_size, int topk) {
+  if (!indexer_two_pass(bf16, H_I, block_size, topk) || T <= 0) return 0;
+  const int cap = indexer_ws_cap(topk, maxlen);
+  return (size_t)T * cap * 8 + (size_t)T * 4;
+}
+
 hipError_t launch_indexer_topk(const void* q, const void* k, const float* w, bool bf16, int T,
                                const int32_t* cu, int nseq, int maxlen, int H_I, int D_I,
                                int block_size, int topk, int force_own, int32_t* out_idx,
-                               float* out_val, hipStream_t st) {
+                               float* out_val, void* ws, hipStream_t st) {
   if (T == 0) return hipSuccess;
   IdxArgs a{};
   a.q = q; a.k = k; a.w = w; a.T = T; a.cu = cu; a.nseq = cu ? nseq : 1; a.B = block_size;
   a.topk = topk; a.force_own = force_own; a.out_idx = out_idx; a.out_val = out_val;
-  return launch_any(a, bf16, H_I, D_I, cu ? maxlen : T, st);
+  const int width = cu ? maxlen : T;
+  if (!ws || !indexer_two_pass(bf16, H_I, block_size, topk))
+    return launch_any(a, bf16, H_I, D_I, width, st);
+  // two passes through the workspace: [T, cap] scores, [T, cap] key ids, [T] counts
+  const int cap = indexer_ws_cap(topk, width);
+  a.ws_cap = cap;
+  a.ws_val = static_cast<float*>(ws);
+  a.ws_idx = reinterpret_cast<int32_t*>(a.ws_val + (size_t)T * cap);
+  a.ws_cnt = a.ws_idx + (size_t)T * cap;
+  hipError_t e = D_I == 64 ? launch_64<64>(a, width, st) : launch_64<128>(a, width, st);
+  if (e != hipSuccess) return e;
+  e = launch_topk_select_counted(a.ws_val, a.ws_idx, a.ws_cnt, cap, T, topk, out_idx, out_val, st);
+  if (e != hipSuccess) return e;
+  // rows whose pivot missed: the exact single-pass kernel, on their workgroups only
+  IdxArgs r = a;
+  r.ws_val = nullptr;
+  r.ws_idx = nullptr;
+  return D_I == 64 ? launch_64<64>(r, width, st) : launch_64<128>(r, width, st);
 }
 
 }  // namespace sa

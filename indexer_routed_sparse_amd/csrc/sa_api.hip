@@ -39,17 +39,27 @@ const char* sa_status_string(int status) {
     case SA_ERR_ALIGN: return "SA_ERR_ALIGN: a pointer is not 16-byte aligned";
     case SA_ERR_UNSUPPORTED: return "SA_ERR_UNSUPPORTED: combination outside the supported limits";
     case SA_ERR_LAUNCH: return "SA_ERR_LAUNCH: kernel launch failed";
+    case SA_ERR_WORKSPACE: return "SA_ERR_WORKSPACE: workspace smaller than the call needs";
     default: return "unknown sa_status";
   }
 }
 
 int sa_abi_version(void) { return SA_ABI_VERSION; }
 
+size_t sa_indexer_workspace_bytes(int dtype, int32_t T, int32_t max_seqlen, int32_t H_I,
+                                  int32_t D_I, int32_t block_size, int32_t topk) {
+  (void)D_I;
+  if (T <= 0 || max_seqlen <= 0 || topk <= 0) return 0;
+  return sa::indexer_ws_bytes(dtype == SA_BF16, T, max_seqlen > T ? T : max_seqlen, H_I,
+                              block_size, topk);
+}
+
 sa_status sa_indexer_scores(const void* q_I, const void* k_I, const float* w, int dtype,
                             int32_t T, const int32_t* cu_seqlens, int32_t num_seqs,
                             int32_t max_seqlen, int32_t H_I, int32_t D_I, int32_t block_size,
                             float* scores, int64_t ld, int32_t topk, int32_t force_own_block,
-                            int32_t* out_idx, float* out_val, void* stream) {
+                            int32_t* out_idx, float* out_val, void* ws, size_t ws_bytes,
+                            void* stream) {
   if (dtype != SA_F32 && dtype != SA_BF16) return SA_ERR_DTYPE;
   int32_t widest = 0;
   sa_status st = check_layout(T, cu_seqlens, num_seqs, max_seqlen, &widest);
@@ -79,9 +89,14 @@ sa_status sa_indexer_scores(const void* q_I, const void* k_I, const float* w, in
   if (scores) return SA_ERR_SHAPE;
   if (!out_idx) return SA_ERR_NULL;
   if (block_size == 1 ? topk > 2048 : topk > 64) return SA_ERR_UNSUPPORTED;
+  if (ws) {
+    if (ws_bytes < sa_indexer_workspace_bytes(dtype, T, widest, H_I, D_I, block_size, topk))
+      return SA_ERR_WORKSPACE;
+    if (!aligned16(ws)) return SA_ERR_ALIGN;
+  }
   return launch_status(sa::launch_indexer_topk(q_I, k_I, w, dtype == SA_BF16, T, cu_seqlens,
                                                num_seqs, widest, H_I, D_I, block_size, topk,
-                                               force_own_block, out_idx, out_val, s));
+                                               force_own_block, out_idx, out_val, ws, s));
 }
 
 sa_status sa_topk_select(const float* vals, const int32_t* cand_idx, int64_t ld, int32_t T,

@@ -11,6 +11,11 @@ int topk_select_max_width();
 hipError_t launch_topk_select(const float* vals, const int32_t* cand, int64_t ld, int T,
                               const int32_t* cu, int nseq, int width, int block_size, int topk,
                               int force_own, int32_t* out_idx, float* out_val, hipStream_t st);
+// Candidate rows [T, ld] whose first cnt[t] entries are valid (ascending ids); rows
+// with cnt[t] < 0 are skipped and their outputs left untouched.
+hipError_t launch_topk_select_counted(const float* vals, const int32_t* cand, const int32_t* cnt,
+                                      int64_t ld, int T, int topk, int32_t* out_idx,
+                                      float* out_val, hipStream_t st);
 
 // sparse_mla.hip
 // Whether the bf16 kernel's LDS (gather stages, q slices, P exchange, index row)
@@ -24,10 +29,14 @@ hipError_t launch_sparse_mla(const void* q, const void* kv, const int32_t* idx, 
 hipError_t launch_indexer_dense(const void* q, const void* k, const float* w, bool bf16, int T,
                                 const int32_t* cu, int nseq, int maxlen, int H_I, int D_I,
                                 int block_size, float* scores, int64_t ld, hipStream_t st);
+// Workspace bytes of a fused selection (0 when the launch runs in one pass), and
+// whether the launch takes the two-pass route when given a workspace.
+size_t indexer_ws_bytes(bool bf16, int T, int maxlen, int H_I, int block_size, int topk);
+bool indexer_two_pass(bool bf16, int H_I, int block_size, int topk);
 hipError_t launch_indexer_topk(const void* q, const void* k, const float* w, bool bf16, int T,
                                const int32_t* cu, int nseq, int maxlen, int H_I, int D_I,
                                int block_size, int topk, int force_own, int32_t* out_idx,
-                               float* out_val, hipStream_t st);
+                               float* out_val, void* ws, hipStream_t st);
 
 // block_gqa.hip
 // Largest route (blocks per query row) the bf16 kernel takes.

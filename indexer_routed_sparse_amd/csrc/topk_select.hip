@@ -283,6 +283,7 @@ struct RowArgs {
   int nseq, block_size, topk, force_own;
   int32_t* out_idx;
   float* out_val;
+  const int32_t* cnt;  // candidate rows only: valid entries per row (< 0: skip the row)
 };
 
 // KIND 0: pivot + candidate buffer (topk <= its capacity). Rows whose pivot fails get
@@ -299,7 +300,8 @@ SA_DEVICE void select_row(int t, const RowArgs& a, S& sm) {
 
   int start = 0, n;
   if (CAND) {
-    n = (int)a.ld;
+    n = a.cnt ? (int)uniform((uint32_t)__ldg(a.cnt + t)) : (int)a.ld;
+    if (n < 0) return;                     // uniform: the row is left to its owner
   } else {
     if (a.cu) start = seq_start_of(a.cu, a.nseq, t);
     const int off = t - start;
@@ -786,7 +788,7 @@ int topk_select_max_width() { return (int)kClasses[kNumClasses - 1].span(); }
 hipError_t launch_topk_select(const float* vals, const int32_t* cand, int64_t ld, int T,
                               const int32_t* cu, int nseq, int width, int block_size, int topk,
                               int force_own, int32_t* out_idx, float* out_val, hipStream_t st) {
-  const RowArgs a{0, vals, cand, ld, cu, nseq, block_size, topk, force_own, out_idx, out_val};
+  const RowArgs a{0, vals, cand, ld, cu, nseq, block_size, topk, force_own, out_idx, out_val, nullptr};
   const int top = class_of(width);
   hipError_t e = hipSuccess;
   bool pivoted = false;  // some class ran the pivot kernel, so rows may await the retry
@@ -806,6 +808,16 @@ hipError_t launch_topk_select(const float* vals, const int32_t* cand, int64_t ld
     pivoted = topk <= cap_of(kClasses[top].nt, kClasses[top].ch);
   }
   if (e != hipSuccess || !pivoted) return e;
+  return retry_class(top, a, T, st);
+}
+
+hipError_t launch_topk_select_counted(const float* vals, const int32_t* cand, const int32_t* cnt,
+                                      int64_t ld, int T, int topk, int32_t* out_idx,
+                                      float* out_val, hipStream_t st) {
+  const RowArgs a{0, vals, cand, ld, nullptr, 1, 1, topk, 0, out_idx, out_val, cnt};
+  const int top = class_of((int)ld);
+  hipError_t e = launch_class(top, a, 0, T, st);
+  if (e != hipSuccess || topk > cap_of(kClasses[top].nt, kClasses[top].ch)) return e;
   return retry_class(top, a, T, st);
 }
 

@@ -34,8 +34,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     import indexer_routed_sparse_amd as sa
-    assert sa.abi_version() == 1
-    for code in range(7):
+    assert sa.abi_version() == 2
+    for code in range(8):
         assert sa.status_string(code).startswith("SA_")
     assert "unknown" in sa.status_string(99)
 
@@ -101,7 +101,37 @@ def test_topk_select_rejects(args, code):
     ((FAKE, FAKE, FAKE, 9, 8, None, 0, 0, 64, 128, 1, FAKE, 8, 0, 0, None, None), 3),  # dtype
 ])
 def test_indexer_rejects(args, code):
-    assert _lib().sa_indexer_scores(*args, None) == code
+    assert _lib().sa_indexer_scores(*args, None, 0, None) == code
+
+
+def _ws_bytes(dtype, T, maxlen, H_I, D_I, B, topk):
+    lib = _lib()
+    lib.sa_indexer_workspace_bytes.restype = ctypes.c_size_t
+    return lib.sa_indexer_workspace_bytes(dtype, T, maxlen, H_I, D_I, B, topk)
+
+
+def test_indexer_workspace_sizes():
+    # two-pass route only for bf16, 64 heads, token mode, fused selection
+    long = _ws_bytes(1, 32768, 32768, 64, 128, 1, 2048)
+    assert 32768 * 2048 * 8 < long < 32768 * 8192 * 8          # a few thousand entries per row
+    assert long % 4 == 0
+    assert _ws_bytes(1, 32768, 32768, 64, 128, 1, 0) == 0          # dense mode
+    assert _ws_bytes(1, 32768, 32768, 16, 128, 1, 2048) == 0       # generic kernel
+    assert _ws_bytes(0, 32768, 32768, 64, 128, 1, 2048) == 0       # fp32
+    assert _ws_bytes(1, 32768, 32768, 64, 128, 64, 16) == 0        # block mode
+    assert _ws_bytes(1, 0, 1, 64, 128, 1, 16) == 0                 # nothing to do
+    # rows never wider than the row: short sequences take the whole row
+    assert _ws_bytes(1, 1000, 1000, 64, 128, 1, 2048) == 1000 * 1024 * 8 + 1000 * 4
+    # packed sequences size by the widest one
+    assert _ws_bytes(1, 65536, 16384, 64, 128, 1, 2048) < _ws_bytes(1, 65536, 65536, 64, 128, 1, 2048)
+
+
+def test_indexer_rejects_small_workspace():
+    need = _ws_bytes(1, 8, 8, 64, 128, 1, 4)
+    assert need > 0
+    args = (FAKE, FAKE, FAKE, 1, 8, None, 0, 0, 64, 128, 1, None, 0, 4, 0, FAKE, None)
+    assert _lib().sa_indexer_scores(*args, FAKE, need - 1, None) == 7     # SA_ERR_WORKSPACE
+    assert _lib().sa_indexer_scores(*args, MIS, need, None) == 4          # misaligned workspace
 
 
 @pytest.mark.parametrize("args,code", [

@@ -362,12 +362,14 @@ def test_block_topk_buffer_cutback_against_oracle(sa, B, k):
     np.testing.assert_array_equal(val.cpu().numpy(), ref_v)
 
 
+@pytest.mark.parametrize("workspace", [True, False])
 @pytest.mark.parametrize("k", [1, 100, 777, 2048])
-def test_indexer64_fused_small_k_against_oracle(sa, k):
+def test_indexer64_fused_small_k_against_oracle(sa, k, workspace):
     """64 indexer heads on the integer grid, one sequence of 4096 tokens and packed
-    sequences: the fused selection (many buffer cut-backs at small k, exact ties at
-    zero) equals the oracle bit for bit on sampled rows, among them each sequence's
-    first and last rows and the last 32 rows."""
+    sequences: the fused selection, in one pass (many buffer cut-backs at small k) and
+    in two passes through a workspace (sampled pivot, then the exact select), equals
+    the oracle bit for bit on sampled rows, among them each sequence's first and last
+    rows and the last 32 rows."""
     wl = W["long_dsa"]
     for lengths in [(4096,), (1000, 3, 2048, 1045)]:
         T = sum(lengths)
@@ -375,7 +377,7 @@ def test_indexer64_fused_small_k_against_oracle(sa, k):
         x = workloads.indexer_inputs(wl, integer=True, T=T)
         kw = dict(cu_seqlens=cu_dev(lengths), max_seqlen=max(lengths)) if multi else {}
         idx, val = sa.indexer_topk(x["q_I"].to(DEV), x["k_I"].to(DEV), x["w"].to(DEV), k,
-                                   with_values=True, **kw)
+                                   with_values=True, workspace=workspace, **kw)
         rows = np.union1d(sample_rows(T, 24, 31 + k, lengths if multi else None),
                           np.arange(T - 32, T))
         ref_i, ref_v = oracle.indexer_topk(x["q_I"], x["k_I"], x["w"], k,
@@ -383,6 +385,34 @@ def test_indexer64_fused_small_k_against_oracle(sa, k):
                                            rows=rows)
         np.testing.assert_array_equal(idx.cpu().numpy()[rows], ref_i, err_msg=f"lengths {lengths}")
         np.testing.assert_array_equal(val.cpu().numpy()[rows], ref_v, err_msg=f"lengths {lengths}")
+
+
+@pytest.mark.parametrize("k", [100, 2048])
+def test_indexer64_two_pass_redo_rows_against_oracle(sa, k):
+    """64 heads with 70 % of the key rows scoring exactly zero (their entries are
+    non-positive while every query entry is non-negative): at k = 2048 the k-th score
+    of the later rows is a zero shared by thousands of keys, so the sampled pivot keeps
+    more keys than a workspace row holds and those rows are marked for the exact
+    one-pass kernel. The marks are read back from the workspace's count array, and
+    every sampled row equals the oracle bit for bit."""
+    import dataclasses
+    wl = dataclasses.replace(W["long_dsa"], neg_key_frac=0.7)
+    T = 4096
+    x = workloads.indexer_inputs(wl, integer=True, T=T)
+    xd = {n: t.to(DEV) for n, t in x.items()}
+    ws = sa.indexer_workspace(xd["q_I"], k)
+    idx, val = sa.indexer_topk(xd["q_I"], xd["k_I"], xd["w"], k, with_values=True, workspace=ws)
+    torch.cuda.synchronize()
+    cap = (ws.numel() - 4 * T) // (8 * T)
+    cnt = ws[8 * T * cap:8 * T * cap + 4 * T].view(torch.int32).cpu().numpy()
+    if k == 2048:
+        assert (cnt == -1).sum() > 100, "no row was left to the exact kernel"
+    assert np.all((cnt == -1) | ((cnt >= np.minimum(k, np.arange(T) + 1)) & (cnt <= cap)))
+    rows = np.union1d(sample_rows(T, 40, 37), np.arange(T - 16, T))
+    rows = np.union1d(rows, np.nonzero(cnt == -1)[0][:16])
+    ref_i, ref_v = oracle.indexer_topk(x["q_I"], x["k_I"], x["w"], k, rows=rows)
+    np.testing.assert_array_equal(idx.cpu().numpy()[rows], ref_i)
+    np.testing.assert_array_equal(val.cpu().numpy()[rows], ref_v)
 
 
 @pytest.mark.parametrize("name", ["nope_unaligned", "block_gqa"])
@@ -420,15 +450,16 @@ def test_indexer64_fused_matches_dense_then_select(sa, k, integer):
         assert torch.equal(v1, v2), f"lengths {lengths}"
 
 
+@pytest.mark.parametrize("workspace", [True, False])
 @pytest.mark.parametrize("name", ["long_dsa", "thd_varlen"])
-def test_indexer_topk_full_size_integer_sampled(sa, name):
+def test_indexer_topk_full_size_integer_sampled(sa, name, workspace):
     wl = W[name]
     T = wl.T
     lengths = wl.lengths if len(wl.lengths) > 1 else None
     x = workloads.indexer_inputs(wl, integer=True, device=DEV)
     assert workloads.exact_sum_bound(x["q_I"][:2048], x["k_I"], x["w"][:2048]) < 2 ** 24
     kw = dict(cu_seqlens=cu_dev(wl.lengths), max_seqlen=max(wl.lengths)) if lengths else {}
-    idx = sa.indexer_topk(x["q_I"], x["k_I"], x["w"], 2048, **kw).cpu().numpy()
+    idx = sa.indexer_topk(x["q_I"], x["k_I"], x["w"], 2048, workspace=workspace, **kw).cpu().numpy()
     rows = sample_rows(T, 8, 11, lengths)
     cu = workloads.cu_seqlens(wl.lengths) if lengths else None
     xc = {n: t.cpu() for n, t in x.items()}
