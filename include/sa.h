@@ -143,6 +143,34 @@ size_t sa_indexer_workspace_bytes(int dtype, int32_t T, int32_t max_seqlen, int3
                                   int32_t D_I, int32_t block_size, int32_t topk);
 
 /*
+ * sa_indexer_scores_noalloc -- sa_indexer_scores without a caller workspace and
+ * without any allocation.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments, results and
+ * errors as sa_indexer_scores, minus ws/ws_bytes: when the call wants a workspace
+ * (sa_indexer_workspace_bytes > 0) it uses a static device array of this library,
+ * sa_noalloc_scratch_bytes() = 128 MiB, which every GPU the library runs on holds
+ * from the library's load until the process ends; the first call on a device looks
+ * up that device's copy. A call that needs more than the array holds returns
+ * SA_ERR_WORKSPACE without launching anything (at topk = 2048 that is about 5000
+ * rows of one 5000-token sequence; pass fewer rows per call, or use
+ * sa_indexer_scores with a workspace). Nothing in the array has to start at zero:
+ * every byte a call reads was written earlier by the same call. All calls on one
+ * GPU share its array, so calls that overlap in time on one GPU (two streams, two
+ * host threads) race and must be serialised by the caller.
+ */
+sa_status sa_indexer_scores_noalloc(const void* q_I, const void* k_I, const float* w, int dtype,
+                                    int32_t T, const int32_t* cu_seqlens, int32_t num_seqs,
+                                    int32_t max_seqlen, int32_t H_I, int32_t D_I,
+                                    int32_t block_size, float* scores, int64_t ld, int32_t topk,
+                                    int32_t force_own_block, int32_t* out_idx, float* out_val,
+                                    void* stream);
+
+/* Bytes of the static device array that sa_indexer_scores_noalloc uses. */
+size_t sa_noalloc_scratch_bytes(void);
+
+/*
  * sa_topk_select -- exact, deterministic top-k of score rows.
  *
  * [QSA] "Describe the solution you'd like": exact selection keyed lexicographically

@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libsa.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["sa_api.hip", "topk_select.hip", "sparse_mla.hip", "indexer.hip", "block_gqa.hip"]
+SOURCES = ["sa_api.hip", "sa_noalloc.hip", "topk_select.hip", "sparse_mla.hip", "indexer.hip",
+           "block_gqa.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
