@@ -213,10 +213,15 @@ def write_traffic(fetch_dir, write_dir, command):
     rec = {"calibration": {"copy_bytes": COPY_ELEMS * 4, "fetch_factor": round(f_cal, 4),
                            "write_factor": round(w_cal, 4)},
            "command": command}
+    topk_kernel = lambda n: any(f"topk_{x}_kernel" in n for x in ("pivot", "full", "retry"))
     groups = {
         "sparse_mla_long_dsa": (lambda n: "sparse_mla_bf16_kernel" in n, ["sparse_mla.hip", "sa_common.h"], 1),
-        "indexer_topk_long_dsa": (lambda n: "indexer64_kernel" in n, ["indexer.hip", "sa_common.h"], None),
-        "topk_select_long_dsa": (lambda n: "topk_pivot_kernel" in n or "topk_retry_kernel" in n,
+        # the fused call: the append pass, the select over its candidate rows (candidate
+        # ids: template flag true) and the exact redo pass of marked rows
+        "indexer_topk_long_dsa": (lambda n: "indexer64_kernel<128, 2>" in n or "indexer64_kernel<128, 1>" in n
+                                  or (topk_kernel(n) and ", true>" in n),
+                                  ["indexer.hip", "topk_select.hip", "sa_common.h"], None),
+        "topk_select_long_dsa": (lambda n: topk_kernel(n) and ", false>" in n,
                                  ["topk_select.hip", "sa_common.h"], None),
     }
     for key, (match, srcs, _) in groups.items():
@@ -224,8 +229,6 @@ def write_traffic(fetch_dir, write_dir, command):
         wv = per_kernel(write, "WRITE_SIZE", match)
         if not fv:
             continue
-        if key == "indexer_topk_long_dsa":   # the fused call is the first indexer dispatch
-            fv, wv = fv[:1], wv[:1]
         fb = sum(fv) * f_cal * 1024.0
         wb = sum(wv) * w_cal * 1024.0
         rec[key] = {"dispatches_per_call": len(fv), "fetch_bytes": round(fb),
@@ -335,14 +338,30 @@ def main():
             "traffic": _traffic("sparse_mla_long_dsa", ["sparse_mla.hip", "sa_common.h"]),
         },
         "roofline_indexer": {
-            "kernel": "indexer64_kernel", "bound": "mfma",
+            "kernel": "indexer64_kernel (append pass) + topk select over its candidates", "bound": "mfma",
             "achieved": round(idx_flops / (t_idx * 1e-3) / 1e12, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(idx_flops / (t_idx * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": _traffic("indexer_topk_long_dsa", ["indexer.hip", "topk_select.hip", "sa_common.h"]),
         },
     }
 
     if not args.no_extras:
+        # ---- the same selection in one pass (no workspace), for comparison
+        print("[bench] indexer top-k in one pass", file=sys.stderr, flush=True)
+        idx1 = torch.empty_like(idx)
+        sa.sa_indexer_scores(x["q_I"], x["k_I"], x["w"], topk=K, out_idx=idx1)
+        t1s = []
+        for _ in range(3):
+            tm = Timer()
+            with tm:
+                sa.sa_indexer_scores(x["q_I"], x["k_I"], x["w"], topk=K, out_idx=idx1)
+            t1s.append(tm)
+        torch.cuda.synchronize()
+        result["indexer_one_pass_ms"] = round(float(np.median([tm.ms() for tm in t1s])), 3)
+        result["indexer_one_pass_same_indices"] = bool(torch.equal(idx1, idx))
+        del idx1, ws
+
         # ---- standalone exact top-k over a materialised causal score matrix (HBM-bound)
         print("[bench] top-k select on materialised scores", file=sys.stderr, flush=True)
         del out, lse

@@ -34,8 +34,14 @@
  *   - Errors: argument checks run on the host before any launch and return a status
  *     without touching the stream ([QSA] "Additional context": fail fast on
  *     unsupported combinations). SA_ERR_LAUNCH reports hipGetLastError after a launch.
- *     Device-side contents (index values, cu_seqlens values) are NOT validated: an
- *     index outside its documented range is undefined behaviour.
+ *     Device-side contents (index values, cu_seqlens values) are NOT validated by
+ *     libsa.so: an index outside its documented range is undefined behaviour. The
+ *     debug build libsa_debug.so (same symbols, same kernels) checks them on the
+ *     device before launching -- idx of sa_sparse_mla_fwd in [-1, S), and cu_seqlens
+ *     (cu[0] = 0, cu[num_seqs] = T, every length in [0, max_seqlen]) -- and returns
+ *     SA_ERR_SHAPE for a value out of range; those checks synchronise the stream.
+ *     Route values of sa_block_sparse_gqa_fwd need no check: any value outside a
+ *     query's blocks [0, own] contributes nothing.
  *   - Determinism: the same inputs give bitwise-identical outputs on every run,
  *     independent of other work on the device ([NOPE] "Validation": forward bit-exact
  *     replay). No call uses floating-point atomics.

@@ -26,6 +26,31 @@ sa_status check_layout(int32_t T, const int32_t* cu, int32_t num_seqs, int32_t m
   return SA_OK;
 }
 
+// Debug build only (SA_DEBUG_CHECKS): device contents are validated before any
+// launch; a value out of its documented range returns SA_ERR_SHAPE.
+#ifdef SA_DEBUG_CHECKS
+sa_status debug_offsets(const int32_t* cu, int32_t nseq, int32_t T, int32_t maxlen, hipStream_t st) {
+  if (!cu) return SA_OK;
+  bool ok = false;
+  if (sa::debug_check_offsets(cu, nseq, T, maxlen, st, &ok) != hipSuccess) return SA_ERR_LAUNCH;
+  return ok ? SA_OK : SA_ERR_SHAPE;
+}
+sa_status debug_range(const int32_t* v, int64_t n, int32_t lo, int32_t hi, hipStream_t st) {
+  bool ok = false;
+  if (sa::debug_check_range(v, n, lo, hi, st, &ok) != hipSuccess) return SA_ERR_LAUNCH;
+  return ok ? SA_OK : SA_ERR_SHAPE;
+}
+#define SA_DEBUG_RETURN(expr)           \
+  do {                                  \
+    const sa_status dbg_ = (expr);      \
+    if (dbg_ != SA_OK) return dbg_;     \
+  } while (0)
+#else
+#define SA_DEBUG_RETURN(expr) \
+  do {                        \
+  } while (0)
+#endif
+
 }  // namespace
 
 extern "C" {
@@ -76,6 +101,7 @@ sa_status sa_indexer_scores(const void* q_I, const void* k_I, const float* w, in
   if (!q_I || !k_I || !w) return SA_ERR_NULL;
   if (!aligned16(q_I) || !aligned16(k_I) || !aligned16(w)) return SA_ERR_ALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  SA_DEBUG_RETURN(debug_offsets(cu_seqlens, num_seqs, T, widest, s));
   if (dense) {
     if (!scores) return SA_ERR_NULL;
     if (out_idx || out_val) return SA_ERR_SHAPE;
@@ -122,6 +148,8 @@ sa_status sa_topk_select(const float* vals, const int32_t* cand_idx, int64_t ld,
   if (T == 0) return SA_OK;
   if (!vals || !out_idx) return SA_ERR_NULL;
   if (!aligned16(vals) || (cand_idx && !aligned16(cand_idx))) return SA_ERR_ALIGN;
+  if (!cand_idx) SA_DEBUG_RETURN(debug_offsets(cu_seqlens, num_seqs, T, max_seqlen,
+                                               reinterpret_cast<hipStream_t>(stream)));
   return launch_status(sa::launch_topk_select(vals, cand_idx, ld, T, cand_idx ? nullptr : cu_seqlens,
                                               num_seqs, width, block_size, topk, force_own_block,
                                               out_idx, out_val, reinterpret_cast<hipStream_t>(stream)));
@@ -145,6 +173,7 @@ sa_status sa_sparse_mla_fwd(const void* q, const void* kv, const int32_t* idx, i
   if (T == 0) return SA_OK;
   if (!q || !kv || !idx || !out) return SA_ERR_NULL;
   if (!aligned16(q) || !aligned16(kv) || !aligned16(out)) return SA_ERR_ALIGN;
+  SA_DEBUG_RETURN(debug_range(idx, (int64_t)T * topk, -1, S, reinterpret_cast<hipStream_t>(stream)));
   return launch_status(sa::launch_sparse_mla(q, kv, idx, dtype == SA_BF16, T, S, H, d_qk, d_v, topk,
                                              scale, out, lse, reinterpret_cast<hipStream_t>(stream)));
 }
@@ -167,6 +196,7 @@ sa_status sa_block_sparse_gqa_fwd(const void* q, const void* k, const void* v, c
   if (T == 0) return SA_OK;
   if (!q || !k || !v || !blk || !out) return SA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SA_ERR_ALIGN;
+  SA_DEBUG_RETURN(debug_offsets(cu_seqlens, num_seqs, T, max_seqlen, reinterpret_cast<hipStream_t>(stream)));
   return launch_status(sa::launch_block_gqa(q, k, v, blk, dtype == SA_BF16, T, cu_seqlens, num_seqs,
                                             Hq, Hkv, D, Dv, block_size, nblk, scale, out, lse,
                                             reinterpret_cast<hipStream_t>(stream)));

@@ -46,4 +46,12 @@ hipError_t launch_block_gqa(const void* q, const void* k, const void* v, const i
                             int Dv, int block_size, int nblk, float scale, void* out, float* lse,
                             hipStream_t st);
 
+// sa_checks.hip (called by the debug build's entry points only): whether every value
+// of v[0..n) lies in [lo, hi); whether cu_seqlens is a valid offset array for T rows
+// with sequences of at most maxlen rows. Both synchronise `st`.
+hipError_t debug_check_range(const int32_t* v, int64_t n, int32_t lo, int32_t hi, hipStream_t st,
+                             bool* ok);
+hipError_t debug_check_offsets(const int32_t* cu, int nseq, int T, int maxlen, hipStream_t st,
+                               bool* ok);
+
 }  // namespace sa

@@ -32,6 +32,14 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
 
 
+def test_debug_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(os.path.join(ROOT, "indexer_routed_sparse_amd", "libsa_debug.so"))
+    for n in _declared():
+        assert hasattr(lib, n), n
+    lib.sa_abi_version.restype = ctypes.c_int
+    assert lib.sa_abi_version() == 2
+
+
 def test_version_and_status_strings():
     import indexer_routed_sparse_amd as sa
     assert sa.abi_version() == 2

@@ -712,6 +712,54 @@ def test_replay_bitwise_and_inputs_preserved(sa):
         assert torch.equal(t, {**x, **m, **gq}[n]), n
 
 
+def test_debug_build_rejects_out_of_range_contents(sa):
+    """libsa_debug.so checks device contents: an index outside [-1, S) in sparse MLA and
+    malformed sequence offsets return SA_ERR_SHAPE before any launch; valid inputs give
+    the release library's results bit for bit."""
+    import ctypes
+    import os
+    dbg = ctypes.CDLL(os.path.join(os.path.dirname(sa.__file__), "libsa_debug.so"))
+    dbg.sa_sparse_mla_fwd.argtypes = sa.lib.sa_sparse_mla_fwd.argtypes
+    dbg.sa_block_sparse_gqa_fwd.argtypes = sa.lib.sa_block_sparse_gqa_fwd.argtypes
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    T, S, H, k = 16, 100, 16, 40
+    g = torch.Generator().manual_seed(3)
+    q = torch.randn((T, H, 576), generator=g).to(torch.bfloat16).to(DEV)
+    kv = torch.randn((S, 576), generator=g).to(torch.bfloat16).to(DEV)
+    idx = torch.randint(-1, S, (T, k), generator=g, dtype=torch.int32).to(DEV)
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=DEV)
+
+    def mla(ix):
+        return dbg.sa_sparse_mla_fwd(p(q), p(kv), p(ix), 1, T, S, H, 576, 512, k, 0.05, p(out), None, stream)
+
+    assert mla(idx) == 0
+    ref = sa.sparse_mla(q, kv, idx, 0.05, with_lse=False)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    for bad in (S, -2, 1 << 30):
+        ix = idx.clone()
+        ix[T - 1, k - 1] = bad
+        assert mla(ix) == 2, bad
+    # sequence offsets: wrong total, a sequence longer than max_seqlen, a negative length
+    gq = workloads.gqa_inputs(W["block_gqa"], T=64)
+    gq = {n: t.to(DEV) for n, t in gq.items()}
+    blk = torch.zeros((64, 2), dtype=torch.int32, device=DEV)
+    o = torch.empty((64, 32, 128), dtype=torch.bfloat16, device=DEV)
+
+    def gqa(cu, maxlen):
+        c = torch.tensor(cu, dtype=torch.int32, device=DEV)
+        return dbg.sa_block_sparse_gqa_fwd(p(gq["q"]), p(gq["k"]), p(gq["v"]), p(blk), 1, 64, p(c),
+                                           len(cu) - 1, maxlen, 32, 4, 128, 128, 64, 2, 0.1, p(o),
+                                           None, stream)
+
+    assert gqa([0, 30, 64], 34) == 0
+    assert gqa([0, 30, 63], 34) == 2
+    assert gqa([0, 30, 64], 33) == 2
+    assert gqa([0, 40, 30, 64], 34) == 2
+    torch.cuda.synchronize()
+
+
 def test_empty_inputs_are_noops(sa):
     z = torch.empty((0, 16, 576), dtype=torch.bfloat16, device=DEV)
     kv = torch.zeros((4, 576), dtype=torch.bfloat16, device=DEV)
