@@ -354,3 +354,109 @@ def indexer_topk(q_I, k_I, w, k: int, cu_seqlens=None, block_size: int = 1,
         i, v = topk_select_dense(sc, k, cu_seqlens, block_size, force_own_block, rows=rr)
         idx[r0:r0 + len(rr)], val[r0:r0 + len(rr)] = i, v
     return idx, val
+
+
+# ------------------------------------------------------- backward of O4 / O5
+#
+# "Enable DSA CP/absorbed/THD paths with TileLang fused ops", file table (sparse-MLA
+# backward kernels) and "Add trainable QSA sparse attention with a TileLang backend",
+# "Is your feature request related to a problem?" (sparse GQA attention forward and
+# backward). Gradients of the forward definitions above, in closed form: for one
+# query row and head over its attended keys j with logits l_j = scale * q . k_j,
+# probabilities p = softmax(l) and output o = sum_j p_j v_j, an upstream gradient g of
+# o gives
+#     dp_j = g . v_j,   D = sum_j p_j dp_j (= g . o),   dl_j = p_j (dp_j - D),
+#     dq   = scale * sum_j dl_j k_j,
+#     dk_j = scale * dl_j q,   dv_j = p_j g,
+# summed over heads (and, for a key attended by several rows or slots, over those).
+
+def sparse_mla_bwd_row(q_t, kv, idx_t, dout_t, scale: float, d_v: int = 512):
+    """Gradients of ``sparse_mla_row`` for one query row.
+
+    q_t [H, d_qk], kv [S, d_qk], idx_t [k], dout_t [H, d_v] (upstream gradient of
+    out). The latent row is both key (all d_qk channels) and value (first d_v), so a
+    slot's gradient row is dk_j on all channels plus dv_j on the first d_v. Returns
+    dq [H, d_qk] and dkv_slots [k, d_qk] (one row per slot, zero for -1 slots; a
+    repeated index gets one row per slot), float64.
+    """
+    q = _f64(q_t)
+    g = _f64(dout_t)
+    idx = _i64(idx_t)
+    H, d_qk = q.shape
+    dq = np.zeros((H, d_qk))
+    dslots = np.zeros((idx.size, d_qk))
+    sel = np.nonzero(idx >= 0)[0]
+    if sel.size == 0:
+        return dq, dslots
+    rows = _f64(kv[idx[sel].tolist()] if hasattr(kv, "detach") else kv[idx[sel]])
+    logits = scale * (q @ rows.T)                     # [H, n]
+    p = np.exp(logits - logits.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    dp = g @ rows[:, :d_v].T                          # [H, n]
+    D = (p * dp).sum(axis=1, keepdims=True)
+    dl = p * (dp - D)
+    dq = scale * (dl @ rows)
+    dk = scale * (dl.T @ q)                           # [n, d_qk], summed over heads
+    dk[:, :d_v] += p.T @ g
+    dslots[sel] = dk
+    return dq, dslots
+
+
+def sparse_mla_bwd(q, kv, idx, dout, scale: float, d_v: int = 512, rows=None):
+    """``sparse_mla_bwd_row`` over every row (or a subset): dq [len(rows), H, d_qk] and
+    dkv [S, d_qk] (the slot gradients of those rows scattered onto their latent rows)."""
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    kvh = _f64(kv)
+    idxh = _i64(idx)
+    H, d_qk = q.shape[1], q.shape[2]
+    dq = np.zeros((len(rows), H, d_qk))
+    dkv = np.zeros(kvh.shape)
+    for r, t in enumerate(rows):
+        dq[r], ds = sparse_mla_bwd_row(q[t], kvh, idxh[t], dout[t], scale, d_v)
+        ok = idxh[t] >= 0
+        np.add.at(dkv, idxh[t][ok], ds[ok])
+    return dq, dkv
+
+
+def _gqa_keys(blk_t, t: int, seq_start: int, block_size: int) -> np.ndarray:
+    keys = []
+    for b in sorted(set(int(x) for x in _i64(blk_t) if x >= 0)):
+        lo = seq_start + b * block_size
+        keys.extend(range(lo, min(lo + block_size - 1, t) + 1))
+    return np.asarray(keys, dtype=np.int64)
+
+
+def block_sparse_gqa_bwd(q, k, v, blk, dout, block_size: int, scale: float,
+                         cu_seqlens=None, rows=None):
+    """Gradients of ``block_sparse_gqa`` (same key sets: the causal keys of the routed
+    blocks, each block once; head h reads kv head h // (Hq / Hkv)). Returns dq
+    [len(rows), Hq, D], dk [S, Hkv, D], dv [S, Hkv, Dv], float64; dk and dv collect the
+    contributions of the listed rows."""
+    T = q.shape[0]
+    start, _ = seq_bounds(T, cu_seqlens)
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    qh, kh, vh, gh = _f64(q), _f64(k), _f64(v), _f64(dout)
+    blkh = _i64(blk)
+    Hq, D = qh.shape[1], qh.shape[2]
+    Hkv = kh.shape[1]
+    group = Hq // Hkv
+    dq = np.zeros((len(rows), Hq, D))
+    dk = np.zeros(kh.shape)
+    dv = np.zeros(vh.shape)
+    for r, t in enumerate(rows):
+        keys = _gqa_keys(blkh[t], int(t), int(start[t]), block_size)
+        if keys.size == 0:
+            continue
+        for h in range(Hq):
+            gi = h // group
+            K = kh[keys, gi, :]
+            V = vh[keys, gi, :]
+            l = scale * (K @ qh[t, h])
+            p = np.exp(l - l.max())
+            p /= p.sum()
+            dp = V @ gh[t, h]
+            dl = p * (dp - (p * dp).sum())
+            dq[r, h] = scale * (dl @ K)
+            np.add.at(dk[:, gi, :], keys, scale * np.outer(dl, qh[t, h]))
+            np.add.at(dv[:, gi, :], keys, np.outer(p, gh[t, h]))
+    return dq, dk, dv

@@ -523,3 +523,141 @@ def test_generators_are_deterministic():
     for t in range(64):
         s = np.nonzero(neg[:t + 1].numpy())[0]
         assert np.all(sc[t, s] == 0)
+
+
+# ------------------------------------------------------- backward of O4 / O5
+
+def _torch_sparse_mla_loss(q, kv, idx, dout, scale, d_v):
+    """sum(out * dout) of sparse attention over the slots of idx, written with torch
+    gathers (each slot on its own, so repeated indices count per slot); differentiated
+    by autograd, it gives the gradients without the oracle's closed form."""
+    total = q.new_zeros(())
+    for t in range(q.shape[0]):
+        sl = [j for j in range(idx.shape[1]) if idx[t, j] >= 0]
+        if not sl:
+            continue
+        rows = kv[torch.as_tensor(idx[t, sl], dtype=torch.long)]
+        p = torch.softmax(scale * q[t] @ rows.T, dim=-1)
+        total = total + (p @ rows[:, :d_v] * dout[t]).sum()
+    return total
+
+
+@pytest.mark.parametrize("d_qk,d_v", [(24, 16), (20, 20)])
+def test_mla_bwd_matches_autograd(d_qk, d_v):
+    """Closed-form dq and dkv against torch autograd through a gather-based forward,
+    with -1 slots, a repeated index (two slots, two contributions), an all-invalid row
+    and a row with one valid slot."""
+    rng = np.random.default_rng(40 + d_qk)
+    T, S, H, k, scale = 7, 30, 3, 9, 0.37
+    q = rng.standard_normal((T, H, d_qk))
+    kv = rng.standard_normal((S, d_qk))
+    dout = rng.standard_normal((T, H, d_v))
+    idx = np.full((T, k), -1)
+    for t in range(T):
+        n = int(rng.integers(2, k + 1))
+        idx[t, rng.permutation(k)[:n]] = rng.integers(0, S, n)
+    idx[2, :3] = [5, 5, 11]                      # repeated index
+    idx[3] = -1                                  # all invalid
+    idx[4] = -1
+    idx[4, 6] = 17                               # one valid slot
+    dq, dkv = oracle.sparse_mla_bwd(q, kv, idx, dout, scale, d_v)
+    qt = torch.from_numpy(q).requires_grad_()
+    kvt = torch.from_numpy(kv).requires_grad_()
+    _torch_sparse_mla_loss(qt, kvt, idx, torch.from_numpy(dout), scale, d_v).backward()
+    np.testing.assert_allclose(dq, qt.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dkv, kvt.grad.numpy(), rtol=1e-11, atol=1e-12)
+    assert np.all(dq[3] == 0) and np.all(dq[4] == 0)         # no key / one key: dq = 0
+    only = np.zeros(d_qk)
+    only[:d_v] = dout[4].sum(0)                               # one key: its gradient is dout
+    _, alone = oracle.sparse_mla_bwd(q[4:5], kv, idx[4:5], dout[4:5], scale, d_v)
+    np.testing.assert_allclose(alone[17], only, atol=1e-12)
+
+
+def test_mla_bwd_matches_library_attention_autograd():
+    """Against autograd through torch's scaled-dot-product attention (float64) with a
+    boolean key mask, on rows without repeated indices."""
+    rng = np.random.default_rng(45)
+    T, S, H, d_qk, d_v, k = 5, 40, 4, 32, 16, 12
+    q = rng.standard_normal((T, H, d_qk))
+    kv = rng.standard_normal((S, d_qk))
+    dout = rng.standard_normal((T, H, d_v))
+    idx = np.stack([rng.permutation(S)[:k] for _ in range(T)])
+    idx[1, 5:] = -1
+    dq, dkv = oracle.sparse_mla_bwd(q, kv, idx, dout, 0.2, d_v)
+    mask = np.zeros((T, S), dtype=bool)
+    for t in range(T):
+        mask[t, idx[t][idx[t] >= 0]] = True
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None].requires_grad_()
+    kvt = torch.from_numpy(kv).requires_grad_()
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt, kvt[None, None].expand(1, H, S, d_qk), kvt[:, :d_v][None, None].expand(1, H, S, d_v),
+        attn_mask=torch.from_numpy(mask)[None, None], scale=0.2)
+    (o * torch.from_numpy(dout).permute(1, 0, 2)[None]).sum().backward()
+    np.testing.assert_allclose(dq, qt.grad[0].permute(1, 0, 2).numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dkv, kvt.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_mla_bwd_finite_differences():
+    """Central differences of sum(out * dout) through the (separately pinned) forward
+    oracle match the backward, for a q entry, a RoPE-slot kv entry and a value entry."""
+    rng = np.random.default_rng(46)
+    T, S, H, d_qk, d_v, k, scale = 3, 12, 2, 10, 6, 5, 0.5
+    q = rng.standard_normal((T, H, d_qk))
+    kv = rng.standard_normal((S, d_qk))
+    dout = rng.standard_normal((T, H, d_v))
+    idx = np.stack([rng.permutation(S)[:k] for _ in range(T)])
+    dq, dkv = oracle.sparse_mla_bwd(q, kv, idx, dout, scale, d_v)
+
+    def loss(qq, kk):
+        o, _ = oracle.sparse_mla(qq, kk, idx, scale, d_v)
+        return float((o * dout).sum())
+
+    eps = 1e-6
+    for (t, h, c) in [(1, 1, 3), (2, 0, 9)]:
+        qp, qm = q.copy(), q.copy()
+        qp[t, h, c] += eps
+        qm[t, h, c] -= eps
+        assert abs((loss(qp, kv) - loss(qm, kv)) / (2 * eps) - dq[t, h, c]) < 1e-7
+    for (s, c) in [(int(idx[0, 0]), 8), (int(idx[1, 2]), 2)]:
+        kp, km = kv.copy(), kv.copy()
+        kp[s, c] += eps
+        km[s, c] -= eps
+        assert abs((loss(q, kp) - loss(q, km)) / (2 * eps) - dkv[s, c]) < 1e-7
+
+
+def test_gqa_bwd_matches_library_attention_autograd_thd():
+    """Block-routed GQA gradients against autograd through torch's SDPA with the block
+    key mask, on packed sequences, with repeated blocks and blocks past the own one."""
+    rng = np.random.default_rng(47)
+    lengths = (13, 20)
+    cu = workloads.cu_seqlens(lengths)
+    T, Hq, Hkv, D, Dv, B, nb = 33, 6, 2, 8, 5, 4, 5
+    q = rng.standard_normal((T, Hq, D))
+    k = rng.standard_normal((T, Hkv, D))
+    v = rng.standard_normal((T, Hkv, Dv))
+    dout = rng.standard_normal((T, Hq, Dv))
+    start, _ = oracle.seq_bounds(T, cu)
+    blk = np.full((T, nb), -1)
+    mask = np.zeros((T, T), dtype=bool)
+    for t in range(T):
+        own = (t - start[t]) // B
+        row = sorted(set(rng.permutation(own + 1)[:2].tolist() + [own]))
+        blk[t, :len(row)] = row                           # at most 3 of the 5 slots
+        blk[t, nb - 1] = row[0]                           # repeated block
+        if t % 3 == 0:
+            blk[t, nb - 2] = own + 1                      # past the own block
+        for b in row:
+            mask[t, start[t] + b * B:min(start[t] + b * B + B - 1, t) + 1] = True
+    dq, dk, dv = oracle.block_sparse_gqa_bwd(q, k, v, blk, dout, B, 0.35, cu_seqlens=cu)
+    rep = Hq // Hkv
+    qt = torch.from_numpy(q).requires_grad_()
+    kt = torch.from_numpy(k).requires_grad_()
+    vt = torch.from_numpy(v).requires_grad_()
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt.permute(1, 0, 2)[None], kt.permute(1, 0, 2).repeat_interleave(rep, 0)[None],
+        vt.permute(1, 0, 2).repeat_interleave(rep, 0)[None],
+        attn_mask=torch.from_numpy(mask)[None, None], scale=0.35)[0].permute(1, 0, 2)
+    (o * torch.from_numpy(dout)).sum().backward()
+    np.testing.assert_allclose(dq, qt.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dk, kt.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dv, vt.grad.numpy(), rtol=1e-11, atol=1e-12)
