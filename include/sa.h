@@ -245,6 +245,37 @@ sa_status sa_sparse_mla_fwd(const void* q, const void* kv, const int32_t* idx, i
                             int32_t topk, float scale, void* out, float* lse, void* stream);
 
 /*
+ * sa_sparse_mla_bwd -- gradients of sa_sparse_mla_fwd.
+ *
+ * [DSA] file table (sparse-MLA backward kernels); [NOPE] "Validation" (output and
+ * Q/K gradients checked against an independent fp32 reference; the backward
+ * accumulates with atomics, so it is checked numerically, not for bitwise replay).
+ * Given the forward's inputs, its lse, and dout = dLoss/dout, with
+ * p_j = exp(scale q.kv[idx_j] - lse), dp_j = dout . kv[idx_j, 0:d_v],
+ * D = sum_j p_j dp_j (= dout . out, summed here from the p_j dp_j, so the forward's
+ * rounded output is not needed) and ds_j = scale p_j (dp_j - D) for every valid slot
+ * j of a row and head:
+ *
+ *     dq[t,h,:]       = sum_j ds_j kv[idx_j, :]
+ *     dkv[idx_j, :]  += sum_(t,h) ds_j q[t,h,:]       (all d_qk channels)
+ *     dkv[idx_j, :d_v] += sum_(t,h) p_j dout[t,h,:]   (the value channels)
+ *
+ * -1 slots contribute nothing; a repeated index contributes once per slot; a row with
+ * no valid slot (lse = -inf) gets dq = 0.
+ * Inputs: q [T,H,d_qk], kv [S,d_qk], dout [T,H,d_v] (dtype), idx [T,topk], lse
+ *   [T,H] fp32 (the forward's). Outputs: dq [T,H,d_qk] (dtype); dkv
+ *   [S,d_qk] fp32, which the call zeroes and then accumulates into with
+ *   floating-point atomics, so dkv's low bits may differ from run to run (every
+ *   other output is deterministic).
+ * Sizes: d_qk in {512, 576}; d_v == 512; H in [1, 128]; topk >= 1 (at most 8192 for
+ *   SA_F32). Pointers 16-byte aligned (lse and idx: 4-byte).
+ */
+sa_status sa_sparse_mla_bwd(const void* q, const void* kv, const int32_t* idx, const void* dout,
+                            const float* lse, int dtype, int32_t T, int32_t S, int32_t H,
+                            int32_t d_qk, int32_t d_v, int32_t topk, float scale, void* dq,
+                            float* dkv, void* stream);
+
+/*
  * sa_block_sparse_gqa_fwd -- grouped-query attention over selected key blocks.
  *
  * [QSA] "Describe the solution you'd like": sparse GQA attention over the blocks

@@ -21,7 +21,8 @@ import torch
 
 __all__ = [
     "SAError", "SA_F32", "SA_BF16", "lib", "abi_version", "status_string",
-    "sa_indexer_workspace_bytes", "indexer_workspace", "sa_indexer_scores", "sa_topk_select", "sa_sparse_mla_fwd", "sa_block_sparse_gqa_fwd",
+    "sa_indexer_workspace_bytes", "indexer_workspace", "sa_indexer_scores", "sa_sparse_mla_bwd",
+    "sparse_mla_bwd", "sa_topk_select", "sa_sparse_mla_fwd", "sa_block_sparse_gqa_fwd",
     "indexer_scores", "indexer_topk", "topk_select", "sparse_mla", "block_sparse_gqa",
 ]
 
@@ -54,6 +55,9 @@ lib.sa_topk_select.argtypes = [_p, _p, _i64, _i32, _p, _i32, _i32, _i32, _i32, _
 lib.sa_sparse_mla_fwd.restype = ctypes.c_int
 lib.sa_sparse_mla_fwd.argtypes = [_p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _i32,
                                   _f32, _p, _p, _p]
+lib.sa_sparse_mla_bwd.restype = ctypes.c_int
+lib.sa_sparse_mla_bwd.argtypes = [_p, _p, _p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32,
+                                  _i32, _f32, _p, _p, _p]
 lib.sa_block_sparse_gqa_fwd.restype = ctypes.c_int
 lib.sa_block_sparse_gqa_fwd.argtypes = [_p, _p, _p, _p, ctypes.c_int, _i32, _p, _i32, _i32, _i32,
                                         _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p]
@@ -210,6 +214,27 @@ def sa_sparse_mla_fwd(q, kv, idx, scale, out, lse=None):
                                  _stream(dev)), "sa_sparse_mla_fwd")
 
 
+def sa_sparse_mla_bwd(q, kv, idx, dout, lse, scale, dq, dkv):
+    """sa_sparse_mla_bwd: gradients dq [T,H,d_qk] (q's dtype) and dkv [S,d_qk] (fp32,
+    overwritten) of sparse MLA from dout, given the forward's lse."""
+    dev = _device_of(q, "q")
+    if q.dim() != 3:
+        raise ValueError("q must be [T, H, d_qk]")
+    T, H, d_qk = q.shape
+    _need(q, "q", dev)
+    _need(kv, "kv", dev, q.dtype, (None, d_qk))
+    S = kv.shape[0]
+    _need(idx, "idx", dev, torch.int32, (T, None))
+    _need(dout, "dout", dev, q.dtype, (T, H, None))
+    d_v = dout.shape[2]
+    _need(lse, "lse", dev, torch.float32, (T, H))
+    _need(dq, "dq", dev, q.dtype, (T, H, d_qk))
+    _need(dkv, "dkv", dev, torch.float32, (S, d_qk))
+    _check(lib.sa_sparse_mla_bwd(_ptr(q), _ptr(kv), _ptr(idx), _ptr(dout), _ptr(lse),
+                                 _dtype_code(q), T, S, H, d_qk, d_v, idx.shape[1], float(scale),
+                                 _ptr(dq), _ptr(dkv), _stream(dev)), "sa_sparse_mla_bwd")
+
+
 def sa_block_sparse_gqa_fwd(q, k, v, blk, scale, out, lse=None, *, block_size, cu_seqlens=None,
                             max_seqlen=None):
     """sa_block_sparse_gqa_fwd: q [T,Hq,D], k/v [T,Hkv,D], blk [T,nblk] -> out [T,Hq,Dv]."""
@@ -287,6 +312,13 @@ def sparse_mla(q, kv, idx, scale, d_v=512, with_lse=True):
     lse = torch.empty((T, H), dtype=torch.float32, device=q.device) if with_lse else None
     sa_sparse_mla_fwd(q, kv, idx, scale, out, lse)
     return (out, lse) if with_lse else out
+
+
+def sparse_mla_bwd(q, kv, idx, dout, lse, scale):
+    dq = torch.empty_like(q)
+    dkv = torch.empty(kv.shape, dtype=torch.float32, device=q.device)
+    sa_sparse_mla_bwd(q, kv, idx, dout, lse, scale, dq, dkv)
+    return dq, dkv
 
 
 def block_sparse_gqa(q, k, v, blk, scale, *, block_size, cu_seqlens=None, max_seqlen=None,

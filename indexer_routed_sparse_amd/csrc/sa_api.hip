@@ -178,6 +178,26 @@ sa_status sa_sparse_mla_fwd(const void* q, const void* kv, const int32_t* idx, i
                                              scale, out, lse, reinterpret_cast<hipStream_t>(stream)));
 }
 
+sa_status sa_sparse_mla_bwd(const void* q, const void* kv, const int32_t* idx, const void* dout,
+                            const float* lse, int dtype, int32_t T, int32_t S, int32_t H,
+                            int32_t d_qk, int32_t d_v, int32_t topk, float scale, void* dq,
+                            float* dkv, void* stream) {
+  if (dtype != SA_F32 && dtype != SA_BF16) return SA_ERR_DTYPE;
+  if (T < 0 || S < 1 || H < 1 || topk < 1 || d_qk < 1 || d_v < 1) return SA_ERR_SHAPE;
+  if (d_qk != 512 && d_qk != 576) return SA_ERR_UNSUPPORTED;
+  if (d_v != 512) return SA_ERR_UNSUPPORTED;
+  if (H > 128) return SA_ERR_UNSUPPORTED;
+  if (dtype == SA_F32 && topk > 8192) return SA_ERR_UNSUPPORTED;   // per-slot terms staged in LDS
+  if (!dkv) return SA_ERR_NULL;
+  if (T > 0 && (!q || !kv || !idx || !dout || !lse || !dq)) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(dout) || !aligned16(dq) || !aligned16(dkv))
+    return SA_ERR_ALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (T > 0) SA_DEBUG_RETURN(debug_range(idx, (int64_t)T * topk, -1, S, s));
+  return launch_status(sa::launch_sparse_mla_bwd(q, kv, idx, dout, lse, dtype == SA_BF16, T, S, H, d_qk,
+                                                 d_v, topk, scale, dq, dkv, s));
+}
+
 sa_status sa_block_sparse_gqa_fwd(const void* q, const void* k, const void* v, const int32_t* blk,
                                   int dtype, int32_t T, const int32_t* cu_seqlens,
                                   int32_t num_seqs, int32_t max_seqlen, int32_t Hq, int32_t Hkv,

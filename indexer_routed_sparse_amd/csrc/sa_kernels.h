@@ -25,6 +25,11 @@ hipError_t launch_sparse_mla(const void* q, const void* kv, const int32_t* idx, 
                              int S, int H, int d_qk, int d_v, int topk, float scale, void* out,
                              float* lse, hipStream_t st);
 
+// sparse_mla_bwd.hip: zeroes dkv [S, d_qk] (fp32), then accumulates into it.
+hipError_t launch_sparse_mla_bwd(const void* q, const void* kv, const int32_t* idx, const void* dout,
+                                 const float* lse, bool bf16, int T, int S, int H, int d_qk, int d_v,
+                                 int topk, float scale, void* dq, float* dkv, hipStream_t st);
+
 // indexer.hip
 hipError_t launch_indexer_dense(const void* q, const void* k, const float* w, bool bf16, int T,
                                 const int32_t* cu, int nseq, int maxlen, int H_I, int D_I,

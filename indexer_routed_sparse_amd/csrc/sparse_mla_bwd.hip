@@ -1,0 +1,399 @@
+// Backward of absorbed-MLA sparse attention: dq and dkv from the upstream gradient of
+// the output ("Enable DSA CP/absorbed/THD paths with TileLang fused ops", file table:
+// sparse-MLA backward kernels; "Support NoPE shapes and unaligned top-k in TileLang
+// sparse MLA", section "Validation": gradients are checked numerically because the
+// backward accumulates with atomics).
+//
+// For query t, head h and valid slot j (latent row s = idx[t,j]):
+//   p_j = exp(scale q.kv_s - lse),  dp_j = dout . kv_s[0:d_v],  D = sum_j p_j dp_j,
+//   ds_j = scale p_j (dp_j - D);
+//   dq[t,h]  = sum_j ds_j kv_s;      dkv[s] += sum_h ds_j q[t,h]  (+ p_j dout[t,h] on [0, d_v)).
+// lse comes from the forward; the logits are recomputed, never stored. D (which
+// equals dout . out) is summed from the p_j dp_j themselves in a first pass over the
+// slots, so the ds_j of a row sum to zero as they must; taken from the forward's
+// bf16 output instead, D is off by up to 2^-9 sum |dout out|, and that error, carried
+// into every ds_j, dominates dq on rows whose few keys nearly cancel.
+//
+// bf16 kernel (gfx950): one workgroup per (token, group of 16 heads), four waves. The
+// slots of the token are split into 16-key sub-tiles and the waves take turns (wave w
+// takes sub-tiles w, w+4, ...), so the group's q and dout sit in LDS once and each
+// wave stages only its own 16 gathered rows:
+//   * S = Q K^T and dP = dout V^T (16 heads x 16 keys, 16x16x32 bf16 MFMA): q's A
+//     operands are held in registers, dout's are read from LDS, the key rows are the
+//     B operands as stored (row-major, one 16-byte read each);
+//   * P and dS in registers: lane (g, n) holds heads 4g..4g+3 of key n, which is the
+//     A-operand layout of dS^T and P^T for the 16x16x16 MFMAs of dkv, whose B operands
+//     (q and dout, heads x channels) come from transposing LDS reads; the 16x16 dkv
+//     block of a sub-tile is added into dkv (fp32) with atomics, one key row per
+//     lane-quad;
+//   * dq^T += K^T dS^T: K^T by transposing reads of the staged rows, dS^T through a
+//     512-byte LDS transpose; 36 accumulators of 16x16 (all of d_qk x 16 heads) per
+//     wave, summed over the four waves through LDS at the end;
+//   * a first pass over the same sub-tiles computes only S and dP, for D.
+// The next sub-tile's rows are loaded into registers while the current one is computed.
+// fp32 inputs use a plain kernel with the same arithmetic.
+#include <type_traits>
+
+#include "sa_common.h"
+#include "sa_kernels.h"
+
+namespace sa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWaves = 4;
+constexpr int kHG = 16;           // heads per workgroup
+constexpr int kSK = 16;           // keys per sub-tile
+
+typedef float floatx4v_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+
+SA_DEVICE floatx4v_t mfma16x32(bf16x8_t a, bf16x8_t b, floatx4v_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+SA_DEVICE floatx4v_t mfma16x16(short4_t a, short4_t b, floatx4v_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+SA_DEVICE short4_t pack4(float a, float b, float c, float d) {
+  const uint32_t lo = pack_bf16x2(a, b), hi = pack_bf16x2(c, d);
+  return __builtin_bit_cast(short4_t, make_uint2(lo, hi));
+}
+
+// Byte strides of the LDS rows: 16 bytes of padding per row keep the 16 rows read by
+// a 16-lane group on distinct banks.
+template <int DQK>
+constexpr int krow_bytes() { return DQK * 2 + 16; }
+constexpr int drow_bytes() { return 512 * 2 + 16; }
+
+template <int DQK>
+constexpr size_t bwd_lds_bytes() {
+  // q and dout of the group, one staged sub-tile per wave, one dS transpose per wave
+  const size_t a = (size_t)kHG * krow_bytes<DQK>() + (size_t)kHG * drow_bytes() +
+                   (size_t)kWaves * kSK * krow_bytes<DQK>() + (size_t)kWaves * kHG * kSK * 2 +
+                   (size_t)kWaves * kHG * 4;
+  // the end-of-kernel dq reduction reuses the staging area: half of d_qk per pass
+  const size_t r = (size_t)kWaves * kHG * (DQK / 2) * 4;
+  return a > r + (size_t)kHG * krow_bytes<DQK>() + (size_t)kHG * drow_bytes() ? a
+                                                                              : r + (size_t)kHG * krow_bytes<DQK>() + (size_t)kHG * drow_bytes();
+}
+
+template <int DQK>
+__global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, int H, int topk, float scale,
+    uint16_t* __restrict__ dq, float* __restrict__ dkv) {
+  constexpr int KRB = krow_bytes<DQK>();
+  constexpr int DRB = drow_bytes();
+  constexpr int NK = DQK / 32;            // 32-wide k-steps of S
+  constexpr int NV = 512 / 32;            // ... of dP
+  constexpr int NCB = DQK / 16;           // 16-channel blocks of dq^T and dkv
+  constexpr int NVB = 512 / 16;           // ... that carry the value part
+  constexpr int CPR = DQK * 2 / 16;       // 16-byte chunks per key row
+  constexpr int NLD = kSK * CPR / 64;     // row chunks per lane per sub-tile
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  char* q_l = lds;                                        // [16 heads][KRB]
+  char* d_l = q_l + kHG * KRB;                            // [16 heads][DRB] dout
+  char* k_l = d_l + kHG * DRB;                            // [waves][16 keys][KRB]
+  char* s_l = k_l + kWaves * kSK * KRB;                   // [waves][16 heads][16 keys] bf16
+  float* dD = reinterpret_cast<float*>(s_l + kWaves * kHG * kSK * 2);   // [waves][16] D partials
+
+  const int t = blockIdx.x;
+  const int h0 = blockIdx.y * kHG;
+  const int tid = threadIdx.x, w = tid >> 6, L = tid & 63;
+  const int g = L >> 4, n = L & 15;
+
+  // ---- q and dout of the 16 heads into LDS (zeros past H)
+  for (int c = tid; c < kHG * CPR; c += kWaves * 64) {
+    const int hh = c / CPR, p = c % CPR;
+    bf16x8_t v = bf16x8_t{};
+    if (h0 + hh < H) v = *reinterpret_cast<const bf16x8_t*>(q + ((int64_t)t * H + h0 + hh) * DQK + 8 * p);
+    *reinterpret_cast<bf16x8_t*>(q_l + hh * KRB + 16 * p) = v;
+  }
+  for (int c = tid; c < kHG * 64; c += kWaves * 64) {
+    const int hh = c >> 6, p = c & 63;
+    bf16x8_t v = bf16x8_t{};
+    if (h0 + hh < H) v = *reinterpret_cast<const bf16x8_t*>(dout + ((int64_t)t * H + h0 + hh) * 512 + 8 * p);
+    *reinterpret_cast<bf16x8_t*>(d_l + hh * DRB + 16 * p) = v;
+  }
+  __syncthreads();
+
+  // per-lane constants: heads 4g..4g+3 (rows of the 16x16 tiles)
+  float lse2[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hh = h0 + 4 * g + i;
+    const float l = hh < H ? lse[(int64_t)t * H + hh] : -__builtin_huge_valf();
+    lse2[i] = l * kLog2e;
+  }
+  // q's A operands (head n, k-step ks): channels 32 ks + 8 g .. + 8
+  bf16x8_t qa[NK];
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks) qa[ks] = *reinterpret_cast<const bf16x8_t*>(q_l + n * KRB + 64 * ks + 16 * g);
+
+  char* kt = k_l + w * kSK * KRB;
+  char* st = s_l + w * kHG * kSK * 2;
+  const int32_t* irow = idx + (int64_t)t * topk;
+  const int nsub = (topk + kSK - 1) / kSK;
+  const float sc2 = scale * kLog2e;
+
+  bf16x8_t nx[NLD];
+  auto load = [&](int sub) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < NLD; ++m) {
+      const int c = L + 64 * m, r = c / CPR, p = c % CPR;
+      const int j = sub * kSK + r;
+      int row = j < topk ? irow[j] : -1;
+      row = row < 0 ? 0 : row;                 // masked slot: any finite row
+      nx[m] = *reinterpret_cast<const bf16x8_t*>(kv + (int64_t)row * DQK + 8 * p);
+    }
+  };
+  // stages the sub-tile held in nx, then starts loading `next` (if any) into nx
+  auto stage = [&](int next) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < NLD; ++m) {
+      const int c = L + 64 * m, r = c / CPR, p = c % CPR;
+      *reinterpret_cast<bf16x8_t*>(kt + r * KRB + 16 * p) = nx[m];
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (next < nsub) load(next);
+  };
+  // S = Q K^T and dP = dout V^T of the staged sub-tile (heads 4g..4g+3 x key n per
+  // lane) and P; returns whether key n's slot is valid
+  auto scores = [&](int sub, float (&P)[4], floatx4v_t& dP) __attribute__((always_inline)) -> int {
+    const int jn = sub * kSK + n;                           // slot of key column n
+    const int rown = jn < topk ? irow[jn] : -1;
+    floatx4v_t S = floatx4v_t{};
+    dP = floatx4v_t{};
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+      const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(kt + n * KRB + 64 * ks + 16 * g);
+      S = mfma16x32(qa[ks], b, S);
+      if (ks < NV) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(d_l + n * DRB + 64 * ks + 16 * g);
+        dP = mfma16x32(a, b, dP);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = rown >= 0 && lse2[i] > -__builtin_huge_valf();
+      P[i] = ok ? __builtin_amdgcn_exp2f(S[i] * sc2 - lse2[i]) : 0.0f;
+    }
+    return rown;
+  };
+
+  // ---- pass 1: D = sum_j p_j dp_j per head
+  float dpart[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (w < nsub) load(w);
+#pragma unroll 1
+  for (int sub = w; sub < nsub; sub += kWaves) {
+    stage(sub + kWaves);
+    float P[4];
+    floatx4v_t dP;
+    scores(sub, P, dP);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dpart[i] = fmaf(P[i], dP[i], dpart[i]);
+    __builtin_amdgcn_wave_barrier();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {          // sum over the 16 keys (lanes n) of each head
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) dpart[i] += __shfl_xor(dpart[i], off, 64);
+    if (n == 0) dD[w * kHG + 4 * g + i] = dpart[i];
+  }
+  __syncthreads();
+  float Dh[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float d = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) d += dD[ww * kHG + 4 * g + i];
+    Dh[i] = d;
+  }
+
+  floatx4v_t acc[NCB];   // dq^T: channel block cb, rows 16 cb + 4 g .. +3, column head n
+#pragma unroll
+  for (int i = 0; i < NCB; ++i) acc[i] = floatx4v_t{};
+
+  // ---- pass 2: dS, dq, dkv
+  if (w < nsub) load(w);
+#pragma unroll 1
+  for (int sub = w; sub < nsub; sub += kWaves) {
+    stage(sub + kWaves);
+    float P[4], dS[4];
+    floatx4v_t dP;
+    scores(sub, P, dP);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dS[i] = P[i] * (dP[i] - Dh[i]) * scale;
+    // dS (heads x keys) transposed through LDS for the B operand of dq^T
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint16_t*>(st + ((4 * g + i) * kSK + n) * 2) = f2bf_bits(dS[i]);
+    const short4_t dsA = pack4(dS[0], dS[1], dS[2], dS[3]);   // dS^T: key n, heads 4g..
+    const short4_t pA = pack4(P[0], P[1], P[2], P[3]);        // P^T
+    __builtin_amdgcn_wave_barrier();
+    const short4_t dsB = *reinterpret_cast<const short4_t*>(st + (n * kSK + 4 * g) * 2);  // dS^T: keys 4g.., head n
+
+    // key rows of this lane's dkv quad: keys 4g..4g+3
+    int krow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = sub * kSK + 4 * g + i;
+      krow[i] = j < topk ? irow[j] : -1;
+    }
+    const bool any_valid = ballot(krow[0] >= 0 || krow[1] >= 0 || krow[2] >= 0 || krow[3] >= 0) != 0;
+
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      // transposing reads: rows 4g..4g+3 (keys or heads), channel 16 cb + n
+      const int toff = 16 * cb + 4 * (n & 3);
+      const short4_t kT = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (SA_LDS short4_t*)(kt + (4 * g + (n >> 2)) * KRB + toff * 2));
+      acc[cb] = mfma16x16(kT, dsB, acc[cb]);
+      if (any_valid) {
+        const short4_t qB = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (SA_LDS short4_t*)(q_l + (4 * g + (n >> 2)) * KRB + toff * 2));
+        floatx4v_t dk = mfma16x16(dsA, qB, floatx4v_t{});
+        if (cb < NVB) {
+          const short4_t gB = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (SA_LDS short4_t*)(d_l + (4 * g + (n >> 2)) * DRB + toff * 2));
+          dk = mfma16x16(pA, gB, dk);
+        }
+        // lane (g, n): keys 4g..4g+3, channel 16 cb + n
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (krow[i] >= 0) atomicAdd(dkv + (int64_t)krow[i] * DQK + 16 * cb + n, dk[i]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- sum the waves' dq^T partials through LDS, half of d_qk per pass
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(k_l);      // [waves][16 heads][DQK / 2]
+  constexpr int HALF = DQK / 2;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int cb = 0; cb < NCB / 2; ++cb) {
+      const int cbb = half * (NCB / 2) + cb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[(w * kHG + n) * HALF + 16 * cb + 4 * g + i] = acc[cbb][i];
+    }
+    __syncthreads();
+    for (int e = tid; e < kHG * HALF; e += kWaves * 64) {
+      const int hh = e / HALF, c = e % HALF;
+      float s = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) s += red[(ww * kHG + hh) * HALF + c];
+      if (h0 + hh < H) dq[((int64_t)t * H + h0 + hh) * DQK + half * HALF + c] = f2bf_bits(s);
+    }
+    __syncthreads();
+  }
+}
+
+// fp32: one workgroup per (token, head); plain arithmetic, dkv by atomics.
+constexpr int kNT = 256;
+
+__global__ __launch_bounds__(kNT) void sparse_mla_bwd_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ kv, const int32_t* __restrict__ idx,
+    const float* __restrict__ dout, const float* __restrict__ lse, int H, int d_qk, int d_v,
+    int topk, float scale, float* __restrict__ dq, float* __restrict__ dkv) {
+  extern __shared__ float sm[];        // [topk] p_j, then [topk] dp_j, then [kNT / 64] reduce slots
+  float* sdp = sm + topk;
+  float* red = sdp + topk;
+  const int t = blockIdx.x / H, h = blockIdx.x % H;
+  const int tid = threadIdx.x, w = tid >> 6, L = tid & 63;
+  const float* qr = q + ((int64_t)t * H + h) * d_qk;
+  const float* gr = dout + ((int64_t)t * H + h) * d_v;
+  const int32_t* ir = idx + (int64_t)t * topk;
+  const float l = lse[(int64_t)t * H + h];
+  // p_j = exp(scale q.kv - lse), dp_j = dout . v_j, and D = sum_j p_j dp_j
+  float part = 0.0f;
+  for (int j = tid; j < topk; j += kNT) {
+    const int r = ir[j];
+    float p = 0.0f, dp = 0.0f;
+    if (r >= 0 && l > -__builtin_huge_valf()) {
+      const float* kr = kv + (int64_t)r * d_qk;
+      float s = 0.0f;
+      for (int c = 0; c < d_qk; ++c) s = fmaf(qr[c], kr[c], s);
+      for (int c = 0; c < d_v; ++c) dp = fmaf(gr[c], kr[c], dp);
+      p = expf(s * scale - l);
+    }
+    sm[j] = p;
+    sdp[j] = dp;
+    part = fmaf(p, dp, part);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+  if (L == 0) red[w] = part;
+  __syncthreads();
+  float D = 0.0f;
+  for (int i = 0; i < kNT / 64; ++i) D += red[i];
+  // ds_j = scale p_j (dp_j - D); dkv by atomics; sm[j] becomes ds_j
+  for (int j = tid; j < topk; j += kNT) {
+    const int r = ir[j];
+    const float p = sm[j];
+    const float ds = scale * p * (sdp[j] - D);
+    if (r >= 0 && p != 0.0f) {
+      for (int c = 0; c < d_qk; ++c) atomicAdd(dkv + (int64_t)r * d_qk + c, ds * qr[c]);
+      for (int c = 0; c < d_v; ++c) atomicAdd(dkv + (int64_t)r * d_qk + c, p * gr[c]);
+    }
+    sm[j] = ds;
+  }
+  __syncthreads();
+  for (int c = tid; c < d_qk; c += kNT) {
+    float a = 0.0f;
+    for (int j = 0; j < topk; ++j) {
+      const int r = ir[j];
+      if (r >= 0) a = fmaf(sm[j], kv[(int64_t)r * d_qk + c], a);
+    }
+    dq[((int64_t)t * H + h) * d_qk + c] = a;
+  }
+}
+
+__global__ void zero_f32_kernel(float* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0.0f;
+}
+
+template <int DQK>
+hipError_t launch_bwd_bf16(const void* q, const void* kv, const int32_t* idx, const void* dout,
+                           const float* lse, int T, int H, int topk, float scale, void* dq,
+                           float* dkv, hipStream_t st) {
+  const size_t shm = bwd_lds_bytes<DQK>();
+  hipError_t e = hipFuncSetAttribute((const void*)sparse_mla_bwd_bf16_kernel<DQK>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((sparse_mla_bwd_bf16_kernel<DQK>), dim3(T, (H + kHG - 1) / kHG), dim3(kWaves * 64),
+                     shm, st, (const uint16_t*)q, (const uint16_t*)kv, idx, (const uint16_t*)dout,
+                     lse, H, topk, scale, (uint16_t*)dq, dkv);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sparse_mla_bwd(const void* q, const void* kv, const int32_t* idx, const void* dout,
+                                 const float* lse, bool bf16, int T, int S, int H, int d_qk, int d_v,
+                                 int topk, float scale, void* dq, float* dkv, hipStream_t st) {
+  const int64_t nkv = (int64_t)S * d_qk;
+  hipLaunchKernelGGL(zero_f32_kernel, dim3(1024), dim3(256), 0, st, dkv, nkv);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || T == 0) return e;
+  if (bf16) {
+    if (d_qk == 576) return launch_bwd_bf16<576>(q, kv, idx, dout, lse, T, H, topk, scale, dq, dkv, st);
+    return launch_bwd_bf16<512>(q, kv, idx, dout, lse, T, H, topk, scale, dq, dkv, st);
+  }
+  const size_t shm = (size_t)(2 * topk + kNT / 64) * sizeof(float);
+  e = hipFuncSetAttribute((const void*)sparse_mla_bwd_f32_kernel,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(sparse_mla_bwd_f32_kernel, dim3(T * H), dim3(kNT), shm, st, (const float*)q,
+                     (const float*)kv, idx, (const float*)dout, lse, H, d_qk, d_v, topk, scale,
+                     (float*)dq, dkv);
+  return hipGetLastError();
+}
+
+size_t sparse_mla_bwd_lds(int d_qk) { return d_qk == 576 ? bwd_lds_bytes<576>() : bwd_lds_bytes<512>(); }
+
+}  // namespace sa
