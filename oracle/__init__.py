@@ -444,19 +444,19 @@ def block_sparse_gqa_bwd(q, k, v, blk, dout, block_size: int, scale: float,
     dk = np.zeros(kh.shape)
     dv = np.zeros(vh.shape)
     for r, t in enumerate(rows):
-        keys = _gqa_keys(blkh[t], int(t), int(start[t]), block_size)
+        keys = _gqa_keys(blkh[t], int(t), int(start[t]), block_size)   # distinct keys
         if keys.size == 0:
             continue
-        for h in range(Hq):
-            gi = h // group
+        for gi in range(Hkv):
+            hs = slice(gi * group, (gi + 1) * group)     # the query heads reading kv head gi
             K = kh[keys, gi, :]
             V = vh[keys, gi, :]
-            l = scale * (K @ qh[t, h])
-            p = np.exp(l - l.max())
-            p /= p.sum()
-            dp = V @ gh[t, h]
-            dl = p * (dp - (p * dp).sum())
-            dq[r, h] = scale * (dl @ K)
-            np.add.at(dk[:, gi, :], keys, scale * np.outer(dl, qh[t, h]))
-            np.add.at(dv[:, gi, :], keys, np.outer(p, gh[t, h]))
+            l = scale * (K @ qh[t, hs].T)                # [n, group]
+            p = np.exp(l - l.max(axis=0))
+            p /= p.sum(axis=0)
+            dp = V @ gh[t, hs].T
+            dl = p * (dp - (p * dp).sum(axis=0))
+            dq[r, hs] = scale * (dl.T @ K)
+            dk[keys, gi, :] += scale * (dl @ qh[t, hs])   # keys are distinct within a row
+            dv[keys, gi, :] += p @ gh[t, hs]
     return dq, dk, dv
