@@ -302,6 +302,31 @@ sa_status sa_block_sparse_gqa_fwd(const void* q, const void* k, const void* v,
                                   int32_t Dv, int32_t block_size, int32_t nblk, float scale,
                                   void* out, float* lse, void* stream);
 
+/*
+ * sa_block_sparse_gqa_bwd -- gradients of sa_block_sparse_gqa_fwd.
+ *
+ * [QSA] "Is your feature request related to a problem?" and "Describe the solution
+ * you'd like" (sparse GQA attention forward and backward; numerical and gradient
+ * tests). Same key sets as the forward (the causal keys of the routed blocks, each
+ * block once). With p_s = exp(scale q[t,h].k[s,g] - lse[t,h]), dp_s = dout[t,h].v[s,g],
+ * D = sum_s p_s dp_s and ds_s = scale p_s (dp_s - D), for g = h / (Hq / Hkv):
+ *
+ *     dq[t,h]   = sum_s ds_s k[s,g]
+ *     dk[s,g]  += sum_(t,h) ds_s q[t,h]
+ *     dv[s,g]  += sum_(t,h) p_s dout[t,h]
+ *
+ * Inputs as the forward plus dout [T,Hq,Dv] (dtype) and the forward's lse [T,Hq] fp32.
+ * Outputs: dq [T,Hq,D] (dtype); dk [T,Hkv,D] and dv [T,Hkv,Dv] fp32, which the call
+ * zeroes and then accumulates into with floating-point atomics (their low bits may
+ * differ from run to run; dq is deterministic). Limits as the forward.
+ */
+sa_status sa_block_sparse_gqa_bwd(const void* q, const void* k, const void* v, const int32_t* blk,
+                                  const void* dout, const float* lse, int dtype, int32_t T,
+                                  const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                                  int32_t Hq, int32_t Hkv, int32_t D, int32_t Dv, int32_t block_size,
+                                  int32_t nblk, float scale, void* dq, float* dk, float* dv,
+                                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "SAError", "SA_F32", "SA_BF16", "lib", "abi_version", "status_string",
     "sa_indexer_workspace_bytes", "indexer_workspace", "sa_indexer_scores", "sa_sparse_mla_bwd",
-    "sparse_mla_bwd", "sa_topk_select", "sa_sparse_mla_fwd", "sa_block_sparse_gqa_fwd",
+    "sparse_mla_bwd", "sa_block_sparse_gqa_bwd", "block_sparse_gqa_bwd", "sa_topk_select", "sa_sparse_mla_fwd", "sa_block_sparse_gqa_fwd",
     "indexer_scores", "indexer_topk", "topk_select", "sparse_mla", "block_sparse_gqa",
 ]
 
@@ -58,6 +58,9 @@ lib.sa_sparse_mla_fwd.argtypes = [_p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i
 lib.sa_sparse_mla_bwd.restype = ctypes.c_int
 lib.sa_sparse_mla_bwd.argtypes = [_p, _p, _p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32,
                                   _i32, _f32, _p, _p, _p]
+lib.sa_block_sparse_gqa_bwd.restype = ctypes.c_int
+lib.sa_block_sparse_gqa_bwd.argtypes = [_p, _p, _p, _p, _p, _p, ctypes.c_int, _i32, _p, _i32, _i32, _i32,
+                                        _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p, _p]
 lib.sa_block_sparse_gqa_fwd.restype = ctypes.c_int
 lib.sa_block_sparse_gqa_fwd.argtypes = [_p, _p, _p, _p, ctypes.c_int, _i32, _p, _i32, _i32, _i32,
                                         _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p]
@@ -257,6 +260,31 @@ def sa_block_sparse_gqa_fwd(q, k, v, blk, scale, out, lse=None, *, block_size, c
                                        _stream(dev)), "sa_block_sparse_gqa_fwd")
 
 
+def sa_block_sparse_gqa_bwd(q, k, v, blk, dout, lse, scale, dq, dk, dv, *, block_size,
+                            cu_seqlens=None, max_seqlen=None):
+    """sa_block_sparse_gqa_bwd: dq [T,Hq,D] (q's dtype), dk/dv [T,Hkv,D] fp32 (overwritten)."""
+    dev = _device_of(q, "q")
+    if q.dim() != 3:
+        raise ValueError("q must be [T, Hq, D]")
+    T, Hq, D = q.shape
+    _need(q, "q", dev)
+    _need(k, "k", dev, q.dtype, (T, None, D))
+    Hkv = k.shape[1]
+    _need(v, "v", dev, q.dtype, (T, Hkv, None))
+    Dv = v.shape[2]
+    _need(blk, "blk", dev, torch.int32, (T, None))
+    _need(dout, "dout", dev, q.dtype, (T, Hq, Dv))
+    _need(lse, "lse", dev, torch.float32, (T, Hq))
+    _need(dq, "dq", dev, q.dtype, (T, Hq, D))
+    _need(dk, "dk", dev, torch.float32, (T, Hkv, D))
+    _need(dv, "dv", dev, torch.float32, (T, Hkv, Dv))
+    cu, nseq, maxlen = _layout(T, cu_seqlens, max_seqlen, dev)
+    _check(lib.sa_block_sparse_gqa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(blk), _ptr(dout), _ptr(lse),
+                                       _dtype_code(q), T, _ptr(cu), nseq, maxlen, Hq, Hkv, D, Dv,
+                                       int(block_size), blk.shape[1], float(scale), _ptr(dq), _ptr(dk),
+                                       _ptr(dv), _stream(dev)), "sa_block_sparse_gqa_bwd")
+
+
 # ------------------------------------------------------- allocating conveniences
 
 def indexer_scores(q_I, k_I, w, *, cu_seqlens=None, max_seqlen=None, block_size=1, ld=None):
@@ -319,6 +347,16 @@ def sparse_mla_bwd(q, kv, idx, dout, lse, scale):
     dkv = torch.empty(kv.shape, dtype=torch.float32, device=q.device)
     sa_sparse_mla_bwd(q, kv, idx, dout, lse, scale, dq, dkv)
     return dq, dkv
+
+
+def block_sparse_gqa_bwd(q, k, v, blk, dout, lse, scale, *, block_size, cu_seqlens=None,
+                         max_seqlen=None):
+    dq = torch.empty_like(q)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    sa_block_sparse_gqa_bwd(q, k, v, blk, dout, lse, scale, dq, dk, dv, block_size=block_size,
+                            cu_seqlens=cu_seqlens, max_seqlen=max_seqlen)
+    return dq, dk, dv
 
 
 def block_sparse_gqa(q, k, v, blk, scale, *, block_size, cu_seqlens=None, max_seqlen=None,

@@ -222,4 +222,32 @@ sa_status sa_block_sparse_gqa_fwd(const void* q, const void* k, const void* v, c
                                             reinterpret_cast<hipStream_t>(stream)));
 }
 
+sa_status sa_block_sparse_gqa_bwd(const void* q, const void* k, const void* v, const int32_t* blk,
+                                  const void* dout, const float* lse, int dtype, int32_t T,
+                                  const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                                  int32_t Hq, int32_t Hkv, int32_t D, int32_t Dv, int32_t block_size,
+                                  int32_t nblk, float scale, void* dq, float* dk, float* dv,
+                                  void* stream) {
+  if (dtype != SA_F32 && dtype != SA_BF16) return SA_ERR_DTYPE;
+  int32_t widest = 0;
+  sa_status st = check_layout(T, cu_seqlens, num_seqs, max_seqlen, &widest);
+  if (st != SA_OK) return st;
+  if (Hq < 1 || Hkv < 1 || D < 1 || Dv < 1 || block_size < 1 || nblk < 1) return SA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return SA_ERR_SHAPE;
+  if (Hq / Hkv > 16) return SA_ERR_UNSUPPORTED;
+  if (!((D == 128 && Dv == 128) || (D == 64 && Dv == 64))) return SA_ERR_UNSUPPORTED;
+  if (block_size % 16 != 0 || block_size > 128) return SA_ERR_UNSUPPORTED;
+  if (nblk > sa::block_gqa_max_route()) return SA_ERR_UNSUPPORTED;
+  if (!dk || !dv) return SA_ERR_NULL;
+  if (T > 0 && (!q || !k || !v || !blk || !dout || !lse || !dq)) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv))
+    return SA_ERR_ALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (T > 0) SA_DEBUG_RETURN(debug_offsets(cu_seqlens, num_seqs, T, max_seqlen, s));
+  return launch_status(sa::launch_block_gqa_bwd(q, k, v, blk, dtype == SA_BF16, T, cu_seqlens, num_seqs,
+                                                Hq, Hkv, D, block_size, nblk, scale, dout, lse, dq, dk,
+                                                dv, s));
+}
+
 }  // extern "C"

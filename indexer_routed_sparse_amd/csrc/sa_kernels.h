@@ -59,4 +59,10 @@ hipError_t debug_check_range(const int32_t* v, int64_t n, int32_t lo, int32_t hi
 hipError_t debug_check_offsets(const int32_t* cu, int nseq, int T, int maxlen, hipStream_t st,
                                bool* ok);
 
+// block_gqa_bwd.hip: zeroes dk and dv [T, Hkv, D] (fp32), then accumulates into them.
+hipError_t launch_block_gqa_bwd(const void* q, const void* k, const void* v, const int32_t* blk,
+                                bool bf16, int T, const int32_t* cu, int nseq, int Hq, int Hkv, int D,
+                                int block_size, int nblk, float scale, const void* dout,
+                                const float* lse, void* dq, float* dk, float* dv, hipStream_t st);
+
 }  // namespace sa
