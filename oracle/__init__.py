@@ -460,3 +460,107 @@ def block_sparse_gqa_bwd(q, k, v, blk, dout, block_size: int, scale: float,
             dk[keys, gi, :] += scale * (dl @ qh[t, hs])   # keys are distinct within a row
             dv[keys, gi, :] += p @ gh[t, hs]
     return dq, dk, dv
+
+
+# ------------------------------------- sparse KL indexer loss and indexer backward
+#
+# "Add trainable QSA sparse attention with a TileLang backend", sections "Is your
+# feature request related to a problem?" and "Describe the solution you'd like"
+# (sparse KL supervision of the indexer, a stage-2 teacher/KL loss), and "Enable DSA
+# CP/absorbed/THD paths with TileLang fused ops" (streaming sparse-KL for the indexer
+# loss; fused indexer backward). The pages do not write the loss out; the reading
+# taken here: over the slots a row selected, the teacher is the sparse attention's
+# probability of each slot averaged over the attention heads (no gradient flows into
+# it), the student is the softmax of the indexer scores of the same slots, and the
+# row's loss is KL(teacher || student). Gradients reach the indexer's q_I, k_I and w.
+
+def attn_teacher_row(q_t, kv, idx_t, scale: float) -> np.ndarray:
+    """Head-averaged sparse attention probability of every slot of one row, float64.
+
+    p[j] = (1/H) sum_h softmax_h(scale q[h] . kv[idx_j])_j over the valid slots (the
+    probabilities ``sparse_mla_row`` weights the values with); 0 on -1 slots.
+    """
+    q = _f64(q_t)
+    idx = _i64(idx_t)
+    p = np.zeros(idx.size)
+    sel = np.nonzero(idx >= 0)[0]
+    if sel.size == 0:
+        return p
+    rows = _f64(kv[idx[sel].tolist()] if hasattr(kv, "detach") else kv[idx[sel]])
+    logits = scale * (q @ rows.T)                      # [H, n]
+    e = np.exp(logits - logits.max(axis=1, keepdims=True))
+    e /= e.sum(axis=1, keepdims=True)
+    p[sel] = e.mean(axis=0)
+    return p
+
+
+def attn_teacher(q, kv, idx, scale: float, rows=None) -> np.ndarray:
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    kvh = _f64(kv)
+    idxh = _i64(idx)
+    return np.stack([attn_teacher_row(q[t], kvh, idxh[t], scale) for t in rows])
+
+
+def indexer_kl_row(q_I_t, k_I, w_t, idx_t, teacher_t):
+    """Sparse KL loss of one row and its gradients, float64.
+
+    Scores of the valid slots I_j = sum_h w_h max(z_hj, 0) with z_hj = q_I[h] . k_I[idx_j]
+    (the indexer definition, unrounded); student s = softmax(I) over them; loss =
+    sum_j p_j (log p_j - log s_j) with 0 log 0 = 0 (p = teacher_t). With dI_j = s_j - p_j
+    (d loss / d I_j, as sum_j p_j = 1):
+      dw_h  = sum_j dI_j max(z_hj, 0)
+      dq_h  = sum_j dI_j w_h [z_hj > 0] k_I[idx_j]
+      dk_j  = sum_h dI_j w_h [z_hj > 0] q_I[h]        (a slot's gradient row)
+    Returns loss, dI [k] (0 on -1 slots), dq [H_I, D_I], dw [H_I], dk_slots [k, D_I].
+    """
+    q = _f64(q_I_t)
+    w = _f64(w_t)
+    idx = _i64(idx_t)
+    p_all = _f64(teacher_t)
+    H, D = q.shape
+    dI = np.zeros(idx.size)
+    dk = np.zeros((idx.size, D))
+    sel = np.nonzero(idx >= 0)[0]
+    if sel.size == 0:
+        return 0.0, dI, np.zeros((H, D)), np.zeros(H), dk
+    K = _f64(k_I[idx[sel].tolist()] if hasattr(k_I, "detach") else k_I[idx[sel]])
+    z = q @ K.T                                        # [H, n]
+    I = np.maximum(z, 0.0).T @ w                       # [n]
+    ls = I - I.max()
+    ls = ls - np.log(np.exp(ls).sum())                 # log student
+    p = p_all[sel]
+    nz = p > 0
+    loss = float((p[nz] * (np.log(p[nz]) - ls[nz])).sum())
+    d = np.exp(ls) - p
+    dI[sel] = d
+    on = (z > 0).astype(np.float64)                    # [H, n]
+    dw = np.maximum(z, 0.0) @ d
+    dz = on * w[:, None] * d[None, :]                  # [H, n]
+    dq = dz @ K
+    dk[sel] = dz.T @ q
+    return loss, dI, dq, dw, dk
+
+
+def indexer_kl(q_I, k_I, w, idx, teacher, grad=None, rows=None):
+    """``indexer_kl_row`` over rows; the gradients are those of sum_t grad[t] * loss[t]
+    (grad = 1 when None). Returns loss [len(rows)], dI, dq_I, dw, and dk_I [S, D_I]
+    (the slot gradients scattered onto their key rows)."""
+    rows = np.arange(q_I.shape[0]) if rows is None else np.asarray(rows)
+    kh = _f64(k_I)
+    idxh = _i64(idx)
+    th = _f64(teacher)
+    g = np.ones(q_I.shape[0]) if grad is None else _f64(grad)
+    H, D = q_I.shape[1], q_I.shape[2]
+    k = idxh.shape[1]
+    loss = np.zeros(len(rows))
+    dI = np.zeros((len(rows), k))
+    dq = np.zeros((len(rows), H, D))
+    dw = np.zeros((len(rows), H))
+    dk = np.zeros(kh.shape)
+    for r, t in enumerate(rows):
+        l, a, b, c, e = indexer_kl_row(q_I[t], kh, w[t], idxh[t], th[t])
+        loss[r] = l
+        dI[r], dq[r], dw[r] = g[t] * a, g[t] * b, g[t] * c
+        ok = idxh[t] >= 0
+        np.add.at(dk, idxh[t][ok], g[t] * e[ok])
+    return loss, dI, dq, dw, dk

@@ -661,3 +661,88 @@ def test_gqa_bwd_matches_library_attention_autograd_thd():
     np.testing.assert_allclose(dq, qt.grad.numpy(), rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(dk, kt.grad.numpy(), rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(dv, vt.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+# ------------------------------------------- sparse KL indexer loss and backward
+
+def test_attn_teacher_is_head_mean_of_attention_weights():
+    """The teacher is the head mean of the probabilities the forward oracle weights
+    the values with: sum_j p_j v_j equals the head mean of sparse_mla's outputs, the
+    teacher sums to one over valid slots, and matches torch.softmax of masked logits."""
+    rng = np.random.default_rng(60)
+    T, S, H, d_qk, d_v, k = 6, 40, 5, 24, 16, 9
+    q = rng.standard_normal((T, H, d_qk))
+    kv = rng.standard_normal((S, d_qk))
+    idx = np.stack([rng.permutation(S)[:k] for _ in range(T)])
+    idx[2, 4:] = -1
+    idx[3] = -1
+    p = oracle.attn_teacher(q, kv, idx, 0.3)
+    out, _ = oracle.sparse_mla(q, kv, idx, 0.3, d_v)
+    for t in range(T):
+        ok = idx[t] >= 0
+        if not ok.any():
+            assert np.all(p[t] == 0)
+            continue
+        np.testing.assert_allclose(p[t][ok].sum(), 1.0, rtol=1e-13)
+        assert np.all(p[t][~ok] == 0)
+        np.testing.assert_allclose(p[t][ok] @ kv[idx[t][ok], :d_v], out[t].mean(0), atol=1e-12)
+        lg = torch.from_numpy(0.3 * q[t] @ kv[idx[t][ok]].T)
+        np.testing.assert_allclose(p[t][ok], torch.softmax(lg, -1).mean(0).numpy(), rtol=1e-12)
+
+
+def test_indexer_kl_matches_autograd_through_library_kl():
+    """Loss and gradients against torch autograd through the indexer score written
+    with torch ops and the library's kl_div, with -1 slots, a zero-probability teacher
+    slot, a repeated key, ReLU zeros from integer inputs, and per-row loss weights."""
+    rng = np.random.default_rng(61)
+    T, S, H, D, k = 5, 30, 4, 6, 8
+    q = rng.integers(-2, 3, (T, H, D)).astype(np.float64)
+    kk = rng.integers(-2, 3, (S, D)).astype(np.float64)
+    w = rng.standard_normal((T, H))
+    idx = np.stack([rng.permutation(S)[:k] for _ in range(T)])
+    idx[1, 6:] = -1
+    idx[2, :2] = [7, 7]                               # a key in two slots
+    teacher = rng.random((T, k)) * (idx >= 0)
+    teacher[0, 3] = 0.0                               # zero teacher probability
+    teacher /= teacher.sum(1, keepdims=True)
+    grad = rng.random(T) + 0.5
+    loss, dI, dq, dw, dk = oracle.indexer_kl(q, kk, w, idx, teacher, grad)
+    qt = torch.from_numpy(q).requires_grad_()
+    kt = torch.from_numpy(kk).requires_grad_()
+    wt = torch.from_numpy(w).requires_grad_()
+    total = qt.new_zeros(())
+    for t in range(T):
+        ok = np.nonzero(idx[t] >= 0)[0]
+        K = kt[torch.as_tensor(idx[t][ok])]
+        I = (torch.relu(qt[t] @ K.T) * wt[t][:, None]).sum(0)
+        pt = torch.from_numpy(teacher[t][ok])
+        lt = torch.nn.functional.kl_div(torch.log_softmax(I, -1), pt, reduction="sum")
+        np.testing.assert_allclose(loss[t], lt.item(), rtol=1e-12, atol=1e-14)
+        total = total + grad[t] * lt
+    total.backward()
+    np.testing.assert_allclose(dq, qt.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dw, wt.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dk, kt.grad.numpy(), rtol=1e-11, atol=1e-12)
+    # dI = grad * (student - teacher) sums to zero per row
+    np.testing.assert_allclose(dI.sum(1), 0.0, atol=1e-13)
+
+
+def test_indexer_kl_zero_when_student_equals_teacher():
+    """KL is zero, with zero gradients, when the teacher is the student's own
+    distribution; and positive otherwise."""
+    rng = np.random.default_rng(62)
+    T, S, H, D, k = 3, 20, 3, 5, 6
+    q = rng.standard_normal((T, H, D))
+    kk = rng.standard_normal((S, D))
+    w = rng.random((T, H))
+    idx = np.stack([rng.permutation(S)[:k] for _ in range(T)])
+    z = np.einsum("thd,tkd->thk", q, kk[idx])          # exact float64 scores of the slots
+    sc = (np.maximum(z, 0) * w[:, :, None]).sum(1)
+    st = np.exp(sc - sc.max(1, keepdims=True))
+    st /= st.sum(1, keepdims=True)
+    loss, dI, dq, dw, dk = oracle.indexer_kl(q, kk, w, idx, st)
+    np.testing.assert_allclose(loss, 0.0, atol=1e-14)
+    np.testing.assert_allclose(dI, 0.0, atol=1e-14)
+    flat = np.full_like(st, 1.0 / k)
+    l2, *_ = oracle.indexer_kl(q, kk, w, idx, flat)
+    assert np.all(l2 > 0)
