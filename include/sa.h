@@ -276,6 +276,55 @@ sa_status sa_sparse_mla_bwd(const void* q, const void* kv, const int32_t* idx, c
                             float* dkv, void* stream);
 
 /*
+ * sa_attn_teacher -- teacher distribution of the sparse KL indexer loss.
+ *
+ * [QSA] "Is your feature request related to a problem?" and "Describe the solution
+ * you'd like" (sparse KL supervision of the indexer; a stage-2 teacher/KL loss); [DSA]
+ * "What does this PR do ?" (streaming sparse-KL for the indexer loss). Reading of the
+ * pages: the teacher of row t is the sparse attention's probability of each of its
+ * slots, averaged over the H attention heads:
+ *
+ *     teacher[t,j] = (1/H) sum_h exp(scale q[t,h,:] . kv[idx[t,j],:] - lse[t,h])
+ *
+ * and 0 on -1 slots (so a row's valid entries sum to 1). q, kv, idx, scale and lse are
+ * those of sa_sparse_mla_fwd (lse its output). teacher [T,topk] fp32 is overwritten;
+ * it is accumulated with floating-point atomics over groups of 16 heads, so its low
+ * bits may vary from run to run. Limits as sa_sparse_mla_fwd's d_qk and H.
+ */
+sa_status sa_attn_teacher(const void* q, const void* kv, const int32_t* idx, const float* lse,
+                          int dtype, int32_t T, int32_t S, int32_t H, int32_t d_qk, int32_t topk,
+                          float scale, float* teacher, void* stream);
+
+/*
+ * sa_indexer_kl_bwd -- sparse KL loss of the indexer and its backward.
+ *
+ * [QSA] (as above); [DSA] file table (fused indexer backward kernel). Over the valid
+ * slots j of row t (key rows s_j = idx[t,j], global rows of k_I), with the indexer
+ * scores I_j = sum_h w[t,h] max(z_hj, 0), z_hj = q_I[t,h,:] . k_I[s_j,:] (the
+ * definition of sa_indexer_scores), the student softmax_j(I) and the given teacher p:
+ *
+ *     loss[t]    = sum_j p_j (log p_j - log softmax(I)_j)       (0 log 0 = 0)
+ *     dI_j       = g_t (softmax(I)_j - p_j)
+ *     dw[t,h]    = sum_j dI_j max(z_hj, 0)
+ *     dq_I[t,h]  = sum_j dI_j w[t,h] [z_hj > 0] k_I[s_j]
+ *     dk_I[s_j] += sum_h dI_j w[t,h] [z_hj > 0] q_I[t,h]
+ *
+ * i.e. the gradients of sum_t g_t loss[t], g = grad [T] fp32 (NULL: every g_t = 1). A
+ * row without a valid slot has loss 0 and zero gradients. Only the topk selected
+ * scores of a row are formed; no [T, T] matrix.
+ * Inputs: q_I [T,H_I,D_I], k_I [S,D_I] (dtype), w [T,H_I] fp32, idx [T,topk] int32 in
+ *   [-1, S), teacher [T,topk] fp32 (e.g. from sa_attn_teacher), grad [T] or NULL.
+ * Outputs: loss [T] fp32, dq_I [T,H_I,D_I] (dtype), dw [T,H_I] fp32, dk_I [S,D_I] fp32
+ *   (zeroed by the call, then accumulated with floating-point atomics: its low bits
+ *   may vary from run to run).
+ * Sizes: D_I in {64, 128}; SA_BF16 needs H_I in {16, 32, 64}; topk <= 4096.
+ */
+sa_status sa_indexer_kl_bwd(const void* q_I, const void* k_I, const float* w, const int32_t* idx,
+                            const float* teacher, const float* grad, int dtype, int32_t T, int32_t S,
+                            int32_t H_I, int32_t D_I, int32_t topk, float* loss, void* dq_I,
+                            float* dw, float* dk_I, void* stream);
+
+/*
  * sa_block_sparse_gqa_fwd -- grouped-query attention over selected key blocks.
  *
  * [QSA] "Describe the solution you'd like": sparse GQA attention over the blocks

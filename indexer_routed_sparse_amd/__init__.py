@@ -22,7 +22,8 @@ import torch
 __all__ = [
     "SAError", "SA_F32", "SA_BF16", "lib", "abi_version", "status_string",
     "sa_indexer_workspace_bytes", "indexer_workspace", "sa_indexer_scores", "sa_sparse_mla_bwd",
-    "sparse_mla_bwd", "sa_block_sparse_gqa_bwd", "block_sparse_gqa_bwd", "sa_topk_select", "sa_sparse_mla_fwd", "sa_block_sparse_gqa_fwd",
+    "sparse_mla_bwd", "sa_block_sparse_gqa_bwd", "block_sparse_gqa_bwd", "sa_attn_teacher",
+    "attn_teacher", "sa_indexer_kl_bwd", "indexer_kl_bwd", "sa_topk_select", "sa_sparse_mla_fwd", "sa_block_sparse_gqa_fwd",
     "indexer_scores", "indexer_topk", "topk_select", "sparse_mla", "block_sparse_gqa",
 ]
 
@@ -61,6 +62,11 @@ lib.sa_sparse_mla_bwd.argtypes = [_p, _p, _p, _p, _p, ctypes.c_int, _i32, _i32, 
 lib.sa_block_sparse_gqa_bwd.restype = ctypes.c_int
 lib.sa_block_sparse_gqa_bwd.argtypes = [_p, _p, _p, _p, _p, _p, ctypes.c_int, _i32, _p, _i32, _i32, _i32,
                                         _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p, _p]
+lib.sa_attn_teacher.restype = ctypes.c_int
+lib.sa_attn_teacher.argtypes = [_p, _p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _f32, _p, _p]
+lib.sa_indexer_kl_bwd.restype = ctypes.c_int
+lib.sa_indexer_kl_bwd.argtypes = [_p, _p, _p, _p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32,
+                                  _p, _p, _p, _p, _p]
 lib.sa_block_sparse_gqa_fwd.restype = ctypes.c_int
 lib.sa_block_sparse_gqa_fwd.argtypes = [_p, _p, _p, _p, ctypes.c_int, _i32, _p, _i32, _i32, _i32,
                                         _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p]
@@ -285,6 +291,44 @@ def sa_block_sparse_gqa_bwd(q, k, v, blk, dout, lse, scale, dq, dk, dv, *, block
                                        _ptr(dv), _stream(dev)), "sa_block_sparse_gqa_bwd")
 
 
+def sa_attn_teacher(q, kv, idx, lse, scale, teacher):
+    """sa_attn_teacher: head-mean attention probability of every slot -> teacher [T,k] fp32."""
+    dev = _device_of(q, "q")
+    if q.dim() != 3:
+        raise ValueError("q must be [T, H, d_qk]")
+    T, H, d_qk = q.shape
+    _need(q, "q", dev)
+    _need(kv, "kv", dev, q.dtype, (None, d_qk))
+    _need(idx, "idx", dev, torch.int32, (T, None))
+    _need(lse, "lse", dev, torch.float32, (T, H))
+    _need(teacher, "teacher", dev, torch.float32, (T, idx.shape[1]))
+    _check(lib.sa_attn_teacher(_ptr(q), _ptr(kv), _ptr(idx), _ptr(lse), _dtype_code(q), T, kv.shape[0], H,
+                               d_qk, idx.shape[1], float(scale), _ptr(teacher), _stream(dev)),
+           "sa_attn_teacher")
+
+
+def sa_indexer_kl_bwd(q_I, k_I, w, idx, teacher, loss, dq_I, dw, dk_I, grad=None):
+    """sa_indexer_kl_bwd: sparse KL loss [T] and its gradients dq_I, dw, dk_I (fp32, overwritten)."""
+    dev = _device_of(q_I, "q_I")
+    if q_I.dim() != 3:
+        raise ValueError("q_I must be [T, H_I, D_I]")
+    T, H_I, D_I = q_I.shape
+    _need(q_I, "q_I", dev)
+    _need(k_I, "k_I", dev, q_I.dtype, (None, D_I))
+    _need(w, "w", dev, torch.float32, (T, H_I))
+    _need(idx, "idx", dev, torch.int32, (T, None))
+    k = idx.shape[1]
+    _need(teacher, "teacher", dev, torch.float32, (T, k))
+    _need(grad, "grad", dev, torch.float32, (T,), optional=True)
+    _need(loss, "loss", dev, torch.float32, (T,))
+    _need(dq_I, "dq_I", dev, q_I.dtype, (T, H_I, D_I))
+    _need(dw, "dw", dev, torch.float32, (T, H_I))
+    _need(dk_I, "dk_I", dev, torch.float32, tuple(k_I.shape))
+    _check(lib.sa_indexer_kl_bwd(_ptr(q_I), _ptr(k_I), _ptr(w), _ptr(idx), _ptr(teacher), _ptr(grad),
+                                 _dtype_code(q_I), T, k_I.shape[0], H_I, D_I, k, _ptr(loss), _ptr(dq_I),
+                                 _ptr(dw), _ptr(dk_I), _stream(dev)), "sa_indexer_kl_bwd")
+
+
 # ------------------------------------------------------- allocating conveniences
 
 def indexer_scores(q_I, k_I, w, *, cu_seqlens=None, max_seqlen=None, block_size=1, ld=None):
@@ -347,6 +391,22 @@ def sparse_mla_bwd(q, kv, idx, dout, lse, scale):
     dkv = torch.empty(kv.shape, dtype=torch.float32, device=q.device)
     sa_sparse_mla_bwd(q, kv, idx, dout, lse, scale, dq, dkv)
     return dq, dkv
+
+
+def attn_teacher(q, kv, idx, lse, scale):
+    teacher = torch.empty(idx.shape, dtype=torch.float32, device=q.device)
+    sa_attn_teacher(q, kv, idx, lse, scale, teacher)
+    return teacher
+
+
+def indexer_kl_bwd(q_I, k_I, w, idx, teacher, grad=None):
+    T = q_I.shape[0]
+    loss = torch.empty(T, dtype=torch.float32, device=q_I.device)
+    dq_I = torch.empty_like(q_I)
+    dw = torch.empty_like(w)
+    dk_I = torch.empty(k_I.shape, dtype=torch.float32, device=q_I.device)
+    sa_indexer_kl_bwd(q_I, k_I, w, idx, teacher, loss, dq_I, dw, dk_I, grad=grad)
+    return loss, dq_I, dw, dk_I
 
 
 def block_sparse_gqa_bwd(q, k, v, blk, dout, lse, scale, *, block_size, cu_seqlens=None,

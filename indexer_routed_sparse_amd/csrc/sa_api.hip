@@ -222,6 +222,40 @@ sa_status sa_block_sparse_gqa_fwd(const void* q, const void* k, const void* v, c
                                             reinterpret_cast<hipStream_t>(stream)));
 }
 
+sa_status sa_attn_teacher(const void* q, const void* kv, const int32_t* idx, const float* lse,
+                          int dtype, int32_t T, int32_t S, int32_t H, int32_t d_qk, int32_t topk,
+                          float scale, float* teacher, void* stream) {
+  if (dtype != SA_F32 && dtype != SA_BF16) return SA_ERR_DTYPE;
+  if (T < 0 || S < 1 || H < 1 || topk < 1 || d_qk < 1) return SA_ERR_SHAPE;
+  if (d_qk != 512 && d_qk != 576) return SA_ERR_UNSUPPORTED;
+  if (H > 128) return SA_ERR_UNSUPPORTED;
+  if (T == 0) return SA_OK;
+  if (!q || !kv || !idx || !lse || !teacher) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(kv)) return SA_ERR_ALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  SA_DEBUG_RETURN(debug_range(idx, (int64_t)T * topk, -1, S, s));
+  return launch_status(sa::launch_attn_teacher(q, kv, idx, lse, dtype == SA_BF16, T, H, d_qk, topk, scale,
+                                               teacher, s));
+}
+
+sa_status sa_indexer_kl_bwd(const void* q_I, const void* k_I, const float* w, const int32_t* idx,
+                            const float* teacher, const float* grad, int dtype, int32_t T, int32_t S,
+                            int32_t H_I, int32_t D_I, int32_t topk, float* loss, void* dq_I,
+                            float* dw, float* dk_I, void* stream) {
+  if (dtype != SA_F32 && dtype != SA_BF16) return SA_ERR_DTYPE;
+  if (T < 0 || S < 1 || H_I < 1 || D_I < 1 || topk < 1) return SA_ERR_SHAPE;
+  if (dtype == SA_BF16 && H_I != 16 && H_I != 32 && H_I != 64) return SA_ERR_UNSUPPORTED;
+  if (D_I != 64 && D_I != 128) return SA_ERR_UNSUPPORTED;
+  if (topk > sa::indexer_kl_max_topk()) return SA_ERR_UNSUPPORTED;
+  if (!dk_I) return SA_ERR_NULL;
+  if (T > 0 && (!q_I || !k_I || !w || !idx || !teacher || !loss || !dq_I || !dw)) return SA_ERR_NULL;
+  if (!aligned16(q_I) || !aligned16(k_I) || !aligned16(dq_I)) return SA_ERR_ALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (T > 0) SA_DEBUG_RETURN(debug_range(idx, (int64_t)T * topk, -1, S, s));
+  return launch_status(sa::launch_indexer_kl(q_I, k_I, w, idx, teacher, grad, dtype == SA_BF16, T, S, H_I,
+                                             D_I, topk, loss, dq_I, dw, dk_I, s));
+}
+
 sa_status sa_block_sparse_gqa_bwd(const void* q, const void* k, const void* v, const int32_t* blk,
                                   const void* dout, const float* lse, int dtype, int32_t T,
                                   const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,

@@ -59,6 +59,18 @@ hipError_t debug_check_range(const int32_t* v, int64_t n, int32_t lo, int32_t hi
 hipError_t debug_check_offsets(const int32_t* cu, int nseq, int T, int maxlen, hipStream_t st,
                                bool* ok);
 
+// sparse_mla_bwd.hip: teacher [T, topk] of the sparse KL loss (zeroed, then accumulated).
+hipError_t launch_attn_teacher(const void* q, const void* kv, const int32_t* idx, const float* lse,
+                               bool bf16, int T, int H, int d_qk, int topk, float scale, float* teacher,
+                               hipStream_t st);
+
+// indexer_kl.hip: sparse KL loss of the indexer and its gradients (dk zeroed first).
+int indexer_kl_max_topk();
+hipError_t launch_indexer_kl(const void* qI, const void* kI, const float* wI, const int32_t* idx,
+                             const float* teacher, const float* grad, bool bf16, int T, int S, int H_I,
+                             int D_I, int topk, float* loss, void* dq, float* dw, float* dk,
+                             hipStream_t st);
+
 // block_gqa_bwd.hip: zeroes dk and dv [T, Hkv, D] (fp32), then accumulates into them.
 hipError_t launch_block_gqa_bwd(const void* q, const void* k, const void* v, const int32_t* blk,
                                 bool bf16, int T, const int32_t* cu, int nseq, int Hq, int Hkv, int D,

@@ -352,6 +352,101 @@ __global__ __launch_bounds__(kNT) void sparse_mla_bwd_f32_kernel(
   }
 }
 
+// Teacher of the sparse KL indexer loss: the head mean of the attention probability of
+// every slot, p[t,j] = (1/H) sum_h exp(scale q[t,h].kv[idx_j] - lse[t,h]); 0 on -1 slots.
+// Same layout as the backward's first pass (one workgroup per token and 16-head group,
+// four waves taking turns over 16-key sub-tiles); each group adds its 16 heads' share
+// to p (fp32, zeroed first) with one atomic per slot.
+template <int DQK>
+__global__ __launch_bounds__(kWaves * 64) void attn_teacher_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
+    const float* __restrict__ lse, int H, int topk, float scale, float* __restrict__ teacher) {
+  constexpr int KRB = krow_bytes<DQK>();
+  constexpr int NK = DQK / 32;
+  constexpr int CPR = DQK * 2 / 16;
+  constexpr int NLD = kSK * CPR / 64;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  char* q_l = lds;                                        // [16 heads][KRB]
+  char* k_l = q_l + kHG * KRB;                            // [waves][16 keys][KRB]
+  const int t = blockIdx.x;
+  const int h0 = blockIdx.y * kHG;
+  const int tid = threadIdx.x, w = tid >> 6, L = tid & 63;
+  const int g = L >> 4, n = L & 15;
+  for (int c = tid; c < kHG * CPR; c += kWaves * 64) {
+    const int hh = c / CPR, p = c % CPR;
+    bf16x8_t v = bf16x8_t{};
+    if (h0 + hh < H) v = *reinterpret_cast<const bf16x8_t*>(q + ((int64_t)t * H + h0 + hh) * DQK + 8 * p);
+    *reinterpret_cast<bf16x8_t*>(q_l + hh * KRB + 16 * p) = v;
+  }
+  __syncthreads();
+  float lse2[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hh = h0 + 4 * g + i;
+    lse2[i] = (hh < H ? lse[(int64_t)t * H + hh] : -__builtin_huge_valf()) * kLog2e;
+  }
+  bf16x8_t qa[NK];
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks) qa[ks] = *reinterpret_cast<const bf16x8_t*>(q_l + n * KRB + 64 * ks + 16 * g);
+  char* kt = k_l + w * kSK * KRB;
+  const int32_t* irow = idx + (int64_t)t * topk;
+  const int nsub = (topk + kSK - 1) / kSK;
+  const float sc2 = scale * kLog2e, invH = 1.0f / (float)H;
+  bf16x8_t nx[NLD];
+  auto load = [&](int sub) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < NLD; ++m) {
+      const int c = L + 64 * m, r = c / CPR, p = c % CPR;
+      const int j = sub * kSK + r;
+      int row = j < topk ? irow[j] : -1;
+      row = row < 0 ? 0 : row;
+      nx[m] = *reinterpret_cast<const bf16x8_t*>(kv + (int64_t)row * DQK + 8 * p);
+    }
+  };
+  if (w < nsub) load(w);
+#pragma unroll 1
+  for (int sub = w; sub < nsub; sub += kWaves) {
+#pragma unroll
+    for (int m = 0; m < NLD; ++m) {
+      const int c = L + 64 * m, r = c / CPR, p = c % CPR;
+      *reinterpret_cast<bf16x8_t*>(kt + r * KRB + 16 * p) = nx[m];
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (sub + kWaves < nsub) load(sub + kWaves);
+    const int jn = sub * kSK + n;
+    const int rown = jn < topk ? irow[jn] : -1;
+    floatx4v_t S = floatx4v_t{};
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks)
+      S = mfma16x32(qa[ks], *reinterpret_cast<const bf16x8_t*>(kt + n * KRB + 64 * ks + 16 * g), S);
+    float ps = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      ps += rown >= 0 && lse2[i] > -__builtin_huge_valf() ? __builtin_amdgcn_exp2f(S[i] * sc2 - lse2[i]) : 0.0f;
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    if (g == 0 && rown >= 0) atomicAdd(teacher + (int64_t)t * topk + jn, ps * invH);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+__global__ __launch_bounds__(kNT) void attn_teacher_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ kv, const int32_t* __restrict__ idx,
+    const float* __restrict__ lse, int H, int d_qk, int topk, float scale, float* __restrict__ teacher) {
+  const int t = blockIdx.x / H, h = blockIdx.x % H;
+  const float* qr = q + ((int64_t)t * H + h) * d_qk;
+  const float l = lse[(int64_t)t * H + h];
+  const int32_t* ir = idx + (int64_t)t * topk;
+  for (int j = threadIdx.x; j < topk; j += kNT) {
+    const int r = ir[j];
+    if (r < 0 || !(l > -__builtin_huge_valf())) continue;
+    const float* kr = kv + (int64_t)r * d_qk;
+    float s = 0.0f;
+    for (int c = 0; c < d_qk; ++c) s = fmaf(qr[c], kr[c], s);
+    atomicAdd(teacher + (int64_t)t * topk + j, expf(s * scale - l) / (float)H);
+  }
+}
+
 __global__ void zero_f32_kernel(float* __restrict__ p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     p[i] = 0.0f;
@@ -394,6 +489,32 @@ hipError_t launch_sparse_mla_bwd(const void* q, const void* kv, const int32_t* i
   return hipGetLastError();
 }
 
-size_t sparse_mla_bwd_lds(int d_qk) { return d_qk == 576 ? bwd_lds_bytes<576>() : bwd_lds_bytes<512>(); }
+hipError_t launch_attn_teacher(const void* q, const void* kv, const int32_t* idx, const float* lse,
+                               bool bf16, int T, int H, int d_qk, int topk, float scale, float* teacher,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(zero_f32_kernel, dim3(1024), dim3(256), 0, st, teacher, (int64_t)T * topk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || T == 0) return e;
+  if (!bf16) {
+    hipLaunchKernelGGL(attn_teacher_f32_kernel, dim3(T * H), dim3(kNT), 0, st, (const float*)q,
+                       (const float*)kv, idx, lse, H, d_qk, topk, scale, teacher);
+    return hipGetLastError();
+  }
+  const dim3 grid(T, (H + kHG - 1) / kHG), block(kWaves * 64);
+  if (d_qk == 576) {
+    const size_t shm = (size_t)(1 + kWaves) * kSK * krow_bytes<576>();
+    e = hipFuncSetAttribute((const void*)attn_teacher_bf16_kernel<576>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_teacher_bf16_kernel<576>), grid, block, shm, st, (const uint16_t*)q,
+                       (const uint16_t*)kv, idx, lse, H, topk, scale, teacher);
+  } else {
+    const size_t shm = (size_t)(1 + kWaves) * kSK * krow_bytes<512>();
+    e = hipFuncSetAttribute((const void*)attn_teacher_bf16_kernel<512>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_teacher_bf16_kernel<512>), grid, block, shm, st, (const uint16_t*)q,
+                       (const uint16_t*)kv, idx, lse, H, topk, scale, teacher);
+  }
+  return hipGetLastError();
+}
 
 }  // namespace sa
