@@ -235,7 +235,7 @@ def topk_select_candidates(cand_val, cand_idx, k: int):
 
 # ------------------------------------------------------------- O4: sparse MLA
 
-def sparse_mla_row(q_t, kv, idx_t, scale: float, d_v: int = 512):
+def sparse_mla_row(q_t, kv, idx_t, scale: float, d_v: int = 512, sink=None):
     """Absorbed-MLA attention of one query row over its selected latent rows.
 
     [DSA] file table: sparse-MLA forward; [NOPE] "What does this PR do?" and the
@@ -247,25 +247,37 @@ def sparse_mla_row(q_t, kv, idx_t, scale: float, d_v: int = 512):
     No valid slot -> out = 0, lse = -inf. Each slot counts once (duplicates count
     per slot).
 
+    ``sink`` [H] (optional; "Add fused SBHD compressed sparse attention", "Scope":
+    the compressed + window + sink attention of DeepSeek-V4): a per-head logit that
+    joins the softmax's denominator and carries no value, i.e. the attention over the
+    slots plus one extra key of logit sink[h] and value 0: Z = sum_j exp(l_j) +
+    exp(sink[h]), out = sum_j exp(l_j) v_j / Z, lse = ln Z (so with no valid slot
+    out = 0 and lse = sink[h]).
+
     q_t [H, d_qk], kv [S, d_qk], idx_t [k] -> out [H, d_v] float64, lse [H].
     """
     q = _f64(q_t)
     idx = _i64(idx_t)
     valid = idx[idx >= 0]
     H = q.shape[0]
+    sk = None if sink is None else _f64(sink)
     if valid.size == 0:
-        return np.zeros((H, d_v)), np.full(H, -np.inf)
+        return np.zeros((H, d_v)), (np.full(H, -np.inf) if sk is None else sk.copy())
     rows = _f64(kv[valid.tolist()] if hasattr(kv, "detach") else kv[valid])
     logits = scale * (q @ rows.T)                    # [H, n]
     m = logits.max(axis=1, keepdims=True)
+    if sk is not None:
+        m = np.maximum(m, sk[:, None])
     p = np.exp(logits - m)
     Z = p.sum(axis=1, keepdims=True)
+    if sk is not None:
+        Z = Z + np.exp(sk[:, None] - m)
     out = (p @ rows[:, :d_v]) / Z
     lse = m[:, 0] + np.log(Z[:, 0])
     return out, lse
 
 
-def sparse_mla(q, kv, idx, scale: float, d_v: int = 512, rows=None):
+def sparse_mla(q, kv, idx, scale: float, d_v: int = 512, rows=None, sink=None):
     """``sparse_mla_row`` for every row (or a subset); returns float64 out, lse."""
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
     kvh = _f64(kv)
@@ -274,7 +286,7 @@ def sparse_mla(q, kv, idx, scale: float, d_v: int = 512, rows=None):
     out = np.zeros((len(rows), H, d_v))
     lse = np.zeros((len(rows), H))
     for r, t in enumerate(rows):
-        out[r], lse[r] = sparse_mla_row(q[t], kvh, idxh[t], scale, d_v)
+        out[r], lse[r] = sparse_mla_row(q[t], kvh, idxh[t], scale, d_v, sink)
     return out, lse
 
 
@@ -370,7 +382,7 @@ def indexer_topk(q_I, k_I, w, k: int, cu_seqlens=None, block_size: int = 1,
 #     dk_j = scale * dl_j q,   dv_j = p_j g,
 # summed over heads (and, for a key attended by several rows or slots, over those).
 
-def sparse_mla_bwd_row(q_t, kv, idx_t, dout_t, scale: float, d_v: int = 512):
+def sparse_mla_bwd_row(q_t, kv, idx_t, dout_t, scale: float, d_v: int = 512, sink=None):
     """Gradients of ``sparse_mla_row`` for one query row.
 
     q_t [H, d_qk], kv [S, d_qk], idx_t [k], dout_t [H, d_v] (upstream gradient of
@@ -378,6 +390,11 @@ def sparse_mla_bwd_row(q_t, kv, idx_t, dout_t, scale: float, d_v: int = 512):
     slot's gradient row is dk_j on all channels plus dv_j on the first d_v. Returns
     dq [H, d_qk] and dkv_slots [k, d_qk] (one row per slot, zero for -1 slots; a
     repeated index gets one row per slot), float64.
+
+    With ``sink`` (see ``sparse_mla_row``) the probabilities p_j share their
+    denominator with the sink's p_sink = exp(sink - lse); the sink holds no value, so
+    D = sum_j p_j dp_j still, and the sink logit's gradient is -p_sink D (returned as
+    a third value, zeros without a sink).
     """
     q = _f64(q_t)
     g = _f64(dout_t)
@@ -385,13 +402,21 @@ def sparse_mla_bwd_row(q_t, kv, idx_t, dout_t, scale: float, d_v: int = 512):
     H, d_qk = q.shape
     dq = np.zeros((H, d_qk))
     dslots = np.zeros((idx.size, d_qk))
+    dsink = np.zeros(H)
     sel = np.nonzero(idx >= 0)[0]
     if sel.size == 0:
-        return dq, dslots
+        return dq, dslots, dsink
     rows = _f64(kv[idx[sel].tolist()] if hasattr(kv, "detach") else kv[idx[sel]])
     logits = scale * (q @ rows.T)                     # [H, n]
-    p = np.exp(logits - logits.max(axis=1, keepdims=True))
-    p /= p.sum(axis=1, keepdims=True)
+    m = logits.max(axis=1, keepdims=True)
+    if sink is not None:
+        m = np.maximum(m, _f64(sink)[:, None])
+    p = np.exp(logits - m)
+    Z = p.sum(axis=1, keepdims=True)
+    if sink is not None:
+        psink = np.exp(_f64(sink)[:, None] - m)
+        Z = Z + psink
+    p /= Z
     dp = g @ rows[:, :d_v].T                          # [H, n]
     D = (p * dp).sum(axis=1, keepdims=True)
     dl = p * (dp - D)
@@ -399,23 +424,28 @@ def sparse_mla_bwd_row(q_t, kv, idx_t, dout_t, scale: float, d_v: int = 512):
     dk = scale * (dl.T @ q)                           # [n, d_qk], summed over heads
     dk[:, :d_v] += p.T @ g
     dslots[sel] = dk
-    return dq, dslots
+    if sink is not None:
+        dsink = -(psink / Z)[:, 0] * D[:, 0]
+    return dq, dslots, dsink
 
 
-def sparse_mla_bwd(q, kv, idx, dout, scale: float, d_v: int = 512, rows=None):
+def sparse_mla_bwd(q, kv, idx, dout, scale: float, d_v: int = 512, rows=None, sink=None):
     """``sparse_mla_bwd_row`` over every row (or a subset): dq [len(rows), H, d_qk] and
-    dkv [S, d_qk] (the slot gradients of those rows scattered onto their latent rows)."""
+    dkv [S, d_qk] (the slot gradients of those rows scattered onto their latent rows);
+    with ``sink`` also dsink [H] (summed over the rows)."""
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
     kvh = _f64(kv)
     idxh = _i64(idx)
     H, d_qk = q.shape[1], q.shape[2]
     dq = np.zeros((len(rows), H, d_qk))
     dkv = np.zeros(kvh.shape)
+    dsink = np.zeros(H)
     for r, t in enumerate(rows):
-        dq[r], ds = sparse_mla_bwd_row(q[t], kvh, idxh[t], dout[t], scale, d_v)
+        dq[r], ds, dsk = sparse_mla_bwd_row(q[t], kvh, idxh[t], dout[t], scale, d_v, sink)
         ok = idxh[t] >= 0
         np.add.at(dkv, idxh[t][ok], ds[ok])
-    return dq, dkv
+        dsink += dsk
+    return (dq, dkv) if sink is None else (dq, dkv, dsink)
 
 
 def _gqa_keys(blk_t, t: int, seq_start: int, block_size: int) -> np.ndarray:
@@ -474,11 +504,14 @@ def block_sparse_gqa_bwd(q, k, v, blk, dout, block_size: int, scale: float,
 # it), the student is the softmax of the indexer scores of the same slots, and the
 # row's loss is KL(teacher || student). Gradients reach the indexer's q_I, k_I and w.
 
-def attn_teacher_row(q_t, kv, idx_t, scale: float) -> np.ndarray:
+def attn_teacher_row(q_t, kv, idx_t, scale: float, sink=None) -> np.ndarray:
     """Head-averaged sparse attention probability of every slot of one row, float64.
 
     p[j] = (1/H) sum_h softmax_h(scale q[h] . kv[idx_j])_j over the valid slots (the
-    probabilities ``sparse_mla_row`` weights the values with); 0 on -1 slots.
+    probabilities ``sparse_mla_row`` weights the values with); 0 on -1 slots. With a
+    sink the denominator keeps the sink's term ("Add fused SBHD compressed sparse
+    attention", "Scope": the teacher keeps the full compressed + window + sink
+    denominator), so the slots' probabilities sum to less than one.
     """
     q = _f64(q_t)
     idx = _i64(idx_t)
@@ -488,17 +521,22 @@ def attn_teacher_row(q_t, kv, idx_t, scale: float) -> np.ndarray:
         return p
     rows = _f64(kv[idx[sel].tolist()] if hasattr(kv, "detach") else kv[idx[sel]])
     logits = scale * (q @ rows.T)                      # [H, n]
-    e = np.exp(logits - logits.max(axis=1, keepdims=True))
-    e /= e.sum(axis=1, keepdims=True)
-    p[sel] = e.mean(axis=0)
+    m = logits.max(axis=1, keepdims=True)
+    if sink is not None:
+        m = np.maximum(m, _f64(sink)[:, None])
+    e = np.exp(logits - m)
+    Z = e.sum(axis=1, keepdims=True)
+    if sink is not None:
+        Z = Z + np.exp(_f64(sink)[:, None] - m)
+    p[sel] = (e / Z).mean(axis=0)
     return p
 
 
-def attn_teacher(q, kv, idx, scale: float, rows=None) -> np.ndarray:
+def attn_teacher(q, kv, idx, scale: float, rows=None, sink=None) -> np.ndarray:
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
     kvh = _f64(kv)
     idxh = _i64(idx)
-    return np.stack([attn_teacher_row(q[t], kvh, idxh[t], scale) for t in rows])
+    return np.stack([attn_teacher_row(q[t], kvh, idxh[t], scale, sink) for t in rows])
 
 
 def indexer_kl_row(q_I_t, k_I, w_t, idx_t, teacher_t):
@@ -506,8 +544,9 @@ def indexer_kl_row(q_I_t, k_I, w_t, idx_t, teacher_t):
 
     Scores of the valid slots I_j = sum_h w_h max(z_hj, 0) with z_hj = q_I[h] . k_I[idx_j]
     (the indexer definition, unrounded); student s = softmax(I) over them; loss =
-    sum_j p_j (log p_j - log s_j) with 0 log 0 = 0 (p = teacher_t). With dI_j = s_j - p_j
-    (d loss / d I_j, as sum_j p_j = 1):
+    sum_j p_j (log p_j - log s_j) with 0 log 0 = 0 (p = teacher_t). With
+    dI_j = s_j sum_i p_i - p_j (d loss / d I_j; s_j - p_j when the teacher sums to one,
+    less when part of the teacher's mass lies outside the slots, e.g. on a sink):
       dw_h  = sum_j dI_j max(z_hj, 0)
       dq_h  = sum_j dI_j w_h [z_hj > 0] k_I[idx_j]
       dk_j  = sum_h dI_j w_h [z_hj > 0] q_I[h]        (a slot's gradient row)
@@ -531,7 +570,7 @@ def indexer_kl_row(q_I_t, k_I, w_t, idx_t, teacher_t):
     p = p_all[sel]
     nz = p > 0
     loss = float((p[nz] * (np.log(p[nz]) - ls[nz])).sum())
-    d = np.exp(ls) - p
+    d = np.exp(ls) * p.sum() - p
     dI[sel] = d
     on = (z > 0).astype(np.float64)                    # [H, n]
     dw = np.maximum(z, 0.0) @ d
@@ -564,3 +603,78 @@ def indexer_kl(q_I, k_I, w, idx, teacher, grad=None, rows=None):
         ok = idxh[t] >= 0
         np.add.at(dk, idxh[t][ok], g[t] * e[ok])
     return loss, dI, dq, dw, dk
+
+
+# --------------------------------------------------- routing variants (pools, window)
+
+def complete_block_topk(scores, k: int, block_size: int, cu_seqlens=None, rows=None):
+    """Top-k over complete key blocks only: row t (offset o = t - start in its
+    sequence) competes its blocks b < (o + 1) // B, the blocks all of whose keys are
+    causal; the block that holds the query is left out unless it is complete. Same
+    order and output convention as ``topk_select_row``; ids local to the sequence.
+
+    "Support NoPE shapes and unaligned top-k in TileLang sparse MLA", the quoted GLM
+    PR body, section "Why": k-pool selection picks among pools of keys, and the
+    query's incomplete tail pool is handled apart (``kpool_expand``).
+    """
+    scores = np.asarray(scores)
+    rows = np.arange(scores.shape[0]) if rows is None else np.asarray(rows)
+    T = int(_i64(cu_seqlens)[-1]) if cu_seqlens is not None else scores.shape[0]
+    start, _ = seq_bounds(T, cu_seqlens)
+    idx = np.full((len(rows), k), -1, dtype=np.int32)
+    val = np.full((len(rows), k), NEG_INF, dtype=np.float32)
+    for r, t in enumerate(rows):
+        n = (int(t - start[t]) + 1) // block_size
+        idx[r], val[r] = topk_select_row(scores[r], n, k)
+    return idx, val
+
+
+def kpool_expand(pool_idx, pool: int, cu_seqlens=None, T: int | None = None):
+    """Token slots of a k-pool route, with the query's incomplete tail pool appended.
+
+    Same passage as ``complete_block_topk`` (width 2048 + 3 = 2051 for 512 pools of
+    four keys). Reading: row t's selected pools c (local ids, -1 skipped) each give
+    their keys start + c*P .. start + c*P + P - 1 (global rows), in slot order; then
+    the keys of the query's own pool when it is incomplete (the o % P + 1 keys
+    start + (o // P) * P .. t, o = t - start, when o % P != P - 1) fill the last P - 1
+    slots, -1 padded. Width k*P + P - 1.
+    """
+    pool_idx = _i64(pool_idx)
+    Tn = pool_idx.shape[0] if T is None else T
+    start, _ = seq_bounds(Tn, cu_seqlens)
+    k = pool_idx.shape[1]
+    out = np.full((Tn, k * pool + pool - 1), -1, dtype=np.int32)
+    for t in range(Tn):
+        s0 = int(start[t])
+        toks = []
+        for c in pool_idx[t]:
+            if c >= 0:
+                toks.extend(range(s0 + c * pool, s0 + c * pool + pool))
+        out[t, :len(toks)] = toks
+        o = t - s0
+        if o % pool != pool - 1:
+            tail = list(range(s0 + (o // pool) * pool, t + 1))
+            out[t, k * pool:k * pool + len(tail)] = tail
+    return out
+
+
+def append_window(idx, window: int, offset: int = 0, cu_seqlens=None):
+    """Selected slots followed by a causal window of raw keys.
+
+    "Add fused SBHD compressed sparse attention", "Scope" (compressed + window + sink).
+    Reading: row t keeps its k selected slots and gains ``window`` slots holding
+    offset + s for the keys s = t - window + 1 .. t of its own sequence (-1 where s
+    falls before the sequence start); ``offset`` places the raw keys after another
+    key table (e.g. compressed entries first). Width k + window.
+    """
+    idx = _i64(idx)
+    T, k = idx.shape
+    start, _ = seq_bounds(T, cu_seqlens)
+    out = np.full((T, k + window), -1, dtype=np.int32)
+    out[:, :k] = idx
+    for t in range(T):
+        for i in range(window):
+            s = t - window + 1 + i
+            if s >= start[t]:
+                out[t, k + i] = offset + s
+    return out

@@ -705,6 +705,7 @@ def test_indexer_kl_matches_autograd_through_library_kl():
     teacher = rng.random((T, k)) * (idx >= 0)
     teacher[0, 3] = 0.0                               # zero teacher probability
     teacher /= teacher.sum(1, keepdims=True)
+    teacher[4] *= 0.6                                 # mass outside the slots (a sink)
     grad = rng.random(T) + 0.5
     loss, dI, dq, dw, dk = oracle.indexer_kl(q, kk, w, idx, teacher, grad)
     qt = torch.from_numpy(q).requires_grad_()
@@ -723,7 +724,7 @@ def test_indexer_kl_matches_autograd_through_library_kl():
     np.testing.assert_allclose(dq, qt.grad.numpy(), rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(dw, wt.grad.numpy(), rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(dk, kt.grad.numpy(), rtol=1e-11, atol=1e-12)
-    # dI = grad * (student - teacher) sums to zero per row
+    # dI = grad * (student * sum(teacher) - teacher) sums to zero per row
     np.testing.assert_allclose(dI.sum(1), 0.0, atol=1e-13)
 
 
@@ -746,3 +747,104 @@ def test_indexer_kl_zero_when_student_equals_teacher():
     flat = np.full_like(st, 1.0 / k)
     l2, *_ = oracle.indexer_kl(q, kk, w, idx, flat)
     assert np.all(l2 > 0)
+
+
+# ------------------------------------------------- variants: sink, pools, window
+
+def test_mla_sink_is_an_extra_zero_value_key():
+    """A sink equals one more key per head with logit sink[h] and value zero: the
+    library softmax over the augmented logits weights the values; lse is its log
+    denominator; with no valid slot out = 0 and lse = sink."""
+    rng = np.random.default_rng(70)
+    S, H, d_qk, d_v, k = 30, 4, 20, 12, 7
+    kv = rng.standard_normal((S, d_qk))
+    q = rng.standard_normal((H, d_qk))
+    sink = rng.standard_normal(H) * 2
+    idx = rng.permutation(S)[:k]
+    idx[2] = -1
+    out, lse = oracle.sparse_mla_row(q, kv, idx, 0.4, d_v, sink=sink)
+    rows = kv[idx[idx >= 0]]
+    aug = torch.cat([torch.from_numpy(0.4 * q @ rows.T), torch.from_numpy(sink)[:, None]], 1)
+    p = torch.softmax(aug, 1).numpy()
+    vals = np.concatenate([rows[:, :d_v], np.zeros((1, d_v))])
+    np.testing.assert_allclose(out, p @ vals, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, torch.logsumexp(aug, 1).numpy(), rtol=1e-13)
+    o0, l0 = oracle.sparse_mla_row(q, kv, np.full(3, -1), 0.4, d_v, sink=sink)
+    assert np.all(o0 == 0) and np.array_equal(l0, sink)
+    # the teacher keeps the sink in its denominator
+    pt = oracle.attn_teacher_row(q, kv, idx, 0.4, sink=sink)
+    np.testing.assert_allclose(pt[idx >= 0], p[:, :-1].mean(0), rtol=1e-12)
+    assert pt.sum() < 1
+
+
+def test_mla_bwd_with_sink_matches_autograd():
+    rng = np.random.default_rng(71)
+    T, S, H, d_qk, d_v, k = 4, 25, 3, 16, 8, 6
+    q = rng.standard_normal((T, H, d_qk))
+    kv = rng.standard_normal((S, d_qk))
+    dout = rng.standard_normal((T, H, d_v))
+    sink = rng.standard_normal(H)
+    idx = np.stack([rng.permutation(S)[:k] for _ in range(T)])
+    idx[1, 3:] = -1
+    idx[2] = -1                                          # only the sink: no gradient but dsink
+    dq, dkv, dsink = oracle.sparse_mla_bwd(q, kv, idx, dout, 0.3, d_v, sink=sink)
+    qt = torch.from_numpy(q).requires_grad_()
+    kvt = torch.from_numpy(kv).requires_grad_()
+    st = torch.from_numpy(sink).requires_grad_()
+    total = qt.new_zeros(())
+    for t in range(T):
+        sl = idx[t][idx[t] >= 0]
+        rows = kvt[torch.as_tensor(sl, dtype=torch.long)]
+        aug = torch.cat([0.3 * qt[t] @ rows.T, st[:, None]], 1)
+        p = torch.softmax(aug, 1)[:, :-1]
+        total = total + (p @ rows[:, :d_v] * torch.from_numpy(dout[t])).sum()
+    total.backward()
+    np.testing.assert_allclose(dq, qt.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dkv, kvt.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dsink, st.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_complete_block_topk_brute_force():
+    """Only blocks whose keys are all causal compete: row offsets o give (o + 1) // B
+    candidates; checked against a tuple sort on packed sequences."""
+    rng = np.random.default_rng(72)
+    lengths = (9, 14, 3)
+    cu = workloads.cu_seqlens(lengths)
+    T, B, k = sum(lengths), 4, 2
+    sc = np.round(rng.standard_normal((T, 4)) * 2).astype(np.float32)
+    got, _ = oracle.complete_block_topk(sc, k, B, cu_seqlens=cu)
+    start, _ = oracle.seq_bounds(T, cu)
+    for t in range(T):
+        n = (t - start[t] + 1) // B
+        assert got[t].tolist() == _brute_topk(sc[t], n, k)
+    # offsets 3 and 7 complete their own block, which then competes
+    assert (3 + 1) // B == 1 and (2 + 1) // B == 0
+
+
+def test_kpool_expand_hand_example():
+    """Pools of four keys: a row at sequence offset 9 (its pool 2 holds keys 8, 9 so
+    far) with pools 0 and 1 selected gets keys 0..7, then the tail 8, 9 and one -1: the
+    width is k*4 + 3, as 512 pools give the quoted 2048 + 3 = 2051."""
+    pools = np.full((12, 2), -1)
+    pools[9] = [0, 1]
+    pools[11] = [2, -1]
+    out = oracle.kpool_expand(pools, 4)
+    assert out.shape == (12, 11)
+    assert out[9].tolist() == [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, -1]
+    assert out[11].tolist() == [8, 9, 10, 11] + [-1] * 7        # offset 11: pool complete, no tail
+    assert out[0].tolist() == [-1] * 8 + [0, -1, -1]             # offset 0: tail is the query
+    assert oracle.kpool_expand(np.full((1, 512), -1), 4).shape[1] == 2051
+    # packed sequences: ids are global rows
+    cu = workloads.cu_seqlens((5, 7))
+    p2 = np.full((12, 1), -1)
+    p2[10] = [1]                                                 # offset 5 in sequence 1
+    o2 = oracle.kpool_expand(p2, 4, cu_seqlens=cu)
+    assert o2[10].tolist() == [9, 10, 11, 12, 9, 10, -1]
+
+
+def test_append_window_hand_example():
+    idx = np.array([[0, -1], [1, 0], [2, 1], [3, 0], [4, -1]])
+    cu = workloads.cu_seqlens((3, 2))
+    out = oracle.append_window(idx, 2, offset=100, cu_seqlens=cu)
+    assert out.tolist() == [[0, -1, -1, 100], [1, 0, 100, 101], [2, 1, 101, 102],
+                            [3, 0, -1, 103], [4, -1, 103, 104]]
