@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 2
+#define SA_ABI_VERSION 3
 
 typedef enum {
   SA_OK = 0,
@@ -98,8 +98,8 @@ int sa_abi_version(void);
  * Inputs:
  *   q_I  [T, H_I, D_I]  dtype        k_I [T, D_I] dtype       w [T, H_I] fp32
  *   dtype  SA_F32 or SA_BF16 (q_I and k_I)
- *   H_I in {4, 8, 16, 32, 64}; D_I in {64, 128}; block_size in {1, 16, 32, 64, 128,
- *   256}; otherwise SA_ERR_UNSUPPORTED.
+ *   H_I in {4, 8, 16, 32, 64}; D_I in {64, 128}; block_size in {1, 2, 4, 8, 16, 32,
+ *   64, 128, 256}; otherwise SA_ERR_UNSUPPORTED.
  * Mode 1, dense (topk == 0): writes scores [T, ld] fp32; row t, column c holds the
  *   score of key start(t)+c (token mode) or of local block c (block mode) for the
  *   causal columns c < n(t), where n(t) = t-start(t)+1 (tokens) or
@@ -111,7 +111,8 @@ int sa_abi_version(void);
  *   never stored. Writes out_idx [T, topk] int32 and, if out_val != NULL, out_val
  *   [T, topk] fp32, with exactly the result sa_topk_select gives on the dense scores
  *   (same indices, same order). Token mode: topk in [1, 2048]; block mode: topk in
- *   [1, 64]. force_own_block as in sa_topk_select (block mode only).
+ *   [1, 64]. force_own_block 0 or 1 as in sa_topk_select (block mode only; for 2,
+ *   write the dense block scores and select them with sa_topk_select).
  *   Two ways to run it (same results, bit for bit):
  *   - ws == NULL: one pass; each row keeps an exact running top-k in on-chip
  *     memory ([QSA] "Describe the solution you'd like": streaming runner with
@@ -192,9 +193,13 @@ size_t sa_noalloc_scratch_bytes(void);
  * Candidates of row t:
  *   cand_idx == NULL (dense causal rows, as written by sa_indexer_scores mode 1):
  *     columns c < n(t) of vals[t, :]; token mode (block_size 1) reports global key
- *     rows start(t)+c; block mode (block_size B > 1) reports local block ids c, and
- *     with force_own_block != 0 the query's own block (c = n(t)-1) is always kept and
- *     counts toward topk.
+ *     rows start(t)+c; block mode (block_size B > 1) reports local block ids c.
+ *     force_own_block (block mode): 0 = the query's own block competes like the
+ *     others; 1 = it (c = n(t)-1) is always kept and counts toward topk; 2 = only
+ *     complete blocks compete, n(t) = (t-start(t)+1) / B, so the own block is left
+ *     out while the query has not reached its last key (k-pool selection, [NOPE]
+ *     quoted GLM body, "Why": the incomplete tail pool is appended apart, see
+ *     sa_kpool_expand).
  *   cand_idx != NULL (explicit candidate lists): vals[t, c] with index cand_idx[t, c]
  *     for every column c < ld whose cand_idx is >= 0; the valid indices of a row must
  *     be strictly ascending left to right (-1 entries may sit anywhere). The layout
@@ -231,6 +236,13 @@ sa_status sa_topk_select(const float* vals, const int32_t* cand_idx, int64_t ld,
  * index counts twice). Slot order does not matter; topk need not be a multiple of
  * anything.
  *
+ * sink (nullable, [H] fp32): a per-head logit that joins the softmax denominator and
+ * carries no value ("Add fused SBHD compressed sparse attention", "Scope": the
+ * compressed + window + sink attention): with Z = sum_j exp(l_j) + exp(sink[h]),
+ * out = sum_j exp(l_j) kv[idx_j, 0:d_v] / Z and lse = ln Z; a row with no valid slot
+ * gives out = 0 and lse = sink[h]. A window of raw keys is attended by appending its
+ * slots to idx (sa_append_window).
+ *
  * Inputs: q [T, H, d_qk], kv [S, d_qk] (dtype), idx [T, topk] int32 with values in
  *   [0, S) or -1. Outputs: out [T, H, d_v] (dtype), lse [T, H] fp32 (nullable).
  * Sizes: d_qk in {512, 576}; d_v == 512; H in [1, 128]; S >= 1; topk in [1, 8192] for
@@ -242,7 +254,8 @@ sa_status sa_topk_select(const float* vals, const int32_t* cand_idx, int64_t ld,
  */
 sa_status sa_sparse_mla_fwd(const void* q, const void* kv, const int32_t* idx, int dtype,
                             int32_t T, int32_t S, int32_t H, int32_t d_qk, int32_t d_v,
-                            int32_t topk, float scale, void* out, float* lse, void* stream);
+                            int32_t topk, float scale, const float* sink, void* out, float* lse,
+                            void* stream);
 
 /*
  * sa_sparse_mla_bwd -- gradients of sa_sparse_mla_fwd.
@@ -261,7 +274,11 @@ sa_status sa_sparse_mla_fwd(const void* q, const void* kv, const int32_t* idx, i
  *     dkv[idx_j, :d_v] += sum_(t,h) p_j dout[t,h,:]   (the value channels)
  *
  * -1 slots contribute nothing; a repeated index contributes once per slot; a row with
- * no valid slot (lse = -inf) gets dq = 0.
+ * no valid slot (lse = -inf) gets dq = 0. With a sink (the forward's sink, whose term
+ * lse includes), p_j already shares its denominator with the sink; dsink (nullable
+ * [H] fp32, zeroed by the call, needs sink) receives
+ *     dsink[h] = -sum_t exp(sink[h] - lse[t,h]) D[t,h]
+ * with atomics.
  * Inputs: q [T,H,d_qk], kv [S,d_qk], dout [T,H,d_v] (dtype), idx [T,topk], lse
  *   [T,H] fp32 (the forward's). Outputs: dq [T,H,d_qk] (dtype); dkv
  *   [S,d_qk] fp32, which the call zeroes and then accumulates into with
@@ -272,8 +289,8 @@ sa_status sa_sparse_mla_fwd(const void* q, const void* kv, const int32_t* idx, i
  */
 sa_status sa_sparse_mla_bwd(const void* q, const void* kv, const int32_t* idx, const void* dout,
                             const float* lse, int dtype, int32_t T, int32_t S, int32_t H,
-                            int32_t d_qk, int32_t d_v, int32_t topk, float scale, void* dq,
-                            float* dkv, void* stream);
+                            int32_t d_qk, int32_t d_v, int32_t topk, float scale, const float* sink,
+                            void* dq, float* dkv, float* dsink, void* stream);
 
 /*
  * sa_attn_teacher -- teacher distribution of the sparse KL indexer loss.
@@ -375,6 +392,35 @@ sa_status sa_block_sparse_gqa_bwd(const void* q, const void* k, const void* v, c
                                   int32_t Hq, int32_t Hkv, int32_t D, int32_t Dv, int32_t block_size,
                                   int32_t nblk, float scale, void* dq, float* dk, float* dv,
                                   void* stream);
+
+/*
+ * sa_kpool_expand -- token slots of a k-pool route, the incomplete tail pool appended.
+ *
+ * [NOPE] quoted GLM PR body, "Why": k-pool selection appends the query's incomplete
+ * tail pool, so the top-k width is 2048 + 3. Reading: pools are runs of `pool` keys of
+ * a sequence (pool c = keys start + c*pool .. + pool - 1); slot i of pools [T, kp]
+ * (a local pool id, e.g. from sa_topk_select with force_own_block = 2, or -1) gives
+ * out slots i*pool .. i*pool + pool - 1 (global key rows; -1 for a -1 pool); the last
+ * pool - 1 slots hold the keys of the query's own pool while it is incomplete
+ * (start + (o / pool) * pool .. t, o = t - start(t), when o % pool != pool - 1), -1
+ * padded. out [T, kp*pool + pool - 1] int32 (2051 for 512 pools of 4), ready for
+ * sa_sparse_mla_fwd. Pool ids must be below the row's complete pools.
+ */
+sa_status sa_kpool_expand(const int32_t* pools, int32_t T, const int32_t* cu_seqlens, int32_t num_seqs,
+                          int32_t max_seqlen, int32_t kp, int32_t pool, int32_t* out, void* stream);
+
+/*
+ * sa_append_window -- selected slots followed by a causal window of raw keys.
+ *
+ * [CSA] "Add fused SBHD compressed sparse attention", "Scope" (compressed + window +
+ * sink attention). out [T, k + window] int32: out[t, 0:k] = idx[t, :]; out[t, k + i] =
+ * offset + s for s = t - window + 1 + i when s >= start(t), else -1. With offset = the
+ * rows of a table that precedes the raw keys (e.g. compressed entries, so kv = [that
+ * table; raw keys]), the result indexes the concatenated table.
+ */
+sa_status sa_append_window(const int32_t* idx, int32_t T, const int32_t* cu_seqlens, int32_t num_seqs,
+                           int32_t max_seqlen, int32_t k, int32_t window, int32_t offset, int32_t* out,
+                           void* stream);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,8 @@ __all__ = [
     "SAError", "SA_F32", "SA_BF16", "lib", "abi_version", "status_string",
     "sa_indexer_workspace_bytes", "indexer_workspace", "sa_indexer_scores", "sa_sparse_mla_bwd",
     "sparse_mla_bwd", "sa_block_sparse_gqa_bwd", "block_sparse_gqa_bwd", "sa_attn_teacher",
-    "attn_teacher", "sa_indexer_kl_bwd", "indexer_kl_bwd", "sa_topk_select", "sa_sparse_mla_fwd", "sa_block_sparse_gqa_fwd",
+    "attn_teacher", "sa_indexer_kl_bwd", "indexer_kl_bwd", "sa_kpool_expand", "kpool_expand",
+    "sa_append_window", "append_window", "sa_topk_select", "sa_sparse_mla_fwd", "sa_block_sparse_gqa_fwd",
     "indexer_scores", "indexer_topk", "topk_select", "sparse_mla", "block_sparse_gqa",
 ]
 
@@ -55,10 +56,14 @@ lib.sa_topk_select.restype = ctypes.c_int
 lib.sa_topk_select.argtypes = [_p, _p, _i64, _i32, _p, _i32, _i32, _i32, _i32, _i32, _p, _p, _p]
 lib.sa_sparse_mla_fwd.restype = ctypes.c_int
 lib.sa_sparse_mla_fwd.argtypes = [_p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _i32,
-                                  _f32, _p, _p, _p]
+                                  _f32, _p, _p, _p, _p]
 lib.sa_sparse_mla_bwd.restype = ctypes.c_int
 lib.sa_sparse_mla_bwd.argtypes = [_p, _p, _p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32,
-                                  _i32, _f32, _p, _p, _p]
+                                  _i32, _f32, _p, _p, _p, _p, _p]
+lib.sa_kpool_expand.restype = ctypes.c_int
+lib.sa_kpool_expand.argtypes = [_p, _i32, _p, _i32, _i32, _i32, _i32, _p, _p]
+lib.sa_append_window.restype = ctypes.c_int
+lib.sa_append_window.argtypes = [_p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _p, _p]
 lib.sa_block_sparse_gqa_bwd.restype = ctypes.c_int
 lib.sa_block_sparse_gqa_bwd.argtypes = [_p, _p, _p, _p, _p, _p, ctypes.c_int, _i32, _p, _i32, _i32, _i32,
                                         _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p, _p]
@@ -191,8 +196,10 @@ def sa_indexer_scores(q_I, k_I, w, *, cu_seqlens=None, max_seqlen=None, block_si
 
 
 def sa_topk_select(vals, out_idx, *, out_val=None, cand_idx=None, cu_seqlens=None, max_seqlen=None,
-                   block_size=1, force_own_block=False):
-    """sa_topk_select: exact top-k of each row of ``vals`` [T, ld] into ``out_idx`` [T, topk]."""
+                   block_size=1, force_own_block=0):
+    """sa_topk_select: exact top-k of each row of ``vals`` [T, ld] into ``out_idx`` [T, topk].
+    force_own_block (block mode): 0 own block competes, 1 own block kept, 2 complete
+    blocks only."""
     dev = _device_of(vals, "vals")
     _need(vals, "vals", dev, torch.float32, (None, None))
     T, ld = vals.shape
@@ -202,12 +209,13 @@ def sa_topk_select(vals, out_idx, *, out_val=None, cand_idx=None, cu_seqlens=Non
     _need(cand_idx, "cand_idx", dev, torch.int32, (T, ld), optional=True)
     cu, nseq, maxlen = _layout(T, cu_seqlens, max_seqlen, dev)
     _check(lib.sa_topk_select(_ptr(vals), _ptr(cand_idx), ld, T, _ptr(cu), nseq, maxlen,
-                              int(block_size), topk, int(bool(force_own_block)), _ptr(out_idx),
+                              int(block_size), topk, int(force_own_block), _ptr(out_idx),
                               _ptr(out_val), _stream(dev)), "sa_topk_select")
 
 
-def sa_sparse_mla_fwd(q, kv, idx, scale, out, lse=None):
-    """sa_sparse_mla_fwd: q [T,H,d_qk], kv [S,d_qk], idx [T,topk] -> out [T,H,d_v], lse [T,H]."""
+def sa_sparse_mla_fwd(q, kv, idx, scale, out, lse=None, sink=None):
+    """sa_sparse_mla_fwd: q [T,H,d_qk], kv [S,d_qk], idx [T,topk] -> out [T,H,d_v], lse [T,H];
+    sink [H] fp32 optional (a per-head logit in the softmax denominator)."""
     dev = _device_of(q, "q")
     if q.dim() != 3:
         raise ValueError("q must be [T, H, d_qk]")
@@ -218,14 +226,16 @@ def sa_sparse_mla_fwd(q, kv, idx, scale, out, lse=None):
     _need(idx, "idx", dev, torch.int32, (T, None))
     _need(out, "out", dev, q.dtype, (T, H, None))
     _need(lse, "lse", dev, torch.float32, (T, H), optional=True)
+    _need(sink, "sink", dev, torch.float32, (H,), optional=True)
     _check(lib.sa_sparse_mla_fwd(_ptr(q), _ptr(kv), _ptr(idx), _dtype_code(q), T, S, H, d_qk,
-                                 out.shape[2], idx.shape[1], float(scale), _ptr(out), _ptr(lse),
-                                 _stream(dev)), "sa_sparse_mla_fwd")
+                                 out.shape[2], idx.shape[1], float(scale), _ptr(sink), _ptr(out),
+                                 _ptr(lse), _stream(dev)), "sa_sparse_mla_fwd")
 
 
-def sa_sparse_mla_bwd(q, kv, idx, dout, lse, scale, dq, dkv):
+def sa_sparse_mla_bwd(q, kv, idx, dout, lse, scale, dq, dkv, sink=None, dsink=None):
     """sa_sparse_mla_bwd: gradients dq [T,H,d_qk] (q's dtype) and dkv [S,d_qk] (fp32,
-    overwritten) of sparse MLA from dout, given the forward's lse."""
+    overwritten) of sparse MLA from dout, given the forward's lse; with the forward's
+    sink, dsink [H] (fp32, overwritten) too."""
     dev = _device_of(q, "q")
     if q.dim() != 3:
         raise ValueError("q must be [T, H, d_qk]")
@@ -239,9 +249,34 @@ def sa_sparse_mla_bwd(q, kv, idx, dout, lse, scale, dq, dkv):
     _need(lse, "lse", dev, torch.float32, (T, H))
     _need(dq, "dq", dev, q.dtype, (T, H, d_qk))
     _need(dkv, "dkv", dev, torch.float32, (S, d_qk))
+    _need(sink, "sink", dev, torch.float32, (H,), optional=True)
+    _need(dsink, "dsink", dev, torch.float32, (H,), optional=True)
     _check(lib.sa_sparse_mla_bwd(_ptr(q), _ptr(kv), _ptr(idx), _ptr(dout), _ptr(lse),
                                  _dtype_code(q), T, S, H, d_qk, d_v, idx.shape[1], float(scale),
-                                 _ptr(dq), _ptr(dkv), _stream(dev)), "sa_sparse_mla_bwd")
+                                 _ptr(sink), _ptr(dq), _ptr(dkv), _ptr(dsink), _stream(dev)),
+           "sa_sparse_mla_bwd")
+
+
+def sa_kpool_expand(pools, pool, out, *, cu_seqlens=None, max_seqlen=None):
+    """sa_kpool_expand: pool routes [T,kp] -> token slots [T, kp*pool + pool - 1]."""
+    dev = _device_of(pools, "pools")
+    _need(pools, "pools", dev, torch.int32, (None, None))
+    T, kp = pools.shape
+    _need(out, "out", dev, torch.int32, (T, kp * pool + pool - 1))
+    cu, nseq, maxlen = _layout(T, cu_seqlens, max_seqlen, dev)
+    _check(lib.sa_kpool_expand(_ptr(pools), T, _ptr(cu), nseq, maxlen, kp, int(pool), _ptr(out),
+                               _stream(dev)), "sa_kpool_expand")
+
+
+def sa_append_window(idx, window, offset, out, *, cu_seqlens=None, max_seqlen=None):
+    """sa_append_window: selected slots [T,k] + a causal window -> [T, k + window]."""
+    dev = _device_of(idx, "idx")
+    _need(idx, "idx", dev, torch.int32, (None, None))
+    T, k = idx.shape
+    _need(out, "out", dev, torch.int32, (T, k + window))
+    cu, nseq, maxlen = _layout(T, cu_seqlens, max_seqlen, dev)
+    _check(lib.sa_append_window(_ptr(idx), T, _ptr(cu), nseq, maxlen, k, int(window), int(offset),
+                                _ptr(out), _stream(dev)), "sa_append_window")
 
 
 def sa_block_sparse_gqa_fwd(q, k, v, blk, scale, out, lse=None, *, block_size, cu_seqlens=None,
@@ -378,19 +413,34 @@ def topk_select(vals, topk, *, cand_idx=None, cu_seqlens=None, max_seqlen=None, 
     return (idx, val) if with_values else idx
 
 
-def sparse_mla(q, kv, idx, scale, d_v=512, with_lse=True):
+def sparse_mla(q, kv, idx, scale, d_v=512, with_lse=True, sink=None):
     T, H, _ = q.shape
     out = torch.empty((T, H, d_v), dtype=q.dtype, device=q.device)
     lse = torch.empty((T, H), dtype=torch.float32, device=q.device) if with_lse else None
-    sa_sparse_mla_fwd(q, kv, idx, scale, out, lse)
+    sa_sparse_mla_fwd(q, kv, idx, scale, out, lse, sink=sink)
     return (out, lse) if with_lse else out
 
 
-def sparse_mla_bwd(q, kv, idx, dout, lse, scale):
+def sparse_mla_bwd(q, kv, idx, dout, lse, scale, sink=None):
     dq = torch.empty_like(q)
     dkv = torch.empty(kv.shape, dtype=torch.float32, device=q.device)
-    sa_sparse_mla_bwd(q, kv, idx, dout, lse, scale, dq, dkv)
-    return dq, dkv
+    dsink = torch.empty(q.shape[1], dtype=torch.float32, device=q.device) if sink is not None else None
+    sa_sparse_mla_bwd(q, kv, idx, dout, lse, scale, dq, dkv, sink=sink, dsink=dsink)
+    return (dq, dkv) if sink is None else (dq, dkv, dsink)
+
+
+def kpool_expand(pools, pool, *, cu_seqlens=None, max_seqlen=None):
+    T, kp = pools.shape
+    out = torch.empty((T, kp * pool + pool - 1), dtype=torch.int32, device=pools.device)
+    sa_kpool_expand(pools, pool, out, cu_seqlens=cu_seqlens, max_seqlen=max_seqlen)
+    return out
+
+
+def append_window(idx, window, offset=0, *, cu_seqlens=None, max_seqlen=None):
+    T, k = idx.shape
+    out = torch.empty((T, k + window), dtype=torch.int32, device=idx.device)
+    sa_append_window(idx, window, offset, out, cu_seqlens=cu_seqlens, max_seqlen=max_seqlen)
+    return out
 
 
 def attn_teacher(q, kv, idx, lse, scale):

@@ -21,7 +21,7 @@ OUT = os.path.join(HERE, "libsa.so")
 OUT_DEBUG = os.path.join(HERE, "libsa_debug.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["sa_api.hip", "sa_noalloc.hip", "sa_checks.hip", "topk_select.hip", "sparse_mla.hip",
-           "sparse_mla_bwd.hip", "indexer.hip", "indexer_kl.hip", "block_gqa.hip", "block_gqa_bwd.hip"]
+           "sparse_mla_bwd.hip", "indexer.hip", "indexer_kl.hip", "block_gqa.hip", "block_gqa_bwd.hip", "routes.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -6,7 +6,8 @@
 // (keys s_j = idx[t,j]) the teacher p_j is given (the head-mean sparse attention
 // probability), the student is softmax_j(I_j) of the indexer scores
 // I_j = sum_h w[t,h] relu(z_hj), z_hj = q_I[t,h] . k_I[s_j], and
-//   loss[t] = sum_j p_j (log p_j - log softmax(I)_j),   dI_j = g_t (softmax(I)_j - p_j),
+//   loss[t] = sum_j p_j (log p_j - log softmax(I)_j),
+//   dI_j = g_t (softmax(I)_j sum_i p_i - p_j)   (sum_i p_i < 1 when a sink holds mass),
 //   dw[t,h] = sum_j dI_j relu(z_hj),
 //   dq_I[t,h] = sum_j dI_j w[t,h] [z_hj > 0] k_I[s_j],
 //   dk_I[s_j] += sum_h dI_j w[t,h] [z_hj > 0] q_I[t,h]       (atomics, fp32),
@@ -143,17 +144,25 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kl_bf16_kernel(
   __syncthreads();
   m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(bc[0], bc[1]),
                                     __builtin_elementwise_maximum(bc[2], bc[3]));
-  float se = 0.0f;
-  for (int j = tid; j < topk; j += kWaves * 64)
-    se += Il[j] > -__builtin_huge_valf() ? __builtin_amdgcn_exp2f((Il[j] - m) * kLog2e) : 0.0f;
+  const float* prow = teacher + (int64_t)t * topk;
+  float se = 0.0f, pm = 0.0f;
+  for (int j = tid; j < topk; j += kWaves * 64) {
+    if (Il[j] > -__builtin_huge_valf()) {
+      se += __builtin_amdgcn_exp2f((Il[j] - m) * kLog2e);
+      pm += prow[j];
+    }
+  }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) se += __shfl_xor(se, off, 64);
-  if (L == 0) bc[4 + w] = se;
+  for (int off = 32; off >= 1; off >>= 1) {
+    se += __shfl_xor(se, off, 64);
+    pm += __shfl_xor(pm, off, 64);
+  }
+  if (L == 0) { bc[4 + w] = se; bc[12 + w] = pm; }
   __syncthreads();
   const bool any = m > -__builtin_huge_valf();
   const float lsum = any ? m + __log2f(bc[4] + bc[5] + bc[6] + bc[7]) * kLn2 : 0.0f;   // log sum exp I
+  const float pmass = bc[12] + bc[13] + bc[14] + bc[15];                              // teacher mass
   const float gt = grad ? grad[t] : 1.0f;
-  const float* prow = teacher + (int64_t)t * topk;
   float lpart = 0.0f;
   for (int j = tid; j < topk; j += kWaves * 64) {
     const float I = Il[j];
@@ -162,7 +171,7 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kl_bf16_kernel(
       const float ls = I - lsum;                                  // log student
       const float p = prow[j];
       if (p > 0.0f) lpart += p * (__log2f(p) * kLn2 - ls);
-      d = gt * (__builtin_amdgcn_exp2f(ls * kLog2e) - p);
+      d = gt * (__builtin_amdgcn_exp2f(ls * kLog2e) * pmass - p);
     }
     Il[j] = d;                                                    // every thread owns its own j
   }
@@ -312,14 +321,23 @@ __global__ __launch_bounds__(kNT) void indexer_kl_f32_kernel(
   if (L == 0) red[w] = m;
   __syncthreads();
   m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  float se = 0.0f;
-  for (int j = tid; j < topk; j += kNT) se += sm[j] > -__builtin_huge_valf() ? expf(sm[j] - m) : 0.0f;
+  float se = 0.0f, pm = 0.0f;
+  for (int j = tid; j < topk; j += kNT) {
+    if (sm[j] > -__builtin_huge_valf()) {
+      se += expf(sm[j] - m);
+      pm += teacher[(int64_t)t * topk + j];
+    }
+  }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) se += __shfl_xor(se, off, 64);
-  if (L == 0) red[4 + w] = se;
+  for (int off = 32; off >= 1; off >>= 1) {
+    se += __shfl_xor(se, off, 64);
+    pm += __shfl_xor(pm, off, 64);
+  }
+  if (L == 0) { red[4 + w] = se; red[12 + w] = pm; }
   __syncthreads();
   const bool any = m > -__builtin_huge_valf();
   const float lsum = any ? m + logf(red[4] + red[5] + red[6] + red[7]) : 0.0f;
+  const float pmass = red[12] + red[13] + red[14] + red[15];
   const float gt = grad ? grad[t] : 1.0f;
   float lpart = 0.0f;
   for (int j = tid; j < topk; j += kNT) {
@@ -327,7 +345,7 @@ __global__ __launch_bounds__(kNT) void indexer_kl_f32_kernel(
     if (sm[j] > -__builtin_huge_valf()) {
       const float ls = sm[j] - lsum, p = teacher[(int64_t)t * topk + j];
       if (p > 0.0f) lpart += p * (logf(p) - ls);
-      d = gt * (expf(ls) - p);
+      d = gt * (expf(ls) * pmass - p);
     }
     sm[j] = d;
   }

@@ -92,10 +92,11 @@ sa_status sa_indexer_scores(const void* q_I, const void* k_I, const float* w, in
   if (H_I < 1 || D_I < 1 || block_size < 1 || topk < 0) return SA_ERR_SHAPE;
   if (H_I != 4 && H_I != 8 && H_I != 16 && H_I != 32 && H_I != 64) return SA_ERR_UNSUPPORTED;
   if (D_I != 64 && D_I != 128) return SA_ERR_UNSUPPORTED;
-  if (block_size != 1 && block_size != 16 && block_size != 32 && block_size != 64 &&
-      block_size != 128 && block_size != 256)
+  if (block_size != 1 && block_size != 2 && block_size != 4 && block_size != 8 && block_size != 16 &&
+      block_size != 32 && block_size != 64 && block_size != 128 && block_size != 256)
     return SA_ERR_UNSUPPORTED;
   if (force_own_block && block_size == 1) return SA_ERR_UNSUPPORTED;
+  if (force_own_block < 0 || force_own_block > 1) return SA_ERR_UNSUPPORTED;   // 2: dense + select
   const bool dense = topk == 0;
   if (T == 0) return SA_OK;
   if (!q_I || !k_I || !w) return SA_ERR_NULL;
@@ -131,6 +132,7 @@ sa_status sa_topk_select(const float* vals, const int32_t* cand_idx, int64_t ld,
                          int32_t* out_idx, float* out_val, void* stream) {
   if (T < 0 || ld < 1 || topk < 1 || block_size < 1) return SA_ERR_SHAPE;
   if (ld % 4 != 0) return SA_ERR_SHAPE;
+  if (force_own_block < 0 || force_own_block > 2) return SA_ERR_UNSUPPORTED;
   if (topk > 65536) return SA_ERR_UNSUPPORTED;
   int32_t width = 0;
   if (cand_idx) {
@@ -157,7 +159,8 @@ sa_status sa_topk_select(const float* vals, const int32_t* cand_idx, int64_t ld,
 
 sa_status sa_sparse_mla_fwd(const void* q, const void* kv, const int32_t* idx, int dtype,
                             int32_t T, int32_t S, int32_t H, int32_t d_qk, int32_t d_v,
-                            int32_t topk, float scale, void* out, float* lse, void* stream) {
+                            int32_t topk, float scale, const float* sink, void* out, float* lse,
+                            void* stream) {
   if (dtype != SA_F32 && dtype != SA_BF16) return SA_ERR_DTYPE;
   if (T < 0 || S < 1 || H < 1 || topk < 1 || d_qk < 1 || d_v < 1) return SA_ERR_SHAPE;
   if (d_qk != 512 && d_qk != 576) return SA_ERR_UNSUPPORTED;
@@ -175,13 +178,13 @@ sa_status sa_sparse_mla_fwd(const void* q, const void* kv, const int32_t* idx, i
   if (!aligned16(q) || !aligned16(kv) || !aligned16(out)) return SA_ERR_ALIGN;
   SA_DEBUG_RETURN(debug_range(idx, (int64_t)T * topk, -1, S, reinterpret_cast<hipStream_t>(stream)));
   return launch_status(sa::launch_sparse_mla(q, kv, idx, dtype == SA_BF16, T, S, H, d_qk, d_v, topk,
-                                             scale, out, lse, reinterpret_cast<hipStream_t>(stream)));
+                                             scale, sink, out, lse, reinterpret_cast<hipStream_t>(stream)));
 }
 
 sa_status sa_sparse_mla_bwd(const void* q, const void* kv, const int32_t* idx, const void* dout,
                             const float* lse, int dtype, int32_t T, int32_t S, int32_t H,
-                            int32_t d_qk, int32_t d_v, int32_t topk, float scale, void* dq,
-                            float* dkv, void* stream) {
+                            int32_t d_qk, int32_t d_v, int32_t topk, float scale, const float* sink,
+                            void* dq, float* dkv, float* dsink, void* stream) {
   if (dtype != SA_F32 && dtype != SA_BF16) return SA_ERR_DTYPE;
   if (T < 0 || S < 1 || H < 1 || topk < 1 || d_qk < 1 || d_v < 1) return SA_ERR_SHAPE;
   if (d_qk != 512 && d_qk != 576) return SA_ERR_UNSUPPORTED;
@@ -189,13 +192,14 @@ sa_status sa_sparse_mla_bwd(const void* q, const void* kv, const int32_t* idx, c
   if (H > 128) return SA_ERR_UNSUPPORTED;
   if (dtype == SA_F32 && topk > 8192) return SA_ERR_UNSUPPORTED;   // per-slot terms staged in LDS
   if (!dkv) return SA_ERR_NULL;
+  if (dsink && !sink) return SA_ERR_NULL;
   if (T > 0 && (!q || !kv || !idx || !dout || !lse || !dq)) return SA_ERR_NULL;
   if (!aligned16(q) || !aligned16(kv) || !aligned16(dout) || !aligned16(dq) || !aligned16(dkv))
     return SA_ERR_ALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (T > 0) SA_DEBUG_RETURN(debug_range(idx, (int64_t)T * topk, -1, S, s));
   return launch_status(sa::launch_sparse_mla_bwd(q, kv, idx, dout, lse, dtype == SA_BF16, T, S, H, d_qk,
-                                                 d_v, topk, scale, dq, dkv, s));
+                                                 d_v, topk, scale, sink, dq, dkv, dsink, s));
 }
 
 sa_status sa_block_sparse_gqa_fwd(const void* q, const void* k, const void* v, const int32_t* blk,
@@ -282,6 +286,35 @@ sa_status sa_block_sparse_gqa_bwd(const void* q, const void* k, const void* v, c
   return launch_status(sa::launch_block_gqa_bwd(q, k, v, blk, dtype == SA_BF16, T, cu_seqlens, num_seqs,
                                                 Hq, Hkv, D, block_size, nblk, scale, dout, lse, dq, dk,
                                                 dv, s));
+}
+
+sa_status sa_kpool_expand(const int32_t* pools, int32_t T, const int32_t* cu_seqlens, int32_t num_seqs,
+                          int32_t max_seqlen, int32_t kp, int32_t pool, int32_t* out, void* stream) {
+  int32_t widest = 0;
+  sa_status st = check_layout(T, cu_seqlens, num_seqs, max_seqlen, &widest);
+  if (st != SA_OK) return st;
+  if (kp < 1 || pool < 1) return SA_ERR_SHAPE;
+  if ((int64_t)kp * pool + pool - 1 > INT32_MAX) return SA_ERR_UNSUPPORTED;
+  if (T == 0) return SA_OK;
+  if (!pools || !out) return SA_ERR_NULL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  SA_DEBUG_RETURN(debug_offsets(cu_seqlens, num_seqs, T, max_seqlen, s));
+  return launch_status(sa::launch_kpool_expand(pools, cu_seqlens, num_seqs, T, kp, pool, out, s));
+}
+
+sa_status sa_append_window(const int32_t* idx, int32_t T, const int32_t* cu_seqlens, int32_t num_seqs,
+                           int32_t max_seqlen, int32_t k, int32_t window, int32_t offset, int32_t* out,
+                           void* stream) {
+  int32_t widest = 0;
+  sa_status st = check_layout(T, cu_seqlens, num_seqs, max_seqlen, &widest);
+  if (st != SA_OK) return st;
+  if (k < 0 || window < 0 || k + window < 1 || offset < 0) return SA_ERR_SHAPE;
+  if ((int64_t)offset + T > INT32_MAX) return SA_ERR_UNSUPPORTED;
+  if (T == 0) return SA_OK;
+  if ((k > 0 && !idx) || !out) return SA_ERR_NULL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  SA_DEBUG_RETURN(debug_offsets(cu_seqlens, num_seqs, T, max_seqlen, s));
+  return launch_status(sa::launch_append_window(idx, cu_seqlens, num_seqs, T, k, window, offset, out, s));
 }
 
 }  // extern "C"

@@ -22,13 +22,14 @@ hipError_t launch_topk_select_counted(const float* vals, const int32_t* cand, co
 // fits one workgroup for this head count, width and top-k.
 bool sparse_mla_bf16_fits(int H, int d_qk, int topk);
 hipError_t launch_sparse_mla(const void* q, const void* kv, const int32_t* idx, bool bf16, int T,
-                             int S, int H, int d_qk, int d_v, int topk, float scale, void* out,
-                             float* lse, hipStream_t st);
+                             int S, int H, int d_qk, int d_v, int topk, float scale, const float* sink,
+                             void* out, float* lse, hipStream_t st);
 
 // sparse_mla_bwd.hip: zeroes dkv [S, d_qk] (fp32), then accumulates into it.
 hipError_t launch_sparse_mla_bwd(const void* q, const void* kv, const int32_t* idx, const void* dout,
                                  const float* lse, bool bf16, int T, int S, int H, int d_qk, int d_v,
-                                 int topk, float scale, void* dq, float* dkv, hipStream_t st);
+                                 int topk, float scale, const float* sink, void* dq, float* dkv,
+                                 float* dsink, hipStream_t st);
 
 // indexer.hip
 hipError_t launch_indexer_dense(const void* q, const void* k, const float* w, bool bf16, int T,
@@ -70,6 +71,12 @@ hipError_t launch_indexer_kl(const void* qI, const void* kI, const float* wI, co
                              const float* teacher, const float* grad, bool bf16, int T, int S, int H_I,
                              int D_I, int topk, float* loss, void* dq, float* dw, float* dk,
                              hipStream_t st);
+
+// routes.hip: k-pool expansion with the incomplete tail pool; selected slots + window.
+hipError_t launch_kpool_expand(const int32_t* pools, const int32_t* cu, int nseq, int T, int kp, int P,
+                               int32_t* out, hipStream_t st);
+hipError_t launch_append_window(const int32_t* idx, const int32_t* cu, int nseq, int T, int k, int W,
+                                int offset, int32_t* out, hipStream_t st);
 
 // block_gqa_bwd.hip: zeroes dk and dv [T, Hkv, D] (fp32), then accumulates into them.
 hipError_t launch_block_gqa_bwd(const void* q, const void* k, const void* v, const int32_t* blk,

@@ -106,7 +106,8 @@ template <int NW, int DQK, int NST, int NKL, bool NEG>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                             const int32_t* __restrict__ idx, int H, int topk, float scale_log2,
-                            uint16_t* __restrict__ out, float* __restrict__ lse) {
+                            const float* __restrict__ sink, uint16_t* __restrict__ out,
+                            float* __restrict__ lse) {
   constexpr int NK = DQK / 16;            // MFMA k-steps of S^T = K . Q^T
   constexpr int NKM = 32;                 // k-steps in the main region
   constexpr int NKR = NK - NKL;           // k-steps whose q slices stay in VGPRs
@@ -456,10 +457,26 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
   // ---- epilogue: per-head 1/l through LDS, normalise, write bf16 out and lse
   const float2_t lh = lane_halves(l_run);
   const float l_tot = lh.x + lh.y;
-  if (hl == 0) s_inv[head] = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  if (lse && hl == 0 && head_ok) {
-    lse[(int64_t)t * H + head] =
-        l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : -__builtin_huge_valf();
+  if (!sink) {
+    if (hl == 0) s_inv[head] = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    if (lse && hl == 0 && head_ok) {
+      lse[(int64_t)t * H + head] =
+          l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : -__builtin_huge_valf();
+    }
+  } else if (hl == 0) {
+    // a sink logit joins the denominator: relative to M = max(m_ref, sink) it is
+    // l_tot 2^(m_ref - M) + 2^(sink - M); the slots' weights are O 2^(m_ref - M) / that
+    const float s2 = (head_ok ? sink[head] : 0.0f) * kLog2e;
+    if (l_tot > 0.0f) {
+      const float M = __builtin_elementwise_maximum(m_ref, s2);
+      const float a = __builtin_amdgcn_exp2f(m_ref - M);
+      const float den = l_tot * a + __builtin_amdgcn_exp2f(s2 - M);
+      s_inv[head] = a / den;
+      if (lse && head_ok) lse[(int64_t)t * H + head] = (M + __log2f(den)) * kLn2;
+    } else {
+      s_inv[head] = 0.0f;                              // no slot: out = 0, lse = sink
+      if (lse && head_ok) lse[(int64_t)t * H + head] = sink[head];
+    }
   }
   __syncthreads();
   uint16_t* __restrict__ orow = out + (int64_t)t * H * 512;
@@ -482,8 +499,8 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 template <int NT>
 __global__ __launch_bounds__(NT) void sparse_mla_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kv, const int32_t* __restrict__ idx,
-    int H, int d_qk, int d_v, int topk, float scale, float* __restrict__ out,
-    float* __restrict__ lse) {
+    int H, int d_qk, int d_v, int topk, float scale, const float* __restrict__ sink,
+    float* __restrict__ out, float* __restrict__ lse) {
   extern __shared__ float sm[];          // [topk] probabilities, then [NT/64] reduce slots
   float* red = sm + topk;
   const int t = blockIdx.x / H, h = blockIdx.x % H;
@@ -508,6 +525,8 @@ __global__ __launch_bounds__(NT) void sparse_mla_f32_kernel(
   __syncthreads();
   mx = red[0];
   for (int i = 1; i < NT / 64; ++i) mx = fmaxf(mx, red[i]);
+  const float sk = sink ? sink[h] : -__builtin_huge_valf();   // sink logit (none: -inf)
+  mx = fmaxf(mx, sk);
   __syncthreads();
   float ps = 0.0f;
   for (int j = tid; j < topk; j += NT) {
@@ -519,7 +538,7 @@ __global__ __launch_bounds__(NT) void sparse_mla_f32_kernel(
   for (int off = 32; off >= 1; off >>= 1) ps += __shfl_xor(ps, off, 64);
   if (L == 0) red[w] = ps;
   __syncthreads();
-  float Z = 0.0f;
+  float Z = sink ? expf(sk - mx) : 0.0f;
   for (int i = 0; i < NT / 64; ++i) Z += red[i];
   const float inv = Z > 0.0f ? 1.0f / Z : 0.0f;
   for (int c = tid; c < d_v; c += NT) {
@@ -549,7 +568,7 @@ int waves_for(int H) { return H <= 32 ? 1 : (H <= 64 ? 2 : 4); }
 
 template <int NW, int DQK>
 hipError_t launch_bf16(const void* q, const void* kv, const int32_t* idx, int T, int H, int topk,
-                       float scale, void* out, float* lse, hipStream_t st) {
+                       float scale, const float* sink, void* out, float* lse, hipStream_t st) {
   constexpr int NKL = q_in_lds<NW, DQK>();
   const size_t shm = mla_lds_bytes<NW, DQK, kStages, NKL>(topk);
   if (shm > kLdsLimit) return hipErrorInvalidValue;
@@ -558,17 +577,18 @@ hipError_t launch_bf16(const void* q, const void* kv, const int32_t* idx, int T,
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(T), dim3(NW * 64), shm, st, (const uint16_t*)q, (const uint16_t*)kv,
-                     idx, H, topk, scale * kLog2e, (uint16_t*)out, lse);
+                     idx, H, topk, scale * kLog2e, sink, (uint16_t*)out, lse);
   return hipGetLastError();
 }
 
 template <int DQK>
 hipError_t dispatch_bf16(const void* q, const void* kv, const int32_t* idx, int T, int H,
-                         int topk, float scale, void* out, float* lse, hipStream_t st) {
+                         int topk, float scale, const float* sink, void* out, float* lse,
+                         hipStream_t st) {
   switch (waves_for(H)) {
-    case 1: return launch_bf16<1, DQK>(q, kv, idx, T, H, topk, scale, out, lse, st);
-    case 2: return launch_bf16<2, DQK>(q, kv, idx, T, H, topk, scale, out, lse, st);
-    default: return launch_bf16<4, DQK>(q, kv, idx, T, H, topk, scale, out, lse, st);
+    case 1: return launch_bf16<1, DQK>(q, kv, idx, T, H, topk, scale, sink, out, lse, st);
+    case 2: return launch_bf16<2, DQK>(q, kv, idx, T, H, topk, scale, sink, out, lse, st);
+    default: return launch_bf16<4, DQK>(q, kv, idx, T, H, topk, scale, sink, out, lse, st);
   }
 }
 
@@ -585,18 +605,18 @@ bool sparse_mla_bf16_fits(int H, int d_qk, int topk) {
 }
 
 hipError_t launch_sparse_mla(const void* q, const void* kv, const int32_t* idx, bool bf16, int T,
-                             int S, int H, int d_qk, int d_v, int topk, float scale, void* out,
-                             float* lse, hipStream_t st) {
+                             int S, int H, int d_qk, int d_v, int topk, float scale, const float* sink,
+                             void* out, float* lse, hipStream_t st) {
   (void)S;
   if (T == 0) return hipSuccess;
   if (bf16) {
-    if (d_qk == 576) return dispatch_bf16<576>(q, kv, idx, T, H, topk, scale, out, lse, st);
-    return dispatch_bf16<512>(q, kv, idx, T, H, topk, scale, out, lse, st);
+    if (d_qk == 576) return dispatch_bf16<576>(q, kv, idx, T, H, topk, scale, sink, out, lse, st);
+    return dispatch_bf16<512>(q, kv, idx, T, H, topk, scale, sink, out, lse, st);
   }
   constexpr int NT = 256;
   const size_t shm = (size_t)(topk + NT / 64) * sizeof(float);
   hipLaunchKernelGGL((sparse_mla_f32_kernel<NT>), dim3(T * H), dim3(NT), shm, st,
-                     (const float*)q, (const float*)kv, idx, H, d_qk, d_v, topk, scale,
+                     (const float*)q, (const float*)kv, idx, H, d_qk, d_v, topk, scale, sink,
                      (float*)out, lse);
   return hipGetLastError();
 }

@@ -82,7 +82,8 @@ template <int DQK>
 __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, int H, int topk, float scale,
-    uint16_t* __restrict__ dq, float* __restrict__ dkv) {
+    const float* __restrict__ sink, uint16_t* __restrict__ dq, float* __restrict__ dkv,
+    float* __restrict__ dsink) {
   constexpr int KRB = krow_bytes<DQK>();
   constexpr int DRB = drow_bytes();
   constexpr int NK = DQK / 32;            // 32-wide k-steps of S
@@ -210,6 +211,14 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_bf16_kernel(
     for (int ww = 0; ww < kWaves; ++ww) d += dD[ww * kHG + 4 * g + i];
     Dh[i] = d;
   }
+  // the sink's probability exp(sink - lse) times -D is its logit's gradient
+  if (dsink && w == 0 && n == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = h0 + 4 * g + i;
+      if (hh < H) atomicAdd(dsink + hh, -__builtin_amdgcn_exp2f(sink[hh] * kLog2e - lse2[i]) * Dh[i]);
+    }
+  }
 
   floatx4v_t acc[NCB];   // dq^T: channel block cb, rows 16 cb + 4 g .. +3, column head n
 #pragma unroll
@@ -298,7 +307,8 @@ constexpr int kNT = 256;
 __global__ __launch_bounds__(kNT) void sparse_mla_bwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kv, const int32_t* __restrict__ idx,
     const float* __restrict__ dout, const float* __restrict__ lse, int H, int d_qk, int d_v,
-    int topk, float scale, float* __restrict__ dq, float* __restrict__ dkv) {
+    int topk, float scale, const float* __restrict__ sink, float* __restrict__ dq,
+    float* __restrict__ dkv, float* __restrict__ dsink) {
   extern __shared__ float sm[];        // [topk] p_j, then [topk] dp_j, then [kNT / 64] reduce slots
   float* sdp = sm + topk;
   float* red = sdp + topk;
@@ -330,6 +340,7 @@ __global__ __launch_bounds__(kNT) void sparse_mla_bwd_f32_kernel(
   __syncthreads();
   float D = 0.0f;
   for (int i = 0; i < kNT / 64; ++i) D += red[i];
+  if (dsink && tid == 0) atomicAdd(dsink + h, -expf(sink[h] - l) * D);
   // ds_j = scale p_j (dp_j - D); dkv by atomics; sm[j] becomes ds_j
   for (int j = tid; j < topk; j += kNT) {
     const int r = ir[j];
@@ -454,15 +465,15 @@ __global__ void zero_f32_kernel(float* __restrict__ p, int64_t n) {
 
 template <int DQK>
 hipError_t launch_bwd_bf16(const void* q, const void* kv, const int32_t* idx, const void* dout,
-                           const float* lse, int T, int H, int topk, float scale, void* dq,
-                           float* dkv, hipStream_t st) {
+                           const float* lse, int T, int H, int topk, float scale, const float* sink,
+                           void* dq, float* dkv, float* dsink, hipStream_t st) {
   const size_t shm = bwd_lds_bytes<DQK>();
   hipError_t e = hipFuncSetAttribute((const void*)sparse_mla_bwd_bf16_kernel<DQK>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((sparse_mla_bwd_bf16_kernel<DQK>), dim3(T, (H + kHG - 1) / kHG), dim3(kWaves * 64),
                      shm, st, (const uint16_t*)q, (const uint16_t*)kv, idx, (const uint16_t*)dout,
-                     lse, H, topk, scale, (uint16_t*)dq, dkv);
+                     lse, H, topk, scale, sink, (uint16_t*)dq, dkv, dsink);
   return hipGetLastError();
 }
 
@@ -470,22 +481,24 @@ hipError_t launch_bwd_bf16(const void* q, const void* kv, const int32_t* idx, co
 
 hipError_t launch_sparse_mla_bwd(const void* q, const void* kv, const int32_t* idx, const void* dout,
                                  const float* lse, bool bf16, int T, int S, int H, int d_qk, int d_v,
-                                 int topk, float scale, void* dq, float* dkv, hipStream_t st) {
+                                 int topk, float scale, const float* sink, void* dq, float* dkv,
+                                 float* dsink, hipStream_t st) {
   const int64_t nkv = (int64_t)S * d_qk;
   hipLaunchKernelGGL(zero_f32_kernel, dim3(1024), dim3(256), 0, st, dkv, nkv);
+  if (dsink) hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(256), 0, st, dsink, (int64_t)H);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || T == 0) return e;
   if (bf16) {
-    if (d_qk == 576) return launch_bwd_bf16<576>(q, kv, idx, dout, lse, T, H, topk, scale, dq, dkv, st);
-    return launch_bwd_bf16<512>(q, kv, idx, dout, lse, T, H, topk, scale, dq, dkv, st);
+    if (d_qk == 576) return launch_bwd_bf16<576>(q, kv, idx, dout, lse, T, H, topk, scale, sink, dq, dkv, dsink, st);
+    return launch_bwd_bf16<512>(q, kv, idx, dout, lse, T, H, topk, scale, sink, dq, dkv, dsink, st);
   }
   const size_t shm = (size_t)(2 * topk + kNT / 64) * sizeof(float);
   e = hipFuncSetAttribute((const void*)sparse_mla_bwd_f32_kernel,
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(sparse_mla_bwd_f32_kernel, dim3(T * H), dim3(kNT), shm, st, (const float*)q,
-                     (const float*)kv, idx, (const float*)dout, lse, H, d_qk, d_v, topk, scale,
-                     (float*)dq, dkv);
+                     (const float*)kv, idx, (const float*)dout, lse, H, d_qk, d_v, topk, scale, sink,
+                     (float*)dq, dkv, dsink);
   return hipGetLastError();
 }
 

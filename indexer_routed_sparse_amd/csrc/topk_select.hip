@@ -305,9 +305,11 @@ SA_DEVICE void select_row(int t, const RowArgs& a, S& sm) {
   } else {
     if (a.cu) start = seq_start_of(a.cu, a.nseq, t);
     const int off = t - start;
-    n = (a.block_size == 1) ? off + 1 : off / a.block_size + 1;
+    n = (a.block_size == 1)   ? off + 1
+        : a.force_own == 2    ? (off + 1) / a.block_size     // complete blocks only
+                              : off / a.block_size + 1;
   }
-  const bool own = !CAND && a.block_size > 1 && a.force_own;
+  const bool own = !CAND && a.block_size > 1 && a.force_own == 1;
   const int n1 = own ? n - 1 : n;          // competing positions
   const int k1 = own ? topk - 1 : topk;    // slots they compete for
   const float* __restrict__ row = a.vals + (int64_t)t * a.ld;

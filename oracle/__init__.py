@@ -619,12 +619,15 @@ def complete_block_topk(scores, k: int, block_size: int, cu_seqlens=None, rows=N
     """
     scores = np.asarray(scores)
     rows = np.arange(scores.shape[0]) if rows is None else np.asarray(rows)
-    T = int(_i64(cu_seqlens)[-1]) if cu_seqlens is not None else scores.shape[0]
-    start, _ = seq_bounds(T, cu_seqlens)
+    if cu_seqlens is None:
+        starts = np.zeros(len(rows), dtype=np.int64)
+    else:
+        cu = _i64(cu_seqlens)
+        starts = seq_bounds(int(cu[-1]), cu)[0][rows]
     idx = np.full((len(rows), k), -1, dtype=np.int32)
     val = np.full((len(rows), k), NEG_INF, dtype=np.float32)
     for r, t in enumerate(rows):
-        n = (int(t - start[t]) + 1) // block_size
+        n = (int(t - starts[r]) + 1) // block_size
         idx[r], val[r] = topk_select_row(scores[r], n, k)
     return idx, val
 
@@ -633,11 +636,11 @@ def kpool_expand(pool_idx, pool: int, cu_seqlens=None, T: int | None = None):
     """Token slots of a k-pool route, with the query's incomplete tail pool appended.
 
     Same passage as ``complete_block_topk`` (width 2048 + 3 = 2051 for 512 pools of
-    four keys). Reading: row t's selected pools c (local ids, -1 skipped) each give
-    their keys start + c*P .. start + c*P + P - 1 (global rows), in slot order; then
-    the keys of the query's own pool when it is incomplete (the o % P + 1 keys
-    start + (o // P) * P .. t, o = t - start, when o % P != P - 1) fill the last P - 1
-    slots, -1 padded. Width k*P + P - 1.
+    four keys). Reading: slot i of row t's pool route (a local pool id c, or -1) gives
+    the P slots i*P .. i*P + P - 1, holding the keys start + c*P .. start + c*P + P - 1
+    (global rows; -1 for a -1 pool); then the keys of the query's own pool when it is
+    incomplete (the o % P + 1 keys start + (o // P) * P .. t, o = t - start, when
+    o % P != P - 1) fill the last P - 1 slots, -1 padded. Width k*P + P - 1.
     """
     pool_idx = _i64(pool_idx)
     Tn = pool_idx.shape[0] if T is None else T
@@ -646,11 +649,9 @@ def kpool_expand(pool_idx, pool: int, cu_seqlens=None, T: int | None = None):
     out = np.full((Tn, k * pool + pool - 1), -1, dtype=np.int32)
     for t in range(Tn):
         s0 = int(start[t])
-        toks = []
-        for c in pool_idx[t]:
+        for i, c in enumerate(pool_idx[t]):
             if c >= 0:
-                toks.extend(range(s0 + c * pool, s0 + c * pool + pool))
-        out[t, :len(toks)] = toks
+                out[t, i * pool:(i + 1) * pool] = range(s0 + c * pool, s0 + c * pool + pool)
         o = t - s0
         if o % pool != pool - 1:
             tail = list(range(s0 + (o // pool) * pool, t + 1))

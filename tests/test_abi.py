@@ -37,12 +37,12 @@ def test_debug_library_exports_every_declared_symbol():
     for n in _declared():
         assert hasattr(lib, n), n
     lib.sa_abi_version.restype = ctypes.c_int
-    assert lib.sa_abi_version() == 2
+    assert lib.sa_abi_version() == 3
 
 
 def test_version_and_status_strings():
     import indexer_routed_sparse_amd as sa
-    assert sa.abi_version() == 2
+    assert sa.abi_version() == 3
     for code in range(8):
         assert sa.status_string(code).startswith("SA_")
     assert "unknown" in sa.status_string(99)
@@ -74,11 +74,13 @@ MIS = P(0x10004)
 ])
 def test_sparse_mla_rejects(args, code):
     lib = _lib()
-    assert lib.sa_sparse_mla_fwd(*args, None) == code
+    a = list(args)
+    a.insert(11, None)                                  # sink
+    assert lib.sa_sparse_mla_fwd(*a, None) == code
 
 
 def test_sparse_mla_empty_is_ok():
-    assert _lib().sa_sparse_mla_fwd(None, None, None, 1, 0, 4, 16, 576, 512, 8, 1.0, None, None, None) == 0
+    assert _lib().sa_sparse_mla_fwd(None, None, None, 1, 0, 4, 16, 576, 512, 8, 1.0, None, None, None, None) == 0
 
 
 @pytest.mark.parametrize("args,code", [
@@ -102,6 +104,7 @@ def test_topk_select_rejects(args, code):
     ((FAKE, FAKE, FAKE, 1, 8, None, 0, 0, 3, 128, 1, FAKE, 8, 0, 0, None, None), 5),   # H_I
     ((FAKE, FAKE, FAKE, 1, 8, None, 0, 0, 64, 96, 1, FAKE, 8, 0, 0, None, None), 5),   # D_I
     ((FAKE, FAKE, FAKE, 1, 8, None, 0, 0, 64, 128, 48, FAKE, 8, 0, 0, None, None), 5), # B
+    ((FAKE, FAKE, FAKE, 1, 8, None, 0, 0, 64, 128, 3, FAKE, 8, 0, 0, None, None), 5),  # B odd
     ((FAKE, FAKE, FAKE, 1, 8, None, 0, 0, 64, 128, 1, FAKE, 4, 0, 0, None, None), 2),  # ld small
     ((FAKE, FAKE, FAKE, 1, 8, None, 0, 0, 64, 128, 1, None, 0, 4096, 0, FAKE, None), 5),  # topk
     ((FAKE, FAKE, FAKE, 1, 8, None, 0, 0, 64, 128, 1, FAKE, 8, 4, 0, FAKE, None), 2),  # both modes

@@ -260,7 +260,7 @@ def test_indexer_dense_normal_within_bound(sa, name, T):
     assert np.all(np.abs(got[fin] - ref[fin]) <= 2e-5 * bound[fin] + 1e-30)
 
 
-@pytest.mark.parametrize("B", [16, 32, 128, 256])
+@pytest.mark.parametrize("B", [2, 4, 8, 16, 32, 128, 256])
 def test_indexer_block_sizes_integer_exact(sa, B):
     """Block mode at every other supported block size (the block max runs over a lane
     group of B lanes up to 64, and across key tiles above): dense block scores equal
@@ -731,7 +731,7 @@ def test_debug_build_rejects_out_of_range_contents(sa):
     out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=DEV)
 
     def mla(ix):
-        return dbg.sa_sparse_mla_fwd(p(q), p(kv), p(ix), 1, T, S, H, 576, 512, k, 0.05, p(out), None, stream)
+        return dbg.sa_sparse_mla_fwd(p(q), p(kv), p(ix), 1, T, S, H, 576, 512, k, 0.05, None, p(out), None, stream)
 
     assert mla(idx) == 0
     ref = sa.sparse_mla(q, kv, idx, 0.05, with_lse=False)

@@ -819,6 +819,14 @@ def test_complete_block_topk_brute_force():
         assert got[t].tolist() == _brute_topk(sc[t], n, k)
     # offsets 3 and 7 complete their own block, which then competes
     assert (3 + 1) // B == 1 and (2 + 1) // B == 0
+    # a row subset (score row r belongs to query rows[r]) gives the same rows
+    sub = np.array([20, 3, 11, 25])
+    part, _ = oracle.complete_block_topk(sc[sub], k, B, cu_seqlens=cu, rows=sub)
+    np.testing.assert_array_equal(part, got[sub])
+    sc2 = np.round(rng.standard_normal((T, 8)) * 2).astype(np.float32)   # one sequence: 26 keys
+    one, _ = oracle.complete_block_topk(sc2[[7, 20]], k, B, rows=[7, 20])
+    full_one, _ = oracle.complete_block_topk(sc2, k, B)
+    np.testing.assert_array_equal(one, full_one[[7, 20]])
 
 
 def test_kpool_expand_hand_example():
@@ -832,6 +840,8 @@ def test_kpool_expand_hand_example():
     assert out.shape == (12, 11)
     assert out[9].tolist() == [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, -1]
     assert out[11].tolist() == [8, 9, 10, 11] + [-1] * 7        # offset 11: pool complete, no tail
+    pools[11] = [-1, 2]                                          # a -1 slot keeps its place
+    assert oracle.kpool_expand(pools, 4)[11].tolist() == [-1] * 4 + [8, 9, 10, 11] + [-1] * 3
     assert out[0].tolist() == [-1] * 8 + [0, -1, -1]             # offset 0: tail is the query
     assert oracle.kpool_expand(np.full((1, 512), -1), 4).shape[1] == 2051
     # packed sequences: ids are global rows
