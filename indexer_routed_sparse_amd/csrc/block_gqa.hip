@@ -25,9 +25,10 @@
 //     and read back transposed with ds_read_b64_tr_b16, in the key order of the S^T
 //     accumulator, which is P^T's operand layout;
 //   * online softmax in exp2 form, fp32 accumulation, no atomics.
-// fp32 inputs use a plain scalar kernel with the same definition.
+// fp32 inputs run a one-wave kernel on 16x16x4 fp32 MFMAs (attn_f32.h).
 #include <type_traits>
 
+#include "attn_f32.h"
 #include "sa_common.h"
 #include "sa_kernels.h"
 
@@ -255,114 +256,55 @@ __global__ __launch_bounds__(kWavesPerGroup * 64) void block_gqa_bf16_kernel(
   }
 }
 
-// fp32 inputs: one workgroup per (token, kv head); plain FMA arithmetic over the
-// deduplicated route, same definition.
-constexpr int kNT = 256;
-
+// fp32 inputs: one wave per (token, kv head) on 16x16x4 fp32 MFMAs (the wave routine
+// of attn_f32.h). The route becomes a list of 16-key sub-tiles as in the bf16 kernel,
+// the G query heads are the MFMA columns and key and value rows are read straight
+// from memory.
 template <int D>
-__global__ __launch_bounds__(kNT) void block_gqa_f32_kernel(
+__global__ __launch_bounds__(64) void block_gqa_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const int32_t* __restrict__ blk, const int32_t* __restrict__ cu, int nseq, int Hq, int Hkv,
     int B, int nblk, float scale_log2, float* __restrict__ out, float* __restrict__ lse) {
-  extern __shared__ float sm[];
-  const int G = Hq / Hkv;                  // q heads per kv head (<= 16)
-  float* sq = sm;                          // [G][D]   (pre-scaled q)
-  float* sk = sq + 16 * D;                 // [B][D+1]
-  float* sv = sk + B * (D + 1);            // [B][D]
-  float* sp = sv + B * D;                  // [G][B]   logits, then probabilities
-  float* salpha = sp + 16 * B;             // [G]
-  float* sl = salpha + 16;                 // [G]      running sums
-  float* smx = sl + 16;                    // [G]      running max
-
-  const int t = blockIdx.x;
-  const int g = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int start = cu ? seq_start_of(cu, nseq, t) : 0;
-  const int own = (t - start) / B;
-
-  for (int i = tid; i < G * D; i += kNT) {
-    const int h = i / D, d = i % D;
-    sq[i] = q[((int64_t)t * Hq + g * G + h) * D + d] * scale_log2;
+  constexpr int ldq = D + 4;
+  constexpr int kList16 = kMaxRoute * 8;  // 16-key sub-tiles per row: B <= 128 -> 8 per block
+  __shared__ __attribute__((aligned(16))) float sq[16 * ldq];
+  __shared__ int2 list[kList16];
+  const int t = blockIdx.x, g = blockIdx.y, L = threadIdx.x;
+  const int G = Hq / Hkv;
+  const int c = cu ? seq_start_of(cu, nseq, t) : 0;
+  const int own = (t - c) / B;
+  const int32_t* __restrict__ brow = blk + (int64_t)t * nblk;
+  int nsub = 0;
+  for (int base = 0; base < nblk; base += 64) {
+    const int j = base + L;
+    const int b = j < nblk ? brow[j] : -1;
+    bool ok = b >= 0 && b <= own;
+    for (int i = 0; i < j && ok; ++i) ok = brow[i] != b;   // a repeated block counts once
+    const int lo = c + b * B;
+    const int nk = ok ? min(B, t - lo + 1) : 0;
+    const int ns = (nk + 15) >> 4;
+    const uint32_t incl = wave_incl_scan((uint32_t)ns);
+    const int pos = nsub + (int)incl - ns;
+    for (int h = 0; h < ns; ++h) list[pos + h] = make_int2(lo + 16 * h, min(16, nk - 16 * h));
+    nsub += __shfl((int)incl, 63, 64);
   }
-  if (tid < 16) { sl[tid] = 0.0f; smx[tid] = -__builtin_huge_valf(); }
-  constexpr int kPer = (16 * D + kNT - 1) / kNT;
-  float acc[kPer];
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) acc[r] = 0.0f;
+  stage_q_f32<D>(q + ((int64_t)t * Hq + g * G) * D, G, sq);
   __syncthreads();
-
-  const int32_t* brow = blk + (int64_t)t * nblk;
+  WaveAttnF32<D, D> at;
+  at.init();
 #pragma unroll 1
-  for (int j = 0; j < nblk; ++j) {
-    const int b = brow[j];
-    if (b < 0 || b > own) continue;
-    bool dup = false;
-    for (int i = 0; i < j; ++i) dup = dup || brow[i] == b;
-    if (dup) continue;
-    const int lo = start + b * B;
-    const int nk = min(lo + B - 1, t) - lo + 1;   // causal keys in the block
-    for (int i = tid; i < nk * D; i += kNT) {
-      const int s = i / D, d = i % D;
-      const int64_t row = ((int64_t)(lo + s) * Hkv + g) * D + d;
-      sk[s * (D + 1) + d] = k[row];
-      sv[s * D + d] = v[row];
-    }
-    __syncthreads();
-    for (int i = tid; i < G * nk; i += kNT) {
-      const int h = i / nk, s = i % nk;
-      float a = 0.0f;
-      for (int d = 0; d < D; ++d) a = fmaf(sq[h * D + d], sk[s * (D + 1) + d], a);
-      sp[h * B + s] = a;
-    }
-    __syncthreads();
-    for (int h = tid >> 6; h < G; h += kNT / 64) {
-      const int L = tid & 63;
-      float m = -__builtin_huge_valf();
-      for (int s = L; s < nk; s += 64) m = fmaxf(m, sp[h * B + s]);
-      m = wave_max(m);
-      const float m_old = smx[h];
-      const float m_new = fmaxf(m_old, m);
-      float ps = 0.0f;
-      for (int s = L; s < nk; s += 64) {
-        const float p = exp2f(sp[h * B + s] - m_new);
-        sp[h * B + s] = p;
-        ps += p;
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) ps += __shfl_xor(ps, off, 64);
-      if (L == 0) {
-        const float al = exp2f(m_old - m_new);   // 0 on the first block
-        salpha[h] = al;
-        sl[h] = sl[h] * al + ps;
-        smx[h] = m_new;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-      const int i = tid + r * kNT;
-      if (i < G * D) {
-        const int h = i / D, d = i % D;
-        float a = acc[r] * salpha[h];
-        for (int s = 0; s < nk; ++s) a = fmaf(sp[h * B + s], sv[s * D + d], a);
-        acc[r] = a;
-      }
-    }
-    __syncthreads();
+  for (int i = 0; i < nsub; ++i) {
+    const int2 e = list[i];
+    auto keys = [&](int r, const float*& kr, const float*& vr) {
+      const int64_t row = ((int64_t)(e.x + (r < e.y ? r : 0)) * Hkv + g) * D;
+      kr = k + row;
+      vr = v + row;
+      return r < e.y;
+    };
+    at.tile(sq, ldq, scale_log2, keys);
   }
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int i = tid + r * kNT;
-    if (i < G * D) {
-      const int h = i / D, d = i % D;
-      const float l = sl[h];
-      out[((int64_t)t * Hq + g * G + h) * D + d] = l > 0.0f ? acc[r] / l : 0.0f;
-    }
-  }
-  if (lse && tid < G) {
-    const float l = sl[tid];
-    lse[(int64_t)t * Hq + g * G + tid] = l > 0.0f ? (smx[tid] + __log2f(l)) * kLn2 : -__builtin_huge_valf();
-  }
+  at.finish(G, nullptr, out + ((int64_t)t * Hq + g * G) * D, D,
+            lse ? lse + (int64_t)t * Hq + g * G : nullptr);
 }
 
 template <int D>
@@ -390,11 +332,7 @@ template <int D>
 hipError_t launch_f32(const void* q, const void* k, const void* v, const int32_t* blk, int T,
                       const int32_t* cu, int nseq, int Hq, int Hkv, int B, int nblk, float scale,
                       void* out, float* lse, hipStream_t st) {
-  const size_t shm = sizeof(float) * ((size_t)16 * D + (size_t)B * (D + 1) + (size_t)B * D + 16 * (size_t)B + 48);
-  hipError_t e = hipFuncSetAttribute((const void*)block_gqa_f32_kernel<D>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((block_gqa_f32_kernel<D>), dim3(T, Hkv), dim3(kNT), shm, st, (const float*)q,
+  hipLaunchKernelGGL((block_gqa_f32_kernel<D>), dim3(T, Hkv), dim3(64), 0, st, (const float*)q,
                      (const float*)k, (const float*)v, blk, cu, nseq, Hq, Hkv, B, nblk,
                      scale * kLog2e, (float*)out, lse);
   return hipGetLastError();

@@ -167,7 +167,7 @@ sa_status sa_sparse_mla_fwd(const void* q, const void* kv, const int32_t* idx, i
   if (d_v != 512) return SA_ERR_UNSUPPORTED;
   if (H > 128) return SA_ERR_UNSUPPORTED;
   if (dtype == SA_BF16 && H >= 16 && H % 16 != 0) return SA_ERR_UNSUPPORTED;
-  // the index row is staged in LDS (bf16) / the probabilities are (fp32)
+  // the index row is staged in LDS (bf16); fp32 keeps the bound of its backward
   if (topk > (dtype == SA_BF16 ? 4096 : 8192)) return SA_ERR_UNSUPPORTED;
   if (dtype == SA_BF16 && !sa::sparse_mla_bf16_fits(H, d_qk, topk)) return SA_ERR_UNSUPPORTED;
   // the bf16 kernel addresses the RoPE channels of gathered rows with 32-bit byte

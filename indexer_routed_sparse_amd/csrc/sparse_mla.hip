@@ -28,10 +28,11 @@
 //     O is never rescaled;
 //   * fp32 accumulation throughout; no atomics, so results are bitwise
 //     reproducible.
-// A plain fp32 kernel serves fp32 inputs.
+// fp32 inputs run a one-wave kernel on 16x16x4 fp32 MFMAs (attn_f32.h).
 #include <type_traits>
 
 #include "sa_common.h"
+#include "attn_f32.h"
 #include "sa_kernels.h"
 
 namespace sa {
@@ -495,61 +496,37 @@ void sparse_mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
   }
 }
 
-// fp32 inputs: one workgroup per (token, head); plain FMA arithmetic, same definition.
-template <int NT>
-__global__ __launch_bounds__(NT) void sparse_mla_f32_kernel(
+// fp32 inputs: one wave per (token, group of 16 heads) on 16x16x4 fp32 MFMAs (the
+// wave routine of attn_f32.h): the group's q rows sit in LDS, the selected kv rows are
+// read as key rows (all d_qk channels) and as value rows (the first 512), 16 slots at
+// a time; -1 slots and the slots past topk are holes.
+template <int DQK>
+__global__ __launch_bounds__(64) void sparse_mla_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kv, const int32_t* __restrict__ idx,
-    int H, int d_qk, int d_v, int topk, float scale, const float* __restrict__ sink,
-    float* __restrict__ out, float* __restrict__ lse) {
-  extern __shared__ float sm[];          // [topk] probabilities, then [NT/64] reduce slots
-  float* red = sm + topk;
-  const int t = blockIdx.x / H, h = blockIdx.x % H;
-  const int tid = threadIdx.x, w = tid >> 6, L = tid & 63;
-  const float* qr = q + ((int64_t)t * H + h) * d_qk;
-  const int32_t* ir = idx + (int64_t)t * topk;
-  float mx = -__builtin_huge_valf();
-  for (int j = tid; j < topk; j += NT) {
-    const int r = ir[j];
-    float lg = -__builtin_huge_valf();
-    if (r >= 0) {
-      const float* kr = kv + (int64_t)r * d_qk;
-      float acc = 0.0f;
-      for (int c = 0; c < d_qk; ++c) acc = fmaf(qr[c], kr[c], acc);
-      lg = acc * scale;
-    }
-    sm[j] = lg;
-    mx = fmaxf(mx, lg);
-  }
-  mx = wave_max(mx);
-  if (L == 0) red[w] = mx;
+    int H, int topk, float scale_log2, const float* __restrict__ sink, float* __restrict__ out,
+    float* __restrict__ lse) {
+  constexpr int ldq = DQK + 4;
+  __shared__ __attribute__((aligned(16))) float sq[16 * ldq];
+  const int t = blockIdx.x, h0 = 16 * (int)blockIdx.y;
+  const int nh = min(16, H - h0);
+  stage_q_f32<DQK>(q + ((int64_t)t * H + h0) * DQK, nh, sq);
   __syncthreads();
-  mx = red[0];
-  for (int i = 1; i < NT / 64; ++i) mx = fmaxf(mx, red[i]);
-  const float sk = sink ? sink[h] : -__builtin_huge_valf();   // sink logit (none: -inf)
-  mx = fmaxf(mx, sk);
-  __syncthreads();
-  float ps = 0.0f;
-  for (int j = tid; j < topk; j += NT) {
-    const float p = (mx == -__builtin_huge_valf()) ? 0.0f : expf(sm[j] - mx);
-    sm[j] = p;
-    ps += p;
+  const int32_t* __restrict__ ir = idx + (int64_t)t * topk;
+  WaveAttnF32<DQK, 512> at;
+  at.init();
+  const int nsub = (topk + 15) / 16;
+#pragma unroll 1
+  for (int i = 0; i < nsub; ++i) {
+    auto keys = [&](int r, const float*& kr, const float*& vr) {
+      const int j = 16 * i + r;
+      const int id = j < topk ? ir[j] : -1;
+      kr = vr = kv + (int64_t)(id >= 0 ? id : 0) * DQK;
+      return id >= 0;
+    };
+    at.tile(sq, ldq, scale_log2, keys);
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) ps += __shfl_xor(ps, off, 64);
-  if (L == 0) red[w] = ps;
-  __syncthreads();
-  float Z = sink ? expf(sk - mx) : 0.0f;
-  for (int i = 0; i < NT / 64; ++i) Z += red[i];
-  const float inv = Z > 0.0f ? 1.0f / Z : 0.0f;
-  for (int c = tid; c < d_v; c += NT) {
-    float acc = 0.0f;
-    for (int j = 0; j < topk; ++j) {
-      const int r = ir[j];
-      if (r >= 0) acc = fmaf(sm[j], kv[(int64_t)r * d_qk + c], acc);
-    }
-    out[((int64_t)t * H + h) * d_v + c] = acc * inv;
-  }
-  if (lse && tid == 0) lse[(int64_t)t * H + h] = Z > 0.0f ? mx + logf(Z) : -__builtin_huge_valf();
+  at.finish(nh, sink ? sink + h0 : nullptr, out + ((int64_t)t * H + h0) * 512, 512,
+            lse ? lse + (int64_t)t * H + h0 : nullptr);
 }
 
 constexpr int kStages = 2;
@@ -613,11 +590,13 @@ hipError_t launch_sparse_mla(const void* q, const void* kv, const int32_t* idx, 
     if (d_qk == 576) return dispatch_bf16<576>(q, kv, idx, T, H, topk, scale, sink, out, lse, st);
     return dispatch_bf16<512>(q, kv, idx, T, H, topk, scale, sink, out, lse, st);
   }
-  constexpr int NT = 256;
-  const size_t shm = (size_t)(topk + NT / 64) * sizeof(float);
-  hipLaunchKernelGGL((sparse_mla_f32_kernel<NT>), dim3(T * H), dim3(NT), shm, st,
-                     (const float*)q, (const float*)kv, idx, H, d_qk, d_v, topk, scale, sink,
-                     (float*)out, lse);
+  const dim3 grid(T, (H + 15) / 16);
+  if (d_qk == 576)
+    hipLaunchKernelGGL((sparse_mla_f32_kernel<576>), grid, dim3(64), 0, st, (const float*)q,
+                       (const float*)kv, idx, H, topk, scale * kLog2e, sink, (float*)out, lse);
+  else
+    hipLaunchKernelGGL((sparse_mla_f32_kernel<512>), grid, dim3(64), 0, st, (const float*)q,
+                       (const float*)kv, idx, H, topk, scale * kLog2e, sink, (float*)out, lse);
   return hipGetLastError();
 }
 

@@ -480,6 +480,29 @@ def test_sparse_mla_tiny_fp32(sa):
     close(lse.cpu().numpy(), rl, **F32_TOL, what="lse")
 
 
+@pytest.mark.parametrize("H,d_qk,k,with_sink", [(20, 576, 37, False), (40, 512, 300, True),
+                                                (1, 576, 16, True), (128, 576, 129, False)])
+def test_sparse_mla_fp32_shapes(sa, H, d_qk, k, with_sink):
+    """fp32 sparse MLA on its MFMA kernel: head counts that leave a partial 16-head
+    group, a slot count with a ragged last sub-tile, -1 slots, an all-invalid row and
+    the optional sink, against the oracle at the fp32 bar."""
+    T, S = 24, 700
+    g = torch.Generator().manual_seed(H * 7 + k)
+    q = torch.randn((T, H, d_qk), generator=g)
+    kv = torch.randn((S, d_qk), generator=g)
+    idx = torch.randint(0, S, (T, k), generator=g, dtype=torch.int32)
+    idx[torch.rand((T, k), generator=g) < 0.2] = -1
+    idx[3] = -1
+    sink = torch.randn(H, generator=g) if with_sink else None
+    scale = 1 / math.sqrt(d_qk)
+    out, lse = sa.sparse_mla(q.to(DEV), kv.to(DEV), idx.to(DEV), scale,
+                             sink=sink.to(DEV) if with_sink else None)
+    ro, rl = oracle.sparse_mla(q, kv, idx.numpy(), scale, sink=sink.numpy() if with_sink else None)
+    close(out.cpu().numpy(), ro, **F32_TOL, what="out")
+    close(lse.cpu().numpy(), rl, **F32_TOL, what="lse")
+    assert torch.all(out[3] == 0)
+
+
 @pytest.mark.parametrize("k", [65, 127])
 def test_sparse_mla_nope_unaligned(sa, k):
     wl = W["nope_unaligned"]
@@ -645,7 +668,8 @@ def test_block_gqa_full_size_thd_sampled(sa):
 
 @pytest.mark.parametrize("Hq,Hkv,D,B,dtype", [(32, 4, 128, 64, "bf16"), (8, 4, 128, 32, "bf16"),
                                               (4, 4, 64, 16, "bf16"), (16, 1, 128, 128, "bf16"),
-                                              (12, 2, 64, 48, "bf16"), (8, 2, 64, 32, "f32")])
+                                              (12, 2, 64, 48, "bf16"), (8, 2, 64, 32, "f32"),
+                                              (32, 4, 128, 64, "f32"), (16, 1, 128, 16, "f32")])
 def test_block_gqa_shapes_routes_with_repeats(sa, Hq, Hkv, D, B, dtype):
     """Head-group sizes 1..16, D 64/128, block sizes 16..128, THD with a sequence shorter
     than a block, and routes holding repeated blocks, blocks past the query's own and
