@@ -688,7 +688,7 @@ SA_DEVICE int wave_cut(uint32_t* keys, int32_t* ids, int n, int cap, int k, int 
 //     a kept one never wins and the strict filter is exact.
 // MODE kAppend (first pass of the two-pass selection): before the stream, the
 // workgroup scores a sample of kSample evenly spaced causal keys; each wave bisects
-// its token's sample for a pivot that about k plus four standard deviations of the
+// its token's sample for a pivot that about k plus 4.3 standard deviations of the
 // sample rank reach, then appends every key at or above it, in index order, to the
 // token's workspace row and records how many it appended. A row whose count falls
 // below k (or overflows the row) is marked -1 and redone by the kFused launch, so

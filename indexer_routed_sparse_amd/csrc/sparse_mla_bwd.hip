@@ -368,77 +368,113 @@ __global__ __launch_bounds__(kNT) void sparse_mla_bwd_f32_kernel(
 // Same layout as the backward's first pass (one workgroup per token and 16-head group,
 // four waves taking turns over 16-key sub-tiles); each group adds its 16 heads' share
 // to p (fp32, zeroed first) with one atomic per slot.
+// Teacher, bf16: one workgroup per token, eight waves; wave w owns heads [16w, 16w+16)
+// (q slices of its heads as A operands in registers, its rows of the forward's lse).
+// The token's slots go in 32-key sub-tiles that the whole workgroup gathers once into
+// LDS (double-buffered, the next sub-tile's rows in registers while the current one
+// is computed); every wave forms S = Q K^T for its heads (16x16x32 MFMAs, key rows as
+// B operands as stored) and sums exp(scale s - lse) over its 16 heads per key; the
+// per-wave sums meet in LDS and one plain store per slot writes p_j / H.
+constexpr int kTW = 8;            // waves of a teacher workgroup
+constexpr int kTK = 32;           // keys per teacher sub-tile
+
 template <int DQK>
-__global__ __launch_bounds__(kWaves * 64) void attn_teacher_bf16_kernel(
+constexpr size_t teacher_lds_bytes() {
+  return (size_t)2 * kTK * krow_bytes<DQK>() + (size_t)2 * kTW * kTK * sizeof(float);
+}
+
+template <int DQK>
+__global__ __launch_bounds__(kTW * 64) void attn_teacher_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     const float* __restrict__ lse, int H, int topk, float scale, float* __restrict__ teacher) {
   constexpr int KRB = krow_bytes<DQK>();
   constexpr int NK = DQK / 32;
   constexpr int CPR = DQK * 2 / 16;
-  constexpr int NLD = kSK * CPR / 64;
+  constexpr int NLD = (kTK * CPR + kTW * 64 - 1) / (kTW * 64);
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  char* q_l = lds;                                        // [16 heads][KRB]
-  char* k_l = q_l + kHG * KRB;                            // [waves][16 keys][KRB]
+  char* stage = lds;                                                    // [2][kTK][KRB]
+  float* part = reinterpret_cast<float*>(lds + 2 * kTK * KRB);          // [2][kTW][kTK]
   const int t = blockIdx.x;
-  const int h0 = blockIdx.y * kHG;
   const int tid = threadIdx.x, w = tid >> 6, L = tid & 63;
   const int g = L >> 4, n = L & 15;
-  for (int c = tid; c < kHG * CPR; c += kWaves * 64) {
-    const int hh = c / CPR, p = c % CPR;
-    bf16x8_t v = bf16x8_t{};
-    if (h0 + hh < H) v = *reinterpret_cast<const bf16x8_t*>(q + ((int64_t)t * H + h0 + hh) * DQK + 8 * p);
-    *reinterpret_cast<bf16x8_t*>(q_l + hh * KRB + 16 * p) = v;
-  }
-  __syncthreads();
-  float lse2[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int hh = h0 + 4 * g + i;
-    lse2[i] = (hh < H ? lse[(int64_t)t * H + hh] : -__builtin_huge_valf()) * kLog2e;
-  }
-  bf16x8_t qa[NK];
-#pragma unroll
-  for (int ks = 0; ks < NK; ++ks) qa[ks] = *reinterpret_cast<const bf16x8_t*>(q_l + n * KRB + 64 * ks + 16 * g);
-  char* kt = k_l + w * kSK * KRB;
-  const int32_t* irow = idx + (int64_t)t * topk;
-  const int nsub = (topk + kSK - 1) / kSK;
+  const int h0 = kHG * w;
+  const bool heads = h0 < H;                       // wave-uniform
+  const int32_t* __restrict__ irow = idx + (int64_t)t * topk;
+  const int nsub = (topk + kTK - 1) / kTK;
   const float sc2 = scale * kLog2e, invH = 1.0f / (float)H;
+
+  bf16x8_t qa[NK];
+  float lse2[4];
+  {
+    const int hq = h0 + n;
+    const uint16_t* qr = q + ((int64_t)t * H + (hq < H ? hq : 0)) * DQK + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+      const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(qr + 32 * ks);
+      qa[ks] = hq < H ? x : bf16x8_t{};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = h0 + 4 * g + i;
+      lse2[i] = (hh < H ? lse[(int64_t)t * H + hh] : -__builtin_huge_valf()) * kLog2e;
+    }
+  }
   bf16x8_t nx[NLD];
   auto load = [&](int sub) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < NLD; ++m) {
-      const int c = L + 64 * m, r = c / CPR, p = c % CPR;
-      const int j = sub * kSK + r;
-      int row = j < topk ? irow[j] : -1;
+      const int c = tid + kTW * 64 * m, r = c / CPR, p = c % CPR;
+      const int j = sub * kTK + r;
+      int row = (c < kTK * CPR && j < topk) ? irow[j] : -1;
       row = row < 0 ? 0 : row;
       nx[m] = *reinterpret_cast<const bf16x8_t*>(kv + (int64_t)row * DQK + 8 * p);
     }
   };
-  if (w < nsub) load(w);
+  auto finish = [&](int sub) __attribute__((always_inline)) {   // threads 0..kTK-1
+    const int j = sub * kTK + tid;
+    if (j < topk) {
+      const float* pp = part + (sub & 1) * kTW * kTK + tid;
+      float sum = 0.0f;
+#pragma unroll
+      for (int v = 0; v < kTW; ++v) sum += pp[v * kTK];
+      teacher[(int64_t)t * topk + j] = irow[j] >= 0 ? sum * invH : 0.0f;
+    }
+  };
+  load(0);
 #pragma unroll 1
-  for (int sub = w; sub < nsub; sub += kWaves) {
+  for (int sub = 0; sub < nsub; ++sub) {
+    char* kt = stage + (sub & 1) * kTK * KRB;
 #pragma unroll
     for (int m = 0; m < NLD; ++m) {
-      const int c = L + 64 * m, r = c / CPR, p = c % CPR;
-      *reinterpret_cast<bf16x8_t*>(kt + r * KRB + 16 * p) = nx[m];
+      const int c = tid + kTW * 64 * m, r = c / CPR, p = c % CPR;
+      if (c < kTK * CPR) *reinterpret_cast<bf16x8_t*>(kt + r * KRB + 16 * p) = nx[m];
     }
-    __builtin_amdgcn_wave_barrier();
-    if (sub + kWaves < nsub) load(sub + kWaves);
-    const int jn = sub * kSK + n;
-    const int rown = jn < topk ? irow[jn] : -1;
-    floatx4v_t S = floatx4v_t{};
+    __syncthreads();
+    if (sub + 1 < nsub) load(sub + 1);
+    if (sub > 0 && tid < kTK) finish(sub - 1);
+    float* pw = part + (sub & 1) * kTW * kTK + w * kTK;
+    if (heads) {
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks)
-      S = mfma16x32(qa[ks], *reinterpret_cast<const bf16x8_t*>(kt + n * KRB + 64 * ks + 16 * g), S);
-    float ps = 0.0f;
+      for (int half = 0; half < 2; ++half) {
+        const char* kr = kt + (16 * half + n) * KRB + 16 * g;
+        floatx4v_t S = floatx4v_t{};
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      ps += rown >= 0 && lse2[i] > -__builtin_huge_valf() ? __builtin_amdgcn_exp2f(S[i] * sc2 - lse2[i]) : 0.0f;
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    if (g == 0 && rown >= 0) atomicAdd(teacher + (int64_t)t * topk + jn, ps * invH);
-    __builtin_amdgcn_wave_barrier();
+        for (int ks = 0; ks < NK; ++ks)
+          S = mfma16x32(qa[ks], *reinterpret_cast<const bf16x8_t*>(kr + 64 * ks), S);
+        float ps = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          ps += lse2[i] > -__builtin_huge_valf() ? __builtin_amdgcn_exp2f(S[i] * sc2 - lse2[i]) : 0.0f;
+        ps += __shfl_xor(ps, 16, 64);
+        ps += __shfl_xor(ps, 32, 64);
+        if (g == 0) pw[16 * half + n] = ps;
+      }
+    } else if (L < kTK) {
+      pw[L] = 0.0f;
+    }
   }
+  __syncthreads();
+  if (tid < kTK && nsub > 0) finish(nsub - 1);
 }
 
 __global__ __launch_bounds__(kNT) void attn_teacher_f32_kernel(
@@ -505,23 +541,25 @@ hipError_t launch_sparse_mla_bwd(const void* q, const void* kv, const int32_t* i
 hipError_t launch_attn_teacher(const void* q, const void* kv, const int32_t* idx, const float* lse,
                                bool bf16, int T, int H, int d_qk, int topk, float scale, float* teacher,
                                hipStream_t st) {
-  hipLaunchKernelGGL(zero_f32_kernel, dim3(1024), dim3(256), 0, st, teacher, (int64_t)T * topk);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || T == 0) return e;
+  if (T == 0) return hipSuccess;
+  hipError_t e;
   if (!bf16) {
+    hipLaunchKernelGGL(zero_f32_kernel, dim3(1024), dim3(256), 0, st, teacher, (int64_t)T * topk);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_teacher_f32_kernel, dim3(T * H), dim3(kNT), 0, st, (const float*)q,
                        (const float*)kv, idx, lse, H, d_qk, topk, scale, teacher);
     return hipGetLastError();
   }
-  const dim3 grid(T, (H + kHG - 1) / kHG), block(kWaves * 64);
+  const dim3 grid(T), block(kTW * 64);
   if (d_qk == 576) {
-    const size_t shm = (size_t)(1 + kWaves) * kSK * krow_bytes<576>();
+    const size_t shm = teacher_lds_bytes<576>();
     e = hipFuncSetAttribute((const void*)attn_teacher_bf16_kernel<576>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_teacher_bf16_kernel<576>), grid, block, shm, st, (const uint16_t*)q,
                        (const uint16_t*)kv, idx, lse, H, topk, scale, teacher);
   } else {
-    const size_t shm = (size_t)(1 + kWaves) * kSK * krow_bytes<512>();
+    const size_t shm = teacher_lds_bytes<512>();
     e = hipFuncSetAttribute((const void*)attn_teacher_bf16_kernel<512>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_teacher_bf16_kernel<512>), grid, block, shm, st, (const uint16_t*)q,
