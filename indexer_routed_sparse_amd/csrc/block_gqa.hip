@@ -256,6 +256,316 @@ __global__ __launch_bounds__(kWavesPerGroup * 64) void block_gqa_bf16_kernel(
   }
 }
 
+// Grouped bf16 kernel: one workgroup per (group of GT consecutive tokens, kv head),
+// eight waves. Neighbouring tokens' routes overlap, so the group loads every block of
+// the union of its tokens' routes once, into LDS, and runs all of the group's
+// GT x G query rows (at most 128: one 16-row column tile per wave) over it as a dense
+// tile, masking each (row, key) by route membership and causality:
+//   * set-up: the routes' blocks, as key rows start + b B, are marked in a bitmap over
+//     the group's key range; a prefix count over its words numbers the distinct blocks
+//     in ascending key order, and each route entry ORs its token into its block's mask;
+//   * the blocks go in 32-key sub-tiles: K rows to a padded LDS stage (A operands of
+//     S^T = K . Q^T, 16x16x32), V rows to a swizzled stage read back transposed for
+//     O^T = V^T . P^T, both double-buffered; the next two sub-tiles' rows are in
+//     registers while the current one is computed;
+//   * a wave skips the MFMAs of a sub-tile none of its rows' tokens routes to; a row's
+//     online softmax ignores masked keys exactly (alpha 1, p 0).
+// Measured on the block-routed workload: two workgroups of four waves with two column
+// tiles each, one sub-tile ahead, 0.89 ms; skipping per column tile 0.79; two sub-tiles
+// ahead 0.77; eight waves of one tile (twice the waves per SIMD) 0.68; 64-key sub-tiles
+// and 256-row groups no faster.
+// Blocks are visited in ascending key order, the same for every row of the group.
+constexpr int kGrpRows = 128;            // query rows of a group (8 column tiles)
+constexpr int kGrpMaxTok = 32;           // tokens of a group (token mask width)
+constexpr int kGrpWaves = 8;             // one column tile each
+
+template <int D>
+constexpr int kstride() { return D * 2 + 16; }   // padded K row in the stage (bytes)
+template <int D>
+constexpr int grp_stage_bytes() { return 32 * kstride<D>() + 32 * D * 2; }
+
+int grp_tokens(int G) { return G >= 4 ? kGrpRows / G : kGrpMaxTok; }
+
+size_t grp_lds_bytes(int D, int G, int nblk, int maxlen) {
+  const int GT = grp_tokens(G);
+  const size_t nw = (size_t)(maxlen + GT + 31) / 32 + 1;          // bitmap words
+  const size_t ne = (size_t)GT * nblk;                              // route entries
+  const size_t st = D == 128 ? grp_stage_bytes<128>() : grp_stage_bytes<64>();
+  return 2 * st + 2 * nw * 4 + 2 * ne * 4 + 64;
+}
+
+template <int D>
+__global__ __launch_bounds__(kGrpWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void block_gqa_group_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ blk, const int32_t* __restrict__ cu, int nseq, int T, int Hq,
+    int Hkv, int B, int nblk, int GT, int nwords, float scale_log2, uint16_t* __restrict__ out,
+    float* __restrict__ lse, int by_xcd) {
+  constexpr int KS = D / 32;             // 32-wide k-steps of S^T
+  constexpr int CPR = D * 2 / 16;        // 16-byte chunks per row
+  constexpr int NDT = D / 16;            // 16-channel tiles of O^T
+  constexpr int KSB = kstride<D>();
+  constexpr int NT = kGrpWaves * 64;
+  constexpr int LDN = (2 * 32 * CPR + NT - 1) / NT;   // 16-byte loads per thread per sub-tile
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  char* stg = lds;                                                   // [2][K stage | V stage]
+  uint32_t* bits = reinterpret_cast<uint32_t*>(lds + 2 * grp_stage_bytes<D>());   // [nwords]
+  uint32_t* pre = bits + nwords;                                     // [nwords]
+  int32_t* ulo = reinterpret_cast<int32_t*>(pre + nwords);           // [GT*nblk] block key rows
+  uint32_t* umask = reinterpret_cast<uint32_t*>(ulo + GT * nblk);    // [GT*nblk] token masks
+  uint32_t* red = umask + GT * nblk;                                 // [16]
+
+  const int tid = threadIdx.x, w = tid >> 6, L = tid & 63;
+  const int n = L & 15, quad = L >> 4;
+  const int G = Hq / Hkv;
+  const int ngrp = (T + GT - 1) / GT;
+  int grp, g;
+  if (by_xcd) {
+    // workgroup b runs on XCD b mod 8; each XCD serves one kv head (8 / Hkv XCDs per
+    // head); groups go from the last (the widest routes' unions) to the first
+    const int b = blockIdx.x, xcd = b & 7, nx = 8 / Hkv;
+    g = xcd % Hkv;
+    grp = (b >> 3) * nx + xcd / Hkv;
+    if (grp >= ngrp) return;                             // whole workgroup leaves together
+  } else {
+    grp = (int)blockIdx.x / Hkv;
+    g = (int)blockIdx.x - grp * Hkv;
+  }
+  grp = ngrp - 1 - grp;
+  const int t0 = grp * GT;
+  const int tlast = min(t0 + GT, T) - 1;
+  const int base = cu ? seq_start_of(cu, nseq, t0) : 0;
+
+  // ---- set-up: distinct blocks of the group's routes, ascending, with token masks
+  for (int i = tid; i < nwords; i += NT) bits[i] = 0u;
+  __syncthreads();
+  const int ne = GT * nblk;
+  for (int e = tid; e < ne; e += NT) {
+    const int tau = e / nblk, j = e - tau * nblk;
+    const int t = t0 + tau;
+    if (t <= tlast) {
+      const int st = cu ? seq_start_of(cu, nseq, t) : 0;
+      const int b = blk[(int64_t)t * nblk + j];
+      if (b >= 0 && b <= (t - st) / B) {
+        const int r = st + b * B - base;
+        atomicOr(&bits[r >> 5], 1u << (r & 31));
+      }
+    }
+  }
+  __syncthreads();
+  {
+    const int wpt = (nwords + NT - 1) / NT;
+    uint32_t cnt = 0;
+    for (int r = 0; r < wpt; ++r) {
+      const int i = tid * wpt + r;
+      if (i < nwords) cnt += (uint32_t)__popc(bits[i]);
+    }
+    const uint32_t inc = wave_incl_scan(cnt);
+    if (L == 63) red[w] = inc;
+    __syncthreads();
+    uint32_t run = inc - cnt;
+    for (int i = 0; i < w; ++i) run += red[i];
+    if (tid == NT - 1) red[15] = run + cnt;                 // distinct blocks
+    for (int r = 0; r < wpt; ++r) {
+      const int i = tid * wpt + r;
+      if (i < nwords) {
+        pre[i] = run;
+        run += (uint32_t)__popc(bits[i]);
+      }
+    }
+  }
+  for (int i = tid; i < ne; i += NT) umask[i] = 0u;
+  __syncthreads();
+  const int nu = (int)red[15];
+  for (int e = tid; e < ne; e += NT) {
+    const int tau = e / nblk, j = e - tau * nblk;
+    const int t = t0 + tau;
+    if (t <= tlast) {
+      const int st = cu ? seq_start_of(cu, nseq, t) : 0;
+      const int b = blk[(int64_t)t * nblk + j];
+      if (b >= 0 && b <= (t - st) / B) {
+        const int r = st + b * B - base;
+        const int u = (int)(pre[r >> 5] + (uint32_t)__popc(bits[r >> 5] & ((1u << (r & 31)) - 1u)));
+        ulo[u] = r + base;
+        atomicOr(&umask[u], 1u << tau);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- this lane's query row: column tile w, row 16 w + n (token tau, head h)
+  const int row = 16 * w + n;
+  const int tau = row / G;
+  const int tq = t0 + tau;
+  const bool row_ok = tau < GT && row < GT * G && tq <= tlast;
+  const int hq = row - tau * G;
+  bf16x8_t qb[KS];
+  {
+    const uint16_t* qr = q + ((int64_t)(row_ok ? tq : t0) * Hq + g * G + hq) * D + 8 * quad;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(qr + 32 * ks);
+      qb[ks] = row_ok ? x : bf16x8_t{};
+    }
+  }
+  uint32_t tile_tok = row_ok ? (1u << tau) : 0u;     // tokens of the wave's rows (uniform)
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) tile_tok |= (uint32_t)__shfl_xor((int)tile_tok, off, 64);
+
+  floatx4v_t O[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i) O[i] = floatx4v_t{};
+  float m_run = -__builtin_huge_valf();   // log2 units, same in the 4 lanes of a row
+  float l_run = 0.0f;                     // this lane's keys only
+
+  // sub-tiles: for each distinct block u, keys ulo[u] .. min(ulo[u] + B, tlast + 1) - 1
+  // in 32-key pieces; (u, piece) advanced in order
+  auto keys_of = [&](int u) { return min(B, tlast + 1 - ulo[u]); };
+  bf16x8_t nx[LDN];
+  auto load = [&](int u, int pc) __attribute__((always_inline)) {
+    const int lo = ulo[u] + 32 * pc;
+    const int nk = min(32, keys_of(u) - 32 * pc);
+#pragma unroll
+    for (int m = 0; m < LDN; ++m) {
+      const int c = tid + NT * m;                  // chunk: [K | V][row][CPR]
+      const int isv = c >= 32 * CPR;
+      const int cc = isv ? c - 32 * CPR : c;
+      const int r = cc / CPR, p = cc % CPR;
+      const int key = lo + (r < nk ? r : 0);
+      const uint16_t* src = (isv ? v : k) + ((int64_t)key * Hkv + g) * D + 8 * p;
+      nx[m] = (c < 2 * 32 * CPR) ? *reinterpret_cast<const bf16x8_t*>(src) : bf16x8_t{};
+    }
+  };
+  auto store = [&](char* st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < LDN; ++m) {
+      const int c = tid + NT * m;
+      if (c < 2 * 32 * CPR) {
+        const int isv = c >= 32 * CPR;
+        const int cc = isv ? c - 32 * CPR : c;
+        const int r = cc / CPR, p = cc % CPR;
+        if (!isv) *reinterpret_cast<bf16x8_t*>(st + r * KSB + 16 * p) = nx[m];
+        else *reinterpret_cast<bf16x8_t*>(st + 32 * KSB + r * (CPR * 16) + ((p ^ vswz<D>(r)) << 4)) = nx[m];
+      }
+    }
+  };
+
+  auto advance = [&](int& uu, int& pp) __attribute__((always_inline)) {
+    if (uu < nu) {
+      ++pp;
+      if (32 * pp >= keys_of(uu)) { ++uu; pp = 0; }
+    }
+  };
+  bf16x8_t nxA[LDN], nxB[LDN];
+  auto loadTo = [&](bf16x8_t (&dst)[LDN], int uu, int pp) __attribute__((always_inline)) {
+    load(uu, pp);
+#pragma unroll
+    for (int m = 0; m < LDN; ++m) dst[m] = nx[m];
+  };
+  auto storeFrom = [&](char* st, const bf16x8_t (&src)[LDN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < LDN; ++m) nx[m] = src[m];
+    store(st);
+  };
+  int u = 0, pc = 0, ua = 0, pa = 0;
+  advance(ua, pa);
+  if (nu > 0) loadTo(nxA, 0, 0);
+  if (ua < nu) loadTo(nxB, ua, pa);
+  auto piece = [&](char* st, bf16x8_t (&buf)[LDN]) __attribute__((always_inline)) {
+    storeFrom(st, buf);
+    __syncthreads();
+    int ub = ua, pb = pa;
+    advance(ub, pb);
+    if (ub < nu) loadTo(buf, ub, pb);
+    const int lo = ulo[u] + 32 * pc;
+    const int nk = min(32, keys_of(u) - 32 * pc);
+    const uint32_t msk = umask[u];
+    if (msk & tile_tok) {                                 // uniform: some row of the wave uses it
+      {
+        floatx4v_t S[2] = {floatx4v_t{}, floatx4v_t{}};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(st + (16 * kt + n) * KSB + 64 * ks + 16 * quad);
+            S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], S[kt], 0, 0, 0);
+          }
+        const bool in = row_ok && ((msk >> tau) & 1u);
+        float mx = -__builtin_huge_valf();
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int kk = 16 * kt + 4 * quad + e;
+            const bool ok = in && kk < nk && lo + kk <= tq;
+            const float x = ok ? S[kt][e] * scale_log2 : -__builtin_huge_valf();
+            S[kt][e] = x;
+            mx = __builtin_elementwise_maximum(mx, x);
+          }
+        mx = quad_max(mx);
+        const float m_new = __builtin_elementwise_maximum(m_run, mx);
+        const bool none = m_new == -__builtin_huge_valf();
+        const float alpha = none ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        if (ballot(alpha != 1.0f)) {
+#pragma unroll
+          for (int i = 0; i < NDT; ++i) O[i] *= alpha;
+        }
+        l_run *= alpha;
+        float pf[8];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pf[4 * kt + e] = none ? 0.0f : __builtin_amdgcn_exp2f(S[kt][e] - m_new);
+            l_run += pf[4 * kt + e];
+          }
+        bf16x2_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk[e] = __builtin_convertvector((float2_t){pf[2 * e], pf[2 * e + 1]}, bf16x2_t);
+        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pk);
+        const char* vst = st + 32 * KSB;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          short4_t lo4, hi4;
+          {
+            const int row0 = 4 * quad + (n >> 2);
+            const int col = 16 * dt + 4 * (n & 3);
+            const int off0 = row0 * (CPR * 16) + (((col >> 3) ^ vswz<D>(row0)) << 4) + (col & 7) * 2;
+            const int row1 = row0 + 16;
+            const int off1 = row1 * (CPR * 16) + (((col >> 3) ^ vswz<D>(row1)) << 4) + (col & 7) * 2;
+            lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(vst + off0));
+            hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(vst + off1));
+          }
+          const short __attribute__((ext_vector_type(8))) a8 = {lo4[0], lo4[1], lo4[2], lo4[3],
+                                                                hi4[0], hi4[1], hi4[2], hi4[3]};
+          O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a8), pb, O[dt], 0, 0, 0);
+        }
+      }
+    }
+    u = ua; pc = pa; ua = ub; pa = pb;
+  };
+#pragma unroll 1
+  while (u < nu) {
+    piece(stg, nxA);
+    if (u < nu) piece(stg + grp_stage_bytes<D>(), nxB);
+  }
+
+  // ---- normalise and write: lane owns row 16 w + n, channels 16 dt + 4 quad + e
+  const float l_tot = quad_sum(l_run);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (row_ok) {
+    uint16_t* orow = out + ((int64_t)tq * Hq + g * G + hq) * D + 4 * quad;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      uint32_t pk0 = pack_bf16x2(O[dt][0] * inv, O[dt][1] * inv);
+      uint32_t pk1 = pack_bf16x2(O[dt][2] * inv, O[dt][3] * inv);
+      *reinterpret_cast<uint2*>(orow + 16 * dt) = make_uint2(pk0, pk1);
+    }
+    if (lse && quad == 0)
+      lse[(int64_t)tq * Hq + g * G + hq] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_huge_valf();
+  }
+}
+
 // fp32 inputs: one wave per (token, kv head) on 16x16x4 fp32 MFMAs (the wave routine
 // of attn_f32.h). The route becomes a list of 16-key sub-tiles as in the bf16 kernel,
 // the G query heads are the MFMA columns and key and value rows are read straight
@@ -308,6 +618,28 @@ __global__ __launch_bounds__(64) void block_gqa_f32_kernel(
 }
 
 template <int D>
+hipError_t launch_grouped(const void* q, const void* k, const void* v, const int32_t* blk, int T,
+                          const int32_t* cu, int nseq, int maxlen, int Hq, int Hkv, int B, int nblk,
+                          float scale, void* out, float* lse, hipStream_t st) {
+  const int G = Hq / Hkv;
+  const int GT = grp_tokens(G);
+  const int nwords = (maxlen + GT + 31) / 32 + 1;
+  const size_t shm = grp_lds_bytes(D, G, nblk, maxlen);
+  if (shm > 160 * 1024) return hipErrorInvalidValue;
+  hipError_t e = hipFuncSetAttribute((const void*)block_gqa_group_kernel<D>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (e != hipSuccess) return e;
+  const int by_xcd = 8 % Hkv == 0;
+  const int64_t ngrp = ((int64_t)T + GT - 1) / GT;
+  int64_t grid = by_xcd ? (ngrp + 8 / Hkv - 1) / (8 / Hkv) * 8 : ngrp * Hkv;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((block_gqa_group_kernel<D>), dim3((unsigned)grid), dim3(kGrpWaves * 64), shm,
+                     st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, blk, cu, nseq, T,
+                     Hq, Hkv, B, nblk, GT, nwords, scale * kLog2e, (uint16_t*)out, lse, by_xcd);
+  return hipGetLastError();
+}
+
+template <int D>
 hipError_t launch_bf16(const void* q, const void* k, const void* v, const int32_t* blk, int T,
                        const int32_t* cu, int nseq, int Hq, int Hkv, int B, int nblk, float scale,
                        void* out, float* lse, hipStream_t st) {
@@ -343,13 +675,19 @@ hipError_t launch_f32(const void* q, const void* k, const void* v, const int32_t
 int block_gqa_max_route() { return kMaxRoute; }
 
 hipError_t launch_block_gqa(const void* q, const void* k, const void* v, const int32_t* blk,
-                            bool bf16, int T, const int32_t* cu, int nseq, int Hq, int Hkv, int D,
-                            int Dv, int block_size, int nblk, float scale, void* out, float* lse,
+                            bool bf16, int T, const int32_t* cu, int nseq, int maxlen, int Hq, int Hkv,
+                            int D, int Dv, int block_size, int nblk, float scale, void* out, float* lse,
                             hipStream_t st) {
   (void)Dv;
   if (T == 0) return hipSuccess;
   const int ns = cu ? nseq : 1;
   if (bf16) {
+    // the grouped kernel when its set-up tables fit the LDS (rows up to ~150K keys)
+    if (grp_lds_bytes(D, Hq / Hkv, nblk, maxlen) <= 160 * 1024) {
+      if (D == 64)
+        return launch_grouped<64>(q, k, v, blk, T, cu, ns, maxlen, Hq, Hkv, block_size, nblk, scale, out, lse, st);
+      return launch_grouped<128>(q, k, v, blk, T, cu, ns, maxlen, Hq, Hkv, block_size, nblk, scale, out, lse, st);
+    }
     if (D == 64) return launch_bf16<64>(q, k, v, blk, T, cu, ns, Hq, Hkv, block_size, nblk, scale, out, lse, st);
     return launch_bf16<128>(q, k, v, blk, T, cu, ns, Hq, Hkv, block_size, nblk, scale, out, lse, st);
   }

@@ -222,7 +222,7 @@ sa_status sa_block_sparse_gqa_fwd(const void* q, const void* k, const void* v, c
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SA_ERR_ALIGN;
   SA_DEBUG_RETURN(debug_offsets(cu_seqlens, num_seqs, T, max_seqlen, reinterpret_cast<hipStream_t>(stream)));
   return launch_status(sa::launch_block_gqa(q, k, v, blk, dtype == SA_BF16, T, cu_seqlens, num_seqs,
-                                            Hq, Hkv, D, Dv, block_size, nblk, scale, out, lse,
+                                            widest, Hq, Hkv, D, Dv, block_size, nblk, scale, out, lse,
                                             reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -48,8 +48,8 @@ hipError_t launch_indexer_topk(const void* q, const void* k, const float* w, boo
 // Largest route (blocks per query row) the bf16 kernel takes.
 int block_gqa_max_route();
 hipError_t launch_block_gqa(const void* q, const void* k, const void* v, const int32_t* blk,
-                            bool bf16, int T, const int32_t* cu, int nseq, int Hq, int Hkv, int D,
-                            int Dv, int block_size, int nblk, float scale, void* out, float* lse,
+                            bool bf16, int T, const int32_t* cu, int nseq, int maxlen, int Hq, int Hkv,
+                            int D, int Dv, int block_size, int nblk, float scale, void* out, float* lse,
                             hipStream_t st);
 
 // sa_checks.hip (called by the debug build's entry points only): whether every value
