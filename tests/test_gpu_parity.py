@@ -666,6 +666,27 @@ def test_block_gqa_full_size_thd_sampled(sa):
     close(lse.cpu().numpy()[rows], rl, **BF16_TOL, what="lse")
 
 
+def test_block_gqa_long_sequence_per_token_kernel(sa):
+    """One 600,000-token sequence: the grouped kernel's set-up bitmap over the group's
+    key range would not fit the LDS, so the per-(token, kv head) kernel serves it.
+    Routes of two blocks (a random earlier or equal block, and the own block, possibly
+    the same); sampled rows against the oracle."""
+    T, Hq, Hkv, D, B = 600_000, 4, 4, 64, 128
+    gen = torch.Generator(device=DEV).manual_seed(77)
+    q = torch.randn((T, Hq, D), generator=gen, device=DEV).to(torch.bfloat16)
+    k = torch.randn((T, Hkv, D), generator=gen, device=DEV).to(torch.bfloat16)
+    v = torch.randn((T, Hkv, D), generator=gen, device=DEV).to(torch.bfloat16)
+    own = torch.arange(T, device=DEV) // B
+    other = (torch.rand(T, generator=gen, device=DEV) * (own + 1).float()).long()
+    other = torch.minimum(other, own)
+    blk = torch.stack([other, own], 1).to(torch.int32).contiguous()
+    out, lse = sa.block_sparse_gqa(q, k, v, blk, 0.125, block_size=B)
+    rows = np.array([0, 1, 127, 128, 5000, 123457, 333333, T - 2, T - 1])
+    ro, rl = oracle.block_sparse_gqa(q.cpu(), k.cpu(), v.cpu(), blk.cpu().numpy(), B, 0.125, rows=rows)
+    close(out.float().cpu().numpy()[rows], ro, **BF16_TOL, what="out")
+    close(lse.cpu().numpy()[rows], rl, **BF16_TOL, what="lse")
+
+
 @pytest.mark.parametrize("Hq,Hkv,D,B,dtype", [(32, 4, 128, 64, "bf16"), (8, 4, 128, 32, "bf16"),
                                               (4, 4, 64, 16, "bf16"), (16, 1, 128, 128, "bf16"),
                                               (12, 2, 64, 48, "bf16"), (8, 2, 64, 32, "f32"),
