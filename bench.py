@@ -116,6 +116,92 @@ def cpu_baseline(wl, x, m, idx_gpu, n_rows=1024):
     }
 
 
+def _median_ms(fn, n):
+    """Median over n timed calls of fn (HIP events), after one untimed call."""
+    fn()
+    tms = []
+    for _ in range(n):
+        tm = Timer()
+        with tm:
+            fn()
+        tms.append(tm)
+    torch.cuda.synchronize()
+    return float(np.median([tm.ms() for tm in tms]))
+
+
+def _mfma_entry(kernel, flops, ms, cpu=None):
+    tf = flops / (ms * 1e-3) / 1e12
+    e = {"kernel": kernel, "bound": "mfma", "ms": round(ms, 3), "achieved": round(tf, 2),
+         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+         "flop": flops}
+    if cpu is not None:
+        e["cpu_oracle"] = cpu
+    return e
+
+
+def gradients_leg(sa, workloads, wl, x, m, idx, lse, n_timed, cpu_rows):
+    """Backward, teacher and sparse-KL kernels on the long workload (the forward's
+    indices and lse), with the oracle's rate on cpu_rows rows when cpu_rows > 0."""
+    import oracle
+    dev = m["q"].device
+    T, H = wl.T, wl.H
+    slots = int((idx >= 0).sum())
+    g = torch.Generator(device=dev).manual_seed(11)
+    dout = torch.randn((T, H, 512), generator=g, device=dev).to(torch.bfloat16)
+    dq = torch.empty_like(m["q"])
+    dkv = torch.empty((T, 576), dtype=torch.float32, device=dev)
+    teacher = torch.empty((T, idx.shape[1]), dtype=torch.float32, device=dev)
+    res = {}
+    rows = np.linspace(T // 8, T - 1, cpu_rows).astype(np.int64) if cpu_rows else None
+
+    def cpu_rate(fn, flop_per_row_slot):
+        if rows is None:
+            return None
+        ih = idx.cpu().numpy()
+        nslot = int((ih[rows] >= 0).sum())
+        t0 = time.perf_counter()
+        fn(ih)
+        dt = time.perf_counter() - t0
+        return {"rows": int(len(rows)), "seconds": round(dt, 2),
+                "tflops": round(flop_per_row_slot * nslot / dt / 1e12, 6)}
+
+    print("[bench] sparse-MLA backward", file=sys.stderr, flush=True)
+    ms = _median_ms(lambda: sa.sa_sparse_mla_bwd(m["q"], m["kv"], idx, dout, lse, wl.scale, dq, dkv), n_timed)
+    f_slot = 2.0 * (576 + 512 + 576 + 576 + 512) * H
+    cpu = None
+    if rows is not None:
+        qh, kvh, dh = m["q"][torch.from_numpy(rows).to(dev)].cpu(), m["kv"].cpu(), dout[torch.from_numpy(rows).to(dev)].cpu()
+        cpu = cpu_rate(lambda ih: oracle.sparse_mla_bwd(qh, kvh, ih[rows], dh, wl.scale), f_slot)
+    res["sparse_mla_bwd"] = _mfma_entry("sparse_mla_bwd_bf16_kernel", f_slot * slots, ms, cpu)
+    del dq, dkv
+    print("[bench] teacher", file=sys.stderr, flush=True)
+    ms = _median_ms(lambda: sa.sa_attn_teacher(m["q"], m["kv"], idx, lse, wl.scale, teacher), n_timed)
+    f_slot = 2.0 * 576 * H
+    cpu = None
+    th = None
+    if rows is not None:
+        holder = {}
+
+        def teach(ih):
+            holder["t"] = oracle.attn_teacher(qh, kvh, ih[rows], wl.scale)
+        cpu = cpu_rate(teach, f_slot)
+        th = np.zeros((T, idx.shape[1]))        # the oracle's own teacher on the sampled rows
+        th[rows] = holder["t"]
+    res["attn_teacher"] = _mfma_entry("attn_teacher_bf16_kernel", f_slot * slots, ms, cpu)
+    print("[bench] indexer sparse-KL loss and gradients", file=sys.stderr, flush=True)
+    ms = _median_ms(lambda: sa.indexer_kl_bwd(x["q_I"], x["k_I"], x["w"], idx, teacher), n_timed)
+    HI, DI = x["q_I"].shape[1], x["q_I"].shape[2]
+    f_slot = 3 * 2.0 * HI * DI
+    cpu = None
+    if rows is not None:
+        qi, ki, wi = x["q_I"].cpu(), x["k_I"].cpu(), x["w"].cpu()
+        cpu = cpu_rate(lambda ih: oracle.indexer_kl(qi, ki, wi, ih, th, rows=rows), f_slot)
+    res["indexer_kl_bwd"] = _mfma_entry("indexer_kl_bf16_kernel", f_slot * slots, ms, cpu)
+    del dout, teacher
+    torch.cuda.synchronize()
+    return res
+
+
 def _host_cpu():
     """Logical CPU count, the CPUs this process may run on, and the CPU model name
     (from /proc/cpuinfo, the source lscpu reads)."""
@@ -259,7 +345,8 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the top-k select and GQA legs")
+    ap.add_argument("--no-extras", action="store_true", help="skip the top-k select, GQA and gradient legs")
+    ap.add_argument("--no-grads", action="store_true", help="skip the backward / loss kernels")
     ap.add_argument("--counters", action="store_true",
                     help="one launch per measured kernel plus a calibration copy (for rocprofv3 --pmc)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -377,6 +464,9 @@ def main():
         del idx1, ws
 
         # ---- standalone exact top-k over a materialised causal score matrix (HBM-bound)
+        if not args.no_grads:
+            result["gradients"] = gradients_leg(sa, workloads, wl, x, m, idx, lse, 3,
+                                                0 if args.no_cpu_baseline else 8)
         print("[bench] top-k select on materialised scores", file=sys.stderr, flush=True)
         del out, lse
         scores = torch.empty((T, T), dtype=torch.float32, device=dev)
@@ -445,6 +535,20 @@ def main():
             "gqa_frac_mfma": round(gqa_flops / (t_gq * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "traffic": _traffic("block_gqa_block_workload", ["block_gqa.hip", "sa_common.h"]),
         }
+        if not args.no_grads:
+            print("[bench] block-routed GQA backward", file=sys.stderr, flush=True)
+            glse = torch.empty((wq.T, wq.Hq), dtype=torch.float32, device=dev)
+            sa.sa_block_sparse_gqa_fwd(gq["q"], gq["k"], gq["v"], blk, wq.scale, go, glse, block_size=64)
+            gg = torch.Generator(device=dev).manual_seed(12)
+            gd = torch.randn(go.shape, generator=gg, device=dev).to(torch.bfloat16)
+            gdq = torch.empty_like(gq["q"])
+            gdk = torch.empty(gq["k"].shape, dtype=torch.float32, device=dev)
+            gdv = torch.empty(gq["v"].shape, dtype=torch.float32, device=dev)
+            ms = _median_ms(lambda: sa.sa_block_sparse_gqa_bwd(gq["q"], gq["k"], gq["v"], blk, gd, glse, wq.scale,
+                                                               gdq, gdk, gdv, block_size=64), 3)
+            # S, dP, dq, dk, dv per attended key and q head
+            result.setdefault("gradients", {})["block_gqa_bwd"] = _mfma_entry(
+                "block_gqa_bwd_bf16_kernel", 2.0 * wq.Hq * (3 * wq.D + 2 * wq.Dv) * attended, ms)
 
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline (bounded sample)", file=sys.stderr, flush=True)
