@@ -29,6 +29,7 @@
 #include <type_traits>
 
 #include "attn_f32.h"
+#include "gqa_group.h"
 #include "sa_common.h"
 #include "sa_kernels.h"
 
@@ -275,23 +276,15 @@ __global__ __launch_bounds__(kWavesPerGroup * 64) void block_gqa_bf16_kernel(
 // ahead 0.77; eight waves of one tile (twice the waves per SIMD) 0.68; 64-key sub-tiles
 // and 256-row groups no faster.
 // Blocks are visited in ascending key order, the same for every row of the group.
-constexpr int kGrpRows = 128;            // query rows of a group (8 column tiles)
-constexpr int kGrpMaxTok = 32;           // tokens of a group (token mask width)
-constexpr int kGrpWaves = 8;             // one column tile each
 
 template <int D>
 constexpr int kstride() { return D * 2 + 16; }   // padded K row in the stage (bytes)
 template <int D>
 constexpr int grp_stage_bytes() { return 32 * kstride<D>() + 32 * D * 2; }
 
-int grp_tokens(int G) { return G >= 4 ? kGrpRows / G : kGrpMaxTok; }
-
 size_t grp_lds_bytes(int D, int G, int nblk, int maxlen) {
-  const int GT = grp_tokens(G);
-  const size_t nw = (size_t)(maxlen + GT + 31) / 32 + 1;          // bitmap words
-  const size_t ne = (size_t)GT * nblk;                              // route entries
   const size_t st = D == 128 ? grp_stage_bytes<128>() : grp_stage_bytes<64>();
-  return 2 * st + 2 * nw * 4 + 2 * ne * 4 + 64;
+  return 2 * st + grp_table_bytes(grp_tokens(G), nblk, maxlen);
 }
 
 template <int D>
@@ -308,11 +301,9 @@ __global__ __launch_bounds__(kGrpWaves * 64) __attribute__((amdgpu_waves_per_eu(
   constexpr int LDN = (2 * 32 * CPR + NT - 1) / NT;   // 16-byte loads per thread per sub-tile
   extern __shared__ __attribute__((aligned(16))) char lds[];
   char* stg = lds;                                                   // [2][K stage | V stage]
-  uint32_t* bits = reinterpret_cast<uint32_t*>(lds + 2 * grp_stage_bytes<D>());   // [nwords]
-  uint32_t* pre = bits + nwords;                                     // [nwords]
-  int32_t* ulo = reinterpret_cast<int32_t*>(pre + nwords);           // [GT*nblk] block key rows
-  uint32_t* umask = reinterpret_cast<uint32_t*>(ulo + GT * nblk);    // [GT*nblk] token masks
-  uint32_t* red = umask + GT * nblk;                                 // [16]
+  const GroupTables tbl = group_tables(lds + 2 * grp_stage_bytes<D>(), GT, nblk, nwords);
+  const int32_t* ulo = tbl.ulo;
+  const uint32_t* umask = tbl.umask;
 
   const int tid = threadIdx.x, w = tid >> 6, L = tid & 63;
   const int n = L & 15, quad = L >> 4;
@@ -336,61 +327,7 @@ __global__ __launch_bounds__(kGrpWaves * 64) __attribute__((amdgpu_waves_per_eu(
   const int base = cu ? seq_start_of(cu, nseq, t0) : 0;
 
   // ---- set-up: distinct blocks of the group's routes, ascending, with token masks
-  for (int i = tid; i < nwords; i += NT) bits[i] = 0u;
-  __syncthreads();
-  const int ne = GT * nblk;
-  for (int e = tid; e < ne; e += NT) {
-    const int tau = e / nblk, j = e - tau * nblk;
-    const int t = t0 + tau;
-    if (t <= tlast) {
-      const int st = cu ? seq_start_of(cu, nseq, t) : 0;
-      const int b = blk[(int64_t)t * nblk + j];
-      if (b >= 0 && b <= (t - st) / B) {
-        const int r = st + b * B - base;
-        atomicOr(&bits[r >> 5], 1u << (r & 31));
-      }
-    }
-  }
-  __syncthreads();
-  {
-    const int wpt = (nwords + NT - 1) / NT;
-    uint32_t cnt = 0;
-    for (int r = 0; r < wpt; ++r) {
-      const int i = tid * wpt + r;
-      if (i < nwords) cnt += (uint32_t)__popc(bits[i]);
-    }
-    const uint32_t inc = wave_incl_scan(cnt);
-    if (L == 63) red[w] = inc;
-    __syncthreads();
-    uint32_t run = inc - cnt;
-    for (int i = 0; i < w; ++i) run += red[i];
-    if (tid == NT - 1) red[15] = run + cnt;                 // distinct blocks
-    for (int r = 0; r < wpt; ++r) {
-      const int i = tid * wpt + r;
-      if (i < nwords) {
-        pre[i] = run;
-        run += (uint32_t)__popc(bits[i]);
-      }
-    }
-  }
-  for (int i = tid; i < ne; i += NT) umask[i] = 0u;
-  __syncthreads();
-  const int nu = (int)red[15];
-  for (int e = tid; e < ne; e += NT) {
-    const int tau = e / nblk, j = e - tau * nblk;
-    const int t = t0 + tau;
-    if (t <= tlast) {
-      const int st = cu ? seq_start_of(cu, nseq, t) : 0;
-      const int b = blk[(int64_t)t * nblk + j];
-      if (b >= 0 && b <= (t - st) / B) {
-        const int r = st + b * B - base;
-        const int u = (int)(pre[r >> 5] + (uint32_t)__popc(bits[r >> 5] & ((1u << (r & 31)) - 1u)));
-        ulo[u] = r + base;
-        atomicOr(&umask[u], 1u << tau);
-      }
-    }
-  }
-  __syncthreads();
+  const int nu = group_union<NT>(tbl, blk, cu, nseq, t0, tlast, GT, B, nblk, base, nwords);
 
   // ---- this lane's query row: column tile w, row 16 w + n (token tau, head h)
   const int row = 16 * w + n;
@@ -623,7 +560,7 @@ hipError_t launch_grouped(const void* q, const void* k, const void* v, const int
                           float scale, void* out, float* lse, hipStream_t st) {
   const int G = Hq / Hkv;
   const int GT = grp_tokens(G);
-  const int nwords = (maxlen + GT + 31) / 32 + 1;
+  const int nwords = grp_words(maxlen, GT);
   const size_t shm = grp_lds_bytes(D, G, nblk, maxlen);
   if (shm > 160 * 1024) return hipErrorInvalidValue;
   hipError_t e = hipFuncSetAttribute((const void*)block_gqa_group_kernel<D>,

@@ -284,8 +284,8 @@ sa_status sa_block_sparse_gqa_bwd(const void* q, const void* k, const void* v, c
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (T > 0) SA_DEBUG_RETURN(debug_offsets(cu_seqlens, num_seqs, T, max_seqlen, s));
   return launch_status(sa::launch_block_gqa_bwd(q, k, v, blk, dtype == SA_BF16, T, cu_seqlens, num_seqs,
-                                                Hq, Hkv, D, block_size, nblk, scale, dout, lse, dq, dk,
-                                                dv, s));
+                                                widest, Hq, Hkv, D, block_size, nblk, scale, dout, lse,
+                                                dq, dk, dv, s));
 }
 
 sa_status sa_kpool_expand(const int32_t* pools, int32_t T, const int32_t* cu_seqlens, int32_t num_seqs,

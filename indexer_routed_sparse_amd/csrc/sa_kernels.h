@@ -80,8 +80,9 @@ hipError_t launch_append_window(const int32_t* idx, const int32_t* cu, int nseq,
 
 // block_gqa_bwd.hip: zeroes dk and dv [T, Hkv, D] (fp32), then accumulates into them.
 hipError_t launch_block_gqa_bwd(const void* q, const void* k, const void* v, const int32_t* blk,
-                                bool bf16, int T, const int32_t* cu, int nseq, int Hq, int Hkv, int D,
-                                int block_size, int nblk, float scale, const void* dout,
-                                const float* lse, void* dq, float* dk, float* dv, hipStream_t st);
+                                bool bf16, int T, const int32_t* cu, int nseq, int maxlen, int Hq,
+                                int Hkv, int D, int block_size, int nblk, float scale,
+                                const void* dout, const float* lse, void* dq, float* dk, float* dv,
+                                hipStream_t st);
 
 }  // namespace sa

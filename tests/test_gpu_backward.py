@@ -188,6 +188,32 @@ def test_block_gqa_bwd_shapes_thd(sa, Hq, Hkv, D, B, dtype):
     assert np.all(dq[50] == 0)
 
 
+def test_block_gqa_bwd_long_sequence_per_token_kernel(sa):
+    """One 130,003-token sequence at D = 128: the grouped backward's rows, stages and
+    set-up tables would exceed the LDS, so the per-(token, kv head) kernel serves it.
+    Routes hold only the own block (16 keys), so a block's dk and dv come from its own
+    16 rows: the oracle runs on the rows of a few sampled blocks and their gradients
+    are compared in full."""
+    T, Hq, Hkv, D, B = 130_003, 2, 2, 128, 16
+    gen = torch.Generator(device=DEV).manual_seed(78)
+    q = torch.randn((T, Hq, D), generator=gen, device=DEV).to(torch.bfloat16)
+    k = torch.randn((T, Hkv, D), generator=gen, device=DEV).to(torch.bfloat16)
+    v = torch.randn((T, Hkv, D), generator=gen, device=DEV).to(torch.bfloat16)
+    dout = torch.randn((T, Hq, D), generator=gen, device=DEV).to(torch.bfloat16)
+    blk = (torch.arange(T, device=DEV) // B).to(torch.int32).reshape(T, 1).contiguous()
+    scale = 1 / math.sqrt(D)
+    out, lse = sa.block_sparse_gqa(q, k, v, blk, scale, block_size=B)
+    dq, dk, dv = sa.block_sparse_gqa_bwd(q, k, v, blk, dout, lse, scale, block_size=B)
+    torch.cuda.synchronize()
+    blocks = [0, 1, 777, 4000, T // B - 1, T // B]           # the last one is partial
+    rows = np.concatenate([np.arange(b * B, min(b * B + B, T)) for b in blocks])
+    rdq, rdk, rdv = oracle.block_sparse_gqa_bwd(q.cpu(), k.cpu(), v.cpu(), blk.cpu().numpy(), dout.cpu(),
+                                                B, scale, rows=rows)
+    grad_close(dq.float().cpu().numpy()[rows], rdq, "dq")
+    grad_close(dk.cpu().numpy()[rows], rdk[rows], "dk")
+    grad_close(dv.cpu().numpy()[rows], rdv[rows], "dv")
+
+
 def test_block_gqa_bwd_block_routed_workload(sa):
     """The block-routed workload's shapes (32/4 heads x 128, 64-key blocks, 16 blocks
     with the own block) on oracle routes over 2048 tokens: dq of every row, dk and dv."""
