@@ -40,6 +40,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaxRoute = 64;            // blocks per query row (API limit)
 constexpr int kWavesPerGroup = 4;
+constexpr float kHeadroom = 8.0f;        // log2 units a row's logits may exceed its reference
 
 typedef float floatx4v_t __attribute__((ext_vector_type(4)));
 
@@ -270,7 +271,8 @@ __global__ __launch_bounds__(kWavesPerGroup * 64) void block_gqa_bf16_kernel(
 //     O^T = V^T . P^T, both double-buffered; the next two sub-tiles' rows are in
 //     registers while the current one is computed;
 //   * a wave skips the MFMAs of a sub-tile none of its rows' tokens routes to; a row's
-//     online softmax ignores masked keys exactly (alpha 1, p 0).
+//     online softmax ignores masked keys exactly (alpha 1, p 0) and rescales O only
+//     when a logit passes the row's reference by more than 2^8.
 // Measured on the block-routed workload: two workgroups of four waves with two column
 // tiles each, one sub-tile ahead, 0.89 ms; skipping per column tile 0.79; two sub-tiles
 // ahead 0.77; eight waves of one tile (twice the waves per SIMD) 0.68; 64-key sub-tiles
@@ -426,28 +428,31 @@ __global__ __launch_bounds__(kGrpWaves * 64) __attribute__((amdgpu_waves_per_eu(
             const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(st + (16 * kt + n) * KSB + 64 * ks + 16 * quad);
             S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], S[kt], 0, 0, 0);
           }
-        const bool in = row_ok && ((msk >> tau) & 1u);
+        // keys 4 quad + e (+16) of the piece count below lim: the row routes here, the
+        // key is in the piece and causal for the row
+        const int lim = (row_ok && ((msk >> tau) & 1u)) ? min(nk, tq - lo + 1) - 4 * quad : 0;
         float mx = -__builtin_huge_valf();
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int kk = 16 * kt + 4 * quad + e;
-            const bool ok = in && kk < nk && lo + kk <= tq;
-            const float x = ok ? S[kt][e] * scale_log2 : -__builtin_huge_valf();
+            const float x = 16 * kt + e < lim ? S[kt][e] * scale_log2 : -__builtin_huge_valf();
             S[kt][e] = x;
             mx = __builtin_elementwise_maximum(mx, x);
           }
         mx = quad_max(mx);
-        const float m_new = __builtin_elementwise_maximum(m_run, mx);
-        const bool none = m_new == -__builtin_huge_valf();
-        const float alpha = none ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        if (ballot(alpha != 1.0f)) {
+        // fixed reference: O and l are rescaled only when a max passes the row's
+        // reference by more than 2^8 (the first valid key always does)
+        if (ballot(mx > m_run + kHeadroom)) {             // uniform
+          const bool up = mx > m_run + kHeadroom;
+          const float alpha = up ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;   // 0 from -inf
+          m_run = up ? mx : m_run;
 #pragma unroll
           for (int i = 0; i < NDT; ++i) O[i] *= alpha;
+          l_run *= alpha;
         }
-        l_run *= alpha;
+        const bool none = m_run == -__builtin_huge_valf();
+        const float m_new = m_run;
         float pf[8];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
