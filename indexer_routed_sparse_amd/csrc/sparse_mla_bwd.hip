@@ -301,6 +301,243 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_bf16_kernel(
   }
 }
 
+// bf16, 32 heads per workgroup (H a multiple of 32): one workgroup per (token, 32-head
+// block), four waves on the same 32-key sub-tile, staged once in LDS (double-buffered,
+// the next sub-tile's rows in registers meanwhile). Wave (hg, kh) = (w / 2, w % 2)
+// forms S and dP of heads 16 hg .. +15 against keys 16 kh .. +15 (16x16x32 MFMAs, q's A
+// operands in registers, dout's from LDS, the key rows as B operands), then P and dS.
+// dS and P of the 32 heads x 32 keys meet in LDS; each wave then takes a quarter of
+// the output tiles (16 x 16) of dkv = dS^T q + P^T dout and of dq = dS K, contracting
+// over all 32 heads or all 32 keys: every kv row of a token receives one atomic add
+// per element from each 32-head block (four at 128 heads) instead of one per 16-head
+// group, and each row is gathered by half as many workgroups. dq accumulates in
+// registers across sub-tiles. A first pass over the same sub-tiles forms D.
+constexpr int kB32 = 32;          // heads per workgroup, keys per sub-tile
+constexpr int kXR = kB32 * 2 + 16;  // [key][head] or [head][key] bf16 exchange rows (bytes)
+
+template <int DQK>
+constexpr size_t bwd32_lds_bytes() {
+  return (size_t)kB32 * krow_bytes<DQK>() + (size_t)kB32 * drow_bytes() +
+         (size_t)2 * kB32 * krow_bytes<DQK>() + (size_t)3 * kB32 * kXR + 2 * kB32 * sizeof(float);
+}
+
+template <int DQK>
+__global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_h32_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, int H, int topk, float scale,
+    const float* __restrict__ sink, uint16_t* __restrict__ dq, float* __restrict__ dkv,
+    float* __restrict__ dsink) {
+  constexpr int KRB = krow_bytes<DQK>();
+  constexpr int DRB = drow_bytes();
+  constexpr int NK = DQK / 32;            // 32-wide k-steps of S
+  constexpr int NV = 512 / 32;            // ... of dP
+  constexpr int NCT = DQK / 16;           // 16-channel tiles of dkv and dq
+  constexpr int NVT = 512 / 16;           // ... that carry the value part
+  constexpr int TPW = 2 * NCT / kWaves;   // output tiles of dkv (and of dq) per wave
+  constexpr int CPR = DQK * 2 / 16;       // 16-byte chunks per key row
+  constexpr int NLD = (kB32 * CPR + kWaves * 64 - 1) / (kWaves * 64);   // chunks per thread
+  static_assert((2 * NCT) % kWaves == 0, "tiles split evenly");
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  char* q_l = lds;                                        // [32 heads][KRB]
+  char* d_l = q_l + kB32 * KRB;                           // [32 heads][DRB]
+  char* k_l = d_l + kB32 * DRB;                           // [2][32 keys][KRB]
+  char* xS = k_l + 2 * kB32 * KRB;                        // dS  [32 keys][kXR] (heads)
+  char* xP = xS + kB32 * kXR;                             // P   [32 keys][kXR]
+  char* xT = xP + kB32 * kXR;                             // dS  [32 heads][kXR] (keys)
+  float* dD = reinterpret_cast<float*>(xT + kB32 * kXR);  // [2 key halves][32 heads]
+
+  const int t = blockIdx.x;
+  const int h0 = blockIdx.y * kB32;
+  const int tid = threadIdx.x, w = tid >> 6, L = tid & 63;
+  const int g = L >> 4, n = L & 15;
+  const int hg = w >> 1, kh = w & 1;
+
+  // ---- q and dout of the 32 heads into LDS
+  for (int c = tid; c < kB32 * CPR; c += kWaves * 64) {
+    const int hh = c / CPR, p = c % CPR;
+    *reinterpret_cast<bf16x8_t*>(q_l + hh * KRB + 16 * p) =
+        *reinterpret_cast<const bf16x8_t*>(q + ((int64_t)t * H + h0 + hh) * DQK + 8 * p);
+  }
+  for (int c = tid; c < kB32 * 64; c += kWaves * 64) {
+    const int hh = c >> 6, p = c & 63;
+    *reinterpret_cast<bf16x8_t*>(d_l + hh * DRB + 16 * p) =
+        *reinterpret_cast<const bf16x8_t*>(dout + ((int64_t)t * H + h0 + hh) * 512 + 8 * p);
+  }
+  __syncthreads();
+
+  // heads 16 hg + 4 g + i of this lane (rows of its S / dP tile)
+  float lse2[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lse2[i] = lse[(int64_t)t * H + h0 + 16 * hg + 4 * g + i] * kLog2e;
+  bf16x8_t qa[NK];                          // A operands: head 16 hg + n, channels 32 ks + 8 g
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks)
+    qa[ks] = *reinterpret_cast<const bf16x8_t*>(q_l + (16 * hg + n) * KRB + 64 * ks + 16 * g);
+
+  const int32_t* irow = idx + (int64_t)t * topk;
+  const int nsub = (topk + kB32 - 1) / kB32;
+  const float sc2 = scale * kLog2e;
+
+  bf16x8_t nx[NLD];
+  auto load = [&](int sub) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < NLD; ++m) {
+      const int c = tid + kWaves * 64 * m, r = c / CPR, p = c % CPR;
+      const int j = sub * kB32 + r;
+      int row = (c < kB32 * CPR && j < topk) ? irow[j] : -1;
+      row = row < 0 ? 0 : row;                 // masked slot: any finite row
+      nx[m] = *reinterpret_cast<const bf16x8_t*>(kv + (int64_t)row * DQK + 8 * p);
+    }
+  };
+  auto stage = [&](char* kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < NLD; ++m) {
+      const int c = tid + kWaves * 64 * m, r = c / CPR, p = c % CPR;
+      if (c < kB32 * CPR) *reinterpret_cast<bf16x8_t*>(kt + r * KRB + 16 * p) = nx[m];
+    }
+  };
+  // S and dP of this wave's 16 heads x 16 keys; P of the valid slots
+  auto scores = [&](const char* kt, int sub, float (&P)[4], floatx4v_t& dP) __attribute__((always_inline)) {
+    const int jn = sub * kB32 + 16 * kh + n;
+    const int rown = jn < topk ? irow[jn] : -1;
+    const char* krow = kt + (16 * kh + n) * KRB + 16 * g;
+    const char* drow = d_l + (16 * hg + n) * DRB + 16 * g;
+    floatx4v_t S = floatx4v_t{};
+    dP = floatx4v_t{};
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+      const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(krow + 64 * ks);
+      S = mfma16x32(qa[ks], b, S);
+      if (ks < NV) dP = mfma16x32(*reinterpret_cast<const bf16x8_t*>(drow + 64 * ks), b, dP);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      P[i] = rown >= 0 && lse2[i] > -__builtin_huge_valf() ? __builtin_amdgcn_exp2f(S[i] * sc2 - lse2[i]) : 0.0f;
+  };
+
+  // ---- pass 1: D = sum_j p_j dp_j per head
+  float dpart[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (nsub > 0) load(0);
+#pragma unroll 1
+  for (int sub = 0; sub < nsub; ++sub) {
+    char* kt = k_l + (sub & 1) * kB32 * KRB;
+    stage(kt);
+    __syncthreads();
+    if (sub + 1 < nsub) load(sub + 1);
+    float P[4];
+    floatx4v_t dP;
+    scores(kt, sub, P, dP);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dpart[i] = fmaf(P[i], dP[i], dpart[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {          // over the 16 keys (lanes n) of the wave's half
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) dpart[i] += __shfl_xor(dpart[i], off, 64);
+    if (n == 0) dD[kh * kB32 + 16 * hg + 4 * g + i] = dpart[i];
+  }
+  __syncthreads();
+  float Dh[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) Dh[i] = dD[16 * hg + 4 * g + i] + dD[kB32 + 16 * hg + 4 * g + i];
+  // the sink's probability exp(sink - lse) times -D is its logit's gradient
+  if (dsink && tid < kB32) {
+    const int hh = h0 + tid;
+    const float D = dD[tid] + dD[kB32 + tid];
+    atomicAdd(dsink + hh, -__builtin_amdgcn_exp2f((sink[hh] - lse[(int64_t)t * H + hh]) * kLog2e) * D);
+  }
+
+  floatx4v_t dqa[TPW];       // dq tiles tt = w + 4 i: head tile tt / NCT, channel tile tt % NCT
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) dqa[i] = floatx4v_t{};
+
+  // ---- pass 2: dS; dkv and dq over the 32 heads / 32 keys
+  if (nsub > 0) load(0);
+#pragma unroll 1
+  for (int sub = 0; sub < nsub; ++sub) {
+    char* kt = k_l + (sub & 1) * kB32 * KRB;
+    stage(kt);
+    __syncthreads();                   // also: every wave is done with the exchange rows
+    if (sub + 1 < nsub) load(sub + 1);
+    float P[4], dS[4];
+    floatx4v_t dP;
+    scores(kt, sub, P, dP);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dS[i] = P[i] * (dP[i] - Dh[i]) * scale;
+    {
+      const int key = 16 * kh + n, head = 16 * hg + 4 * g;
+      *reinterpret_cast<short4_t*>(xS + key * kXR + head * 2) = pack4(dS[0], dS[1], dS[2], dS[3]);
+      *reinterpret_cast<short4_t*>(xP + key * kXR + head * 2) = pack4(P[0], P[1], P[2], P[3]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint16_t*>(xT + (head + i) * kXR + key * 2) = f2bf_bits(dS[i]);
+    }
+    // kv rows of this lane's dkv keys: 16 kt2 + 4 g + i
+    int krow[2][4];
+#pragma unroll
+    for (int kt2 = 0; kt2 < 2; ++kt2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = sub * kB32 + 16 * kt2 + 4 * g + i;
+        krow[kt2][i] = j < topk ? irow[j] : -1;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int tt = w + kWaves * i;
+      const int t2 = tt / NCT, ct = tt % NCT;
+      const int toff = (16 * ct + 4 * (n & 3)) * 2;
+      // dkv tile: keys 16 t2 + ..., channels 16 ct + ...; k = heads {4g + e, 16 + 4g + e}
+      {
+        const char* ar = xS + (16 * t2 + n) * kXR + 8 * g;
+        const uint2 a0 = *reinterpret_cast<const uint2*>(ar);
+        const uint2 a1 = *reinterpret_cast<const uint2*>(ar + 32);
+        const short4_t b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(q_l + (4 * g + (n >> 2)) * KRB + toff));
+        const short4_t b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(q_l + (16 + 4 * g + (n >> 2)) * KRB + toff));
+        const short __attribute__((ext_vector_type(8))) b8 = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        floatx4v_t acc = mfma16x32(__builtin_bit_cast(bf16x8_t, make_uint4(a0.x, a0.y, a1.x, a1.y)),
+                                   __builtin_bit_cast(bf16x8_t, b8), floatx4v_t{});
+        if (ct < NVT) {
+          const char* pr = xP + (16 * t2 + n) * kXR + 8 * g;
+          const uint2 p0 = *reinterpret_cast<const uint2*>(pr);
+          const uint2 p1 = *reinterpret_cast<const uint2*>(pr + 32);
+          const short4_t c0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(d_l + (4 * g + (n >> 2)) * DRB + toff));
+          const short4_t c1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(d_l + (16 + 4 * g + (n >> 2)) * DRB + toff));
+          const short __attribute__((ext_vector_type(8))) c8 = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+          acc = mfma16x32(__builtin_bit_cast(bf16x8_t, make_uint4(p0.x, p0.y, p1.x, p1.y)),
+                          __builtin_bit_cast(bf16x8_t, c8), acc);
+        }
+        // lane (g, n): keys 16 t2 + 4 g + e, channel 16 ct + n
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = t2 ? krow[1][e] : krow[0][e];
+          if (r >= 0) atomicAdd(dkv + (int64_t)r * DQK + 16 * ct + n, acc[e]);
+        }
+      }
+      // dq tile: heads 16 t2 + ..., channels 16 ct + ...; k = keys {4g + e, 16 + 4g + e}
+      {
+        const char* ar = xT + (16 * t2 + n) * kXR + 8 * g;
+        const uint2 a0 = *reinterpret_cast<const uint2*>(ar);
+        const uint2 a1 = *reinterpret_cast<const uint2*>(ar + 32);
+        const short4_t b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(kt + (4 * g + (n >> 2)) * KRB + toff));
+        const short4_t b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(kt + (16 + 4 * g + (n >> 2)) * KRB + toff));
+        const short __attribute__((ext_vector_type(8))) b8 = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        dqa[i] = mfma16x32(__builtin_bit_cast(bf16x8_t, make_uint4(a0.x, a0.y, a1.x, a1.y)),
+                           __builtin_bit_cast(bf16x8_t, b8), dqa[i]);
+      }
+    }
+  }
+
+  // ---- dq: lane (g, n) of tile tt holds heads 16 (tt / NCT) + 4 g + e, channel 16 (tt % NCT) + n
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int tt = w + kWaves * i;
+    const int ht = tt / NCT, ct = tt % NCT;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      dq[((int64_t)t * H + h0 + 16 * ht + 4 * g + e) * DQK + 16 * ct + n] = f2bf_bits(dqa[i][e]);
+  }
+}
+
 // fp32: one workgroup per (token, head); plain arithmetic, dkv by atomics.
 constexpr int kNT = 256;
 
@@ -513,6 +750,20 @@ hipError_t launch_bwd_bf16(const void* q, const void* kv, const int32_t* idx, co
   return hipGetLastError();
 }
 
+template <int DQK>
+hipError_t launch_bwd32(const void* q, const void* kv, const int32_t* idx, const void* dout,
+                        const float* lse, int T, int H, int topk, float scale, const float* sink,
+                        void* dq, float* dkv, float* dsink, hipStream_t st) {
+  const size_t shm = bwd32_lds_bytes<DQK>();
+  hipError_t e = hipFuncSetAttribute((const void*)sparse_mla_bwd_h32_kernel<DQK>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((sparse_mla_bwd_h32_kernel<DQK>), dim3(T, H / kB32), dim3(kWaves * 64), shm, st,
+                     (const uint16_t*)q, (const uint16_t*)kv, idx, (const uint16_t*)dout, lse, H, topk,
+                     scale, sink, (uint16_t*)dq, dkv, dsink);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_sparse_mla_bwd(const void* q, const void* kv, const int32_t* idx, const void* dout,
@@ -525,6 +776,10 @@ hipError_t launch_sparse_mla_bwd(const void* q, const void* kv, const int32_t* i
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || T == 0) return e;
   if (bf16) {
+    if (H % kB32 == 0) {
+      if (d_qk == 576) return launch_bwd32<576>(q, kv, idx, dout, lse, T, H, topk, scale, sink, dq, dkv, dsink, st);
+      return launch_bwd32<512>(q, kv, idx, dout, lse, T, H, topk, scale, sink, dq, dkv, dsink, st);
+    }
     if (d_qk == 576) return launch_bwd_bf16<576>(q, kv, idx, dout, lse, T, H, topk, scale, sink, dq, dkv, dsink, st);
     return launch_bwd_bf16<512>(q, kv, idx, dout, lse, T, H, topk, scale, sink, dq, dkv, dsink, st);
   }
