@@ -15,12 +15,15 @@
 // ever formed ("streaming": no [T, T] matrix).
 //
 // bf16 kernel (gfx950): one workgroup per row, four waves taking turns over 16-slot
-// sub-tiles. The row's heads are the rows of 16x16x32 MFMA tiles (q_I as A operands
-// in registers, the 16 gathered key rows as B operands straight from memory). Pass 1
-// forms the scores I_j into LDS; the row's log-sum-exp, loss and dI follow; pass 2
-// recomputes z per sub-tile for dw, dq_I^T += K^T dz^T (K^T by transposing reads of the
-// staged rows, dz^T through a small LDS transpose) and dk_I = dz^T q_I (q_I by
-// transposing LDS reads), added to k_I's gradient with atomics.
+// sub-tiles; the row's slot indices are staged in LDS first. The row's heads are the
+// rows of 16x16x32 MFMA tiles (q_I as A operands in registers, the 16 gathered key
+// rows as B operands). Pass 1 reads the rows straight into B operands and forms the
+// scores I_j into LDS; the row's log-sum-exp, loss and dI follow; pass 2 stages the
+// rows in LDS and recomputes z per sub-tile for dw, dq_I^T += K^T dz^T (K^T by
+// transposing reads of the staged rows, dz^T through a small LDS transpose) and
+// dk_I = dz^T q_I (q_I by transposing LDS reads), added to k_I's gradient with atomics.
+// In both passes each wave requests its next sub-tile's rows before computing the
+// current one.
 #include "sa_common.h"
 #include "sa_kernels.h"
 
@@ -53,7 +56,7 @@ SA_DEVICE __host__ inline int score_slots(int topk) { return (topk + 3) & ~3; }
 
 template <int NHB, int DI>
 constexpr size_t kl_lds_bytes(int topk) {
-  const size_t head = (size_t)16 * NHB * rowb<DI>() + (size_t)score_slots(topk) * 4 + 64;
+  const size_t head = (size_t)16 * NHB * rowb<DI>() + (size_t)score_slots(topk) * 8 + 64;
   const size_t work = (size_t)kWaves * (kSK * rowb<DI>() + 16 * NHB * kSK * 2) + (size_t)kWaves * 16 * NHB * 4;
   const size_t red = (size_t)kWaves * 16 * NHB * (DI / 2) * 4;    // dq_I reduction, half of DI per pass
   return head + (work > red ? work : red);
@@ -75,7 +78,8 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kl_bf16_kernel(
   extern __shared__ __attribute__((aligned(16))) char lds[];
   char* q_l = lds;                                              // [H][RB]
   float* Il = reinterpret_cast<float*>(q_l + H * RB);           // [topk] scores, then dI
-  float* bc = Il + score_slots(topk);                           // [16] broadcast slots
+  int32_t* il = reinterpret_cast<int32_t*>(Il + score_slots(topk));   // [topk] slot indices
+  float* bc = reinterpret_cast<float*>(il + score_slots(topk));       // [16] broadcast slots
   char* work = reinterpret_cast<char*>(bc + 16);
   const int t = blockIdx.x;
   const int tid = threadIdx.x, w = tid >> 6, L = tid & 63;
@@ -89,6 +93,8 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kl_bf16_kernel(
     *reinterpret_cast<bf16x8_t*>(q_l + hh * RB + 16 * p) =
         *reinterpret_cast<const bf16x8_t*>(qI + ((int64_t)t * H + hh) * DI + 8 * p);
   }
+  // the row's slot indices, staged once: every later row load takes its index from LDS
+  for (int j = tid; j < topk; j += kWaves * 64) il[j] = idx[(int64_t)t * topk + j];
   __syncthreads();
   bf16x8_t qa[NHB][KS];                // head 16 hb + n, dims 32 ks + 8 g
   float wr[NHB][4];                    // w of heads 16 hb + 4 g + i
@@ -100,17 +106,11 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kl_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) wr[hb][i] = wI[(int64_t)t * H + 16 * hb + 4 * g + i];
   }
-  const int32_t* irow = idx + (int64_t)t * topk;
   const int nsub = (topk + kSK - 1) / kSK;
+  auto slot = [&](int j) __attribute__((always_inline)) { return j < topk ? il[j] : -1; };
 
-  // z tiles of one sub-tile: key rows read straight into B operands (key n, dims 32ks+8g)
-  auto ztiles = [&](int sub, floatx4v_t (&Z)[NHB], int& row) __attribute__((always_inline)) {
-    const int j = sub * kSK + n;
-    row = j < topk ? irow[j] : -1;
-    const uint16_t* kr = kI + (int64_t)(row < 0 ? 0 : row) * DI + 8 * g;
-    bf16x8_t kb[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kb[ks] = *reinterpret_cast<const bf16x8_t*>(kr + 32 * ks);
+  // z tiles of one sub-tile from the B operands kb (key n, dims 32 ks + 8 g)
+  auto ztiles = [&](const bf16x8_t (&kb)[KS], floatx4v_t (&Z)[NHB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
       Z[hb] = floatx4v_t{};
@@ -118,13 +118,21 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kl_bf16_kernel(
       for (int ks = 0; ks < KS; ++ks) Z[hb] = mfma16x32(qa[hb][ks], kb[ks], Z[hb]);
     }
   };
+  // key row of slot column n of a sub-tile, read straight into B operands
+  auto kload = [&](int sub, bf16x8_t (&kb)[KS]) __attribute__((always_inline)) {
+    const int row = slot(sub * kSK + n);
+    const uint16_t* kr = kI + (int64_t)(row < 0 ? 0 : row) * DI + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kb[ks] = *reinterpret_cast<const bf16x8_t*>(kr + 32 * ks);
+  };
 
-  // ---- pass 1: scores of the slots (-inf on -1 slots)
-#pragma unroll 1
-  for (int sub = w; sub < nsub; sub += kWaves) {
+  // ---- pass 1: scores of the slots (-inf on -1 slots). The wave's next sub-tile is
+  //      requested before the current one is computed; the loop body is written out
+  //      twice with the two operand buffers swapped, so no in-flight load is copied.
+  auto pass1 = [&](int sub, const bf16x8_t (&kb)[KS], bf16x8_t (&kn)[KS]) __attribute__((always_inline)) {
+    if (sub + kWaves < nsub) kload(sub + kWaves, kn);
     floatx4v_t Z[NHB];
-    int row;
-    ztiles(sub, Z, row);
+    ztiles(kb, Z);
     float acc = 0.0f;
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
@@ -133,7 +141,16 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kl_bf16_kernel(
     acc += __shfl_xor(acc, 16, 64);
     acc += __shfl_xor(acc, 32, 64);
     const int j = sub * kSK + n;
-    if (g == 0 && j < topk) Il[j] = row >= 0 ? acc : -__builtin_huge_valf();
+    if (g == 0 && j < topk) Il[j] = il[j] >= 0 ? acc : -__builtin_huge_valf();
+  };
+  {
+    bf16x8_t kbA[KS], kbB[KS];
+    if (w < nsub) kload(w, kbA);
+#pragma unroll 1
+    for (int sub = w; sub < nsub; sub += 2 * kWaves) {
+      pass1(sub, kbA, kbB);
+      if (sub + kWaves < nsub) pass1(sub + kWaves, kbB, kbA);
+    }
   }
   __syncthreads();
   // ---- row max, log-sum-exp, loss and dI (block-wide over the slots)
@@ -192,22 +209,33 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kl_bf16_kernel(
   for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) dwl[hb][i] = 0.0f;
-#pragma unroll 1
-  for (int sub = w; sub < nsub; sub += kWaves) {
-    // stage the 16 key rows for the transposing reads of K^T
+  // the 16 key rows of a sub-tile, as 16-byte chunks of this lane
+  auto rload = [&](int sub, bf16x8_t (&nx)[NLD]) __attribute__((always_inline)) {
 #pragma unroll
     for (int mm = 0; mm < NLD; ++mm) {
       const int c = L + 64 * mm, r = c / CPR, p = c % CPR;
-      const int j = sub * kSK + r;
-      int row = j < topk ? irow[j] : -1;
-      row = row < 0 ? 0 : row;
-      *reinterpret_cast<bf16x8_t*>(kt + r * RB + 16 * p) = *reinterpret_cast<const bf16x8_t*>(kI + (int64_t)row * DI + 8 * p);
+      const int row = slot(sub * kSK + r);
+      nx[mm] = *reinterpret_cast<const bf16x8_t*>(kI + (int64_t)(row < 0 ? 0 : row) * DI + 8 * p);
     }
+  };
+  // Pass 2 body: stages the sub-tile's rows (held in nx) for the transposing reads of
+  // K^T and reads its B operands back from there; the wave's next sub-tile is requested
+  // into nn first (again two buffers taking turns).
+  auto pass2 = [&](int sub, const bf16x8_t (&nx)[NLD], bf16x8_t (&nn)[NLD]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mm = 0; mm < NLD; ++mm) {
+      const int c = L + 64 * mm, r = c / CPR, p = c % CPR;
+      *reinterpret_cast<bf16x8_t*>(kt + r * RB + 16 * p) = nx[mm];
+    }
+    if (sub + kWaves < nsub) rload(sub + kWaves, nn);
+    __builtin_amdgcn_wave_barrier();
+    bf16x8_t kb[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kb[ks] = *reinterpret_cast<const bf16x8_t*>(kt + n * RB + 64 * ks + 16 * g);
     floatx4v_t Z[NHB];
-    int row;
-    ztiles(sub, Z, row);
+    ztiles(kb, Z);
     const int j = sub * kSK + n;
-    const float dI = (j < topk && row >= 0) ? Il[j] : 0.0f;
+    const float dI = slot(j) >= 0 ? Il[j] : 0.0f;
     short4_t dzA[NHB];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
@@ -224,10 +252,7 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kl_bf16_kernel(
     __builtin_amdgcn_wave_barrier();
     int krow[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int jj = sub * kSK + 4 * g + i;
-      krow[i] = jj < topk ? irow[jj] : -1;
-    }
+    for (int i = 0; i < 4; ++i) krow[i] = slot(sub * kSK + 4 * g + i);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const int toff = (16 * db + 4 * (n & 3)) * 2;
@@ -248,6 +273,15 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kl_bf16_kernel(
         if (krow[i] >= 0) atomicAdd(dk + (int64_t)krow[i] * DI + 16 * db + n, dkt[i]);
     }
     __builtin_amdgcn_wave_barrier();
+  };
+  {
+    bf16x8_t nxA[NLD], nxB[NLD];
+    if (w < nsub) rload(w, nxA);
+#pragma unroll 1
+    for (int sub = w; sub < nsub; sub += 2 * kWaves) {
+      pass2(sub, nxA, nxB);
+      if (sub + kWaves < nsub) pass2(sub + kWaves, nxB, nxA);
+    }
   }
   // dw: sum over the keys (lanes n), then over the waves
 #pragma unroll

@@ -533,10 +533,11 @@ constexpr int kStages = 2;
 constexpr size_t kLdsLimit = 160 * 1024;
 
 // k-steps of q kept in LDS (the rest stay in VGPRs): one wave has LDS to spare and
-// keeps all of q there; two waves keep 20 k-steps there, four waves 16 (the most
-// that leaves two gather stages and a 2048-slot index row in 160 KiB).
+// keeps all of q there; two waves keep 20 k-steps there, four waves 12 (24 k-steps in
+// VGPRs is the most that compiles without spills; each k-step moved out of LDS saves
+// 1 KiB of LDS reads per wave and key tile).
 template <int NW, int DQK>
-constexpr int q_in_lds() { return NW == 1 ? DQK / 16 : (NW == 2 ? 20 : 16); }
+constexpr int q_in_lds() { return NW == 1 ? DQK / 16 : (NW == 2 ? 20 : 12); }
 
 template <int NW, int DQK>
 size_t lds_bytes(int topk) { return mla_lds_bytes<NW, DQK, kStages, q_in_lds<NW, DQK>()>(topk); }

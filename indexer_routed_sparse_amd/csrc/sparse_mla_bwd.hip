@@ -138,14 +138,17 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_bf16_kernel(
   const int nsub = (topk + kSK - 1) / kSK;
   const float sc2 = scale * kLog2e;
 
+  // One index load per lane (slot kSK sub + (l mod 16), clamped to the last slot) and
+  // lane shuffles hand each chunk its row: a sub-tile's row loads wait for one index
+  // load, not for one per chunk.
   bf16x8_t nx[NLD];
   auto load = [&](int sub) __attribute__((always_inline)) {
+    const int ix = irow[min(sub * kSK + (L & (kSK - 1)), topk - 1)];
 #pragma unroll
     for (int m = 0; m < NLD; ++m) {
       const int c = L + 64 * m, r = c / CPR, p = c % CPR;
-      const int j = sub * kSK + r;
-      int row = j < topk ? irow[j] : -1;
-      row = row < 0 ? 0 : row;                 // masked slot: any finite row
+      int row = __shfl(ix, r, 64);
+      row = row < 0 ? 0 : row;                 // masked slot (or past topk): any finite row
       nx[m] = *reinterpret_cast<const bf16x8_t*>(kv + (int64_t)row * DQK + 8 * p);
     }
   };
@@ -337,6 +340,7 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_h32_kernel(
   constexpr int CPR = DQK * 2 / 16;       // 16-byte chunks per key row
   constexpr int NLD = (kB32 * CPR + kWaves * 64 - 1) / (kWaves * 64);   // chunks per thread
   static_assert((2 * NCT) % kWaves == 0, "tiles split evenly");
+  static_assert(NLD * kWaves * 64 == kB32 * CPR, "every thread loads NLD chunks");
   extern __shared__ __attribute__((aligned(16))) char lds[];
   char* q_l = lds;                                        // [32 heads][KRB]
   char* d_l = q_l + kB32 * KRB;                           // [32 heads][DRB]
@@ -378,14 +382,23 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_h32_kernel(
   const int nsub = (topk + kB32 - 1) / kB32;
   const float sc2 = scale * kLog2e;
 
+  // Slot indices of a sub-tile: lane l holds slot 32 sub + (l mod 32), clamped to the
+  // last slot (positions past topk are masked where they are used). Two registers
+  // take turns: the one of sub-tile `sub` is reloaded with sub-tile sub + 2's indices
+  // after its last use, and the loop body is written out twice with the two roles
+  // swapped, so no in-flight load is ever copied (a copy would wait for every memory
+  // operation issued before it, the dkv atomics included). The row loads take their
+  // indices by lane shuffles a whole sub-tile after the index load was issued.
+  auto idx_of = [&](int sub) __attribute__((always_inline)) {
+    return irow[min(sub * kB32 + (L & 31), topk - 1)];
+  };
   bf16x8_t nx[NLD];
-  auto load = [&](int sub) __attribute__((always_inline)) {
+  auto load = [&](int ix) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < NLD; ++m) {
       const int c = tid + kWaves * 64 * m, r = c / CPR, p = c % CPR;
-      const int j = sub * kB32 + r;
-      int row = (c < kB32 * CPR && j < topk) ? irow[j] : -1;
-      row = row < 0 ? 0 : row;                 // masked slot: any finite row
+      int row = __shfl(ix, r, 64);
+      row = row < 0 ? 0 : row;                 // masked slot (or past topk): any finite row
       nx[m] = *reinterpret_cast<const bf16x8_t*>(kv + (int64_t)row * DQK + 8 * p);
     }
   };
@@ -393,13 +406,13 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_h32_kernel(
 #pragma unroll
     for (int m = 0; m < NLD; ++m) {
       const int c = tid + kWaves * 64 * m, r = c / CPR, p = c % CPR;
-      if (c < kB32 * CPR) *reinterpret_cast<bf16x8_t*>(kt + r * KRB + 16 * p) = nx[m];
+      *reinterpret_cast<bf16x8_t*>(kt + r * KRB + 16 * p) = nx[m];
     }
   };
-  // S and dP of this wave's 16 heads x 16 keys; P of the valid slots
-  auto scores = [&](const char* kt, int sub, float (&P)[4], floatx4v_t& dP) __attribute__((always_inline)) {
-    const int jn = sub * kB32 + 16 * kh + n;
-    const int rown = jn < topk ? irow[jn] : -1;
+  // S and dP of this wave's 16 heads x 16 keys; P of the valid slots (ix: the
+  // sub-tile's slot indices)
+  auto scores = [&](const char* kt, int sub, int ix, float (&P)[4], floatx4v_t& dP) __attribute__((always_inline)) {
+    const int rown = sub * kB32 + 16 * kh + n < topk ? __shfl(ix, 16 * kh + n, 64) : -1;
     const char* krow = kt + (16 * kh + n) * KRB + 16 * g;
     const char* drow = d_l + (16 * hg + n) * DRB + 16 * g;
     floatx4v_t S = floatx4v_t{};
@@ -417,18 +430,28 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_h32_kernel(
 
   // ---- pass 1: D = sum_j p_j dp_j per head
   float dpart[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (nsub > 0) load(0);
-#pragma unroll 1
-  for (int sub = 0; sub < nsub; ++sub) {
+  auto pass1 = [&](int sub, int& ixc, int ixn) __attribute__((always_inline)) {
     char* kt = k_l + (sub & 1) * kB32 * KRB;
     stage(kt);
     __syncthreads();
-    if (sub + 1 < nsub) load(sub + 1);
+    if (sub + 1 < nsub) load(ixn);
     float P[4];
     floatx4v_t dP;
-    scores(kt, sub, P, dP);
+    scores(kt, sub, ixc, P, dP);
+    ixc = idx_of(sub + 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dpart[i] = fmaf(P[i], dP[i], dpart[i]);
+  };
+  int ixa = 0, ixb = 0;       // indices of sub-tiles of even / odd number
+  if (nsub > 0) {
+    ixa = idx_of(0);
+    ixb = idx_of(1);
+    load(ixa);
+  }
+#pragma unroll 1
+  for (int sub = 0; sub < nsub; sub += 2) {
+    pass1(sub, ixa, ixb);
+    if (sub + 1 < nsub) pass1(sub + 1, ixb, ixa);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {          // over the 16 keys (lanes n) of the wave's half
@@ -452,16 +475,13 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_h32_kernel(
   for (int i = 0; i < TPW; ++i) dqa[i] = floatx4v_t{};
 
   // ---- pass 2: dS; dkv and dq over the 32 heads / 32 keys
-  if (nsub > 0) load(0);
-#pragma unroll 1
-  for (int sub = 0; sub < nsub; ++sub) {
+  auto pass2 = [&](int sub, int& ixc, int ixn) __attribute__((always_inline)) {
     char* kt = k_l + (sub & 1) * kB32 * KRB;
     stage(kt);
     __syncthreads();                   // also: every wave is done with the exchange rows
-    if (sub + 1 < nsub) load(sub + 1);
     float P[4], dS[4];
     floatx4v_t dP;
-    scores(kt, sub, P, dP);
+    scores(kt, sub, ixc, P, dP);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dS[i] = P[i] * (dP[i] - Dh[i]) * scale;
     {
@@ -477,12 +497,18 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_h32_kernel(
     for (int kt2 = 0; kt2 < 2; ++kt2)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int j = sub * kB32 + 16 * kt2 + 4 * g + i;
-        krow[kt2][i] = j < topk ? irow[j] : -1;
+        const int r = 16 * kt2 + 4 * g + i;
+        krow[kt2][i] = sub * kB32 + r < topk ? __shfl(ixc, r, 64) : -1;
       }
+    ixc = idx_of(sub + 2);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
+      // The next sub-tile's rows are requested after the first third of the tiles: the
+      // wait for them (at the next staging) then spans at most the atomics of the other
+      // two thirds (48 at d_qk 576, within the 63 the wait counter can name), not the
+      // atomics issued before the loads.
+      if (i == TPW / 3 && sub + 1 < nsub) load(ixn);
       const int tt = w + kWaves * i;
       const int t2 = tt / NCT, ct = tt % NCT;
       const int toff = (16 * ct + 4 * (n & 3)) * 2;
@@ -525,6 +551,16 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_h32_kernel(
                            __builtin_bit_cast(bf16x8_t, b8), dqa[i]);
       }
     }
+  };
+  if (nsub > 0) {
+    ixa = idx_of(0);
+    ixb = idx_of(1);
+    load(ixa);
+  }
+#pragma unroll 1
+  for (int sub = 0; sub < nsub; sub += 2) {
+    pass2(sub, ixa, ixb);
+    if (sub + 1 < nsub) pass2(sub + 1, ixb, ixa);
   }
 
   // ---- dq: lane (g, n) of tile tt holds heads 16 (tt / NCT) + 4 g + e, channel 16 (tt % NCT) + n
@@ -656,30 +692,36 @@ __global__ __launch_bounds__(kTW * 64) void attn_teacher_bf16_kernel(
       lse2[i] = (hh < H ? lse[(int64_t)t * H + hh] : -__builtin_huge_valf()) * kLog2e;
     }
   }
+  // Slot indices of a sub-tile: lane l holds slot kTK sub + (l mod 32), clamped to the
+  // last slot. As in the backward: two registers take turns (the loop body is written
+  // out twice), each reloaded two sub-tiles ahead after its last use, and the row loads
+  // take their indices by lane shuffles, so no load waits for an index load.
+  auto idx_of = [&](int sub) __attribute__((always_inline)) {
+    return irow[min(sub * kTK + (L & 31), topk - 1)];
+  };
   bf16x8_t nx[NLD];
-  auto load = [&](int sub) __attribute__((always_inline)) {
+  auto load = [&](int ix) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < NLD; ++m) {
       const int c = tid + kTW * 64 * m, r = c / CPR, p = c % CPR;
-      const int j = sub * kTK + r;
-      int row = (c < kTK * CPR && j < topk) ? irow[j] : -1;
-      row = row < 0 ? 0 : row;
+      int row = __shfl(ix, r < kTK ? r : 0, 64);
+      row = row < 0 || c >= kTK * CPR ? 0 : row;
       nx[m] = *reinterpret_cast<const bf16x8_t*>(kv + (int64_t)row * DQK + 8 * p);
     }
   };
-  auto finish = [&](int sub) __attribute__((always_inline)) {   // threads 0..kTK-1
+  // threads 0..kTK-1: slot sub kTK + tid; ok: the slot exists and is not -1
+  auto finish = [&](int sub, bool ok) __attribute__((always_inline)) {
     const int j = sub * kTK + tid;
     if (j < topk) {
       const float* pp = part + (sub & 1) * kTW * kTK + tid;
       float sum = 0.0f;
 #pragma unroll
       for (int v = 0; v < kTW; ++v) sum += pp[v * kTK];
-      teacher[(int64_t)t * topk + j] = irow[j] >= 0 ? sum * invH : 0.0f;
+      teacher[(int64_t)t * topk + j] = ok ? sum * invH : 0.0f;
     }
   };
-  load(0);
-#pragma unroll 1
-  for (int sub = 0; sub < nsub; ++sub) {
+  bool okc = false;   // this lane's slot of the previous sub-tile is valid (threads < kTK)
+  auto body = [&](int sub, int& ixc, int ixn) __attribute__((always_inline)) {
     char* kt = stage + (sub & 1) * kTK * KRB;
 #pragma unroll
     for (int m = 0; m < NLD; ++m) {
@@ -687,8 +729,10 @@ __global__ __launch_bounds__(kTW * 64) void attn_teacher_bf16_kernel(
       if (c < kTK * CPR) *reinterpret_cast<bf16x8_t*>(kt + r * KRB + 16 * p) = nx[m];
     }
     __syncthreads();
-    if (sub + 1 < nsub) load(sub + 1);
-    if (sub > 0 && tid < kTK) finish(sub - 1);
+    if (sub + 1 < nsub) load(ixn);
+    if (sub > 0 && tid < kTK) finish(sub - 1, okc);
+    okc = sub * kTK + L < topk && ixc >= 0;
+    ixc = idx_of(sub + 2);
     float* pw = part + (sub & 1) * kTW * kTK + w * kTK;
     if (heads) {
 #pragma unroll
@@ -709,9 +753,20 @@ __global__ __launch_bounds__(kTW * 64) void attn_teacher_bf16_kernel(
     } else if (L < kTK) {
       pw[L] = 0.0f;
     }
+  };
+  int ixa = 0, ixb = 0;       // indices of sub-tiles of even / odd number
+  if (nsub > 0) {
+    ixa = idx_of(0);
+    ixb = idx_of(1);
+    load(ixa);
+  }
+#pragma unroll 1
+  for (int sub = 0; sub < nsub; sub += 2) {
+    body(sub, ixa, ixb);
+    if (sub + 1 < nsub) body(sub + 1, ixb, ixa);
   }
   __syncthreads();
-  if (tid < kTK && nsub > 0) finish(nsub - 1);
+  if (tid < kTK && nsub > 0) finish(nsub - 1, okc);
 }
 
 __global__ __launch_bounds__(kNT) void attn_teacher_f32_kernel(
