@@ -172,7 +172,7 @@ def gradients_leg(sa, workloads, wl, x, m, idx, lse, n_timed, cpu_rows):
     if rows is not None:
         qh, kvh, dh = m["q"][torch.from_numpy(rows).to(dev)].cpu(), m["kv"].cpu(), dout[torch.from_numpy(rows).to(dev)].cpu()
         cpu = cpu_rate(lambda ih: oracle.sparse_mla_bwd(qh, kvh, ih[rows], dh, wl.scale), f_slot)
-    res["sparse_mla_bwd"] = _mfma_entry("sparse_mla_bwd_bf16_kernel", f_slot * slots, ms, cpu)
+    res["sparse_mla_bwd"] = _mfma_entry("sparse_mla_bwd_h32_kernel" if H % 32 == 0 else "sparse_mla_bwd_bf16_kernel", f_slot * slots, ms, cpu)
     del dq, dkv
     print("[bench] teacher", file=sys.stderr, flush=True)
     ms = _median_ms(lambda: sa.sa_attn_teacher(m["q"], m["kv"], idx, lse, wl.scale, teacher), n_timed)
@@ -548,7 +548,7 @@ def main():
                                                                gdq, gdk, gdv, block_size=64), 3)
             # S, dP, dq, dk, dv per attended key and q head
             result.setdefault("gradients", {})["block_gqa_bwd"] = _mfma_entry(
-                "block_gqa_bwd_bf16_kernel", 2.0 * wq.Hq * (3 * wq.D + 2 * wq.Dv) * attended, ms)
+                "block_gqa_bwd_group_kernel", 2.0 * wq.Hq * (3 * wq.D + 2 * wq.Dv) * attended, ms)
 
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline (bounded sample)", file=sys.stderr, flush=True)
