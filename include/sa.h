@@ -304,9 +304,10 @@ sa_status sa_sparse_mla_bwd(const void* q, const void* kv, const int32_t* idx, c
  *     teacher[t,j] = (1/H) sum_h exp(scale q[t,h,:] . kv[idx[t,j],:] - lse[t,h])
  *
  * and 0 on -1 slots (so a row's valid entries sum to 1). q, kv, idx, scale and lse are
- * those of sa_sparse_mla_fwd (lse its output). teacher [T,topk] fp32 is overwritten;
- * it is accumulated with floating-point atomics over groups of 16 heads, so its low
- * bits may vary from run to run. Limits as sa_sparse_mla_fwd's d_qk and H.
+ * those of sa_sparse_mla_fwd (lse its output). teacher [T,topk] fp32 is overwritten:
+ * for SA_BF16 one plain store per slot after the sum over all heads (deterministic);
+ * for SA_F32 accumulated with floating-point atomics over the heads (low bits may vary
+ * from run to run). Limits as sa_sparse_mla_fwd's d_qk and H.
  */
 sa_status sa_attn_teacher(const void* q, const void* kv, const int32_t* idx, const float* lse,
                           int dtype, int32_t T, int32_t S, int32_t H, int32_t d_qk, int32_t topk,

@@ -638,9 +638,6 @@ __global__ __launch_bounds__(kNT) void sparse_mla_bwd_f32_kernel(
 
 // Teacher of the sparse KL indexer loss: the head mean of the attention probability of
 // every slot, p[t,j] = (1/H) sum_h exp(scale q[t,h].kv[idx_j] - lse[t,h]); 0 on -1 slots.
-// Same layout as the backward's first pass (one workgroup per token and 16-head group,
-// four waves taking turns over 16-key sub-tiles); each group adds its 16 heads' share
-// to p (fp32, zeroed first) with one atomic per slot.
 // Teacher, bf16: one workgroup per token, eight waves; wave w owns heads [16w, 16w+16)
 // (q slices of its heads as A operands in registers, its rows of the forward's lse).
 // The token's slots go in 32-key sub-tiles that the whole workgroup gathers once into
@@ -769,6 +766,8 @@ __global__ __launch_bounds__(kTW * 64) void attn_teacher_bf16_kernel(
   if (tid < kTK && nsub > 0) finish(nsub - 1, okc);
 }
 
+// Teacher, fp32: one workgroup per (token, head), plain arithmetic; each head adds its
+// share exp(s - lse) / H to the slot with an atomic (the slots are zeroed first).
 __global__ __launch_bounds__(kNT) void attn_teacher_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kv, const int32_t* __restrict__ idx,
     const float* __restrict__ lse, int H, int d_qk, int topk, float scale, float* __restrict__ teacher) {
