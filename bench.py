@@ -129,11 +129,11 @@ def _median_ms(fn, n):
     return float(np.median([tm.ms() for tm in tms]))
 
 
-def _mfma_entry(kernel, flops, ms, cpu=None):
+def _mfma_entry(kernel, flops, ms, cpu=None, traffic=None):
     tf = flops / (ms * 1e-3) / 1e12
     e = {"kernel": kernel, "bound": "mfma", "ms": round(ms, 3), "achieved": round(tf, 2),
          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-         "flop": flops}
+         "flop": flops, "traffic": traffic}
     if cpu is not None:
         e["cpu_oracle"] = cpu
     return e
@@ -172,7 +172,9 @@ def gradients_leg(sa, workloads, wl, x, m, idx, lse, n_timed, cpu_rows):
     if rows is not None:
         qh, kvh, dh = m["q"][torch.from_numpy(rows).to(dev)].cpu(), m["kv"].cpu(), dout[torch.from_numpy(rows).to(dev)].cpu()
         cpu = cpu_rate(lambda ih: oracle.sparse_mla_bwd(qh, kvh, ih[rows], dh, wl.scale), f_slot)
-    res["sparse_mla_bwd"] = _mfma_entry("sparse_mla_bwd_h32_kernel" if H % 32 == 0 else "sparse_mla_bwd_bf16_kernel", f_slot * slots, ms, cpu)
+    res["sparse_mla_bwd"] = _mfma_entry("sparse_mla_bwd_h32_kernel" if H % 32 == 0 else "sparse_mla_bwd_bf16_kernel",
+                                        f_slot * slots, ms, cpu,
+                                        _traffic("sparse_mla_bwd_long_dsa", ["sparse_mla_bwd.hip", "sa_common.h"]))
     del dq, dkv
     print("[bench] teacher", file=sys.stderr, flush=True)
     ms = _median_ms(lambda: sa.sa_attn_teacher(m["q"], m["kv"], idx, lse, wl.scale, teacher), n_timed)
@@ -187,7 +189,8 @@ def gradients_leg(sa, workloads, wl, x, m, idx, lse, n_timed, cpu_rows):
         cpu = cpu_rate(teach, f_slot)
         th = np.zeros((T, idx.shape[1]))        # the oracle's own teacher on the sampled rows
         th[rows] = holder["t"]
-    res["attn_teacher"] = _mfma_entry("attn_teacher_bf16_kernel", f_slot * slots, ms, cpu)
+    res["attn_teacher"] = _mfma_entry("attn_teacher_bf16_kernel", f_slot * slots, ms, cpu,
+                                      _traffic("attn_teacher_long_dsa", ["sparse_mla_bwd.hip", "sa_common.h"]))
     print("[bench] indexer sparse-KL loss and gradients", file=sys.stderr, flush=True)
     ms = _median_ms(lambda: sa.indexer_kl_bwd(x["q_I"], x["k_I"], x["w"], idx, teacher), n_timed)
     HI, DI = x["q_I"].shape[1], x["q_I"].shape[2]
@@ -196,7 +199,8 @@ def gradients_leg(sa, workloads, wl, x, m, idx, lse, n_timed, cpu_rows):
     if rows is not None:
         qi, ki, wi = x["q_I"].cpu(), x["k_I"].cpu(), x["w"].cpu()
         cpu = cpu_rate(lambda ih: oracle.indexer_kl(qi, ki, wi, ih, th, rows=rows), f_slot)
-    res["indexer_kl_bwd"] = _mfma_entry("indexer_kl_bf16_kernel", f_slot * slots, ms, cpu)
+    res["indexer_kl_bwd"] = _mfma_entry("indexer_kl_bf16_kernel", f_slot * slots, ms, cpu,
+                                        _traffic("indexer_kl_long_dsa", ["indexer_kl.hip", "sa_common.h"]))
     del dout, teacher
     torch.cuda.synchronize()
     return res
@@ -229,8 +233,9 @@ def counters_pass():
 
     First a plain elementwise copy of COPY_ELEMS fp32 values (out = in * 1), whose
     FETCH_SIZE / WRITE_SIZE readings calibrate the counters against known bytes; then
-    the fused indexer + sparse MLA step once, then the standalone top-k select over
-    the materialised causal score matrix once.
+    the fused indexer + sparse MLA step once, the standalone top-k select over the
+    materialised causal score matrix once, the backward, teacher and KL kernels once
+    each on the same long-workload rows, and the block-routed GQA forward and backward.
     """
     import indexer_routed_sparse_amd as sa
     import workloads
@@ -255,7 +260,7 @@ def counters_pass():
     sa.sa_indexer_scores(x["q_I"], x["k_I"], x["w"], topk=K, out_idx=idx, ws=ws)
     sa.sa_sparse_mla_fwd(m["q"], m["kv"], idx, wl.scale, out, lse)
     torch.cuda.synchronize()
-    del out, lse
+    del out
     scores = torch.empty((T, T), dtype=torch.float32, device=dev)
     sa.sa_indexer_scores(x["q_I"], x["k_I"], x["w"], scores=scores)
     sel = torch.empty((T, K), dtype=torch.int32, device=dev)
@@ -263,7 +268,19 @@ def counters_pass():
     print("[counters] top-k select on materialised scores", file=sys.stderr, flush=True)
     sa.sa_topk_select(scores, sel)
     torch.cuda.synchronize()
-    del scores, sel, x, m, idx, ws
+    del scores, sel, ws
+    g = torch.Generator(device=dev).manual_seed(5)
+    dout = torch.randn((T, H, 512), generator=g, device=dev).to(torch.bfloat16)
+    dq = torch.empty_like(m["q"])
+    dkv = torch.empty((T, 576), dtype=torch.float32, device=dev)
+    teacher = torch.empty((T, K), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    print("[counters] sparse-MLA backward, teacher, indexer KL", file=sys.stderr, flush=True)
+    sa.sa_sparse_mla_bwd(m["q"], m["kv"], idx, dout, lse, wl.scale, dq, dkv)
+    sa.sa_attn_teacher(m["q"], m["kv"], idx, lse, wl.scale, teacher)
+    sa.indexer_kl_bwd(x["q_I"], x["k_I"], x["w"], idx, teacher)
+    torch.cuda.synchronize()
+    del dout, dq, dkv, teacher, lse, x, m, idx
     wq = workloads.WORKLOADS["block_gqa"]
     xq = workloads.indexer_inputs(wq, device=dev)
     gq = workloads.gqa_inputs(wq, device=dev)
@@ -273,7 +290,16 @@ def counters_pass():
                          out_idx=blk)
     torch.cuda.synchronize()
     print("[counters] block-routed GQA", file=sys.stderr, flush=True)
-    sa.sa_block_sparse_gqa_fwd(gq["q"], gq["k"], gq["v"], blk, wq.scale, go, block_size=64)
+    glse = torch.empty((wq.T, wq.Hq), dtype=torch.float32, device=dev)
+    sa.sa_block_sparse_gqa_fwd(gq["q"], gq["k"], gq["v"], blk, wq.scale, go, glse, block_size=64)
+    torch.cuda.synchronize()
+    gd = torch.randn(go.shape, generator=torch.Generator(device=dev).manual_seed(6), device=dev).to(torch.bfloat16)
+    gdq = torch.empty_like(gq["q"])
+    gdk = torch.empty(gq["k"].shape, dtype=torch.float32, device=dev)
+    gdv = torch.empty(gq["v"].shape, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    print("[counters] block-routed GQA backward", file=sys.stderr, flush=True)
+    sa.sa_block_sparse_gqa_bwd(gq["q"], gq["k"], gq["v"], blk, gd, glse, wq.scale, gdq, gdk, gdv, block_size=64)
     torch.cuda.synchronize()
     print("[counters] done", file=sys.stderr, flush=True)
 
@@ -323,6 +349,13 @@ def write_traffic(fetch_dir, write_dir, command):
                                  ["topk_select.hip", "sa_common.h"], None),
         "block_gqa_block_workload": (lambda n: "block_gqa_group_kernel" in n,
                                      ["block_gqa.hip", "sa_common.h"], 1),
+        "sparse_mla_bwd_long_dsa": (lambda n: "sparse_mla_bwd_h32_kernel" in n or "zero_f32_kernel" in n,
+                                    ["sparse_mla_bwd.hip", "sa_common.h"], None),
+        "attn_teacher_long_dsa": (lambda n: "attn_teacher_bf16_kernel" in n, ["sparse_mla_bwd.hip", "sa_common.h"], 1),
+        "indexer_kl_long_dsa": (lambda n: "indexer_kl_bf16_kernel" in n or "zero_kernel" in n,
+                                ["indexer_kl.hip", "sa_common.h"], None),
+        "block_gqa_bwd_block_workload": (lambda n: "block_gqa_bwd_group_kernel" in n or "zero2_f32_kernel" in n,
+                                         ["block_gqa_bwd.hip", "sa_common.h"], None),
     }
     for key, (match, srcs, _) in groups.items():
         fv = per_kernel(fetch, "FETCH_SIZE", match)
@@ -548,7 +581,8 @@ def main():
                                                                gdq, gdk, gdv, block_size=64), 3)
             # S, dP, dq, dk, dv per attended key and q head
             result.setdefault("gradients", {})["block_gqa_bwd"] = _mfma_entry(
-                "block_gqa_bwd_group_kernel", 2.0 * wq.Hq * (3 * wq.D + 2 * wq.Dv) * attended, ms)
+                "block_gqa_bwd_group_kernel", 2.0 * wq.Hq * (3 * wq.D + 2 * wq.Dv) * attended, ms,
+                traffic=_traffic("block_gqa_bwd_block_workload", ["block_gqa_bwd.hip", "sa_common.h"]))
 
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline (bounded sample)", file=sys.stderr, flush=True)
