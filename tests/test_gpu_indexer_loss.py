@@ -54,6 +54,23 @@ def test_attn_teacher_shapes(sa, H, k, d_qk):
     assert np.all(got[4] == 0)
 
 
+def test_attn_teacher_long_rows_sampled(sa):
+    """The bench's teacher launch shape: 128 heads, k = 2048 over the long workload's
+    32768-row latent, on its last 64 query rows (2048-wide index rows, 5 % -1 slots)."""
+    wl = W["long_dsa"]
+    T = 64
+    m = workloads.mla_inputs(wl, device=DEV)
+    q = m["q"][-T:].contiguous()
+    idx = workloads.random_causal_index(wl.T, 2048, wl.seed, device=DEV)[-T:].contiguous()
+    _, lse = sa.sparse_mla(q, m["kv"], idx, wl.scale)
+    got = sa.attn_teacher(q, m["kv"], idx, lse, wl.scale)
+    got2 = sa.attn_teacher(q, m["kv"], idx, lse, wl.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(got, got2)                          # one plain store per slot: bitwise replay
+    ref = oracle.attn_teacher(q.cpu(), m["kv"].cpu(), idx.cpu().numpy(), wl.scale)
+    close(got.cpu().numpy(), ref, 1e-6, 1e-3, "teacher")
+
+
 def test_attn_teacher_fp32_tiny(sa):
     wl = W["tiny_fp32"]
     x = workloads.indexer_inputs(wl)
@@ -99,6 +116,26 @@ def test_indexer_kl_bwd_shapes(sa, H_I, D_I, k):
     grad_close(dw.cpu().numpy(), rdw, "dw")
     grad_close(dk.cpu().numpy(), rdk, "dk_I")
     assert loss[3].item() == 0 and torch.all(dq[3] == 0)
+
+
+def test_indexer_kl_bwd_long_rows_sampled(sa):
+    """The bench's KL launch shape: 64 indexer heads x 128, k = 2048 over the long
+    workload's 32768 key rows, on 32 of its query rows (T is the only difference); dk_I
+    is complete, since only these rows contribute."""
+    wl = W["long_dsa"]
+    rows = np.linspace(wl.T // 2, wl.T - 1, 32).astype(np.int64)
+    x = workloads.indexer_inputs(wl, device=DEV)
+    sel = torch.from_numpy(rows).to(DEV)
+    qI, wv, kI = x["q_I"][sel].contiguous(), x["w"][sel].contiguous(), x["k_I"]
+    idx = workloads.random_causal_index(wl.T, 2048, wl.seed, device=DEV)[sel].contiguous()
+    teacher = _random_teacher(idx.cpu().numpy(), 11)
+    loss, dq, dw, dk = sa.indexer_kl_bwd(qI, kI, wv, idx, torch.from_numpy(teacher).to(DEV))
+    torch.cuda.synchronize()
+    rl, _, rdq, rdw, rdk = oracle.indexer_kl(qI.cpu(), kI.cpu(), wv.cpu(), idx.cpu().numpy(), teacher)
+    close(loss.cpu().numpy(), rl, 1e-4, 1e-3, "loss")
+    grad_close(dq.float().cpu().numpy(), rdq, "dq_I")
+    grad_close(dw.cpu().numpy(), rdw, "dw")
+    grad_close(dk.cpu().numpy(), rdk, "dk_I")
 
 
 def test_indexer_kl_bwd_fp32_tiny(sa):
