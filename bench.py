@@ -287,7 +287,7 @@ def counters_pass():
     blk = torch.empty((wq.T, 16), dtype=torch.int32, device=dev)
     go = torch.empty((wq.T, wq.Hq, wq.Dv), dtype=torch.bfloat16, device=dev)
     sa.sa_indexer_scores(xq["q_I"], xq["k_I"], xq["w"], block_size=64, topk=16, force_own_block=True,
-                         out_idx=blk)
+                         out_idx=blk, ws=sa.indexer_workspace(xq["q_I"], 16, block_size=64))
     torch.cuda.synchronize()
     print("[counters] block-routed GQA", file=sys.stderr, flush=True)
     glse = torch.empty((wq.T, wq.Hq), dtype=torch.float32, device=dev)
@@ -534,16 +534,17 @@ def main():
         gq = workloads.gqa_inputs(wq, device=dev)
         blk = torch.empty((wq.T, 16), dtype=torch.int32, device=dev)
         go = torch.empty((wq.T, wq.Hq, wq.Dv), dtype=torch.bfloat16, device=dev)
+        bws = sa.indexer_workspace(xq["q_I"], 16, block_size=64)   # split key ranges + merge
         for _ in range(2):
             sa.sa_indexer_scores(xq["q_I"], xq["k_I"], xq["w"], block_size=64, topk=16,
-                                 force_own_block=True, out_idx=blk)
+                                 force_own_block=True, out_idx=blk, ws=bws)
             sa.sa_block_sparse_gqa_fwd(gq["q"], gq["k"], gq["v"], blk, wq.scale, go, block_size=64)
         tis, tgs = [], []
         for _ in range(max(5, args.steps)):
             ti, tg = Timer(), Timer()
             with ti:
                 sa.sa_indexer_scores(xq["q_I"], xq["k_I"], xq["w"], block_size=64, topk=16,
-                                     force_own_block=True, out_idx=blk)
+                                     force_own_block=True, out_idx=blk, ws=bws)
             with tg:
                 sa.sa_block_sparse_gqa_fwd(gq["q"], gq["k"], gq["v"], blk, wq.scale, go, block_size=64)
             tis.append(ti)

@@ -118,16 +118,21 @@ int sa_abi_version(void);
  *     memory ([QSA] "Describe the solution you'd like": streaming runner with
  *     bounded memory).
  *   - ws != NULL with ws_bytes >= sa_indexer_workspace_bytes(...): when that size is
- *     non-zero (bf16, 64 indexer heads, token mode), two passes ([DSA] file table: the
- *     fused top-k's cached scratch buffers): the first appends, per row, the keys
- *     at or above a pivot drawn from a sample of the row's scores to the row's slice
- *     of the workspace (a per-tile partial selection; a few thousand entries per
- *     row), then the exact selection of sa_topk_select finishes each row; a row
- *     whose pivot kept fewer than topk keys is redone by the one-pass kernel. The
- *     workspace holds [T, cap] fp32 scores, [T, cap] int32 key ids and [T] int32
- *     counts; its contents on return are unspecified, and two calls in flight must
- *     not share one. A smaller ws_bytes returns SA_ERR_WORKSPACE; ws must be 16-byte
- *     aligned. When the size is zero, ws is ignored.
+ *     non-zero, two passes ([DSA] file table: the fused top-k's cached scratch
+ *     buffers). Token mode (bf16, 64 indexer heads): the first pass appends, per row,
+ *     the keys at or above a pivot drawn from a sample of the row's scores to the
+ *     row's slice of the workspace (a per-tile partial selection; a few thousand
+ *     entries per row), then the exact selection of sa_topk_select finishes each row;
+ *     a row whose pivot kept fewer than topk keys is redone by the one-pass kernel.
+ *     The workspace holds [T, cap] fp32 scores, [T, cap] int32 key ids and [T] int32
+ *     counts. Block mode with sequences of more than 32 key tiles of 64 keys: the key
+ *     range of each group of query rows is split over up to 4 workgroups, each
+ *     keeping the exact top-k of its blocks, and a merge keeps the exact top-k of
+ *     their union (the same blocks as one pass). The workspace holds [T, splits,
+ *     topk] order keys and block ids, [T, splits] counts and [T] own-block values.
+ *     Its contents on return are unspecified, and two calls in flight must not share
+ *     one. A smaller ws_bytes returns SA_ERR_WORKSPACE; ws must be 16-byte aligned.
+ *     When the size is zero, ws is ignored.
  */
 sa_status sa_indexer_scores(const void* q_I, const void* k_I, const float* w, int dtype,
                             int32_t T, const int32_t* cu_seqlens, int32_t num_seqs,
@@ -142,9 +147,10 @@ sa_status sa_indexer_scores(const void* q_I, const void* k_I, const float* w, in
  *
  * Bytes that the two-pass fused selection needs for these arguments (T, the widest
  * sequence max_seqlen -- T for one sequence --, dtype, H_I, D_I, block_size, topk);
- * 0 when the call runs in one pass (dense mode, block mode, fp32, or H_I != 64).
- * For T = 32768 one-sequence rows at topk = 2048 it is about 1.3 GB. Host-only; no
- * device access.
+ * 0 when the call runs in one pass (dense mode; token mode in fp32 or with H_I != 64;
+ * block mode with sequences of at most 2048 keys). For T = 32768 one-sequence rows
+ * at topk = 2048 it is about 1.3 GB; for 8192-token rows in blocks of 64 at topk = 16,
+ * 4.2 MB. Host-only; no device access.
  */
 size_t sa_indexer_workspace_bytes(int dtype, int32_t T, int32_t max_seqlen, int32_t H_I,
                                   int32_t D_I, int32_t block_size, int32_t topk);

@@ -63,6 +63,14 @@ struct IdxArgs {
   int32_t* ws_idx;
   int32_t* ws_cnt;
   int ws_cap;
+  // block mode with a workspace: the key tiles of each token chunk split over nsplit
+  // workgroups (grid.z), each leaving its exact partial top-k [T, nsplit, topk] (order
+  // keys, block ids, counts) for a merge kernel; the own block's value per token
+  int nsplit;
+  uint32_t* sp_key;
+  int32_t* sp_id;
+  int32_t* sp_cnt;
+  float* sp_own;
 };
 
 // Launch modes of the 64-head kernel.
@@ -242,6 +250,18 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer_kernel(IdxArgs a) {
   if (t0 >= ce) return;
   const int t1 = min(t0 + QT, ce);
   const int ntiles = (t1 - 1 - cs) / kKT + 1;
+  // key tiles [tb, te) of this workgroup: all of them, or, split over grid.z
+  // workgroups, an equal share in whole blocks (so a block's running max stays in one
+  // workgroup)
+  int tb = 0, te = ntiles;
+  const bool split = a.nsplit > 1;
+  if (split) {
+    const int tpb = a.B > kKT ? a.B / kKT : 1;          // tiles per block
+    const int units = (ntiles + tpb - 1) / tpb;
+    const int per = (units + a.nsplit - 1) / a.nsplit;
+    tb = min((int)blockIdx.z * per * tpb, ntiles);
+    te = min(tb + per * tpb, ntiles);
+  }
 
   // ---- this wave's A operand (q rows) and head weights
   const int wt0 = t0 + w * TW;               // first token of this wave
@@ -273,13 +293,15 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer_kernel(IdxArgs a) {
     }
   }
 
-  // ---- per-token state
+  // ---- per-token state (visible to every wave before its first use: the tile loop's
+  //      barrier comes first, except in a split workgroup whose window holds no tile)
   for (int i = tid; i < QT; i += nw * 64) {
     s_n[i] = 0;
     s_tau[i] = 0u;
     s_bmax[i] = -__builtin_huge_valf();
     s_own[i] = 0.0f;
   }
+  if (tb >= te) __syncthreads();            // uniform
 
   // B operand offsets (K^T slices) inside a tile: row = 32*nt + (L&31)
   int b_off[2][KSTEPS];
@@ -311,12 +333,12 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer_kernel(IdxArgs a) {
     }
   };
 
-  gather(0);
+  if (tb < te) gather(tb);
 #pragma unroll 1
-  for (int tile = 0; tile < ntiles; ++tile) {
+  for (int tile = tb; tile < te; ++tile) {
     wait_vmcnt0();
     __syncthreads();                      // tile resident; previous tile fully consumed
-    if (tile + 1 < ntiles) gather(tile + 1);
+    if (tile + 1 < te) gather(tile + 1);
     const char* tb = ktiles + (tile & 1) * TILE_BYTES;
     const int k0 = cs + tile * kKT;
 
@@ -468,6 +490,20 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer_kernel(IdxArgs a) {
     int n = s_n[qi];
     if (n > a.topk) { wave_shrink(keys, ids, n, a.topk, hist + w * 256); n = a.topk; }
     const int own = a.B > 1 ? (t - cs) / a.B : -1;
+    if (split) {
+      // this workgroup's exact partial top-k, in ascending block order, for the merge
+      const size_t slot = (size_t)t * a.nsplit + blockIdx.z;
+      for (int j = L; j < n; j += kWave) {
+        a.sp_key[slot * a.topk + j] = keys[j];
+        a.sp_id[slot * a.topk + j] = ids[j];
+      }
+      if (L == 0) {
+        a.sp_cnt[slot] = n;
+        const int own_tile = own * a.B / kKT;
+        if (a.force_own && own_tile >= tb && own_tile < te) a.sp_own[t] = s_own[qi];
+      }
+      continue;
+    }
     int32_t* orow = a.out_idx + (int64_t)t * a.topk;
     float* vrow = a.out_val ? a.out_val + (int64_t)t * a.topk : nullptr;
     for (int j = L; j < a.topk; j += kWave) {
@@ -480,6 +516,85 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer_kernel(IdxArgs a) {
         if (vrow) vrow[j] = -__builtin_huge_valf();
       }
     }
+  }
+}
+
+// Merge of the partial block top-k lists of a split launch: one wave per token. The
+// token's candidates (at most nsplit x topk <= 256) sit in split order, which is
+// ascending block order (the splits cover consecutive key ranges and each list is
+// ascending); a candidate is kept when fewer than topk others beat it under (key
+// desc, block asc), and the kept ones are written in that same order.
+constexpr int kMergeWaves = 4;
+constexpr int kMergeMax = 256;          // candidates per token: nsplit <= 4, topk <= 64
+
+__global__ __launch_bounds__(kMergeWaves * 64) void indexer_merge_kernel(IdxArgs a) {
+  constexpr int R = kMergeMax / kWave;
+  const int L = lane_id();
+  const int t = (int)blockIdx.x * kMergeWaves + (int)(threadIdx.x >> 6);
+  if (t >= a.T) return;                    // whole wave
+  const int topk = a.topk;
+  // offsets of the splits' lists in the concatenation
+  int cnt[4] = {0, 0, 0, 0};
+  int m = 0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    if (p < a.nsplit) {
+      cnt[p] = __ldg(a.sp_cnt + (size_t)t * a.nsplit + p);
+      m += cnt[p];
+    }
+  }
+  uint32_t key[R];
+  int32_t id[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int c = L + kWave * r;           // concatenated position
+    key[r] = 0u;
+    id[r] = INT32_MAX;
+    if (c < m) {
+      int p = 0, base = 0;
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+        if (p == q && c >= base + cnt[q]) { base += cnt[q]; p = q + 1; }
+      const size_t e = ((size_t)t * a.nsplit + p) * topk + (c - base);
+      key[r] = a.sp_key[e];
+      id[r] = a.sp_id[e];
+    }
+  }
+  // rank of each candidate: how many others beat it
+  int rank[R] = {};
+#pragma unroll 1
+  for (int j = 0; j < m; ++j) {
+    const int r0 = j / kWave, l0 = j % kWave;
+    uint32_t kj = 0u;
+    int32_t ij = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r == r0) {
+        kj = (uint32_t)__builtin_amdgcn_readlane((int)key[r], l0);
+        ij = __builtin_amdgcn_readlane(id[r], l0);
+      }
+#pragma unroll
+    for (int r = 0; r < R; ++r) rank[r] += (kj > key[r] || (kj == key[r] && ij < id[r])) ? 1 : 0;
+  }
+  int32_t* orow = a.out_idx + (int64_t)t * topk;
+  float* vrow = a.out_val ? a.out_val + (int64_t)t * topk : nullptr;
+  const int cs = a.cu ? seq_start_of(a.cu, a.nseq, t) : 0;
+  const int own = (t - cs) / a.B;
+  int pos = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const bool keep = L + kWave * r < m && rank[r] < topk;
+    const uint64_t b = ballot(keep);
+    if (keep) {
+      const int o = pos + (int)mbcnt(b);
+      orow[o] = id[r];
+      if (vrow) vrow[o] = (a.force_own && id[r] == own) ? a.sp_own[t] : key_value(key[r]);
+    }
+    pos += __popcll(b);
+  }
+  for (int j = pos + L; j < topk; j += kWave) {
+    orow[j] = -1;
+    if (vrow) vrow[j] = -__builtin_huge_valf();
   }
 }
 
@@ -1131,7 +1246,8 @@ hipError_t launch_hi(const IdxArgs& a0, int maxlen, hipStream_t st) {
   hipError_t e = hipFuncSetAttribute((const void*)indexer_kernel<BF16, HI, DI>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((indexer_kernel<BF16, HI, DI>), dim3(a.chunks, a.nseq), dim3(nw * 64), shm, st, a);
+  hipLaunchKernelGGL((indexer_kernel<BF16, HI, DI>), dim3(a.chunks, a.nseq, a.nsplit > 1 ? a.nsplit : 1),
+                     dim3(nw * 64), shm, st, a);
   return hipGetLastError();
 }
 
@@ -1185,8 +1301,22 @@ int indexer_ws_cap(int topk, int maxlen) {
   return (int)((cap + 63) / 64 * 64);
 }
 
+// Workgroups over which block mode splits each token chunk's key tiles when a
+// workspace is given: about 32 tiles each, at most 4 (so that a token's partial lists
+// hold at most 4 x 64 candidates); 1 (no split) for rows of up to 32 tiles.
+int indexer_block_splits(int maxlen, int block_size, int topk) {
+  if (block_size == 1 || topk <= 0) return 1;
+  const int tiles = (maxlen + kKT - 1) / kKT;
+  const int ns = (tiles + 31) / 32;
+  return ns < 1 ? 1 : (ns > 4 ? 4 : ns);
+}
+
 size_t indexer_ws_bytes(bool bf16, int T, int maxlen, int H_I, int block_size, int topk) {
-  if (!indexer_two_pass(bf16, H_I, block_size, topk) || T <= 0) return 0;
+  if (T <= 0) return 0;
+  const int ns = indexer_block_splits(maxlen, block_size, topk);
+  if (ns > 1)   // partial lists: keys, block ids, counts; the own block's value
+    return (size_t)T * ns * topk * 8 + (size_t)T * ns * 4 + (size_t)T * 4;
+  if (!indexer_two_pass(bf16, H_I, block_size, topk)) return 0;
   const int cap = indexer_ws_cap(topk, maxlen);
   return (size_t)T * cap * 8 + (size_t)T * 4;
 }
@@ -1200,6 +1330,20 @@ hipError_t launch_indexer_topk(const void* q, const void* k, const float* w, boo
   a.q = q; a.k = k; a.w = w; a.T = T; a.cu = cu; a.nseq = cu ? nseq : 1; a.B = block_size;
   a.topk = topk; a.force_own = force_own; a.out_idx = out_idx; a.out_val = out_val;
   const int width = cu ? maxlen : T;
+  const int ns = indexer_block_splits(width, block_size, topk);
+  if (ws && ns > 1) {
+    // block mode: partial top-k lists of ns key ranges per token chunk, then the merge
+    a.nsplit = ns;
+    a.sp_key = static_cast<uint32_t*>(ws);
+    a.sp_id = reinterpret_cast<int32_t*>(a.sp_key + (size_t)T * ns * topk);
+    a.sp_cnt = a.sp_id + (size_t)T * ns * topk;
+    a.sp_own = reinterpret_cast<float*>(a.sp_cnt + (size_t)T * ns);
+    hipError_t e = launch_any(a, bf16, H_I, D_I, width, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(indexer_merge_kernel, dim3((T + kMergeWaves - 1) / kMergeWaves),
+                       dim3(kMergeWaves * 64), 0, st, a);
+    return hipGetLastError();
+  }
   if (!ws || !indexer_two_pass(bf16, H_I, block_size, topk))
     return launch_any(a, bf16, H_I, D_I, width, st);
   // two passes through the workspace: [T, cap] scores, [T, cap] key ids, [T] counts

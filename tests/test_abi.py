@@ -122,15 +122,21 @@ def _ws_bytes(dtype, T, maxlen, H_I, D_I, B, topk):
 
 
 def test_indexer_workspace_sizes():
-    # two-pass route only for bf16, 64 heads, token mode, fused selection
+    # token mode: two-pass route only for bf16, 64 heads, fused selection
     long = _ws_bytes(1, 32768, 32768, 64, 128, 1, 2048)
     assert 32768 * 2048 * 8 < long < 32768 * 8192 * 8          # a few thousand entries per row
     assert long % 4 == 0
     assert _ws_bytes(1, 32768, 32768, 64, 128, 1, 0) == 0          # dense mode
     assert _ws_bytes(1, 32768, 32768, 16, 128, 1, 2048) == 0       # generic kernel
     assert _ws_bytes(0, 32768, 32768, 64, 128, 1, 2048) == 0       # fp32
-    assert _ws_bytes(1, 32768, 32768, 64, 128, 64, 16) == 0        # block mode
     assert _ws_bytes(1, 0, 1, 64, 128, 1, 16) == 0                 # nothing to do
+    # block mode: key ranges split in runs of 32 tiles of 64 keys, at most 4, each run's
+    # top-k ([T, splits, topk] keys and ids), [T, splits] counts, [T] own values
+    assert _ws_bytes(1, 2048, 2048, 16, 128, 64, 16) == 0          # 32 tiles: one pass
+    assert _ws_bytes(1, 4096, 4096, 16, 128, 64, 16) == 4096 * (2 * 16 * 8 + 2 * 4 + 4)
+    assert _ws_bytes(1, 8192, 8192, 16, 128, 64, 16) == 8192 * (4 * 16 * 8 + 4 * 4 + 4)
+    assert _ws_bytes(0, 32768, 32768, 64, 128, 64, 16) == 32768 * (4 * 16 * 8 + 4 * 4 + 4)   # fp32 too
+    assert _ws_bytes(1, 8192, 8192, 16, 128, 64, 0) == 0           # dense block scores
     # rows never wider than the row: short sequences take the whole row
     assert _ws_bytes(1, 1000, 1000, 64, 128, 1, 2048) == 1000 * 1024 * 8 + 1000 * 4
     # packed sequences size by the widest one

@@ -312,15 +312,18 @@ def test_indexer_topk_fused_integer_exact(sa, name, k, T, B):
     np.testing.assert_array_equal(val.cpu().numpy(), ref_v)
 
 
+@pytest.mark.parametrize("workspace", [True, False])
 @pytest.mark.parametrize("lengths", [(8192,), (3000, 64, 5128)])
-def test_block_routed_path_full_size_against_oracle(sa, lengths):
+def test_block_routed_path_full_size_against_oracle(sa, lengths, workspace):
     """The block-routed workload at its stated size (8192 tokens, 16 indexer heads x 128,
     64-key blocks, top 16 blocks with the query's own block forced) on the integer grid:
     the fused block top-k equals the oracle bit for bit (ids and values) on sampled rows,
     among them the last 64 rows, whose candidate blocks (128 on one sequence, 81 in the
     last packed sequence) overflow the 80-entry candidate buffer so that it is cut back
     mid-stream; then sparse GQA over those GPU
-    routes equals the oracle's attention on the same rows."""
+    routes equals the oracle's attention on the same rows. With a workspace the key
+    range of each group of rows is split over 4 (3) workgroups and their partial
+    top-k lists are merged; without one, one workgroup walks it all."""
     wl = W["block_gqa"]
     T = sum(lengths)
     assert T == wl.T
@@ -331,7 +334,7 @@ def test_block_routed_path_full_size_against_oracle(sa, lengths):
     kw = dict(cu_seqlens=cu_dev(lengths), max_seqlen=max(lengths)) if multi else {}
     xd = {n: t.to(DEV) for n, t in x.items()}
     blk, val = sa.indexer_topk(xd["q_I"], xd["k_I"], xd["w"], 16, block_size=64,
-                               force_own_block=True, with_values=True, **kw)
+                               force_own_block=True, with_values=True, workspace=workspace, **kw)
     rows = sample_rows(T, 64, 29, lengths if multi else None)
     rows = np.union1d(rows, np.arange(T - 64, T))
     ref_i, ref_v = oracle.indexer_topk(x["q_I"], x["k_I"], x["w"], 16, cu_seqlens=cu, block_size=64,
@@ -344,6 +347,37 @@ def test_block_routed_path_full_size_against_oracle(sa, lengths):
                                      wl.scale, cu_seqlens=cu, rows=rows)
     close(out.float().cpu().numpy()[rows], ro, **BF16_TOL, what="out")
     close(lse.cpu().numpy()[rows], rl, **BF16_TOL, what="lse")
+
+
+@pytest.mark.parametrize("B,k,own", [(64, 16, True), (16, 64, True), (128, 8, True), (256, 3, False),
+                                      (32, 1, False)])
+def test_block_topk_split_key_ranges(sa, B, k, own):
+    """Block top-k with a workspace: each group of rows' key tiles split over 2-3
+    workgroups (windows of whole blocks: 4 tiles per block at B = 256, 4 blocks per
+    tile at B = 16) whose exact partial lists a merge combines. Ids and values equal
+    the one-pass kernel bit for bit on every row, and the oracle on sampled rows, for
+    one sequence and for packed ones (short sequences whose windows hold no tile)."""
+    wl = W["block_gqa"]
+    for lengths in [(6000,), (2100, 37, 4000, 1900)]:
+        T = sum(lengths)
+        multi = len(lengths) > 1
+        x = workloads.indexer_inputs(wl, integer=True, T=T)
+        xd = {n: t.to(DEV) for n, t in x.items()}
+        kw = dict(cu_seqlens=cu_dev(lengths), max_seqlen=max(lengths)) if multi else {}
+        ws = sa.indexer_workspace(xd["q_I"], k, max_seqlen=max(lengths), block_size=B)
+        assert ws is not None and ws.numel() > 0
+        i1, v1 = sa.indexer_topk(xd["q_I"], xd["k_I"], xd["w"], k, block_size=B, force_own_block=own,
+                                 with_values=True, workspace=ws, **kw)
+        i2, v2 = sa.indexer_topk(xd["q_I"], xd["k_I"], xd["w"], k, block_size=B, force_own_block=own,
+                                 with_values=True, workspace=False, **kw)
+        assert torch.equal(i1, i2), f"lengths {lengths}"
+        assert torch.equal(v1, v2), f"lengths {lengths}"
+        rows = np.union1d(sample_rows(T, 16, 41 + B, lengths if multi else None), np.arange(T - 8, T))
+        ref_i, ref_v = oracle.indexer_topk(x["q_I"], x["k_I"], x["w"], k,
+                                           cu_seqlens=workloads.cu_seqlens(lengths) if multi else None,
+                                           block_size=B, force_own_block=own, rows=rows)
+        np.testing.assert_array_equal(i1.cpu().numpy()[rows], ref_i, err_msg=f"lengths {lengths}")
+        np.testing.assert_array_equal(v1.cpu().numpy()[rows], ref_v, err_msg=f"lengths {lengths}")
 
 
 @pytest.mark.parametrize("B,k", [(16, 5), (32, 1), (16, 64)])
