@@ -431,36 +431,45 @@ __global__ __launch_bounds__(kGrpWaves * 64) __attribute__((amdgpu_waves_per_eu(
         // keys 4 quad + e (+16) of the piece count below lim: the row routes here, the
         // key is in the piece and causal for the row
         const int lim = (row_ok && ((msk >> tau) & 1u)) ? min(nk, tq - lo + 1) - 4 * quad : 0;
-        float mx = -__builtin_huge_valf();
+        // logits in log2 units relative to the row's reference m_run (absolute for a row
+        // that has no reference yet), -inf where the row does not route here: one fma
+        // per logit; only a piece in which some row's causal limit falls (uniform test)
+        // masks key by key
+        const bool seen = m_run != -__builtin_huge_valf();
+        const float bias = lim > 0 ? (seen ? -m_run : 0.0f) : -__builtin_huge_valf();
+        float x[8];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x = 16 * kt + e < lim ? S[kt][e] * scale_log2 : -__builtin_huge_valf();
-            S[kt][e] = x;
-            mx = __builtin_elementwise_maximum(mx, x);
-          }
+          for (int e = 0; e < 4; ++e) x[4 * kt + e] = fmaf(S[kt][e], scale_log2, bias);
+        if (ballot(lim > 0 && lim < 20)) {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              x[4 * kt + e] = 16 * kt + e < lim ? x[4 * kt + e] : -__builtin_huge_valf();
+        }
+        float mx = __builtin_elementwise_maximum(
+            __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[0], x[1]), __builtin_elementwise_maximum(x[2], x[3])),
+            __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[4], x[5]), __builtin_elementwise_maximum(x[6], x[7])));
         mx = quad_max(mx);
-        // fixed reference: O and l are rescaled only when a max passes the row's
-        // reference by more than 2^8 (the first valid key always does)
-        if (ballot(mx > m_run + kHeadroom)) {             // uniform
-          const bool up = mx > m_run + kHeadroom;
-          const float alpha = up ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;   // 0 from -inf
-          m_run = up ? mx : m_run;
+        // fixed reference: a row takes a new one at its first keys and when a max passes
+        // the reference by more than 2^8; O and l are rescaled then only
+        const bool up = mx > -__builtin_huge_valf() && (!seen || mx > kHeadroom);
+        if (ballot(up)) {                                  // uniform
+          const float alpha = up && seen ? __builtin_amdgcn_exp2f(-mx) : 1.0f;
+          const float shift = up ? mx : 0.0f;
+          m_run = up ? (seen ? m_run + mx : mx) : m_run;
 #pragma unroll
           for (int i = 0; i < NDT; ++i) O[i] *= alpha;
           l_run *= alpha;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) x[i] -= shift;
         }
-        const bool none = m_run == -__builtin_huge_valf();
-        const float m_new = m_run;
         float pf[8];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            pf[4 * kt + e] = none ? 0.0f : __builtin_amdgcn_exp2f(S[kt][e] - m_new);
-            l_run += pf[4 * kt + e];
-          }
+        for (int i = 0; i < 8; ++i) pf[i] = __builtin_amdgcn_exp2f(x[i]);
+        l_run += ((pf[0] + pf[1]) + (pf[2] + pf[3])) + ((pf[4] + pf[5]) + (pf[6] + pf[7]));
         bf16x2_t pk[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) pk[e] = __builtin_convertvector((float2_t){pf[2 * e], pf[2 * e + 1]}, bf16x2_t);
