@@ -266,28 +266,57 @@ __global__ __launch_bounds__(kWavesPerGroup * 64) void block_gqa_bf16_kernel(
 //   * set-up: the routes' blocks, as key rows start + b B, are marked in a bitmap over
 //     the group's key range; a prefix count over its words numbers the distinct blocks
 //     in ascending key order, and each route entry ORs its token into its block's mask;
-//   * the blocks go in 32-key sub-tiles: K rows to a padded LDS stage (A operands of
-//     S^T = K . Q^T, 16x16x32), V rows to a swizzled stage read back transposed for
-//     O^T = V^T . P^T, both double-buffered; the next two sub-tiles' rows are in
-//     registers while the current one is computed;
-//   * a wave skips the MFMAs of a sub-tile none of its rows' tokens routes to; a row's
-//     online softmax ignores masked keys exactly (alpha 1, p 0) and rescales O only
-//     when a logit passes the row's reference by more than 2^8.
+//   * the blocks go in 32-key pieces, one per step (one barrier each): K and V rows
+//     are copied straight from memory into a four-piece LDS ring by 16-byte
+//     global_load_lds with a scalar row base and fixed per-lane offsets, three pieces
+//     ahead of the one computed; both regions are XOR-swizzled per row, K for the
+//     operand reads of S^T = K . Q^T (16x16x32), V for the transposed reads of
+//     O^T = V^T . P^T. The step is written out once per ring slot, so every LDS
+//     address is a lane offset plus an immediate, and each piece's description (first
+//     key, keys, token mask) sits in scalar registers, read from the tables once per
+//     block. Every wave copies every piece, so this per-piece work is what the waves
+//     that skip a piece still pay;
+//   * a wave skips the MFMAs of a piece none of its rows' tokens routes to; a row's
+//     online softmax ignores masked keys exactly (p 0) and rescales O only when a logit
+//     passes the row's reference by more than 2^8.
 // Measured on the block-routed workload: two workgroups of four waves with two column
 // tiles each, one sub-tile ahead, 0.89 ms; skipping per column tile 0.79; two sub-tiles
-// ahead 0.77; eight waves of one tile (twice the waves per SIMD) 0.68; 64-key sub-tiles
-// and 256-row groups no faster.
+// ahead 0.77; eight waves of one tile (twice the waves per SIMD) 0.68; fixed softmax
+// reference 0.58; copies with scalar bases and piece descriptions in scalar registers
+// instead of per-lane 64-bit addresses and table reads per copy, 0.50. 64-key sub-tiles,
+// two pieces per barrier and 256-row groups were no faster.
 // Blocks are visited in ascending key order, the same for every row of the group.
+constexpr int kGrpRing = 4;                      // pieces in the LDS ring (two steps)
 
 template <int D>
-constexpr int kstride() { return D * 2 + 16; }   // padded K row in the stage (bytes)
+constexpr int piece_bytes() { return 2 * 32 * D * 2; }   // K rows, then V rows
+
+// K-region chunk swizzle: the 16 rows of an operand read land on distinct chunks.
 template <int D>
-constexpr int grp_stage_bytes() { return 32 * kstride<D>() + 32 * D * 2; }
+SA_DEVICE int kswz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
 
 size_t grp_lds_bytes(int D, int G, int nblk, int maxlen) {
-  const size_t st = D == 128 ? grp_stage_bytes<128>() : grp_stage_bytes<64>();
-  return 2 * st + grp_table_bytes(grp_tokens(G), nblk, maxlen);
+  const size_t st = D == 128 ? piece_bytes<128>() : piece_bytes<64>();
+  return kGrpRing * st + grp_table_bytes(grp_tokens(G), nblk, maxlen);
 }
+
+// 16-byte global -> LDS copy per lane: lane l writes LDS bytes [lds + 16 l, +16); lds
+// and base are wave-uniform, voff is the lane's byte offset from base. Issued through inline asm so that later LDS reads are not ordered
+// behind it; completion is tracked with s_waitcnt vmcnt. M0 is set here and nowhere
+// else in these kernels.
+SA_DEVICE void grp_dma16(uint32_t lds, const void* base, uint32_t voff) {
+  // readfirstlane returns a signed int: zero-extend each half before recombining
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint64_t sb = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(
+                   __builtin_amdgcn_readfirstlane(lds)),
+               "v"(voff), "s"(sb)
+               : "memory");
+}
+
+// s_waitcnt vmcnt(0) with the other counters left alone.
+constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
 
 template <int D>
 __global__ __launch_bounds__(kGrpWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void block_gqa_group_kernel(
@@ -297,15 +326,18 @@ __global__ __launch_bounds__(kGrpWaves * 64) __attribute__((amdgpu_waves_per_eu(
     float* __restrict__ lse, int by_xcd) {
   constexpr int KS = D / 32;             // 32-wide k-steps of S^T
   constexpr int CPR = D * 2 / 16;        // 16-byte chunks per row
+  constexpr int RB = CPR * 16;           // bytes per row in a region
   constexpr int NDT = D / 16;            // 16-channel tiles of O^T
-  constexpr int KSB = kstride<D>();
+  constexpr int PB = piece_bytes<D>();
   constexpr int NT = kGrpWaves * 64;
-  constexpr int LDN = (2 * 32 * CPR + NT - 1) / NT;   // 16-byte loads per thread per sub-tile
+  constexpr int DPP = 2 * 32 * CPR / 64; // 1 KiB copies per piece (K and V)
+  constexpr int DPW = 2 * DPP / kGrpWaves;   // copies per wave per step
+  static_assert(DPW * kGrpWaves == 2 * DPP && DPP % 2 == 0, "copies split evenly");
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  char* stg = lds;                                                   // [2][K stage | V stage]
-  const GroupTables tbl = group_tables(lds + 2 * grp_stage_bytes<D>(), GT, nblk, nwords);
+  const GroupTables tbl = group_tables(lds + kGrpRing * PB, GT, nblk, nwords);
   const int32_t* ulo = tbl.ulo;
   const uint32_t* umask = tbl.umask;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(SA_LDS char*)lds;
 
   const int tid = threadIdx.x, w = tid >> 6, L = tid & 63;
   const int n = L & 15, quad = L >> 4;
@@ -356,149 +388,183 @@ __global__ __launch_bounds__(kGrpWaves * 64) __attribute__((amdgpu_waves_per_eu(
   float m_run = -__builtin_huge_valf();   // log2 units, same in the 4 lanes of a row
   float l_run = 0.0f;                     // this lane's keys only
 
-  // sub-tiles: for each distinct block u, keys ulo[u] .. min(ulo[u] + B, tlast + 1) - 1
-  // in 32-key pieces; (u, piece) advanced in order
-  auto keys_of = [&](int u) { return min(B, tlast + 1 - ulo[u]); };
-  bf16x8_t nx[LDN];
-  auto load = [&](int u, int pc) __attribute__((always_inline)) {
-    const int lo = ulo[u] + 32 * pc;
-    const int nk = min(32, keys_of(u) - 32 * pc);
-#pragma unroll
-    for (int m = 0; m < LDN; ++m) {
-      const int c = tid + NT * m;                  // chunk: [K | V][row][CPR]
-      const int isv = c >= 32 * CPR;
-      const int cc = isv ? c - 32 * CPR : c;
-      const int r = cc / CPR, p = cc % CPR;
-      const int key = lo + (r < nk ? r : 0);
-      const uint16_t* src = (isv ? v : k) + ((int64_t)key * Hkv + g) * D + 8 * p;
-      nx[m] = (c < 2 * 32 * CPR) ? *reinterpret_cast<const bf16x8_t*>(src) : bf16x8_t{};
-    }
+  // pieces: for each distinct block u, keys ulo[u] .. min(ulo[u] + B, tlast + 1) - 1 in
+  // 32-key pieces, walked in order. A piece's description (block, piece of the block,
+  // first key, keys, keys of its block, token mask) is wave-uniform and lives in scalar
+  // registers; the LDS tables are read once per block.
+  struct Piece {
+    int u, pc, lo, nk, kof;
+    uint32_t m;
   };
-  auto store = [&](char* st) __attribute__((always_inline)) {
+  auto first_of = [&](int u) __attribute__((always_inline)) {
+    Piece p{u, 0, 0, 0, 0, 0u};
+    if (u < nu) {
+      p.lo = __builtin_amdgcn_readfirstlane(ulo[u]);
+      p.m = (uint32_t)__builtin_amdgcn_readfirstlane((int)umask[u]);
+      p.kof = min(B, tlast + 1 - p.lo);
+      p.nk = min(32, p.kof);
+    }
+    return p;
+  };
+  auto next_of = [&](const Piece& a) __attribute__((always_inline)) {
+    Piece p = a;
+    if (a.u < nu) {
+      if (32 * (a.pc + 1) < a.kof) {
+        p.pc = a.pc + 1;
+        p.lo = a.lo + 32;
+        p.nk = min(32, a.kof - 32 * p.pc);
+      } else {
+        p = first_of(a.u + 1);
+      }
+    }
+    return p;
+  };
+
+  // copies: wave w moves DP1 of a piece's 1 KiB runs (K rows, then V rows); lane L of
+  // run j holds row r, chunk slot L mod CPR (the swizzled chunk ch of the source row).
+  // Rows past a piece's last key repeat its first key.
+  constexpr int DP1 = DPP / kGrpWaves;
+  uint32_t voff[DP1], voff0[DP1];
+  int vrow[DP1];
 #pragma unroll
-    for (int m = 0; m < LDN; ++m) {
-      const int c = tid + NT * m;
-      if (c < 2 * 32 * CPR) {
-        const int isv = c >= 32 * CPR;
-        const int cc = isv ? c - 32 * CPR : c;
-        const int r = cc / CPR, p = cc % CPR;
-        if (!isv) *reinterpret_cast<bf16x8_t*>(st + r * KSB + 16 * p) = nx[m];
-        else *reinterpret_cast<bf16x8_t*>(st + 32 * KSB + r * (CPR * 16) + ((p ^ vswz<D>(r)) << 4)) = nx[m];
+  for (int i = 0; i < DP1; ++i) {
+    const int j = w * DP1 + i;
+    const int isv = j >= DPP / 2;
+    const int jj = j - isv * (DPP / 2);
+    const int r = jj * (64 / CPR) + L / CPR;
+    const int ch = (L % CPR) ^ (isv ? vswz<D>(r) : kswz<D>(r));
+    vrow[i] = r;
+    voff0[i] = (uint32_t)ch * 16u;
+    voff[i] = (uint32_t)r * (uint32_t)(Hkv * D * 2) + voff0[i];
+  }
+  auto fetch = [&](const Piece& p, int slot) __attribute__((always_inline)) {
+    if (p.u < nu) {                                     // uniform
+#pragma unroll
+      for (int i = 0; i < DP1; ++i) {
+        const int j = w * DP1 + i;
+        const int isv = j >= DPP / 2;
+        const int jj = j - isv * (DPP / 2);
+        const uint16_t* src = (isv ? v : k) + ((int64_t)p.lo * Hkv + g) * D;
+        grp_dma16(lds0 + (uint32_t)(slot * PB + isv * 32 * RB + jj * 1024), src,
+                  vrow[i] < p.nk ? voff[i] : voff0[i]);
       }
     }
   };
 
-  auto advance = [&](int& uu, int& pp) __attribute__((always_inline)) {
-    if (uu < nu) {
-      ++pp;
-      if (32 * pp >= keys_of(uu)) { ++uu; pp = 0; }
+  // S^T of one piece: rows = keys 16 kt + (0..15), columns = the wave's 16 query rows
+  auto logits = [&](const char* st, floatx4v_t* S) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int r = 16 * kt + n;
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(st + r * RB + (((4 * ks + quad) ^ kswz<D>(r)) << 4));
+        S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], S[kt], 0, 0, 0);
+      }
+  };
+  // O^T += V^T . P^T of one piece (P^T: this lane's 8 keys 4 quad + e, 16 + 4 quad + e)
+  auto values = [&](const char* st, bf16x8_t pb) __attribute__((always_inline)) {
+    const char* vst = st + 32 * RB;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int row0 = 4 * quad + (n >> 2);
+      const int col = 16 * dt + 4 * (n & 3);
+      const int off0 = row0 * RB + (((col >> 3) ^ vswz<D>(row0)) << 4) + (col & 7) * 2;
+      const int row1 = row0 + 16;
+      const int off1 = row1 * RB + (((col >> 3) ^ vswz<D>(row1)) << 4) + (col & 7) * 2;
+      const short4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(vst + off0));
+      const short4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(vst + off1));
+      const short __attribute__((ext_vector_type(8))) a8 = {lo4[0], lo4[1], lo4[2], lo4[3],
+                                                            hi4[0], hi4[1], hi4[2], hi4[3]};
+      O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a8), pb, O[dt], 0, 0, 0);
     }
   };
-  bf16x8_t nxA[LDN], nxB[LDN];
-  auto loadTo = [&](bf16x8_t (&dst)[LDN], int uu, int pp) __attribute__((always_inline)) {
-    load(uu, pp);
+
+  // one piece in ring slot SLOT (a constant, so every LDS address is a lane offset plus
+  // an immediate): wait for its copies, barrier, copy the piece three ahead into the
+  // slot freed by the previous step, compute
+  Piece p0 = first_of(0);
+  Piece p1 = next_of(p0);
+  Piece p2 = next_of(p1);
+  Piece p3 = next_of(p2);
+  fetch(p0, 0);
+  fetch(p1, 1);
+  fetch(p2, 2);
+  auto step = [&](auto slot_c) __attribute__((always_inline)) {
+    constexpr int SLOT = decltype(slot_c)::value;
+    const int newer = (p1.u < nu) + (p2.u < nu);       // pieces whose copies may stay in flight
+    if (newer == 2) __builtin_amdgcn_s_waitcnt((2 * DP1) | kWaitVm0);
+    else if (newer == 1) __builtin_amdgcn_s_waitcnt(DP1 | kWaitVm0);
+    else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();                                    // every wave's copies have landed
+    fetch(p3, (SLOT + 3) & 3);
+    const Piece p4 = next_of(p3);
+    const char* st = lds + SLOT * PB;
+    if (p0.m & tile_tok) {                              // uniform: some row of the wave uses it
+      floatx4v_t S[2] = {floatx4v_t{}, floatx4v_t{}};
+      logits(st, S);
+      // keys 4 quad + e (+16) of the piece count below lim: the row routes here, the
+      // key is in the piece and causal for the row
+      const int lim = (row_ok && ((p0.m >> tau) & 1u)) ? min(p0.nk, tq - p0.lo + 1) - 4 * quad : 0;
+      // logits in log2 units relative to the row's reference m_run (absolute for a row
+      // that has no reference yet), -inf where the row does not route here: one fma
+      // per logit; only a piece in which some row's causal limit falls (uniform test)
+      // masks key by key
+      const bool seen = m_run != -__builtin_huge_valf();
+      const float bias = lim > 0 ? (seen ? -m_run : 0.0f) : -__builtin_huge_valf();
+      float x[8];
 #pragma unroll
-    for (int m = 0; m < LDN; ++m) dst[m] = nx[m];
-  };
-  auto storeFrom = [&](char* st, const bf16x8_t (&src)[LDN]) __attribute__((always_inline)) {
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int m = 0; m < LDN; ++m) nx[m] = src[m];
-    store(st);
-  };
-  int u = 0, pc = 0, ua = 0, pa = 0;
-  advance(ua, pa);
-  if (nu > 0) loadTo(nxA, 0, 0);
-  if (ua < nu) loadTo(nxB, ua, pa);
-  auto piece = [&](char* st, bf16x8_t (&buf)[LDN]) __attribute__((always_inline)) {
-    storeFrom(st, buf);
-    __syncthreads();
-    int ub = ua, pb = pa;
-    advance(ub, pb);
-    if (ub < nu) loadTo(buf, ub, pb);
-    const int lo = ulo[u] + 32 * pc;
-    const int nk = min(32, keys_of(u) - 32 * pc);
-    const uint32_t msk = umask[u];
-    if (msk & tile_tok) {                                 // uniform: some row of the wave uses it
-      {
-        floatx4v_t S[2] = {floatx4v_t{}, floatx4v_t{}};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt) {
-            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(st + (16 * kt + n) * KSB + 64 * ks + 16 * quad);
-            S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], S[kt], 0, 0, 0);
-          }
-        // keys 4 quad + e (+16) of the piece count below lim: the row routes here, the
-        // key is in the piece and causal for the row
-        const int lim = (row_ok && ((msk >> tau) & 1u)) ? min(nk, tq - lo + 1) - 4 * quad : 0;
-        // logits in log2 units relative to the row's reference m_run (absolute for a row
-        // that has no reference yet), -inf where the row does not route here: one fma
-        // per logit; only a piece in which some row's causal limit falls (uniform test)
-        // masks key by key
-        const bool seen = m_run != -__builtin_huge_valf();
-        const float bias = lim > 0 ? (seen ? -m_run : 0.0f) : -__builtin_huge_valf();
-        float x[8];
+        for (int e = 0; e < 4; ++e) x[4 * kt + e] = fmaf(S[kt][e], scale_log2, bias);
+      if (ballot(lim > 0 && lim < 20)) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[4 * kt + e] = fmaf(S[kt][e], scale_log2, bias);
-        if (ballot(lim > 0 && lim < 20)) {
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              x[4 * kt + e] = 16 * kt + e < lim ? x[4 * kt + e] : -__builtin_huge_valf();
-        }
-        float mx = __builtin_elementwise_maximum(
-            __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[0], x[1]), __builtin_elementwise_maximum(x[2], x[3])),
-            __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[4], x[5]), __builtin_elementwise_maximum(x[6], x[7])));
-        mx = quad_max(mx);
-        // fixed reference: a row takes a new one at its first keys and when a max passes
-        // the reference by more than 2^8; O and l are rescaled then only
-        const bool up = mx > -__builtin_huge_valf() && (!seen || mx > kHeadroom);
-        if (ballot(up)) {                                  // uniform
-          const float alpha = up && seen ? __builtin_amdgcn_exp2f(-mx) : 1.0f;
-          const float shift = up ? mx : 0.0f;
-          m_run = up ? (seen ? m_run + mx : mx) : m_run;
-#pragma unroll
-          for (int i = 0; i < NDT; ++i) O[i] *= alpha;
-          l_run *= alpha;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) x[i] -= shift;
-        }
-        float pf[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pf[i] = __builtin_amdgcn_exp2f(x[i]);
-        l_run += ((pf[0] + pf[1]) + (pf[2] + pf[3])) + ((pf[4] + pf[5]) + (pf[6] + pf[7]));
-        bf16x2_t pk[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pk[e] = __builtin_convertvector((float2_t){pf[2 * e], pf[2 * e + 1]}, bf16x2_t);
-        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pk);
-        const char* vst = st + 32 * KSB;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          short4_t lo4, hi4;
-          {
-            const int row0 = 4 * quad + (n >> 2);
-            const int col = 16 * dt + 4 * (n & 3);
-            const int off0 = row0 * (CPR * 16) + (((col >> 3) ^ vswz<D>(row0)) << 4) + (col & 7) * 2;
-            const int row1 = row0 + 16;
-            const int off1 = row1 * (CPR * 16) + (((col >> 3) ^ vswz<D>(row1)) << 4) + (col & 7) * 2;
-            lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(vst + off0));
-            hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(vst + off1));
-          }
-          const short __attribute__((ext_vector_type(8))) a8 = {lo4[0], lo4[1], lo4[2], lo4[3],
-                                                                hi4[0], hi4[1], hi4[2], hi4[3]};
-          O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a8), pb, O[dt], 0, 0, 0);
-        }
+          for (int e = 0; e < 4; ++e)
+            x[4 * kt + e] = 16 * kt + e < lim ? x[4 * kt + e] : -__builtin_huge_valf();
       }
+      float mx = __builtin_elementwise_maximum(
+          __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[0], x[1]), __builtin_elementwise_maximum(x[2], x[3])),
+          __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[4], x[5]), __builtin_elementwise_maximum(x[6], x[7])));
+      mx = quad_max(mx);
+      // fixed reference: a row takes a new one at its first keys and when a max passes
+      // the reference by more than 2^8; O and l are rescaled then only
+      const bool up = mx > -__builtin_huge_valf() && (!seen || mx > kHeadroom);
+      if (ballot(up)) {                                  // uniform
+        const float alpha = up && seen ? __builtin_amdgcn_exp2f(-mx) : 1.0f;
+        const float shift = up ? mx : 0.0f;
+        m_run = up ? (seen ? m_run + mx : mx) : m_run;
+#pragma unroll
+        for (int i = 0; i < NDT; ++i) O[i] *= alpha;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] -= shift;
+      }
+      float pf[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pf[i] = __builtin_amdgcn_exp2f(x[i]);
+      l_run += ((pf[0] + pf[1]) + (pf[2] + pf[3])) + ((pf[4] + pf[5]) + (pf[6] + pf[7]));
+      bf16x2_t pk[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pk[e] = __builtin_convertvector((float2_t){pf[2 * e], pf[2 * e + 1]}, bf16x2_t);
+      values(st, __builtin_bit_cast(bf16x8_t, pk));
     }
-    u = ua; pc = pa; ua = ub; pa = pb;
+    p0 = p1;
+    p1 = p2;
+    p2 = p3;
+    p3 = p4;
   };
 #pragma unroll 1
-  while (u < nu) {
-    piece(stg, nxA);
-    if (u < nu) piece(stg + grp_stage_bytes<D>(), nxB);
+  for (;;) {                                            // uniform exits
+    if (p0.u >= nu) break;
+    step(std::integral_constant<int, 0>{});
+    if (p0.u >= nu) break;
+    step(std::integral_constant<int, 1>{});
+    if (p0.u >= nu) break;
+    step(std::integral_constant<int, 2>{});
+    if (p0.u >= nu) break;
+    step(std::integral_constant<int, 3>{});
   }
 
   // ---- normalise and write: lane owns row 16 w + n, channels 16 dt + 4 quad + e
