@@ -129,6 +129,34 @@ def test_topk_select_full_size_sampled(sa, name):
     np.testing.assert_array_equal(val.cpu().numpy()[rows], ref_v)
 
 
+@pytest.mark.parametrize("T", [17884, 32768])
+def test_topk_select_wide_rows(sa, T):
+    """Rows of 16K-32K token positions of one sequence (the widest class of the bench's
+    materialised matrix): dense normal scores, with rows of four distinct values (ties at
+    the k-th key), constant rows (every pivot fails, so the retry launch takes them) and
+    rows that repeat one value over their first 4096 positions; sampled rows against the
+    oracle, ids and values bit for bit."""
+    gen = torch.Generator(device=DEV).manual_seed(T)
+    ld = T
+    vals = torch.randn((T, ld), generator=gen, device=DEV)
+    lo = 16384
+    tied = torch.arange(lo + 1, T, 7, device=DEV)
+    vals[tied] = torch.randint(0, 4, (tied.numel(), ld), generator=gen, device=DEV).float()
+    const = torch.arange(lo + 3, T, 61, device=DEV)
+    vals[const] = 0.5
+    front = torch.arange(lo + 5, T, 97, device=DEV)
+    vals[front, :4096] = 3.0
+    rows = np.unique(np.concatenate([
+        np.arange(lo, lo + 12), np.arange(lo + 508, lo + 520), np.arange(lo + 1020, lo + 1030),
+        np.arange(T - 8, T), tied.cpu().numpy()[-3:], const.cpu().numpy()[:4], front.cpu().numpy()[:3]]))
+    rows = rows[(rows >= lo) & (rows < T)]
+    idx, val = sa.topk_select(vals, 2048, with_values=True)
+    sc = vals[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    ref_i, ref_v = oracle.topk_select_dense(sc, 2048, rows=rows)
+    np.testing.assert_array_equal(idx.cpu().numpy()[rows], ref_i)
+    np.testing.assert_array_equal(val.cpu().numpy()[rows].view(np.uint32), ref_v.view(np.uint32))
+
+
 def _cand_case(case, rng):
     """(vals [T, ld] fp32, cand [T, ld] int32, topk) for one selection stress case.
 
