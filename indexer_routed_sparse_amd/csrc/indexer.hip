@@ -392,7 +392,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer_kernel(IdxArgs a) {
 #pragma unroll
           for (int sg = 0; sg < 16; ++sg) {
             const int tl = (32 * mt + 8 * (sg >> 2)) / HI;
-            acc[tl] = fmaf(wr[mt][sg], fmaxf(S[mt][nt][sg], 0.0f), acc[tl]);
+            acc[tl] = fmaf(wr[mt][sg], __builtin_elementwise_maximum(S[mt][nt][sg], 0.0f), acc[tl]);
           }
 #pragma unroll
         for (int i = 0; i < TW; ++i) {
@@ -407,7 +407,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer_kernel(IdxArgs a) {
           for (int g = 0; g < 4; ++g) {
             float v = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v = fmaf(wr[mt][4 * g + j], fmaxf(S[mt][nt][4 * g + j], 0.0f), v);
+            for (int j = 0; j < 4; ++j) v = fmaf(wr[mt][4 * g + j], __builtin_elementwise_maximum(S[mt][nt][4 * g + j], 0.0f), v);
             const int tl = 8 * mt + 2 * g + hl;
             wst[tl * kKT + key] = v;
           }
@@ -451,7 +451,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer_kernel(IdxArgs a) {
           emit = (L % B == 0) && (k0 + L <= t);
         } else {
           m = wave_max(m);
-          m = fmaxf(m, s_bmax[qi]);
+          m = __builtin_elementwise_maximum(m, s_bmax[qi]);
           blk = (k0 - cs) / B;
           const bool last_of_block = ((k0 - cs + kKT) % B == 0) || (k0 + kKT > t);
           __builtin_amdgcn_wave_barrier();

@@ -121,12 +121,14 @@ SA_DEVICE float dpp_f32(float x) {
 // 32-lane swaps. Each step pairs every lane with one of the other half of its group,
 // so no value goes through LDS.
 SA_DEVICE float group_max(float x, int B) {
-  if (B >= 2) x = fmaxf(x, dpp_f32<0xB1>(x));    // quad_perm [1,0,3,2]
-  if (B >= 4) x = fmaxf(x, dpp_f32<0x4E>(x));    // quad_perm [2,3,0,1]
-  if (B >= 8) x = fmaxf(x, dpp_f32<0x141>(x));   // row_half_mirror
-  if (B >= 16) x = fmaxf(x, dpp_f32<0x140>(x));  // row_mirror
-  if (B >= 32) { const float2_t r = lane_rows16(x); x = fmaxf(r.x, r.y); }
-  if (B >= 64) { const float2_t h = lane_halves(x); x = fmaxf(h.x, h.y); }
+  // elementwise_maximum (v_maximum3) needs no quieting of its inputs, where fmaxf pays
+  // a canonicalising max per operand; the values here are never NaN
+  if (B >= 2) x = __builtin_elementwise_maximum(x, dpp_f32<0xB1>(x));    // quad_perm [1,0,3,2]
+  if (B >= 4) x = __builtin_elementwise_maximum(x, dpp_f32<0x4E>(x));    // quad_perm [2,3,0,1]
+  if (B >= 8) x = __builtin_elementwise_maximum(x, dpp_f32<0x141>(x));   // row_half_mirror
+  if (B >= 16) x = __builtin_elementwise_maximum(x, dpp_f32<0x140>(x));  // row_mirror
+  if (B >= 32) { const float2_t r = lane_rows16(x); x = __builtin_elementwise_maximum(r.x, r.y); }
+  if (B >= 64) { const float2_t h = lane_halves(x); x = __builtin_elementwise_maximum(h.x, h.y); }
   return x;
 }
 
