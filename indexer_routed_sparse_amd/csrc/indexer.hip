@@ -415,6 +415,78 @@ __global__ __launch_bounds__(kMaxWaves * 64) void indexer_kernel(IdxArgs a) {
     }
     __builtin_amdgcn_wave_barrier();
 
+    // ---- blocks of at least a tile: every token of the wave gets at most one block
+    //      value per tile, so all TW tokens are handled in one pass, HI lanes per token
+    //      (lane j of token i takes keys j KPL .. j KPL + KPL - 1 of the staged row)
+    if (a.B >= kKT) {
+      constexpr int KPL = kKT / HI;
+      const int i = L / HI, j = L % HI;
+      const int t = wt0 + i;
+      const int qi = w * TW + i;
+      const bool live = t < t1 && k0 <= t;   // the token has a causal key in this tile
+      float m = -__builtin_huge_valf();
+      if (live) {
+        const float* src = wst + i * kKT + j * KPL;
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) {
+          float sc = src[e];
+          if (sc == 0.0f) sc = 0.0f;           // -0 -> +0
+          if (k0 + j * KPL + e <= t) m = __builtin_elementwise_maximum(m, sc);
+        }
+      }
+      m = group_max(m, HI);
+      const int B = a.B;
+      const int blk = (k0 - cs) / B;
+      bool emit = live;
+      if (B > kKT) {
+        // running max over the tiles of a block; the value goes out at its last tile
+        m = __builtin_elementwise_maximum(m, live ? s_bmax[qi] : -__builtin_huge_valf());
+        const bool last = ((k0 - cs + kKT) % B == 0) || (k0 + kKT > t);
+        if (live && j == 0) s_bmax[qi] = last ? -__builtin_huge_valf() : m;
+        emit = live && last;
+      }
+      emit = emit && j == 0;
+      if (!fused) {
+        if (emit) a.scores[(int64_t)t * a.ld + blk] = m;
+      } else {
+        uint32_t kk = order_key(m);
+        if (emit && a.force_own && blk == (t - cs) / B) {
+          kk = 0xFFFFFFFFu;
+          s_own[qi] = m == 0.0f ? 0.0f : m;
+        }
+        uint32_t tau = emit ? s_tau[qi] : 0u;
+        int n = emit ? s_n[qi] : 0;
+        bool take = emit && kk > tau;
+        // a full buffer is first cut back to topk by the whole wave, one token at a time
+        uint64_t full = ballot(take && n + 1 > a.cap);
+#pragma unroll 1
+        while (full) {                          // uniform
+          const int srcl = (int)__builtin_ctzll(full);
+          const int qs = w * TW + srcl / HI;
+          const int ns = __builtin_amdgcn_readlane(n, srcl);
+          const uint32_t tnew = wave_shrink(bkeys + (size_t)qs * a.cap, bids + (size_t)qs * a.cap, ns,
+                                            a.topk, hist + w * 256);
+          if (L == srcl) {
+            tau = tnew;
+            n = a.topk;
+            take = kk > tau;
+          }
+          full &= full - 1;
+        }
+        if (take) {
+          bkeys[(size_t)qi * a.cap + n] = kk;
+          bids[(size_t)qi * a.cap + n] = blk;
+          ++n;
+        }
+        if (emit) {
+          s_n[qi] = n;
+          s_tau[qi] = tau;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      continue;
+    }
+
     // ---- per token of this wave: dense write, or fused selection
 #pragma unroll 1
     for (int i = 0; i < TW; ++i) {
