@@ -424,6 +424,26 @@ def test_block_topk_buffer_cutback_against_oracle(sa, B, k):
     np.testing.assert_array_equal(val.cpu().numpy(), ref_v)
 
 
+@pytest.mark.parametrize("B,k,own,T", [(64, 1, True, 8192), (128, 3, False, 12288), (256, 2, True, 20480)])
+def test_block_topk_wide_blocks_cutback_against_oracle(sa, B, k, own, T):
+    """Blocks of one or more 64-key tiles, one pass (no workspace), on the integer grid:
+    each row's block maxima (running over a block's tiles at B = 128 and 256) go to the
+    token's buffer, which fills after k + 64 blocks and is cut back mid-stream (twice on
+    the last rows at B = 64, k = 1); sampled rows, among them the last 48, equal the
+    oracle bit for bit."""
+    wl = W["block_gqa"]
+    x = workloads.indexer_inputs(wl, integer=True, T=T)
+    assert workloads.exact_sum_bound(x["q_I"], x["k_I"], x["w"]) < 2 ** 24
+    xd = {n: t.to(DEV) for n, t in x.items()}
+    idx, val = sa.indexer_topk(xd["q_I"], xd["k_I"], xd["w"], k, block_size=B, force_own_block=own,
+                               with_values=True)
+    rows = np.union1d(sample_rows(T, 24, B + k), np.arange(T - 48, T))
+    ref_i, ref_v = oracle.indexer_topk(x["q_I"], x["k_I"], x["w"], k, block_size=B,
+                                       force_own_block=own, rows=rows)
+    np.testing.assert_array_equal(idx.cpu().numpy()[rows], ref_i)
+    np.testing.assert_array_equal(val.cpu().numpy()[rows], ref_v)
+
+
 @pytest.mark.parametrize("workspace", [True, False])
 @pytest.mark.parametrize("k", [1, 100, 777, 2048])
 def test_indexer64_fused_small_k_against_oracle(sa, k, workspace):
