@@ -266,25 +266,27 @@ __global__ __launch_bounds__(kWavesPerGroup * 64) void block_gqa_bf16_kernel(
 //   * set-up: the routes' blocks, as key rows start + b B, are marked in a bitmap over
 //     the group's key range; a prefix count over its words numbers the distinct blocks
 //     in ascending key order, and each route entry ORs its token into its block's mask;
-//   * the blocks go in 32-key pieces, one per step (one barrier each): K and V rows
+//   * the blocks go in 32-key pieces, two per step (one barrier each): K and V rows
 //     are copied straight from memory into a four-piece LDS ring by 16-byte
-//     global_load_lds with a scalar row base and fixed per-lane offsets, three pieces
-//     ahead of the one computed; both regions are XOR-swizzled per row, K for the
-//     operand reads of S^T = K . Q^T (16x16x32), V for the transposed reads of
-//     O^T = V^T . P^T. The step is written out once per ring slot, so every LDS
-//     address is a lane offset plus an immediate, and each piece's description (first
-//     key, keys, token mask) sits in scalar registers, read from the tables once per
-//     block. Every wave copies every piece, so this per-piece work is what the waves
-//     that skip a piece still pay;
-//   * a wave skips the MFMAs of a piece none of its rows' tokens routes to; a row's
-//     online softmax ignores masked keys exactly (p 0) and rescales O only when a logit
-//     passes the row's reference by more than 2^8.
+//     global_load_lds with a scalar row base and fixed per-lane offsets, the next
+//     step's pieces while the current step's are computed; both regions are
+//     XOR-swizzled per row, K for the operand reads of S^T = K . Q^T (16x16x32), V for
+//     the transposed reads of O^T = V^T . P^T. The step is written out once per half of
+//     the ring, so every LDS address is a lane offset plus an immediate, and each
+//     piece's description (first key, keys, token mask) sits in scalar registers, read
+//     from the tables once per block. Every wave copies every piece, so this per-piece
+//     work is what the waves that skip a piece still pay;
+//   * a wave skips the MFMAs of a piece none of its rows' tokens routes to; the two
+//     pieces of a step share one online-softmax update (one max, one rescale test); a
+//     row ignores masked keys exactly (p 0) and rescales O only when a logit passes the
+//     row's reference by more than 2^8.
 // Measured on the block-routed workload: two workgroups of four waves with two column
 // tiles each, one sub-tile ahead, 0.89 ms; skipping per column tile 0.79; two sub-tiles
 // ahead 0.77; eight waves of one tile (twice the waves per SIMD) 0.68; fixed softmax
 // reference 0.58; copies with scalar bases and piece descriptions in scalar registers
-// instead of per-lane 64-bit addresses and table reads per copy, 0.50. 64-key sub-tiles,
-// two pieces per barrier and 256-row groups were no faster.
+// instead of per-lane 64-bit addresses and table reads per copy, 0.50; two pieces per
+// barrier, 0.48 (the same change had measured 4 % slower while the copies still paid
+// per-lane addresses). 256-row groups were no faster.
 // Blocks are visited in ascending key order, the same for every row of the group.
 constexpr int kGrpRing = 4;                      // pieces in the LDS ring (two steps)
 
@@ -331,8 +333,7 @@ __global__ __launch_bounds__(kGrpWaves * 64) __attribute__((amdgpu_waves_per_eu(
   constexpr int PB = piece_bytes<D>();
   constexpr int NT = kGrpWaves * 64;
   constexpr int DPP = 2 * 32 * CPR / 64; // 1 KiB copies per piece (K and V)
-  constexpr int DPW = 2 * DPP / kGrpWaves;   // copies per wave per step
-  static_assert(DPW * kGrpWaves == 2 * DPP && DPP % 2 == 0, "copies split evenly");
+  static_assert(DPP % kGrpWaves == 0 && DPP % 2 == 0, "copies split evenly");
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const GroupTables tbl = group_tables(lds + kGrpRing * PB, GT, nblk, nwords);
   const int32_t* ulo = tbl.ulo;
@@ -480,91 +481,110 @@ __global__ __launch_bounds__(kGrpWaves * 64) __attribute__((amdgpu_waves_per_eu(
     }
   };
 
-  // one piece in ring slot SLOT (a constant, so every LDS address is a lane offset plus
-  // an immediate): wait for its copies, barrier, copy the piece three ahead into the
-  // slot freed by the previous step, compute
   Piece p0 = first_of(0);
   Piece p1 = next_of(p0);
-  Piece p2 = next_of(p1);
-  Piece p3 = next_of(p2);
   fetch(p0, 0);
   fetch(p1, 1);
-  fetch(p2, 2);
-  auto step = [&](auto slot_c) __attribute__((always_inline)) {
-    constexpr int SLOT = decltype(slot_c)::value;
-    const int newer = (p1.u < nu) + (p2.u < nu);       // pieces whose copies may stay in flight
-    if (newer == 2) __builtin_amdgcn_s_waitcnt((2 * DP1) | kWaitVm0);
-    else if (newer == 1) __builtin_amdgcn_s_waitcnt(DP1 | kWaitVm0);
-    else __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();                                    // every wave's copies have landed
-    fetch(p3, (SLOT + 3) & 3);
-    const Piece p4 = next_of(p3);
-    const char* st = lds + SLOT * PB;
-    if (p0.m & tile_tok) {                              // uniform: some row of the wave uses it
-      floatx4v_t S[2] = {floatx4v_t{}, floatx4v_t{}};
-      logits(st, S);
-      // keys 4 quad + e (+16) of the piece count below lim: the row routes here, the
+  // one step: pieces p0 and p1 in ring slots SA and SA + 1 (constants, so every LDS
+  // address is a lane offset plus an immediate); wait for their copies (the only ones
+  // in flight), barrier, copy the next step's two pieces into the other half of the ring
+  // (free once every wave has passed the barrier), then compute both pieces with one
+  // online-softmax update
+  auto step2 = [&](auto sa_c) __attribute__((always_inline)) {
+    constexpr int SA = decltype(sa_c)::value;
+    const Piece p2 = next_of(p1);
+    const Piece p3 = next_of(p2);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    fetch(p2, (SA + 2) & 3);
+    fetch(p3, (SA + 3) & 3);
+    const char* stA = lds + SA * PB;
+    const char* stB = stA + PB;
+    const bool cA = (p0.m & tile_tok) != 0u, cB = (p1.m & tile_tok) != 0u;
+    if (cA || cB) {
+      floatx4v_t S[4] = {floatx4v_t{}, floatx4v_t{}, floatx4v_t{}, floatx4v_t{}};
+      if (cA) logits(stA, S);
+      __builtin_amdgcn_sched_barrier(0);          // (keeps the register peak of the two pieces apart)
+      if (cB) logits(stB, S + 2);
+      // keys 4 quad + e (+16) of a piece count below its lim: the row routes there, the
       // key is in the piece and causal for the row
-      const int lim = (row_ok && ((p0.m >> tau) & 1u)) ? min(p0.nk, tq - p0.lo + 1) - 4 * quad : 0;
+      const int limA = (row_ok && ((p0.m >> tau) & 1u)) ? min(p0.nk, tq - p0.lo + 1) - 4 * quad : 0;
+      const int limB = (row_ok && ((p1.m >> tau) & 1u)) ? min(p1.nk, tq - p1.lo + 1) - 4 * quad : 0;
       // logits in log2 units relative to the row's reference m_run (absolute for a row
-      // that has no reference yet), -inf where the row does not route here: one fma
-      // per logit; only a piece in which some row's causal limit falls (uniform test)
-      // masks key by key
+      // that has no reference yet), -inf where the row does not route to the piece: one
+      // fma per logit; only a piece in which some row's causal limit falls (uniform
+      // test) masks key by key
       const bool seen = m_run != -__builtin_huge_valf();
-      const float bias = lim > 0 ? (seen ? -m_run : 0.0f) : -__builtin_huge_valf();
-      float x[8];
+      const float ref = seen ? -m_run : 0.0f;
+      const float bA = limA > 0 ? ref : -__builtin_huge_valf();
+      const float bB = limB > 0 ? ref : -__builtin_huge_valf();
+      float x[16];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * kt + e] = fmaf(S[kt][e], scale_log2, bias);
-      if (ballot(lim > 0 && lim < 20)) {
+        for (int e = 0; e < 4; ++e) {
+          x[4 * kt + e] = fmaf(S[kt][e], scale_log2, bA);
+          x[8 + 4 * kt + e] = fmaf(S[2 + kt][e], scale_log2, bB);
+        }
+      if (ballot(limA > 0 && limA < 20)) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            x[4 * kt + e] = 16 * kt + e < lim ? x[4 * kt + e] : -__builtin_huge_valf();
+            x[4 * kt + e] = 16 * kt + e < limA ? x[4 * kt + e] : -__builtin_huge_valf();
       }
-      float mx = __builtin_elementwise_maximum(
-          __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[0], x[1]), __builtin_elementwise_maximum(x[2], x[3])),
-          __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[4], x[5]), __builtin_elementwise_maximum(x[6], x[7])));
-      mx = quad_max(mx);
+      if (ballot(limB > 0 && limB < 20)) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            x[8 + 4 * kt + e] = 16 * kt + e < limB ? x[8 + 4 * kt + e] : -__builtin_huge_valf();
+      }
+      float mx[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mx[i] = __builtin_elementwise_maximum(x[2 * i], x[2 * i + 1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx[i] = __builtin_elementwise_maximum(mx[2 * i], mx[2 * i + 1]);
+      float m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx[0], mx[1]),
+                                              __builtin_elementwise_maximum(mx[2], mx[3]));
+      m = quad_max(m);
       // fixed reference: a row takes a new one at its first keys and when a max passes
       // the reference by more than 2^8; O and l are rescaled then only
-      const bool up = mx > -__builtin_huge_valf() && (!seen || mx > kHeadroom);
+      const bool up = m > -__builtin_huge_valf() && (!seen || m > kHeadroom);
       if (ballot(up)) {                                  // uniform
-        const float alpha = up && seen ? __builtin_amdgcn_exp2f(-mx) : 1.0f;
-        const float shift = up ? mx : 0.0f;
-        m_run = up ? (seen ? m_run + mx : mx) : m_run;
+        const float alpha = up && seen ? __builtin_amdgcn_exp2f(-m) : 1.0f;
+        const float shift = up ? m : 0.0f;
+        m_run = up ? (seen ? m_run + m : m) : m_run;
 #pragma unroll
         for (int i = 0; i < NDT; ++i) O[i] *= alpha;
         l_run *= alpha;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] -= shift;
+        for (int i = 0; i < 16; ++i) x[i] -= shift;
       }
-      float pf[8];
+      // P of each piece (bf16, the B operand of O^T += V^T . P^T), then its values
+      auto probs = [&](int o) __attribute__((always_inline)) {
+        float pf[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pf[i] = __builtin_amdgcn_exp2f(x[i]);
-      l_run += ((pf[0] + pf[1]) + (pf[2] + pf[3])) + ((pf[4] + pf[5]) + (pf[6] + pf[7]));
-      bf16x2_t pk[4];
+        for (int i = 0; i < 8; ++i) pf[i] = __builtin_amdgcn_exp2f(x[o + i]);
+        l_run += ((pf[0] + pf[1]) + (pf[2] + pf[3])) + ((pf[4] + pf[5]) + (pf[6] + pf[7]));
+        bf16x2_t pk[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pk[e] = __builtin_convertvector((float2_t){pf[2 * e], pf[2 * e + 1]}, bf16x2_t);
-      values(st, __builtin_bit_cast(bf16x8_t, pk));
+        for (int e = 0; e < 4; ++e) pk[e] = __builtin_convertvector((float2_t){pf[2 * e], pf[2 * e + 1]}, bf16x2_t);
+        return __builtin_bit_cast(bf16x8_t, pk);
+      };
+      if (cA) values(stA, probs(0));
+      __builtin_amdgcn_sched_barrier(0);
+      if (cB) values(stB, probs(8));
     }
-    p0 = p1;
-    p1 = p2;
-    p2 = p3;
-    p3 = p4;
+    p0 = p2;
+    p1 = p3;
   };
 #pragma unroll 1
   for (;;) {                                            // uniform exits
     if (p0.u >= nu) break;
-    step(std::integral_constant<int, 0>{});
+    step2(std::integral_constant<int, 0>{});
     if (p0.u >= nu) break;
-    step(std::integral_constant<int, 1>{});
-    if (p0.u >= nu) break;
-    step(std::integral_constant<int, 2>{});
-    if (p0.u >= nu) break;
-    step(std::integral_constant<int, 3>{});
+    step2(std::integral_constant<int, 2>{});
   }
 
   // ---- normalise and write: lane owns row 16 w + n, channels 16 dt + 4 quad + e
