@@ -813,14 +813,23 @@ hipError_t launch_topk_select(const float* vals, const int32_t* cand, int64_t ld
   return retry_class(top, a, T, st);
 }
 
+// Candidate rows counted by a first pass hold only the keys at or above a sampled pivot,
+// a few standard deviations more than topk, so every row takes the register radix
+// select over all of its candidates: a second sample, pivot and compaction would cost
+// more than they remove.
 hipError_t launch_topk_select_counted(const float* vals, const int32_t* cand, const int32_t* cnt,
                                       int64_t ld, int T, int topk, int32_t* out_idx,
                                       float* out_val, hipStream_t st) {
   const RowArgs a{0, vals, cand, ld, nullptr, 1, 1, topk, 0, out_idx, out_val, cnt};
-  const int top = class_of((int)ld);
-  hipError_t e = launch_class(top, a, 0, T, st);
-  if (e != hipSuccess || topk > cap_of(kClasses[top].nt, kClasses[top].ch)) return e;
-  return retry_class(top, a, T, st);
+  switch (class_of((int)ld)) {
+    case 0: hipLaunchKernelGGL((topk_full_kernel<1, 512, true>), dim3(T), dim3(512), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((topk_full_kernel<2, 512, true>), dim3(T), dim3(512), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((topk_full_kernel<4, 512, true>), dim3(T), dim3(512), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((topk_full_kernel<8, 512, true>), dim3(T), dim3(512), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((topk_full_kernel<8, 1024, true>), dim3(T), dim3(1024), 0, st, a); break;
+    default: hipLaunchKernelGGL((topk_full_kernel<16, 1024, true>), dim3(T), dim3(1024), 0, st, a); break;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace sa
