@@ -444,6 +444,33 @@ def test_block_topk_wide_blocks_cutback_against_oracle(sa, B, k, own, T):
     np.testing.assert_array_equal(val.cpu().numpy()[rows], ref_v)
 
 
+@pytest.mark.parametrize("H_I,dtype,B", [(4, "f32", 64), (4, "bf16", 128), (8, "bf16", 64), (32, "bf16", 64),
+                                          (64, "bf16", 64), (64, "bf16", 128), (16, "f32", 256)])
+def test_block_topk_head_counts_against_oracle(sa, H_I, dtype, B):
+    """Block top-k with blocks of one to four key tiles at every indexer head count the
+    kernels take (4..64 heads, so 16..1 tokens per wave share a tile's block pass), bf16
+    and fp32, packed sequences, one pass and through a workspace: rows past k + 64
+    blocks cut their buffers back; sampled rows equal the oracle bit for bit."""
+    import dataclasses
+    wl = dataclasses.replace(W["block_gqa"], H_I=H_I, dtype=dtype, name=f"block_h{H_I}")
+    lengths = (6000, 37, 4500) if B == 64 else (9000, 300, 7000)
+    T = sum(lengths)
+    x = workloads.indexer_inputs(wl, integer=True, T=T)
+    assert workloads.exact_sum_bound(x["q_I"], x["k_I"], x["w"]) < 2 ** 24
+    xd = {n: t.to(DEV) for n, t in x.items()}
+    cu = workloads.cu_seqlens(lengths)
+    rows = np.union1d(sample_rows(T, 24, H_I + B, lengths), np.arange(T - 16, T))
+    rows = np.union1d(rows, np.arange(lengths[0] - 16, lengths[0]))
+    ref_i, ref_v = oracle.indexer_topk(x["q_I"], x["k_I"], x["w"], 4, cu_seqlens=cu, block_size=B,
+                                       force_own_block=True, rows=rows)
+    for workspace in (False, True):
+        idx, val = sa.indexer_topk(xd["q_I"], xd["k_I"], xd["w"], 4, block_size=B, force_own_block=True,
+                                   with_values=True, workspace=workspace, cu_seqlens=cu_dev(lengths),
+                                   max_seqlen=max(lengths))
+        np.testing.assert_array_equal(idx.cpu().numpy()[rows], ref_i, err_msg=f"workspace={workspace}")
+        np.testing.assert_array_equal(val.cpu().numpy()[rows], ref_v, err_msg=f"workspace={workspace}")
+
+
 @pytest.mark.parametrize("workspace", [True, False])
 @pytest.mark.parametrize("k", [1, 100, 777, 2048])
 def test_indexer64_fused_small_k_against_oracle(sa, k, workspace):
