@@ -315,6 +315,9 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_bf16_kernel(
 // per element from each 32-head block (four at 128 heads) instead of one per 16-head
 // group, and each row is gathered by half as many workgroups. dq accumulates in
 // registers across sub-tiles. A first pass over the same sub-tiles forms D.
+// With DQO (dq only, after the all-heads dkv kernel at 64 and 128 heads) the dkv
+// tiles, their atomics and the first pass are left out, and D is read from the
+// first four bytes of each head's dq row, where the dkv kernel left it.
 constexpr int kB32 = 32;          // heads per workgroup, keys per sub-tile
 constexpr int kXR = kB32 * 2 + 16;  // [key][head] or [head][key] bf16 exchange rows (bytes)
 
@@ -324,7 +327,7 @@ constexpr size_t bwd32_lds_bytes() {
          (size_t)2 * kB32 * krow_bytes<DQK>() + (size_t)3 * kB32 * kXR + 2 * kB32 * sizeof(float);
 }
 
-template <int DQK>
+template <int DQK, bool DQO>
 __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_h32_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, int H, int topk, float scale,
@@ -428,46 +431,53 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_h32_kernel(
       P[i] = rown >= 0 && lse2[i] > -__builtin_huge_valf() ? __builtin_amdgcn_exp2f(S[i] * sc2 - lse2[i]) : 0.0f;
   };
 
-  // ---- pass 1: D = sum_j p_j dp_j per head
-  float dpart[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto pass1 = [&](int sub, int& ixc, int ixn) __attribute__((always_inline)) {
-    char* kt = k_l + (sub & 1) * kB32 * KRB;
-    stage(kt);
-    __syncthreads();
-    if (sub + 1 < nsub) load(ixn);
-    float P[4];
-    floatx4v_t dP;
-    scores(kt, sub, ixc, P, dP);
-    ixc = idx_of(sub + 2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dpart[i] = fmaf(P[i], dP[i], dpart[i]);
-  };
-  int ixa = 0, ixb = 0;       // indices of sub-tiles of even / odd number
-  if (nsub > 0) {
-    ixa = idx_of(0);
-    ixb = idx_of(1);
-    load(ixa);
-  }
-#pragma unroll 1
-  for (int sub = 0; sub < nsub; sub += 2) {
-    pass1(sub, ixa, ixb);
-    if (sub + 1 < nsub) pass1(sub + 1, ixb, ixa);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {          // over the 16 keys (lanes n) of the wave's half
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) dpart[i] += __shfl_xor(dpart[i], off, 64);
-    if (n == 0) dD[kh * kB32 + 16 * hg + 4 * g + i] = dpart[i];
-  }
-  __syncthreads();
   float Dh[4];
+  int ixa = 0, ixb = 0;       // indices of sub-tiles of even / odd number
+  if constexpr (DQO) {
+    // D of each head, left by the dkv kernel in the first four bytes of its dq row
 #pragma unroll
-  for (int i = 0; i < 4; ++i) Dh[i] = dD[16 * hg + 4 * g + i] + dD[kB32 + 16 * hg + 4 * g + i];
-  // the sink's probability exp(sink - lse) times -D is its logit's gradient
-  if (dsink && tid < kB32) {
-    const int hh = h0 + tid;
-    const float D = dD[tid] + dD[kB32 + tid];
-    atomicAdd(dsink + hh, -__builtin_amdgcn_exp2f((sink[hh] - lse[(int64_t)t * H + hh]) * kLog2e) * D);
+    for (int i = 0; i < 4; ++i)
+      Dh[i] = *reinterpret_cast<const float*>(dq + ((int64_t)t * H + h0 + 16 * hg + 4 * g + i) * DQK);
+  } else {
+    // ---- pass 1: D = sum_j p_j dp_j per head
+    float dpart[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto pass1 = [&](int sub, int& ixc, int ixn) __attribute__((always_inline)) {
+      char* kt = k_l + (sub & 1) * kB32 * KRB;
+      stage(kt);
+      __syncthreads();
+      if (sub + 1 < nsub) load(ixn);
+      float P[4];
+      floatx4v_t dP;
+      scores(kt, sub, ixc, P, dP);
+      ixc = idx_of(sub + 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dpart[i] = fmaf(P[i], dP[i], dpart[i]);
+    };
+    if (nsub > 0) {
+      ixa = idx_of(0);
+      ixb = idx_of(1);
+      load(ixa);
+    }
+#pragma unroll 1
+    for (int sub = 0; sub < nsub; sub += 2) {
+      pass1(sub, ixa, ixb);
+      if (sub + 1 < nsub) pass1(sub + 1, ixb, ixa);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {          // over the 16 keys (lanes n) of the wave's half
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) dpart[i] += __shfl_xor(dpart[i], off, 64);
+      if (n == 0) dD[kh * kB32 + 16 * hg + 4 * g + i] = dpart[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Dh[i] = dD[16 * hg + 4 * g + i] + dD[kB32 + 16 * hg + 4 * g + i];
+    // the sink's probability exp(sink - lse) times -D is its logit's gradient
+    if (dsink && tid < kB32) {
+      const int hh = h0 + tid;
+      const float D = dD[tid] + dD[kB32 + tid];
+      atomicAdd(dsink + hh, -__builtin_amdgcn_exp2f((sink[hh] - lse[(int64_t)t * H + hh]) * kLog2e) * D);
+    }
   }
 
   floatx4v_t dqa[TPW];       // dq tiles tt = w + 4 i: head tile tt / NCT, channel tile tt % NCT
@@ -486,8 +496,10 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_h32_kernel(
     for (int i = 0; i < 4; ++i) dS[i] = P[i] * (dP[i] - Dh[i]) * scale;
     {
       const int key = 16 * kh + n, head = 16 * hg + 4 * g;
-      *reinterpret_cast<short4_t*>(xS + key * kXR + head * 2) = pack4(dS[0], dS[1], dS[2], dS[3]);
-      *reinterpret_cast<short4_t*>(xP + key * kXR + head * 2) = pack4(P[0], P[1], P[2], P[3]);
+      if constexpr (!DQO) {
+        *reinterpret_cast<short4_t*>(xS + key * kXR + head * 2) = pack4(dS[0], dS[1], dS[2], dS[3]);
+        *reinterpret_cast<short4_t*>(xP + key * kXR + head * 2) = pack4(P[0], P[1], P[2], P[3]);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) *reinterpret_cast<uint16_t*>(xT + (head + i) * kXR + key * 2) = f2bf_bits(dS[i]);
     }
@@ -513,7 +525,7 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_h32_kernel(
       const int t2 = tt / NCT, ct = tt % NCT;
       const int toff = (16 * ct + 4 * (n & 3)) * 2;
       // dkv tile: keys 16 t2 + ..., channels 16 ct + ...; k = heads {4g + e, 16 + 4g + e}
-      {
+      if constexpr (!DQO) {
         const char* ar = xS + (16 * t2 + n) * kXR + 8 * g;
         const uint2 a0 = *reinterpret_cast<const uint2*>(ar);
         const uint2 a1 = *reinterpret_cast<const uint2*>(ar + 32);
@@ -571,6 +583,256 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_h32_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       dq[((int64_t)t * H + h0 + 16 * ht + 4 * g + e) * DQK + 16 * ct + n] = f2bf_bits(dqa[i][e]);
+  }
+}
+
+// bf16 dkv with every head of a token in one workgroup (H = 16 NW heads, NW waves),
+// for H in {64, 128}. Floating-point atomic adds into dkv run at a fixed rate per
+// element whatever the lanes' address pattern, and they bound this backward; summing
+// the whole token's heads before the adds issues one add per element of each gathered
+// row instead of one per 32-head block. The token's q and dout (278 KB at 128 heads)
+// do not both fit in LDS, so:
+//   * dout of the H heads stays in LDS; wave w reads its S-phase A operands (heads
+//     16 w + n, channel-contiguous) and, by transposing reads, the B operands of
+//     dv = P^T dout (head-contiguous) from there;
+//   * q passes through LDS once at the start, from which each wave keeps in registers
+//     the A operands of S for its 16 heads and the B operands of dk = dS^T q for its
+//     channel tiles (16 ct + n, ct = w + NW i) over all H heads;
+//   * per 16-key sub-tile: S and dP of (wave's 16 heads) x 16 keys, P and dS into LDS
+//     as [key][head]; then each wave contracts over all H heads for its channel tiles
+//     and adds each 16x16 tile into the gathered rows (one add per element).
+// A first pass over the same sub-tiles sums D = sum_j p_j dp_j per head; it is stored,
+// as fp32, in the first four bytes of the head's dq row, which the dq kernel launched
+// next reads before it overwrites the row (and dsink is formed here).
+template <int DQK, int NW>
+constexpr size_t dkv_lds_bytes() {
+  constexpr size_t HH = 16 * NW;
+  const size_t main = HH * drow_bytes() + (size_t)kSK * krow_bytes<DQK>() + 2 * (size_t)kSK * (HH * 2 + 16);
+  const size_t qst = HH * krow_bytes<DQK>();        // q, staged once at the start
+  return main > qst ? main : qst;
+}
+
+template <int DQK, int NW>
+__global__ __launch_bounds__(NW * 64) void sparse_mla_bwd_dkv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, int topk, float scale,
+    const float* __restrict__ sink, uint16_t* __restrict__ dq, float* __restrict__ dkv,
+    float* __restrict__ dsink) {
+  constexpr int H = 16 * NW;
+  constexpr int KRB = krow_bytes<DQK>();
+  constexpr int DRB = drow_bytes();
+  constexpr int XRB = H * 2 + 16;         // [key][head] bf16 exchange rows (bytes)
+  constexpr int NK = DQK / 32;            // 32-wide k-steps of S
+  constexpr int NV = 512 / 32;            // ... of dP
+  constexpr int NCT = DQK / 16;           // 16-channel tiles of dkv
+  constexpr int NVT = 512 / 16;           // ... that carry the value part
+  constexpr int TPW = (NCT + NW - 1) / NW;  // channel tiles per wave (the last may be past NCT)
+  constexpr int KS = H / 32;              // 32-head k-steps of the dkv contraction
+  constexpr int CPR = DQK * 2 / 16;       // 16-byte chunks per key row
+  constexpr int NT = NW * 64;
+  constexpr int NLD = (kSK * CPR + NT - 1) / NT;   // chunks per thread (the last partial)
+  static_assert(NW % 2 == 0, "whole 32-head k-steps");
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  char* d_l = lds;                                        // [H heads][DRB] dout
+  char* k_l = d_l + H * DRB;                              // [16 keys][KRB]
+  char* xS = k_l + kSK * KRB;                             // dS [16 keys][XRB]
+  char* xP = xS + kSK * XRB;                              // P  [16 keys][XRB]
+
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, L = tid & 63;
+  const int g = L >> 4, n = L & 15;
+
+  // ---- q of the H heads through LDS into registers
+  for (int c = tid; c < H * CPR; c += NT) {
+    const int hh = c / CPR, p = c % CPR;
+    *reinterpret_cast<bf16x8_t*>(lds + hh * KRB + 16 * p) =
+        *reinterpret_cast<const bf16x8_t*>(q + ((int64_t)t * H + hh) * DQK + 8 * p);
+  }
+  __syncthreads();
+  bf16x8_t qa[NK];                        // A operands of S: head 16 w + n, channels 32 ks + 8 g
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks)
+    qa[ks] = *reinterpret_cast<const bf16x8_t*>(lds + (16 * w + n) * KRB + 64 * ks + 16 * g);
+  bf16x8_t qb[TPW][KS];                   // B operands of dk: heads {32 s + 4 g + e, +16} x channel 16 ct + n
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int ct = w + NW * i;
+    const int toff = (16 * (ct < NCT ? ct : 0) + 4 * (n & 3)) * 2;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const short4_t b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(lds + (32 * s + 4 * g + (n >> 2)) * KRB + toff));
+      const short4_t b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(lds + (32 * s + 16 + 4 * g + (n >> 2)) * KRB + toff));
+      const short __attribute__((ext_vector_type(8))) b8 = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+      qb[i][s] = __builtin_bit_cast(bf16x8_t, b8);
+    }
+  }
+  __syncthreads();                        // q's staging area becomes dout's and the key rows'
+  for (int c = tid; c < H * 64; c += NT) {
+    const int hh = c >> 6, p = c & 63;
+    *reinterpret_cast<bf16x8_t*>(d_l + hh * DRB + 16 * p) =
+        *reinterpret_cast<const bf16x8_t*>(dout + ((int64_t)t * H + hh) * 512 + 8 * p);
+  }
+
+  float lse2[4];                          // heads 16 w + 4 g + i (rows of this lane's S tile)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lse2[i] = lse[(int64_t)t * H + 16 * w + 4 * g + i] * kLog2e;
+  const int32_t* irow = idx + (int64_t)t * topk;
+  const int nsub = (topk + kSK - 1) / kSK;
+  const float sc2 = scale * kLog2e;
+
+  // Slot indices of a sub-tile: lane l holds slot 16 sub + (l mod 16), clamped to the
+  // last slot. As in the 32-head kernel, two registers take turns and the loop body is
+  // written out twice, so no in-flight load is copied (a copy would wait for the dkv
+  // atomics issued before it).
+  auto idx_of = [&](int sub) __attribute__((always_inline)) {
+    return irow[min(sub * kSK + n, topk - 1)];
+  };
+  bf16x8_t nx[NLD];
+  auto load = [&](int ix) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < NLD; ++m) {
+      const int c = tid + NT * m, r = (c / CPR) & (kSK - 1), p = c % CPR;
+      int row = __shfl(ix, r, 64);
+      row = row < 0 ? 0 : row;                 // masked slot (or past topk): any finite row
+      if (c < kSK * CPR) nx[m] = *reinterpret_cast<const bf16x8_t*>(kv + (int64_t)row * DQK + 8 * p);
+    }
+  };
+  auto stage = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < NLD; ++m) {
+      const int c = tid + NT * m, r = c / CPR, p = c % CPR;
+      if (c < kSK * CPR) *reinterpret_cast<bf16x8_t*>(k_l + r * KRB + 16 * p) = nx[m];
+    }
+  };
+  // S and dP of this wave's 16 heads x the 16 keys; P of the valid slots
+  auto scores = [&](int sub, int ix, float (&P)[4], floatx4v_t& dP) __attribute__((always_inline)) {
+    const int rown = sub * kSK + n < topk ? __shfl(ix, n, 64) : -1;
+    const char* krow = k_l + n * KRB + 16 * g;
+    const char* drow = d_l + (16 * w + n) * DRB + 16 * g;
+    floatx4v_t S = floatx4v_t{};
+    dP = floatx4v_t{};
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+      const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(krow + 64 * ks);
+      S = mfma16x32(qa[ks], b, S);
+      if (ks < NV) dP = mfma16x32(*reinterpret_cast<const bf16x8_t*>(drow + 64 * ks), b, dP);
+      // a fence every few k-steps keeps the LDS reads from being hoisted all at once
+      // (their registers would not fit beside q's operands)
+      if (ks % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      P[i] = rown >= 0 && lse2[i] > -__builtin_huge_valf() ? __builtin_amdgcn_exp2f(S[i] * sc2 - lse2[i]) : 0.0f;
+  };
+
+  // ---- pass 1: D = sum_j p_j dp_j per head
+  float dpart[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto pass1 = [&](int sub, int& ixc, int ixn) __attribute__((always_inline)) {
+    __syncthreads();                   // every wave is done with the previous key rows
+    stage();
+    __syncthreads();
+    if (sub + 1 < nsub) load(ixn);
+    float P[4];
+    floatx4v_t dP;
+    scores(sub, ixc, P, dP);
+    ixc = idx_of(sub + 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dpart[i] = fmaf(P[i], dP[i], dpart[i]);
+  };
+  int ixa = 0, ixb = 0;       // indices of sub-tiles of even / odd number
+  if (nsub > 0) {
+    ixa = idx_of(0);
+    ixb = idx_of(1);
+    load(ixa);
+  }
+#pragma unroll 1
+  for (int sub = 0; sub < nsub; sub += 2) {
+    pass1(sub, ixa, ixb);
+    if (sub + 1 < nsub) pass1(sub + 1, ixb, ixa);
+  }
+  float Dh[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {          // over the 16 keys (lanes n)
+    float d = dpart[i];
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) d += __shfl_xor(d, off, 64);
+    Dh[i] = d;
+  }
+  if (n == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = 16 * w + 4 * g + i;
+      *reinterpret_cast<float*>(dq + ((int64_t)t * H + hh) * DQK) = Dh[i];
+      // the sink's probability exp(sink - lse) times -D is its logit's gradient
+      if (dsink)
+        atomicAdd(dsink + hh, -__builtin_amdgcn_exp2f((sink[hh] - lse[(int64_t)t * H + hh]) * kLog2e) * Dh[i]);
+    }
+  }
+
+  // ---- pass 2: dS; dkv = dS^T q + P^T dout over all H heads
+  auto pass2 = [&](int sub, int& ixc, int ixn) __attribute__((always_inline)) {
+    stage();
+    __syncthreads();                   // also: every wave is done with the exchange rows
+    if (sub + 1 < nsub) load(ixn);
+    float P[4], dS[4];
+    floatx4v_t dP;
+    scores(sub, ixc, P, dP);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dS[i] = P[i] * (dP[i] - Dh[i]) * scale;
+    {
+      const int head = 16 * w + 4 * g;
+      *reinterpret_cast<short4_t*>(xS + n * XRB + head * 2) = pack4(dS[0], dS[1], dS[2], dS[3]);
+      *reinterpret_cast<short4_t*>(xP + n * XRB + head * 2) = pack4(P[0], P[1], P[2], P[3]);
+    }
+    int krow[4];                       // kv rows of this lane's dkv keys 4 g + e
+#pragma unroll
+    for (int e = 0; e < 4; ++e) krow[e] = sub * kSK + 4 * g + e < topk ? __shfl(ixc, 4 * g + e, 64) : -1;
+    ixc = idx_of(sub + 2);
+    __syncthreads();                   // also: every wave is done with the key rows
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int ct = w + NW * i;
+      if (ct < NCT) {
+        const int toff = (16 * ct + 4 * (n & 3)) * 2;
+        floatx4v_t acc = floatx4v_t{};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const char* ar = xS + n * XRB + 64 * s + 8 * g;
+          const uint2 a0 = *reinterpret_cast<const uint2*>(ar);
+          const uint2 a1 = *reinterpret_cast<const uint2*>(ar + 32);
+          acc = mfma16x32(__builtin_bit_cast(bf16x8_t, make_uint4(a0.x, a0.y, a1.x, a1.y)), qb[i][s], acc);
+        }
+        if (ct < NVT) {
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            const char* pr = xP + n * XRB + 64 * s + 8 * g;
+            const uint2 p0 = *reinterpret_cast<const uint2*>(pr);
+            const uint2 p1 = *reinterpret_cast<const uint2*>(pr + 32);
+            const short4_t c0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(d_l + (32 * s + 4 * g + (n >> 2)) * DRB + toff));
+            const short4_t c1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(d_l + (32 * s + 16 + 4 * g + (n >> 2)) * DRB + toff));
+            const short __attribute__((ext_vector_type(8))) c8 = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+            acc = mfma16x32(__builtin_bit_cast(bf16x8_t, make_uint4(p0.x, p0.y, p1.x, p1.y)),
+                            __builtin_bit_cast(bf16x8_t, c8), acc);
+          }
+        }
+        // lane (g, n): keys 4 g + e, channel 16 ct + n
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (krow[e] >= 0) atomicAdd(dkv + (int64_t)krow[e] * DQK + 16 * ct + n, acc[e]);
+      }
+      __builtin_amdgcn_sched_barrier(0);   // one tile's operands live at a time
+    }
+  };
+  if (nsub > 0) {
+    ixa = idx_of(0);
+    ixb = idx_of(1);
+    __syncthreads();                   // every wave is done with pass 1's key rows
+    load(ixa);
+  }
+#pragma unroll 1
+  for (int sub = 0; sub < nsub; sub += 2) {
+    pass2(sub, ixa, ixb);
+    if (sub + 1 < nsub) pass2(sub + 1, ixb, ixa);
   }
 }
 
@@ -809,12 +1071,37 @@ hipError_t launch_bwd32(const void* q, const void* kv, const int32_t* idx, const
                         const float* lse, int T, int H, int topk, float scale, const float* sink,
                         void* dq, float* dkv, float* dsink, hipStream_t st) {
   const size_t shm = bwd32_lds_bytes<DQK>();
-  hipError_t e = hipFuncSetAttribute((const void*)sparse_mla_bwd_h32_kernel<DQK>,
+  hipError_t e = hipFuncSetAttribute((const void*)sparse_mla_bwd_h32_kernel<DQK, false>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((sparse_mla_bwd_h32_kernel<DQK>), dim3(T, H / kB32), dim3(kWaves * 64), shm, st,
+  hipLaunchKernelGGL((sparse_mla_bwd_h32_kernel<DQK, false>), dim3(T, H / kB32), dim3(kWaves * 64), shm, st,
                      (const uint16_t*)q, (const uint16_t*)kv, idx, (const uint16_t*)dout, lse, H, topk,
                      scale, sink, (uint16_t*)dq, dkv, dsink);
+  return hipGetLastError();
+}
+
+// H = 16 NW in {64, 128}: dkv (and D, dsink) with all heads per workgroup, then dq by
+// the 32-head kernel in its dq-only form.
+template <int DQK, int NW>
+hipError_t launch_bwd_split(const void* q, const void* kv, const int32_t* idx, const void* dout,
+                            const float* lse, int T, int topk, float scale, const float* sink,
+                            void* dq, float* dkv, float* dsink, hipStream_t st) {
+  const size_t shm_k = dkv_lds_bytes<DQK, NW>();
+  hipError_t e = hipFuncSetAttribute((const void*)sparse_mla_bwd_dkv_kernel<DQK, NW>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm_k);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((sparse_mla_bwd_dkv_kernel<DQK, NW>), dim3(T), dim3(NW * 64), shm_k, st,
+                     (const uint16_t*)q, (const uint16_t*)kv, idx, (const uint16_t*)dout, lse, topk,
+                     scale, sink, (uint16_t*)dq, dkv, dsink);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t shm = bwd32_lds_bytes<DQK>();
+  e = hipFuncSetAttribute((const void*)sparse_mla_bwd_h32_kernel<DQK, true>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((sparse_mla_bwd_h32_kernel<DQK, true>), dim3(T, 16 * NW / kB32), dim3(kWaves * 64), shm,
+                     st, (const uint16_t*)q, (const uint16_t*)kv, idx, (const uint16_t*)dout, lse, 16 * NW,
+                     topk, scale, sink, (uint16_t*)dq, dkv, dsink);
   return hipGetLastError();
 }
 
@@ -830,6 +1117,14 @@ hipError_t launch_sparse_mla_bwd(const void* q, const void* kv, const int32_t* i
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || T == 0) return e;
   if (bf16) {
+    if (H == 128) {
+      if (d_qk == 576) return launch_bwd_split<576, 8>(q, kv, idx, dout, lse, T, topk, scale, sink, dq, dkv, dsink, st);
+      return launch_bwd_split<512, 8>(q, kv, idx, dout, lse, T, topk, scale, sink, dq, dkv, dsink, st);
+    }
+    if (H == 64) {
+      if (d_qk == 576) return launch_bwd_split<576, 4>(q, kv, idx, dout, lse, T, topk, scale, sink, dq, dkv, dsink, st);
+      return launch_bwd_split<512, 4>(q, kv, idx, dout, lse, T, topk, scale, sink, dq, dkv, dsink, st);
+    }
     if (H % kB32 == 0) {
       if (d_qk == 576) return launch_bwd32<576>(q, kv, idx, dout, lse, T, H, topk, scale, sink, dq, dkv, dsink, st);
       return launch_bwd32<512>(q, kv, idx, dout, lse, T, H, topk, scale, sink, dq, dkv, dsink, st);
