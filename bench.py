@@ -357,7 +357,8 @@ def write_traffic(fetch_dir, write_dir, command):
         "attn_teacher_long_dsa": (lambda n: "attn_teacher_bf16_kernel" in n, ["sparse_mla_bwd.hip", "sa_common.h"], 1),
         "indexer_kl_long_dsa": (lambda n: "indexer_kl_bf16_kernel" in n or "zero_kernel" in n,
                                 ["indexer_kl.hip", "sa_common.h"], None),
-        "block_gqa_bwd_block_workload": (lambda n: "block_gqa_bwd_group_kernel" in n or "zero2_f32_kernel" in n,
+        "block_gqa_bwd_block_workload": (lambda n: "block_gqa_bwd_group_kernel" in n or "block_gqa_bwd_kmaj_kernel" in n
+                                         or "zero2_f32_kernel" in n,
                                          ["block_gqa_bwd.hip", "sa_common.h"], None),
     }
     for key, (match, srcs, _) in groups.items():
@@ -585,7 +586,8 @@ def main():
                                                                gdq, gdk, gdv, block_size=64), 3)
             # S, dP, dq, dk, dv per attended key and q head
             result.setdefault("gradients", {})["block_gqa_bwd"] = _mfma_entry(
-                "block_gqa_bwd_group_kernel", 2.0 * wq.Hq * (3 * wq.D + 2 * wq.Dv) * attended, ms,
+                "block_gqa_bwd_group_kernel (D, then dq) + block_gqa_bwd_kmaj_kernel (dk, dv)",
+                2.0 * wq.Hq * (3 * wq.D + 2 * wq.Dv) * attended, ms,
                 traffic=_traffic("block_gqa_bwd_block_workload", ["block_gqa_bwd.hip", "sa_common.h"]))
 
     if not args.no_cpu_baseline:

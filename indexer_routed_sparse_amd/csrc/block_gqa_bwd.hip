@@ -10,7 +10,12 @@
 //   dq[t,h] = sum_s ds_s k_s;  dk[s,g] += sum_h ds_s q[t,h];  dv[s,g] += sum_h p_s dout[t,h].
 // lse comes from the forward; D is summed from the p_s dp_s (a first pass).
 //
-// bf16 kernel (gfx950): one wave per (token, kv head), four per workgroup, each with
+// bf16, where a token group's set-up tables fit the LDS: three launches after the dk/dv
+// zero fill. The grouped kernel's D pass (D of every row into the first four bytes of
+// its dq row), the key-major dk/dv kernel (one add per element per 64-key block and
+// 2048-token chunk), then the grouped dq pass (D read back, dq written over it).
+//
+// bf16 otherwise (gfx950): one wave per (token, kv head), four per workgroup, each with
 // its own LDS: the G <= 16 query heads of the group are the 16 rows of 16x16 MFMA tiles
 // over 16-key sub-tiles of the route. S = Q K^T and dP = dout V^T take q and dout as A
 // operands from registers and the staged key and value rows as B operands; P and dS
@@ -303,35 +308,31 @@ __global__ __launch_bounds__(kNT) void block_gqa_bwd_f32_kernel(
   }
 }
 
-// Grouped bf16 backward: one workgroup per (group of GT consecutive tokens, kv head),
-// eight waves, over the distinct blocks of the group's routes (gqa_group.h) in 32-key
-// sub-tiles staged in LDS, twice: pass 1 forms D = sum p dp of every query row, pass
-// 2 forms dS, dq (per row, in registers) and the sub-tile's dk and dv over all of the
-// group's rows, added to dk and dv with one atomic per element and sub-tile instead
-// of one per element and token. Wave w owns rows 16w .. 16w+15 (token row / G, head
-// row mod G):
+// Grouped bf16 passes of the backward: one workgroup per (group of GT consecutive
+// tokens, kv head), eight waves, over the distinct blocks of the group's routes
+// (gqa_group.h) in 32-key sub-tiles staged in LDS. MODE 1 forms D = sum p dp of every
+// query row and leaves it, as fp32, in the first four bytes of the row's dq; MODE 2,
+// launched after the key-major dk/dv kernel, reads it back and forms dS and dq (per
+// row, in registers), then overwrites the row with dq. Wave w owns rows 16w .. 16w+15
+// (token row / G, head row mod G):
 //   * S^T = K Q^T and dP^T = V dout^T on 16x16x32 MFMAs: key and value rows from
 //     padded stages as A operands, the row's q and dout as B operands in registers;
 //     lane (n, quad) holds keys 4 quad + e and 16 + 4 quad + e of row n;
 //   * dq^T += K^T dS^T: K^T by transposing reads of a swizzled copy of the key rows,
-//     dS^T as it stands in registers;
-//   * dS and P (bf16) meet in LDS as [key][row]; wave w then takes its share of the
-//     output tiles (16 keys x 16 channels) of dk = dS^T Q and dv = P^T dout over all
-//     128 rows, with the group's q and dout rows in LDS read transposed.
+//     dS^T as it stands in registers.
 template <int D>
 constexpr int gb_stage_bytes() { return 32 * (D * 2 + 16) * 2 + 32 * D * 2; }   // K pad, V pad, K swz
 constexpr int kXRB = kGrpRows * 2 + 16;                                           // [key][row] bf16 rows
 
 size_t grp_bwd_lds_bytes(int D, int G, int nblk, int maxlen) {
-  const size_t rows = (size_t)kGrpRows * D * 2 * 2;                    // q and dout rows
   const size_t st = D == 128 ? gb_stage_bytes<128>() : gb_stage_bytes<64>();
-  return rows + 2 * st + 2 * 32 * (size_t)kXRB + grp_table_bytes(grp_tokens(G), nblk, maxlen);
+  return 2 * st + grp_table_bytes(grp_tokens(G), nblk, maxlen);
 }
 
 template <int D>
 SA_DEVICE int gswz(int row) { return D == 128 ? 2 * (row & 7) : 2 * (row & 3); }
 
-template <int D>
+template <int D, int MODE>
 __global__ __launch_bounds__(kGrpWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void block_gqa_bwd_group_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -346,15 +347,10 @@ void block_gqa_bwd_group_kernel(
   constexpr int RWB = D * 2;              // swizzled row bytes
   constexpr int NT = kGrpWaves * 64;
   constexpr int LDN = (2 * 32 * CPR + NT - 1) / NT;   // 16-byte loads per thread per sub-tile
-  constexpr int NTILE = 2 * 2 * NDT;      // output tiles of dk and dv per sub-tile
-  constexpr int TPW = NTILE / kGrpWaves;  // ... per wave
-  static_assert(NTILE % kGrpWaves == 0, "tiles split evenly");
+  static_assert(MODE == 1 || MODE == 2, "D-only or dq-only");
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  char* q_l = lds;                                          // [128 rows][RWB] swizzled
-  char* d_l = q_l + kGrpRows * RWB;                         // [128 rows][RWB] dout
-  char* stg = d_l + kGrpRows * RWB;                         // [2][K pad | V pad | K swz]
-  char* xs = stg + 2 * gb_stage_bytes<D>();                 // [dS | P][32 keys][kXRB]
-  const GroupTables tbl = group_tables(xs + 2 * 32 * kXRB, GT, nblk, nwords);
+  char* stg = lds;                                          // [2][K pad | V pad | K swz]
+  const GroupTables tbl = group_tables(stg + 2 * gb_stage_bytes<D>(), GT, nblk, nwords);
 
   const int tid = threadIdx.x, w = tid >> 6, L = tid & 63;
   const int n = L & 15, quad = L >> 4;
@@ -376,20 +372,6 @@ void block_gqa_bwd_group_kernel(
   const int base = cu ? seq_start_of(cu, nseq, t0) : 0;
   const int nrows = GT * G;
 
-  // ---- the group's q and dout rows (zeros for rows past the group) into LDS
-  for (int c = tid; c < kGrpRows * CPR; c += NT) {
-    const int r = c / CPR, p = c % CPR;
-    const int tau = r / G, h = r - tau * G;
-    bf16x8_t a = bf16x8_t{}, b2 = bf16x8_t{};
-    if (r < nrows && t0 + tau <= tlast) {
-      const int64_t off = ((int64_t)(t0 + tau) * Hq + g * G + h) * D + 8 * p;
-      a = *reinterpret_cast<const bf16x8_t*>(q + off);
-      b2 = *reinterpret_cast<const bf16x8_t*>(dout + off);
-    }
-    const int so = r * RWB + ((p ^ gswz<D>(r)) << 4);
-    *reinterpret_cast<bf16x8_t*>(q_l + so) = a;
-    *reinterpret_cast<bf16x8_t*>(d_l + so) = b2;
-  }
   const int nu = group_union<NT>(tbl, blk, cu, nseq, t0, tlast, GT, B, nblk, base, nwords);
   const int32_t* ulo = tbl.ulo;
   const uint32_t* umask = tbl.umask;
@@ -480,9 +462,10 @@ void block_gqa_bwd_group_kernel(
       }
   };
 
-  // ---- pass 1: D = sum_s p_s dp_s of every row
+  // ---- pass 1: D = sum_s p_s dp_s of every row (MODE 2: left in the first four bytes
+  // of the row's dq by the MODE 1 launch)
   float dpart = 0.0f;
-  {
+  if constexpr (MODE != 2) {
     bf16x8_t nxA[LDN], nxB[LDN];
     int u = 0, pc = 0, ua = 0, pa = 0;
     advance(ua, pa);
@@ -509,14 +492,21 @@ void block_gqa_bwd_group_kernel(
       if (u < nu) piece(stg + gb_stage_bytes<D>(), nxB);
     }
   }
-  const float Drow = quad_sum(dpart);
+  float Drow;
+  if constexpr (MODE == 2) {
+    Drow = row_ok ? *reinterpret_cast<const float*>(dq + ((int64_t)tq * Hq + g * G + hq) * D) : 0.0f;
+  } else {
+    Drow = quad_sum(dpart);
+  }
+  if constexpr (MODE == 1) {
+    if (row_ok && quad == 0) *reinterpret_cast<float*>(dq + ((int64_t)tq * Hq + g * G + hq) * D) = Drow;
+    return;
+  }
 
-  // ---- pass 2: dS, dq, dk, dv
+  // ---- pass 2: dS and dq
   floatx4v_t dqa[NDT];
 #pragma unroll
   for (int i = 0; i < NDT; ++i) dqa[i] = floatx4v_t{};
-  char* xds = xs;
-  char* xp = xs + 32 * kXRB;
   {
     bf16x8_t nxA[LDN], nxB[LDN];
     int u = 0, pc = 0, ua = 0, pa = 0;
@@ -561,52 +551,6 @@ void block_gqa_bwd_group_kernel(
           dqa[dt] = mfma16x32(__builtin_bit_cast(bf16x8_t, a8), dsb, dqa[dt]);
         }
       }
-      // dS and P of this wave's rows -> [key][row] (zeros when the wave skipped)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = 16 * kt + 4 * quad + e;
-          *reinterpret_cast<uint16_t*>(xds + key * kXRB + row * 2) = f2bf_bits(dS[4 * kt + e]);
-          *reinterpret_cast<uint16_t*>(xp + key * kXRB + row * 2) = f2bf_bits(P[4 * kt + e]);
-        }
-      __syncthreads();
-      // dk = dS^T Q and dv = P^T dout over the 128 rows: tile (which, key tile, channel tile)
-#pragma unroll
-      for (int i = 0; i < TPW; ++i) {
-        const int tt = w * TPW + i;
-        const int which = tt / (2 * NDT);                     // 0: dk, 1: dv
-        const int ktile = (tt / NDT) & 1, dtile = tt % NDT;
-        const char* xa = which ? xp : xds;
-        const char* rb = which ? d_l : q_l;
-        floatx4v_t acc = floatx4v_t{};
-#pragma unroll
-        for (int ks = 0; ks < kGrpRows / 32; ++ks) {
-          // A: key 16 ktile + n, rows 32 ks + 4 quad + e and 32 ks + 16 + 4 quad + e
-          const char* ar = xa + (16 * ktile + n) * kXRB + (32 * ks + 4 * quad) * 2;
-          const uint2 alo = *reinterpret_cast<const uint2*>(ar);
-          const uint2 ahi = *reinterpret_cast<const uint2*>(ar + 32);
-          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(alo.x, alo.y, ahi.x, ahi.y));
-          // B: the same rows, channel 16 dtile + n, by transposing reads
-          const int r0 = 32 * ks + 4 * quad + (n >> 2);
-          const int col = 16 * dtile + 4 * (n & 3);
-          const int o0 = r0 * RWB + (((col >> 3) ^ gswz<D>(r0)) << 4) + (col & 7) * 2;
-          const int r1 = r0 + 16;
-          const int o1 = r1 * RWB + (((col >> 3) ^ gswz<D>(r1)) << 4) + (col & 7) * 2;
-          const short4_t b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(rb + o0));
-          const short4_t b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(rb + o1));
-          const short __attribute__((ext_vector_type(8))) b8 = {b0[0], b0[1], b0[2], b0[3],
-                                                                b1[0], b1[1], b1[2], b1[3]};
-          acc = mfma16x32(a, __builtin_bit_cast(bf16x8_t, b8), acc);
-        }
-        // lane (quad, n): keys 16 ktile + 4 quad + e, channel 16 dtile + n
-        float* dst = which ? dv : dk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int kk = 16 * ktile + 4 * quad + e;
-          if (kk < nk) atomicAdd(dst + ((int64_t)(lo + kk) * Hkv + g) * D + 16 * dtile + n, acc[e]);
-        }
-      }
       u = ua; pc = pa; ua = ub; pa = pb;
     };
 #pragma unroll 1
@@ -624,6 +568,286 @@ void block_gqa_bwd_group_kernel(
       const uint32_t p0 = pack_bf16x2(dqa[dt][0], dqa[dt][1]);
       const uint32_t p1 = pack_bf16x2(dqa[dt][2], dqa[dt][3]);
       *reinterpret_cast<uint2*>(orow + 16 * dt) = make_uint2(p0, p1);
+    }
+  }
+}
+
+// Key-major dk and dv (bf16), between the D-only and the dq-only launches of the
+// grouped kernel: one workgroup per (64-key block K0 = 64 kb of the packed key rows,
+// kv head, chunk of 256 consecutive tokens). Each fp32 atomic add costs the same
+// whatever the lanes' layout, so the grouped kernel's adds (one per element of every
+// 32-key sub-tile of every token group's union) bound it; here a key row gets one add
+// per element from each chunk whose tokens attend it, and only the rows that do attend
+// it are computed (the grouped kernel runs its whole group over every block of the
+// union).
+//   * set-up: thread i takes token t0 + i and ORs, over its routed blocks (0 <= b <=
+//     own block, repeats included once), the causal keys that fall in the workgroup's
+//     64 into a 64-bit mask; the tokens with a nonzero mask are listed in token order;
+//   * the K and V rows of the block are staged once; the listed tokens' G query rows go
+//     in tiles of 128 rows (128 / G tokens): wave w forms S^T = K Q^T and dP^T = V dout^T
+//     of rows 16 w .. 16 w + 15 against the 64 keys (16x16x32 MFMAs, the rows' q and
+//     dout from LDS as B operands), P from the token's mask and the forward's lse, dS
+//     from D (left in the dq rows by the D-only launch); dS and P meet in LDS as
+//     [key][row], and each wave contracts over the tile's rows for its share of the
+//     16 x 16 output tiles of dk = dS^T Q and dv = P^T dout, kept in registers over the
+//     tiles and added to dk and dv at the end.
+constexpr int kKB = 64;          // keys per workgroup
+constexpr int kCT = 2048;        // tokens per chunk
+
+template <int D>
+constexpr size_t kmaj_lds_bytes() {
+  return (size_t)2 * kKB * (D * 2 + 16) + (size_t)2 * kGrpRows * D * 2 + (size_t)2 * kKB * kXRB +
+         (size_t)kCT * 12 + (kCT / 64 + 16) * 4;
+}
+
+template <int D>
+__global__ __launch_bounds__(kGrpWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void block_gqa_bwd_kmaj_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ blk, const int32_t* __restrict__ cu, int nseq, int T, int Hq, int Hkv,
+    int B, int nblk, float scale, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
+    const uint16_t* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv) {
+  constexpr int KS = D / 32;              // 32-wide k-steps of S^T and dP^T
+  constexpr int NDT = D / 16;             // 16-channel tiles
+  constexpr int CPR = D * 2 / 16;         // 16-byte chunks per row
+  constexpr int KSB = D * 2 + 16;         // padded key row bytes
+  constexpr int RWB = D * 2;              // swizzled q / dout row bytes
+  constexpr int NT = kGrpWaves * 64;
+  constexpr int NKT = kKB / 16;           // 16-key tiles
+  constexpr int NTILE = 2 * NKT * NDT;    // output tiles of dk and dv
+  constexpr int TPW = NTILE / kGrpWaves;  // ... per wave: all key tiles of DPW channel tiles
+  constexpr int DPW = NDT / (kGrpWaves / 2);
+  static_assert(NTILE % kGrpWaves == 0 && DPW * NKT == TPW, "tiles split evenly");
+  constexpr int NR = kCT / NT;            // tokens per thread in the set-up
+  static_assert(NR * NT == kCT, "whole rounds of tokens");
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  char* k_l = lds;                                        // [64 keys][KSB]
+  char* v_l = k_l + kKB * KSB;                            // [64 keys][KSB]
+  char* q_l = v_l + kKB * KSB;                            // [128 rows][RWB] swizzled
+  char* d_l = q_l + kGrpRows * RWB;                       // [128 rows][RWB] dout
+  char* xds = d_l + kGrpRows * RWB;                       // dS [64 keys][kXRB]
+  char* xp = xds + kKB * kXRB;                            // P  [64 keys][kXRB]
+  uint64_t* lmask = reinterpret_cast<uint64_t*>(xp + kKB * kXRB);   // [kCT] key masks
+  int* ltok = reinterpret_cast<int*>(lmask + kCT);                  // [kCT] tokens
+  int* cnt = ltok + kCT;                                 // [NR][8] counts, then [16] key-mask words
+
+  const int tid = threadIdx.x, w = tid >> 6, L = tid & 63;
+  const int n = L & 15, quad = L >> 4;
+  const int t0 = (int)blockIdx.x * kCT;
+  const int K0 = (int)blockIdx.y * kKB;
+  const int g = (int)blockIdx.z;
+  if (t0 + kCT - 1 < K0) return;                          // no token of the chunk reaches the block
+  const int G = Hq / Hkv;
+  const int TT = kGrpRows / G;                            // tokens per row tile
+  const int nrows = TT * G;
+  if (TT == 0) return;                                    // G > 128: not launched
+
+  // ---- the chunk's tokens that attend keys of the block, with their key masks (token
+  // t0 + NT r + tid in round r)
+  uint64_t mr[NR], balr[NR];
+  uint32_t mlo = 0u, mhi = 0u;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    uint64_t m = 0;
+    const int t = t0 + NT * r + tid;
+    if (t < T && t >= K0) {
+      const int st = cu ? seq_start_of(cu, nseq, t) : 0;
+      const int own = (t - st) / B;
+      const int32_t* br = blk + (int64_t)t * nblk;
+      for (int j0 = 0; j0 < nblk; j0 += 16) {
+        int bb[16];                                         // 16 route loads in flight
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) bb[jj] = j0 + jj < nblk ? br[j0 + jj] : -1;
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          const int b = bb[jj];
+          if (b >= 0 && b <= own) {
+            const int r0 = max(st + b * B, K0);
+            const int r1 = min(min(st + b * B + B, t + 1), K0 + kKB);
+            if (r0 < r1) {
+              const int a = r0 - K0, e = r1 - K0;             // keys [a, e), 0 <= a < e <= 64
+              const uint64_t below_e = e == 64 ? ~0ull : ((1ull << e) - 1ull);
+              m |= below_e & ~((1ull << a) - 1ull);
+            }
+          }
+        }
+      }
+    }
+    mr[r] = m;
+    balr[r] = __ballot(m != 0ull);
+    mlo |= (uint32_t)m;
+    mhi |= (uint32_t)(m >> 32);
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    mlo |= (uint32_t)__shfl_xor((int)mlo, off, 64);
+    mhi |= (uint32_t)__shfl_xor((int)mhi, off, 64);
+  }
+  if (L == 0) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) cnt[kGrpWaves * r + w] = __popcll(balr[r]);
+    cnt[kGrpWaves * NR + 2 * w] = (int)mlo;
+    cnt[kGrpWaves * NR + 2 * w + 1] = (int)mhi;
+  }
+  __syncthreads();
+  int nl = 0;
+  uint64_t kmask = 0;                                     // keys any listed token attends
+#pragma unroll
+  for (int i = 0; i < kGrpWaves; ++i)
+    kmask |= (uint64_t)(uint32_t)cnt[kGrpWaves * NR + 2 * i] | ((uint64_t)(uint32_t)cnt[kGrpWaves * NR + 2 * i + 1] << 32);
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    int at = nl;                                          // listed before wave w of round r
+#pragma unroll
+    for (int i = 0; i < kGrpWaves; ++i) {
+      at += i < w ? cnt[kGrpWaves * r + i] : 0;
+      nl += cnt[kGrpWaves * r + i];
+    }
+    if (mr[r] != 0ull) {
+      const int slot = at + __popcll(balr[r] & ((1ull << L) - 1ull));
+      ltok[slot] = t0 + NT * r + tid;
+      lmask[slot] = mr[r];
+    }
+  }
+  if (nl == 0) return;                                    // uniform
+  // ---- the block's K and V rows (zeros past T)
+  for (int c = tid; c < 2 * kKB * CPR; c += NT) {
+    const int isv = c >= kKB * CPR;
+    const int cc = isv ? c - kKB * CPR : c;
+    const int r = cc / CPR, p = cc % CPR;
+    bf16x8_t x = bf16x8_t{};
+    if (K0 + r < T) x = *reinterpret_cast<const bf16x8_t*>((isv ? v : k) + ((int64_t)(K0 + r) * Hkv + g) * D + 8 * p);
+    *reinterpret_cast<bf16x8_t*>((isv ? v_l : k_l) + r * KSB + 16 * p) = x;
+  }
+
+  const float sc2 = scale * kLog2e;
+  const int row = 16 * w + n;                             // this lane's row of a tile (S phase)
+  floatx4v_t acc[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) acc[i] = floatx4v_t{};
+
+  // The next row tile's q and dout rows, and the lse and D of this lane's row in it,
+  // are loaded into registers while the current tile is computed.
+  constexpr int NPF = kGrpRows * CPR / NT;                // 16-byte chunks per thread per tile
+  static_assert(NPF * NT == kGrpRows * CPR, "whole chunks per thread");
+  bf16x8_t pq[NPF], pd[NPF];
+  float plse = 0.0f, pD = 0.0f;
+  uint64_t pmask = 0ull;
+  auto fetch = [&](int it) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m2 = 0; m2 < NPF; ++m2) {
+      const int c = tid + NT * m2, r = c / CPR, p = c % CPR;
+      const int i = it + r / G, h = r % G;
+      pq[m2] = bf16x8_t{};
+      pd[m2] = bf16x8_t{};
+      if (r < nrows && i < nl) {
+        const int64_t off = ((int64_t)ltok[i] * Hq + g * G + h) * D + 8 * p;
+        pq[m2] = *reinterpret_cast<const bf16x8_t*>(q + off);
+        pd[m2] = *reinterpret_cast<const bf16x8_t*>(dout + off);
+      }
+    }
+    const int ri = it + row / G;
+    const bool ok = row < nrows && ri < nl;
+    const int64_t hrow = (int64_t)(ok ? ltok[ri] : 0) * Hq + g * G + row % G;
+    pmask = ok ? lmask[ri] : 0ull;
+    plse = ok ? lse[hrow] * kLog2e : -__builtin_huge_valf();
+    pD = ok ? *reinterpret_cast<const float*>(dq + hrow * D) : 0.0f;
+  };
+  __syncthreads();                     // the list (and the K and V rows) are in place
+  fetch(0);
+
+#pragma unroll 1
+  for (int it = 0; it < nl; it += TT) {
+#pragma unroll
+    for (int m2 = 0; m2 < NPF; ++m2) {
+      const int c = tid + NT * m2, r = c / CPR, p = c % CPR;
+      const int so = r * RWB + ((p ^ gswz<D>(r)) << 4);
+      *reinterpret_cast<bf16x8_t*>(q_l + so) = pq[m2];
+      *reinterpret_cast<bf16x8_t*>(d_l + so) = pd[m2];
+    }
+    const uint64_t rmask = pmask;
+    const float lse2 = plse;
+    const float Drow = pD;
+    if (it + TT < nl) fetch(it + TT);
+    __syncthreads();
+    bf16x8_t qb[KS], gb[KS];           // B operands: row 16 w + n, channels 32 ks + 8 quad
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int so = row * RWB + (((4 * ks + quad) ^ gswz<D>(row)) << 4);
+      qb[ks] = *reinterpret_cast<const bf16x8_t*>(q_l + so);
+      gb[ks] = *reinterpret_cast<const bf16x8_t*>(d_l + so);
+    }
+    // S^T and dP^T: lane (quad, n) holds keys 16 kt + 4 quad + e of row n
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+      floatx4v_t S = floatx4v_t{}, dP = floatx4v_t{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(k_l + (16 * kt + n) * KSB + 64 * ks + 16 * quad);
+        const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(v_l + (16 * kt + n) * KSB + 64 * ks + 16 * quad);
+        S = mfma16x32(ka, qb[ks], S);
+        dP = mfma16x32(va, gb[ks], dP);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = 16 * kt + 4 * quad + e;
+        const bool ok = ((rmask >> key) & 1ull) && lse2 > -__builtin_huge_valf();
+        const float P = ok ? __builtin_amdgcn_exp2f(S[e] * sc2 - lse2) : 0.0f;
+        const float dS = P * (dP[e] - Drow) * scale;
+        *reinterpret_cast<uint16_t*>(xds + key * kXRB + row * 2) = f2bf_bits(dS);
+        *reinterpret_cast<uint16_t*>(xp + key * kXRB + row * 2) = f2bf_bits(P);
+      }
+    }
+    __syncthreads();
+    // dk = dS^T Q and dv = P^T dout over the tile's rows. Wave w: dk (w < 4) or dv, channel
+    // tiles DPW (w mod 4) + d, every key tile; each B operand (the rows' q or dout by
+    // transposing reads) serves the four key tiles.
+    {
+      const int which = w >> 2;
+      const char* xa = which ? xp : xds;
+      const char* rb = which ? d_l : q_l;
+#pragma unroll
+      for (int ks = 0; ks < kGrpRows / 32; ++ks) {
+        bf16x8_t bop[DPW];
+#pragma unroll
+        for (int d = 0; d < DPW; ++d) {
+          // B: rows 32 ks + 4 quad + (n >> 2) (+16), channel 16 dtile + 4 (n & 3) ..
+          const int dtile = DPW * (w & 3) + d;
+          const int r0 = 32 * ks + 4 * quad + (n >> 2);
+          const int col = 16 * dtile + 4 * (n & 3);
+          const int o0 = r0 * RWB + (((col >> 3) ^ gswz<D>(r0)) << 4) + (col & 7) * 2;
+          const int r1 = r0 + 16;
+          const int o1 = r1 * RWB + (((col >> 3) ^ gswz<D>(r1)) << 4) + (col & 7) * 2;
+          const short4_t b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(rb + o0));
+          const short4_t b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(rb + o1));
+          const short __attribute__((ext_vector_type(8))) b8 = {b0[0], b0[1], b0[2], b0[3],
+                                                                b1[0], b1[1], b1[2], b1[3]};
+          bop[d] = __builtin_bit_cast(bf16x8_t, b8);
+        }
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) {
+          // A: key 16 kt + n, rows 32 ks + 4 quad + e and 32 ks + 16 + 4 quad + e
+          const char* ar = xa + (16 * kt + n) * kXRB + (32 * ks + 4 * quad) * 2;
+          const uint2 alo = *reinterpret_cast<const uint2*>(ar);
+          const uint2 ahi = *reinterpret_cast<const uint2*>(ar + 32);
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(alo.x, alo.y, ahi.x, ahi.y));
+#pragma unroll
+          for (int d = 0; d < DPW; ++d) acc[kt * DPW + d] = mfma16x32(a, bop[d], acc[kt * DPW + d]);
+        }
+      }
+    }
+    __syncthreads();                   // every wave is done with this tile's rows and dS, P
+  }
+  // ---- one add per element: lane (quad, n) holds keys 16 ktile + 4 quad + e, channel 16 dtile + n
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int ktile = i / DPW, dtile = DPW * (w & 3) + i % DPW;
+    float* dst = (w >> 2) ? dv : dk;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int key = 16 * ktile + 4 * quad + e;
+      if ((kmask >> key) & 1ull)
+        atomicAdd(dst + ((int64_t)(K0 + key) * Hkv + g) * D + 16 * dtile + n, acc[i][e]);
     }
   }
 }
@@ -672,18 +896,33 @@ hipError_t launch_grouped(const void* q, const void* k, const void* v, const int
   const int G = Hq / Hkv;
   const int GT = grp_tokens(G);
   const size_t shm = grp_bwd_lds_bytes(D, G, nblk, maxlen);
-  hipError_t e = hipFuncSetAttribute((const void*)block_gqa_bwd_group_kernel<D>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-  if (e != hipSuccess) return e;
   const int by_xcd = 8 % Hkv == 0;
   const int64_t ngrp = ((int64_t)T + GT - 1) / GT;
   const int64_t grid = by_xcd ? (ngrp + 8 / Hkv - 1) / (8 / Hkv) * 8 : ngrp * Hkv;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((block_gqa_bwd_group_kernel<D>), dim3((unsigned)grid), dim3(kGrpWaves * 64), shm, st,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, blk, cu, nseq, T, Hq,
-                     Hkv, B, nblk, GT, grp_words(maxlen, GT), scale, (const uint16_t*)dout, lse,
-                     (uint16_t*)dq, dk, dv, by_xcd);
-  return hipGetLastError();
+  // D of every row (into the first four bytes of its dq row), then dk and dv key-major,
+  // then dq
+  auto grouped = [&](auto kern) -> hipError_t {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kGrpWaves * 64), shm, st, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, blk, cu, nseq, T, Hq, Hkv, B, nblk, GT,
+                       grp_words(maxlen, GT), scale, (const uint16_t*)dout, lse, (uint16_t*)dq, dk, dv,
+                       by_xcd);
+    return hipGetLastError();
+  };
+  hipError_t e = grouped(block_gqa_bwd_group_kernel<D, 1>);
+  if (e != hipSuccess) return e;
+  const size_t shk = kmaj_lds_bytes<D>();
+  e = hipFuncSetAttribute((const void*)block_gqa_bwd_kmaj_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shk);
+  if (e != hipSuccess) return e;
+  const dim3 kgrid((unsigned)((T + kCT - 1) / kCT), (unsigned)((T + kKB - 1) / kKB), (unsigned)Hkv);
+  hipLaunchKernelGGL((block_gqa_bwd_kmaj_kernel<D>), kgrid, dim3(kGrpWaves * 64), shk, st, (const uint16_t*)q,
+                     (const uint16_t*)k, (const uint16_t*)v, blk, cu, nseq, T, Hq, Hkv, B, nblk, scale,
+                     (const uint16_t*)dout, lse, (const uint16_t*)dq, dk, dv);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return grouped(block_gqa_bwd_group_kernel<D, 2>);
 }
 
 }  // namespace

@@ -488,6 +488,10 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_h32_kernel(
   auto pass2 = [&](int sub, int& ixc, int ixn) __attribute__((always_inline)) {
     char* kt = k_l + (sub & 1) * kB32 * KRB;
     stage(kt);
+    // without atomics to wait behind, the next rows are requested a whole sub-tile ahead
+    if constexpr (DQO) {
+      if (sub + 1 < nsub) load(ixn);
+    }
     __syncthreads();                   // also: every wave is done with the exchange rows
     float P[4], dS[4];
     floatx4v_t dP;
@@ -520,7 +524,7 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_h32_kernel(
       // wait for them (at the next staging) then spans at most the atomics of the other
       // two thirds (48 at d_qk 576, within the 63 the wait counter can name), not the
       // atomics issued before the loads.
-      if (i == TPW / 3 && sub + 1 < nsub) load(ixn);
+      if (!DQO && i == TPW / 3 && sub + 1 < nsub) load(ixn);
       const int tt = w + kWaves * i;
       const int t2 = tt / NCT, ct = tt % NCT;
       const int toff = (16 * ct + 4 * (n & 3)) * 2;

@@ -188,6 +188,28 @@ def test_block_gqa_bwd_shapes_thd(sa, Hq, Hkv, D, B, dtype):
     assert np.all(dq[50] == 0)
 
 
+@pytest.mark.parametrize("lengths,Hq,Hkv,D,B", [((1500, 2900, 777), 8, 2, 128, 48),
+                                                 ((4100,), 16, 4, 64, 64),
+                                                 ((2047, 1, 2049), 4, 4, 128, 32)])
+def test_block_gqa_bwd_key_major_chunks(sa, lengths, Hq, Hkv, D, B):
+    """dk and dv are summed key-major over chunks of 2048 tokens per 64-key block: packed
+    sequences that cross chunk boundaries, block sizes that do not align with the
+    64-key blocks, a one-token sequence; every row of dq, dk and dv against the oracle."""
+    T = sum(lengths)
+    gen = torch.Generator().manual_seed(T + Hq + D + B)
+    q = torch.randn((T, Hq, D), generator=gen).to(torch.bfloat16)
+    k = torch.randn((T, Hkv, D), generator=gen).to(torch.bfloat16)
+    v = torch.randn((T, Hkv, D), generator=gen).to(torch.bfloat16)
+    dout = torch.randn((T, Hq, D), generator=gen).to(torch.bfloat16)
+    blk = workloads.random_block_index(T, 8, B, 31, lengths=lengths)
+    dq, dk, dv = _run_gqa_bwd(sa, q, k, v, blk, dout, B, 0.2, lengths)
+    rdq, rdk, rdv = oracle.block_sparse_gqa_bwd(q, k, v, blk.numpy(), dout, B, 0.2,
+                                                cu_seqlens=workloads.cu_seqlens(lengths))
+    grad_close(dq, rdq, "dq")
+    grad_close(dk, rdk, "dk")
+    grad_close(dv, rdv, "dv")
+
+
 def test_block_gqa_bwd_long_sequence_per_token_kernel(sa):
     """One 130,003-token sequence at D = 128: the grouped backward's rows, stages and
     set-up tables would exceed the LDS, so the per-(token, kv head) kernel serves it.
