@@ -172,7 +172,7 @@ def gradients_leg(sa, workloads, wl, x, m, idx, lse, n_timed, cpu_rows):
     if rows is not None:
         qh, kvh, dh = m["q"][torch.from_numpy(rows).to(dev)].cpu(), m["kv"].cpu(), dout[torch.from_numpy(rows).to(dev)].cpu()
         cpu = cpu_rate(lambda ih: oracle.sparse_mla_bwd(qh, kvh, ih[rows], dh, wl.scale), f_slot)
-    res["sparse_mla_bwd"] = _mfma_entry("sparse_mla_bwd_dkv_kernel + sparse_mla_bwd_h32_kernel (dq only)"
+    res["sparse_mla_bwd"] = _mfma_entry("sparse_mla_bwd_dkv_kernel + sparse_mla_bwd_dq64_kernel"
                                         if H in (64, 128) else
                                         "sparse_mla_bwd_h32_kernel" if H % 32 == 0 else "sparse_mla_bwd_bf16_kernel",
                                         f_slot * slots, ms, cpu,
@@ -351,8 +351,8 @@ def write_traffic(fetch_dir, write_dir, command):
                                  ["topk_select.hip", "sa_common.h"], None),
         "block_gqa_block_workload": (lambda n: "block_gqa_group_kernel" in n,
                                      ["block_gqa.hip", "sa_common.h"], 1),
-        "sparse_mla_bwd_long_dsa": (lambda n: "sparse_mla_bwd_dkv_kernel" in n or "sparse_mla_bwd_h32_kernel" in n
-                                    or "zero_f32_kernel" in n,
+        "sparse_mla_bwd_long_dsa": (lambda n: "sparse_mla_bwd_dkv_kernel" in n or "sparse_mla_bwd_dq64_kernel" in n
+                                    or "sparse_mla_bwd_h32_kernel" in n or "zero_f32_kernel" in n,
                                     ["sparse_mla_bwd.hip", "sa_common.h"], None),
         "attn_teacher_long_dsa": (lambda n: "attn_teacher_bf16_kernel" in n, ["sparse_mla_bwd.hip", "sa_common.h"], 1),
         "indexer_kl_long_dsa": (lambda n: "indexer_kl_bf16_kernel" in n or "zero_kernel" in n,

@@ -315,9 +315,6 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_bf16_kernel(
 // per element from each 32-head block (four at 128 heads) instead of one per 16-head
 // group, and each row is gathered by half as many workgroups. dq accumulates in
 // registers across sub-tiles. A first pass over the same sub-tiles forms D.
-// With DQO (dq only, after the all-heads dkv kernel at 64 and 128 heads) the dkv
-// tiles, their atomics and the first pass are left out, and D is read from the
-// first four bytes of each head's dq row, where the dkv kernel left it.
 constexpr int kB32 = 32;          // heads per workgroup, keys per sub-tile
 constexpr int kXR = kB32 * 2 + 16;  // [key][head] or [head][key] bf16 exchange rows (bytes)
 
@@ -327,7 +324,7 @@ constexpr size_t bwd32_lds_bytes() {
          (size_t)2 * kB32 * krow_bytes<DQK>() + (size_t)3 * kB32 * kXR + 2 * kB32 * sizeof(float);
 }
 
-template <int DQK, bool DQO>
+template <int DQK>
 __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_h32_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, int H, int topk, float scale,
@@ -431,53 +428,46 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_h32_kernel(
       P[i] = rown >= 0 && lse2[i] > -__builtin_huge_valf() ? __builtin_amdgcn_exp2f(S[i] * sc2 - lse2[i]) : 0.0f;
   };
 
-  float Dh[4];
-  int ixa = 0, ixb = 0;       // indices of sub-tiles of even / odd number
-  if constexpr (DQO) {
-    // D of each head, left by the dkv kernel in the first four bytes of its dq row
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      Dh[i] = *reinterpret_cast<const float*>(dq + ((int64_t)t * H + h0 + 16 * hg + 4 * g + i) * DQK);
-  } else {
-    // ---- pass 1: D = sum_j p_j dp_j per head
-    float dpart[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    auto pass1 = [&](int sub, int& ixc, int ixn) __attribute__((always_inline)) {
-      char* kt = k_l + (sub & 1) * kB32 * KRB;
-      stage(kt);
-      __syncthreads();
-      if (sub + 1 < nsub) load(ixn);
-      float P[4];
-      floatx4v_t dP;
-      scores(kt, sub, ixc, P, dP);
-      ixc = idx_of(sub + 2);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dpart[i] = fmaf(P[i], dP[i], dpart[i]);
-    };
-    if (nsub > 0) {
-      ixa = idx_of(0);
-      ixb = idx_of(1);
-      load(ixa);
-    }
-#pragma unroll 1
-    for (int sub = 0; sub < nsub; sub += 2) {
-      pass1(sub, ixa, ixb);
-      if (sub + 1 < nsub) pass1(sub + 1, ixb, ixa);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {          // over the 16 keys (lanes n) of the wave's half
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) dpart[i] += __shfl_xor(dpart[i], off, 64);
-      if (n == 0) dD[kh * kB32 + 16 * hg + 4 * g + i] = dpart[i];
-    }
+  // ---- pass 1: D = sum_j p_j dp_j per head
+  float dpart[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto pass1 = [&](int sub, int& ixc, int ixn) __attribute__((always_inline)) {
+    char* kt = k_l + (sub & 1) * kB32 * KRB;
+    stage(kt);
     __syncthreads();
+    if (sub + 1 < nsub) load(ixn);
+    float P[4];
+    floatx4v_t dP;
+    scores(kt, sub, ixc, P, dP);
+    ixc = idx_of(sub + 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Dh[i] = dD[16 * hg + 4 * g + i] + dD[kB32 + 16 * hg + 4 * g + i];
-    // the sink's probability exp(sink - lse) times -D is its logit's gradient
-    if (dsink && tid < kB32) {
-      const int hh = h0 + tid;
-      const float D = dD[tid] + dD[kB32 + tid];
-      atomicAdd(dsink + hh, -__builtin_amdgcn_exp2f((sink[hh] - lse[(int64_t)t * H + hh]) * kLog2e) * D);
-    }
+    for (int i = 0; i < 4; ++i) dpart[i] = fmaf(P[i], dP[i], dpart[i]);
+  };
+  int ixa = 0, ixb = 0;       // indices of sub-tiles of even / odd number
+  if (nsub > 0) {
+    ixa = idx_of(0);
+    ixb = idx_of(1);
+    load(ixa);
+  }
+#pragma unroll 1
+  for (int sub = 0; sub < nsub; sub += 2) {
+    pass1(sub, ixa, ixb);
+    if (sub + 1 < nsub) pass1(sub + 1, ixb, ixa);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {          // over the 16 keys (lanes n) of the wave's half
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) dpart[i] += __shfl_xor(dpart[i], off, 64);
+    if (n == 0) dD[kh * kB32 + 16 * hg + 4 * g + i] = dpart[i];
+  }
+  __syncthreads();
+  float Dh[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) Dh[i] = dD[16 * hg + 4 * g + i] + dD[kB32 + 16 * hg + 4 * g + i];
+  // the sink's probability exp(sink - lse) times -D is its logit's gradient
+  if (dsink && tid < kB32) {
+    const int hh = h0 + tid;
+    const float D = dD[tid] + dD[kB32 + tid];
+    atomicAdd(dsink + hh, -__builtin_amdgcn_exp2f((sink[hh] - lse[(int64_t)t * H + hh]) * kLog2e) * D);
   }
 
   floatx4v_t dqa[TPW];       // dq tiles tt = w + 4 i: head tile tt / NCT, channel tile tt % NCT
@@ -488,10 +478,6 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_h32_kernel(
   auto pass2 = [&](int sub, int& ixc, int ixn) __attribute__((always_inline)) {
     char* kt = k_l + (sub & 1) * kB32 * KRB;
     stage(kt);
-    // without atomics to wait behind, the next rows are requested a whole sub-tile ahead
-    if constexpr (DQO) {
-      if (sub + 1 < nsub) load(ixn);
-    }
     __syncthreads();                   // also: every wave is done with the exchange rows
     float P[4], dS[4];
     floatx4v_t dP;
@@ -500,10 +486,8 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_h32_kernel(
     for (int i = 0; i < 4; ++i) dS[i] = P[i] * (dP[i] - Dh[i]) * scale;
     {
       const int key = 16 * kh + n, head = 16 * hg + 4 * g;
-      if constexpr (!DQO) {
-        *reinterpret_cast<short4_t*>(xS + key * kXR + head * 2) = pack4(dS[0], dS[1], dS[2], dS[3]);
-        *reinterpret_cast<short4_t*>(xP + key * kXR + head * 2) = pack4(P[0], P[1], P[2], P[3]);
-      }
+      *reinterpret_cast<short4_t*>(xS + key * kXR + head * 2) = pack4(dS[0], dS[1], dS[2], dS[3]);
+      *reinterpret_cast<short4_t*>(xP + key * kXR + head * 2) = pack4(P[0], P[1], P[2], P[3]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) *reinterpret_cast<uint16_t*>(xT + (head + i) * kXR + key * 2) = f2bf_bits(dS[i]);
     }
@@ -524,12 +508,12 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_mla_bwd_h32_kernel(
       // wait for them (at the next staging) then spans at most the atomics of the other
       // two thirds (48 at d_qk 576, within the 63 the wait counter can name), not the
       // atomics issued before the loads.
-      if (!DQO && i == TPW / 3 && sub + 1 < nsub) load(ixn);
+      if (i == TPW / 3 && sub + 1 < nsub) load(ixn);
       const int tt = w + kWaves * i;
       const int t2 = tt / NCT, ct = tt % NCT;
       const int toff = (16 * ct + 4 * (n & 3)) * 2;
       // dkv tile: keys 16 t2 + ..., channels 16 ct + ...; k = heads {4g + e, 16 + 4g + e}
-      if constexpr (!DQO) {
+      {
         const char* ar = xS + (16 * t2 + n) * kXR + 8 * g;
         const uint2 a0 = *reinterpret_cast<const uint2*>(ar);
         const uint2 a1 = *reinterpret_cast<const uint2*>(ar + 32);
@@ -840,6 +824,146 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_bwd_dkv_kernel(
   }
 }
 
+// bf16 dq with 64 heads per workgroup (H = 64 or 128), after the all-heads dkv kernel,
+// which leaves D in the first four bytes of each head's dq row. dq needs q and dout
+// only as the A operands of S and dP (channel-contiguous), so a wave keeps its 16
+// heads' q and dout in VGPRs and its dq tiles (16 heads x d_qk) in AGPRs, and each
+// gathered 32-key sub-tile serves 64 heads (the 32-head kernel gathers every row once
+// per 32 heads). The token's slot indices are staged in LDS first, so the rows of
+// sub-tile s + 2 are requested while sub-tile s is computed (two register buffers,
+// the loop body written out twice). Per sub-tile each wave forms S and dP of its 16
+// heads x 32 keys (16x16x32 MFMAs, key rows as B operands), dS into a wave-private LDS
+// block as [head][key], and dq += dS K over the 32 keys (K^T by transposing reads): no
+// exchange between waves, one barrier per sub-tile (two key stages).
+constexpr int kQH = 64;            // heads per dq workgroup
+constexpr int kXQ = 32 * 2 + 16;   // wave-private dS rows [16 heads][32 keys] bf16 (bytes)
+
+template <int DQK>
+constexpr size_t dq64_lds_bytes(int topk) {
+  return (size_t)2 * kB32 * krow_bytes<DQK>() + (size_t)kWaves * 16 * kXQ +
+         (size_t)((topk + kB32 - 1) / kB32) * kB32 * 4;
+}
+
+template <int DQK>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void sparse_mla_bwd_dq64_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+                                const int32_t* __restrict__ idx, const uint16_t* __restrict__ dout,
+                                const float* __restrict__ lse, int H, int topk, float scale,
+                                uint16_t* __restrict__ dq) {
+  constexpr int KRB = krow_bytes<DQK>();
+  constexpr int NK = DQK / 32;            // 32-wide k-steps of S
+  constexpr int NV = 512 / 32;            // ... of dP
+  constexpr int NCT = DQK / 16;           // 16-channel tiles of dq
+  constexpr int CPR = DQK * 2 / 16;       // 16-byte chunks per key row
+  constexpr int NT = kWaves * 64;
+  constexpr int NLD = kB32 * CPR / NT;    // chunks per thread per sub-tile
+  static_assert(NLD * NT == kB32 * CPR, "every thread loads NLD chunks");
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  char* k_l = lds;                                        // [2][32 keys][KRB]
+  char* x_l = k_l + 2 * kB32 * KRB;                       // [4 waves][16 heads][kXQ]
+  int* ix_l = reinterpret_cast<int*>(x_l + kWaves * 16 * kXQ);   // [nsub * 32] slots (-1 past topk)
+
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, L = tid & 63;
+  const int g = L >> 4, n = L & 15;
+  const int hw = (int)blockIdx.y * kQH + 16 * w;          // the wave's first head
+  const int nsub = (topk + kB32 - 1) / kB32;
+  const float sc2 = scale * kLog2e;
+
+  const int32_t* irow = idx + (int64_t)t * topk;
+  for (int j = tid; j < nsub * kB32; j += NT) ix_l[j] = j < topk ? irow[j] : -1;
+
+  bf16x8_t qa[NK], da[NV];                // A operands: head hw + n, channels 32 ks + 8 g
+  {
+    const int64_t hr = (int64_t)t * H + hw + n;
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) qa[ks] = *reinterpret_cast<const bf16x8_t*>(q + hr * DQK + 32 * ks + 8 * g);
+#pragma unroll
+    for (int ks = 0; ks < NV; ++ks) da[ks] = *reinterpret_cast<const bf16x8_t*>(dout + hr * 512 + 32 * ks + 8 * g);
+  }
+  float lse2[4], Dh[4];                   // heads hw + 4 g + i (rows of the S tile)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t hr = (int64_t)t * H + hw + 4 * g + i;
+    lse2[i] = lse[hr] * kLog2e;
+    Dh[i] = *reinterpret_cast<const float*>(dq + hr * DQK);
+  }
+  floatx4v_t dqa[NCT];                    // dq tile ct: heads hw + 4 g + e, channel 16 ct + n
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) dqa[ct] = floatx4v_t{};
+  __syncthreads();                        // the slot indices are in place
+
+  auto load = [&](bf16x8_t (&nx)[NLD], int sub) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < NLD; ++m) {
+      const int c = tid + NT * m, r = c / CPR, p = c % CPR;
+      int row = ix_l[sub * kB32 + r];
+      row = row < 0 ? 0 : row;                 // masked slot (or past topk): any finite row
+      nx[m] = *reinterpret_cast<const bf16x8_t*>(kv + (int64_t)row * DQK + 8 * p);
+    }
+  };
+  char* xw = x_l + w * 16 * kXQ;
+  auto step = [&](int sub, bf16x8_t (&nx)[NLD]) __attribute__((always_inline)) {
+    char* kt = k_l + (sub & 1) * kB32 * KRB;
+#pragma unroll
+    for (int m = 0; m < NLD; ++m) {
+      const int c = tid + NT * m, r = c / CPR, p = c % CPR;
+      *reinterpret_cast<bf16x8_t*>(kt + r * KRB + 16 * p) = nx[m];
+    }
+    __syncthreads();                     // this stage is in place; the other one is free
+    if (sub + 2 < nsub) load(nx, sub + 2);
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const int key = 16 * kh + n;
+      const int rown = ix_l[sub * kB32 + key];
+      const char* krow = kt + key * KRB + 16 * g;
+      floatx4v_t S = floatx4v_t{}, dP = floatx4v_t{};
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks) {
+        const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(krow + 64 * ks);
+        S = mfma16x32(qa[ks], b, S);
+        if (ks < NV) dP = mfma16x32(da[ks], b, dP);
+        if (ks % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float P = rown >= 0 && lse2[i] > -__builtin_huge_valf()
+                            ? __builtin_amdgcn_exp2f(S[i] * sc2 - lse2[i]) : 0.0f;
+        *reinterpret_cast<uint16_t*>(xw + (4 * g + i) * kXQ + key * 2) = f2bf_bits(P * (dP[i] - Dh[i]) * scale);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();      // the wave's dS rows are written (LDS runs in order)
+    // dq += dS K: A = dS of head n, keys {4 g + e, 16 + 4 g + e}; B = K^T by transposing reads
+    const char* ar = xw + n * kXQ + 8 * g;
+    const uint2 a0 = *reinterpret_cast<const uint2*>(ar);
+    const uint2 a1 = *reinterpret_cast<const uint2*>(ar + 32);
+    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(a0.x, a0.y, a1.x, a1.y));
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int toff = (16 * ct + 4 * (n & 3)) * 2;
+      const short4_t b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(kt + (4 * g + (n >> 2)) * KRB + toff));
+      const short4_t b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS short4_t*)(kt + (16 + 4 * g + (n >> 2)) * KRB + toff));
+      const short __attribute__((ext_vector_type(8))) b8 = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+      dqa[ct] = mfma16x32(a, __builtin_bit_cast(bf16x8_t, b8), dqa[ct]);
+    }
+    __builtin_amdgcn_wave_barrier();      // the dS rows are read before the next sub-tile's writes
+  };
+  bf16x8_t nxA[NLD], nxB[NLD];
+  load(nxA, 0);
+  if (nsub > 1) load(nxB, 1);
+#pragma unroll 1
+  for (int sub = 0; sub < nsub; sub += 2) {
+    step(sub, nxA);
+    if (sub + 1 < nsub) step(sub + 1, nxB);
+  }
+  // lane (g, n) of tile ct: heads hw + 4 g + e, channel 16 ct + n
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      dq[((int64_t)t * H + hw + 4 * g + e) * DQK + 16 * ct + n] = f2bf_bits(dqa[ct][e]);
+}
+
 // fp32: one workgroup per (token, head); plain arithmetic, dkv by atomics.
 constexpr int kNT = 256;
 
@@ -1075,17 +1199,17 @@ hipError_t launch_bwd32(const void* q, const void* kv, const int32_t* idx, const
                         const float* lse, int T, int H, int topk, float scale, const float* sink,
                         void* dq, float* dkv, float* dsink, hipStream_t st) {
   const size_t shm = bwd32_lds_bytes<DQK>();
-  hipError_t e = hipFuncSetAttribute((const void*)sparse_mla_bwd_h32_kernel<DQK, false>,
+  hipError_t e = hipFuncSetAttribute((const void*)sparse_mla_bwd_h32_kernel<DQK>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((sparse_mla_bwd_h32_kernel<DQK, false>), dim3(T, H / kB32), dim3(kWaves * 64), shm, st,
+  hipLaunchKernelGGL((sparse_mla_bwd_h32_kernel<DQK>), dim3(T, H / kB32), dim3(kWaves * 64), shm, st,
                      (const uint16_t*)q, (const uint16_t*)kv, idx, (const uint16_t*)dout, lse, H, topk,
                      scale, sink, (uint16_t*)dq, dkv, dsink);
   return hipGetLastError();
 }
 
-// H = 16 NW in {64, 128}: dkv (and D, dsink) with all heads per workgroup, then dq by
-// the 32-head kernel in its dq-only form.
+// H = 16 NW in {64, 128} (slot rows that fit the dq kernel's LDS): dkv (and D, dsink)
+// with all heads per workgroup, then dq by the 64-head kernel.
 template <int DQK, int NW>
 hipError_t launch_bwd_split(const void* q, const void* kv, const int32_t* idx, const void* dout,
                             const float* lse, int T, int topk, float scale, const float* sink,
@@ -1099,13 +1223,13 @@ hipError_t launch_bwd_split(const void* q, const void* kv, const int32_t* idx, c
                      scale, sink, (uint16_t*)dq, dkv, dsink);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t shm = bwd32_lds_bytes<DQK>();
-  e = hipFuncSetAttribute((const void*)sparse_mla_bwd_h32_kernel<DQK, true>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  const size_t shq = dq64_lds_bytes<DQK>(topk);
+  e = hipFuncSetAttribute((const void*)sparse_mla_bwd_dq64_kernel<DQK>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)shq);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((sparse_mla_bwd_h32_kernel<DQK, true>), dim3(T, 16 * NW / kB32), dim3(kWaves * 64), shm,
-                     st, (const uint16_t*)q, (const uint16_t*)kv, idx, (const uint16_t*)dout, lse, 16 * NW,
-                     topk, scale, sink, (uint16_t*)dq, dkv, dsink);
+  hipLaunchKernelGGL((sparse_mla_bwd_dq64_kernel<DQK>), dim3(T, 16 * NW / kQH), dim3(kWaves * 64), shq, st,
+                     (const uint16_t*)q, (const uint16_t*)kv, idx, (const uint16_t*)dout, lse, 16 * NW,
+                     topk, scale, (uint16_t*)dq);
   return hipGetLastError();
 }
 
@@ -1121,11 +1245,12 @@ hipError_t launch_sparse_mla_bwd(const void* q, const void* kv, const int32_t* i
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || T == 0) return e;
   if (bf16) {
-    if (H == 128) {
+    const bool split = d_qk == 576 ? dq64_lds_bytes<576>(topk) <= 160 * 1024 : dq64_lds_bytes<512>(topk) <= 160 * 1024;
+    if (H == 128 && split) {
       if (d_qk == 576) return launch_bwd_split<576, 8>(q, kv, idx, dout, lse, T, topk, scale, sink, dq, dkv, dsink, st);
       return launch_bwd_split<512, 8>(q, kv, idx, dout, lse, T, topk, scale, sink, dq, dkv, dsink, st);
     }
-    if (H == 64) {
+    if (H == 64 && split) {
       if (d_qk == 576) return launch_bwd_split<576, 4>(q, kv, idx, dout, lse, T, topk, scale, sink, dq, dkv, dsink, st);
       return launch_bwd_split<512, 4>(q, kv, idx, dout, lse, T, topk, scale, sink, dq, dkv, dsink, st);
     }
