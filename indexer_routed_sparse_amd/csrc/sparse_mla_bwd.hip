@@ -675,26 +675,31 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_bwd_dkv_kernel(
   auto idx_of = [&](int sub) __attribute__((always_inline)) {
     return irow[min(sub * kSK + n, topk - 1)];
   };
-  bf16x8_t nx[NLD];
-  auto load = [&](int ix) __attribute__((always_inline)) {
+  bf16x8_t nx[NLD], nx2[NLD];
+  auto loadTo = [&](bf16x8_t (&buf)[NLD], int ix) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < NLD; ++m) {
       const int c = tid + NT * m, r = (c / CPR) & (kSK - 1), p = c % CPR;
       int row = __shfl(ix, r, 64);
       row = row < 0 ? 0 : row;                 // masked slot (or past topk): any finite row
-      if (c < kSK * CPR) nx[m] = *reinterpret_cast<const bf16x8_t*>(kv + (int64_t)row * DQK + 8 * p);
+      if (c < kSK * CPR) buf[m] = *reinterpret_cast<const bf16x8_t*>(kv + (int64_t)row * DQK + 8 * p);
     }
   };
-  auto stage = [&]() __attribute__((always_inline)) {
+  auto load = [&](int ix) __attribute__((always_inline)) { loadTo(nx, ix); };
+  auto stageFrom = [&](const bf16x8_t (&buf)[NLD]) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < NLD; ++m) {
       const int c = tid + NT * m, r = c / CPR, p = c % CPR;
-      if (c < kSK * CPR) *reinterpret_cast<bf16x8_t*>(k_l + r * KRB + 16 * p) = nx[m];
+      if (c < kSK * CPR) *reinterpret_cast<bf16x8_t*>(k_l + r * KRB + 16 * p) = buf[m];
     }
   };
+  auto stage = [&]() __attribute__((always_inline)) { stageFrom(nx); };
+  // kv row of key n of a sub-tile (-1: masked slot or past topk)
+  auto row_of = [&](int sub, int ix) __attribute__((always_inline)) {
+    return sub * kSK + n < topk ? __shfl(ix, n, 64) : -1;
+  };
   // S and dP of this wave's 16 heads x the 16 keys; P of the valid slots
-  auto scores = [&](int sub, int ix, float (&P)[4], floatx4v_t& dP) __attribute__((always_inline)) {
-    const int rown = sub * kSK + n < topk ? __shfl(ix, n, 64) : -1;
+  auto scores = [&](int rown, float (&P)[4], floatx4v_t& dP) __attribute__((always_inline)) {
     const char* krow = k_l + n * KRB + 16 * g;
     const char* drow = d_l + (16 * w + n) * DRB + 16 * g;
     floatx4v_t S = floatx4v_t{};
@@ -713,31 +718,35 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_bwd_dkv_kernel(
       P[i] = rown >= 0 && lse2[i] > -__builtin_huge_valf() ? __builtin_amdgcn_exp2f(S[i] * sc2 - lse2[i]) : 0.0f;
   };
 
-  // ---- pass 1: D = sum_j p_j dp_j per head
+  // ---- pass 1: D = sum_j p_j dp_j per head. No atomics here, so the rows go two
+  // sub-tiles ahead: sub-tile s's rows sit in buffer s mod 2, requested at s - 2 with
+  // the indices loaded at s - 4 (ja / jb), and its key rows (ra / rb) taken then.
   float dpart[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto pass1 = [&](int sub, int& ixc, int ixn) __attribute__((always_inline)) {
+  int ja = idx_of(0), jb = idx_of(1);
+  int ra = row_of(0, ja), rb = row_of(1, jb);
+  loadTo(nx, ja);
+  if (nsub > 1) loadTo(nx2, jb);
+  ja = idx_of(2);
+  jb = idx_of(3);
+  auto pass1 = [&](int sub, bf16x8_t (&buf)[NLD], int& jc, int& rc) __attribute__((always_inline)) {
     __syncthreads();                   // every wave is done with the previous key rows
-    stage();
+    stageFrom(buf);
     __syncthreads();
-    if (sub + 1 < nsub) load(ixn);
+    if (sub + 2 < nsub) loadTo(buf, jc);
     float P[4];
     floatx4v_t dP;
-    scores(sub, ixc, P, dP);
-    ixc = idx_of(sub + 2);
+    scores(rc, P, dP);
+    rc = row_of(sub + 2, jc);
+    jc = idx_of(sub + 4);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dpart[i] = fmaf(P[i], dP[i], dpart[i]);
   };
-  int ixa = 0, ixb = 0;       // indices of sub-tiles of even / odd number
-  if (nsub > 0) {
-    ixa = idx_of(0);
-    ixb = idx_of(1);
-    load(ixa);
-  }
 #pragma unroll 1
   for (int sub = 0; sub < nsub; sub += 2) {
-    pass1(sub, ixa, ixb);
-    if (sub + 1 < nsub) pass1(sub + 1, ixb, ixa);
+    pass1(sub, nx, ja, ra);
+    if (sub + 1 < nsub) pass1(sub + 1, nx2, jb, rb);
   }
+  int ixa = 0, ixb = 0;       // pass 2: indices of sub-tiles of even / odd number
   float Dh[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {          // over the 16 keys (lanes n)
@@ -764,7 +773,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_bwd_dkv_kernel(
     if (sub + 1 < nsub) load(ixn);
     float P[4], dS[4];
     floatx4v_t dP;
-    scores(sub, ixc, P, dP);
+    scores(row_of(sub, ixc), P, dP);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dS[i] = P[i] * (dP[i] - Dh[i]) * scale;
     {
