@@ -605,7 +605,7 @@ __global__ __launch_bounds__(kGrpWaves * 64) __attribute__((amdgpu_waves_per_eu(
 void block_gqa_bwd_kmaj_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ blk, const int32_t* __restrict__ cu, int nseq, int T, int Hq, int Hkv,
-    int B, int nblk, float scale, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
+    int B, int nblk, int maxlen, float scale, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
     const uint16_t* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv) {
   constexpr int KS = D / 32;              // 32-wide k-steps of S^T and dP^T
   constexpr int NDT = D / 16;             // 16-channel tiles
@@ -633,10 +633,13 @@ void block_gqa_bwd_kmaj_kernel(
 
   const int tid = threadIdx.x, w = tid >> 6, L = tid & 63;
   const int n = L & 15, quad = L >> 4;
+  // The chunk's tokens attend keys in [t0 - maxlen + 1, t0 + kCT - 1] only (a sequence
+  // holds at most maxlen rows), so blockIdx.y counts 64-key blocks from the one holding
+  // key max(0, t0 - maxlen + 1).
   const int t0 = (int)blockIdx.x * kCT;
-  const int K0 = (int)blockIdx.y * kKB;
+  const int K0 = (max(0, t0 - maxlen + 1) / kKB + (int)blockIdx.y) * kKB;
   const int g = (int)blockIdx.z;
-  if (t0 + kCT - 1 < K0) return;                          // no token of the chunk reaches the block
+  if (t0 + kCT - 1 < K0 || K0 >= T) return;               // no token of the chunk reaches the block
   const int G = Hq / Hkv;
   const int TT = kGrpRows / G;                            // tokens per row tile
   const int nrows = TT * G;
@@ -916,9 +919,11 @@ hipError_t launch_grouped(const void* q, const void* k, const void* v, const int
   const size_t shk = kmaj_lds_bytes<D>();
   e = hipFuncSetAttribute((const void*)block_gqa_bwd_kmaj_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shk);
   if (e != hipSuccess) return e;
-  const dim3 kgrid((unsigned)((T + kCT - 1) / kCT), (unsigned)((T + kKB - 1) / kKB), (unsigned)Hkv);
+  const int64_t nkb = ((int64_t)maxlen + kCT + kKB - 1) / kKB + 1;   // blocks a chunk can reach
+  if (nkb > 65535) return hipErrorInvalidValue;
+  const dim3 kgrid((unsigned)((T + kCT - 1) / kCT), (unsigned)nkb, (unsigned)Hkv);
   hipLaunchKernelGGL((block_gqa_bwd_kmaj_kernel<D>), kgrid, dim3(kGrpWaves * 64), shk, st, (const uint16_t*)q,
-                     (const uint16_t*)k, (const uint16_t*)v, blk, cu, nseq, T, Hq, Hkv, B, nblk, scale,
+                     (const uint16_t*)k, (const uint16_t*)v, blk, cu, nseq, T, Hq, Hkv, B, nblk, maxlen, scale,
                      (const uint16_t*)dout, lse, (const uint16_t*)dq, dk, dv);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
