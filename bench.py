@@ -396,8 +396,7 @@ def main():
         counters_pass()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the sharding design is described in DESIGN.md).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import indexer_routed_sparse_amd as sa

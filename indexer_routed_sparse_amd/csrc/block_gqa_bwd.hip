@@ -646,7 +646,7 @@ void block_gqa_bwd_kmaj_kernel(
   if (TT == 0) return;                                    // G > 128: not launched
 
   // ---- the chunk's tokens that attend keys of the block, with their key masks (token
-  // t0 + NT r + tid in round r)
+  // t0 + NT r + tid in step r of the set-up loop)
   uint64_t mr[NR], balr[NR];
   uint32_t mlo = 0u, mhi = 0u;
 #pragma unroll
@@ -700,7 +700,7 @@ void block_gqa_bwd_kmaj_kernel(
     kmask |= (uint64_t)(uint32_t)cnt[kGrpWaves * NR + 2 * i] | ((uint64_t)(uint32_t)cnt[kGrpWaves * NR + 2 * i + 1] << 32);
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
-    int at = nl;                                          // listed before wave w of round r
+    int at = nl;                                          // listed before wave w of step r
 #pragma unroll
     for (int i = 0; i < kGrpWaves; ++i) {
       at += i < w ? cnt[kGrpWaves * r + i] : 0;

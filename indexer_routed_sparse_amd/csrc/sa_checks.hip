@@ -53,7 +53,7 @@ __global__ void offsets_kernel(const int32_t* __restrict__ cu, int nseq, int T, 
   if (bad) atomicOr(flag, 1);
 }
 
-// Runs `launch(flag)` after clearing the flag and waits for the verdict.
+// Runs `launch(flag)` after clearing the flag and waits for the result.
 template <class F>
 hipError_t run_check(hipStream_t st, bool* ok, F launch) {
   int* flag = flag_ptr();
