@@ -1037,14 +1037,17 @@ __global__ __launch_bounds__(kNT) void sparse_mla_bwd_f32_kernel(
 
 // Teacher of the sparse KL indexer loss: the head mean of the attention probability of
 // every slot, p[t,j] = (1/H) sum_h exp(scale q[t,h].kv[idx_j] - lse[t,h]); 0 on -1 slots.
-// Teacher, bf16: one workgroup per token, eight waves; wave w owns heads [16w, 16w+16)
-// (q slices of its heads as A operands in registers, its rows of the forward's lse).
+// Teacher, bf16: one workgroup per token, four waves; wave w owns heads
+// [16 HB w, 16 HB (w + 1)), HB = 2 above 64 heads, else 1 (q slices of its heads as A
+// operands in registers, its rows of the forward's lse). Four waves of up to 32 heads
+// take one wave per SIMD and 76 KB of LDS, so two workgroups share a CU and two tokens'
+// gathers are in flight there (eight waves of 16 heads held one workgroup per CU).
 // The token's slots go in 32-key sub-tiles that the whole workgroup gathers once into
 // LDS (double-buffered, the next sub-tile's rows in registers while the current one
 // is computed); every wave forms S = Q K^T for its heads (16x16x32 MFMAs, key rows as
 // B operands as stored) and sums exp(scale s - lse) over its 16 heads per key; the
 // per-wave sums meet in LDS and one plain store per slot writes p_j / H.
-constexpr int kTW = 8;            // waves of a teacher workgroup
+constexpr int kTW = 4;            // waves of a teacher workgroup
 constexpr int kTK = 32;           // keys per teacher sub-tile
 
 template <int DQK>
@@ -1052,40 +1055,41 @@ constexpr size_t teacher_lds_bytes() {
   return (size_t)2 * kTK * krow_bytes<DQK>() + (size_t)2 * kTW * kTK * sizeof(float);
 }
 
-template <int DQK>
-__global__ __launch_bounds__(kTW * 64) void attn_teacher_bf16_kernel(
+template <int DQK, int NW, int HB>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_teacher_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     const float* __restrict__ lse, int H, int topk, float scale, float* __restrict__ teacher) {
   constexpr int KRB = krow_bytes<DQK>();
   constexpr int NK = DQK / 32;
   constexpr int CPR = DQK * 2 / 16;
-  constexpr int NLD = (kTK * CPR + kTW * 64 - 1) / (kTW * 64);
+  constexpr int NT = NW * 64;
+  constexpr int NLD = (kTK * CPR + NT - 1) / NT;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   char* stage = lds;                                                    // [2][kTK][KRB]
-  float* part = reinterpret_cast<float*>(lds + 2 * kTK * KRB);          // [2][kTW][kTK]
+  float* part = reinterpret_cast<float*>(lds + 2 * kTK * KRB);          // [2][NW][kTK]
   const int t = blockIdx.x;
   const int tid = threadIdx.x, w = tid >> 6, L = tid & 63;
   const int g = L >> 4, n = L & 15;
-  const int h0 = kHG * w;
-  const bool heads = h0 < H;                       // wave-uniform
+  const int h0 = kHG * HB * w;                     // the wave's first head (HB blocks of 16)
   const int32_t* __restrict__ irow = idx + (int64_t)t * topk;
   const int nsub = (topk + kTK - 1) / kTK;
   const float sc2 = scale * kLog2e, invH = 1.0f / (float)H;
 
-  bf16x8_t qa[NK];
-  float lse2[4];
-  {
-    const int hq = h0 + n;
+  bf16x8_t qa[HB][NK];
+  float lse2[HB][4];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const int hq = h0 + kHG * hb + n;
     const uint16_t* qr = q + ((int64_t)t * H + (hq < H ? hq : 0)) * DQK + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
       const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(qr + 32 * ks);
-      qa[ks] = hq < H ? x : bf16x8_t{};
+      qa[hb][ks] = hq < H ? x : bf16x8_t{};
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int hh = h0 + 4 * g + i;
-      lse2[i] = (hh < H ? lse[(int64_t)t * H + hh] : -__builtin_huge_valf()) * kLog2e;
+      const int hh = h0 + kHG * hb + 4 * g + i;
+      lse2[hb][i] = (hh < H ? lse[(int64_t)t * H + hh] : -__builtin_huge_valf()) * kLog2e;
     }
   }
   // Slot indices of a sub-tile: lane l holds slot kTK sub + (l mod 32), clamped to the
@@ -1099,7 +1103,7 @@ __global__ __launch_bounds__(kTW * 64) void attn_teacher_bf16_kernel(
   auto load = [&](int ix) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < NLD; ++m) {
-      const int c = tid + kTW * 64 * m, r = c / CPR, p = c % CPR;
+      const int c = tid + NT * m, r = c / CPR, p = c % CPR;
       int row = __shfl(ix, r < kTK ? r : 0, 64);
       row = row < 0 || c >= kTK * CPR ? 0 : row;
       nx[m] = *reinterpret_cast<const bf16x8_t*>(kv + (int64_t)row * DQK + 8 * p);
@@ -1109,10 +1113,10 @@ __global__ __launch_bounds__(kTW * 64) void attn_teacher_bf16_kernel(
   auto finish = [&](int sub, bool ok) __attribute__((always_inline)) {
     const int j = sub * kTK + tid;
     if (j < topk) {
-      const float* pp = part + (sub & 1) * kTW * kTK + tid;
+      const float* pp = part + (sub & 1) * NW * kTK + tid;
       float sum = 0.0f;
 #pragma unroll
-      for (int v = 0; v < kTW; ++v) sum += pp[v * kTK];
+      for (int v = 0; v < NW; ++v) sum += pp[v * kTK];
       teacher[(int64_t)t * topk + j] = ok ? sum * invH : 0.0f;
     }
   };
@@ -1121,7 +1125,7 @@ __global__ __launch_bounds__(kTW * 64) void attn_teacher_bf16_kernel(
     char* kt = stage + (sub & 1) * kTK * KRB;
 #pragma unroll
     for (int m = 0; m < NLD; ++m) {
-      const int c = tid + kTW * 64 * m, r = c / CPR, p = c % CPR;
+      const int c = tid + NT * m, r = c / CPR, p = c % CPR;
       if (c < kTK * CPR) *reinterpret_cast<bf16x8_t*>(kt + r * KRB + 16 * p) = nx[m];
     }
     __syncthreads();
@@ -1129,25 +1133,30 @@ __global__ __launch_bounds__(kTW * 64) void attn_teacher_bf16_kernel(
     if (sub > 0 && tid < kTK) finish(sub - 1, okc);
     okc = sub * kTK + L < topk && ixc >= 0;
     ixc = idx_of(sub + 2);
-    float* pw = part + (sub & 1) * kTW * kTK + w * kTK;
-    if (heads) {
+    float* pw = part + (sub & 1) * NW * kTK + w * kTK;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const char* kr = kt + (16 * half + n) * KRB + 16 * g;
-        floatx4v_t S = floatx4v_t{};
+    for (int half = 0; half < 2; ++half) {
+      const char* kr = kt + (16 * half + n) * KRB + 16 * g;
+      float ps = 0.0f;
 #pragma unroll
-        for (int ks = 0; ks < NK; ++ks)
-          S = mfma16x32(qa[ks], *reinterpret_cast<const bf16x8_t*>(kr + 64 * ks), S);
-        float ps = 0.0f;
+      for (int hb = 0; hb < HB; ++hb) {
+        if (h0 + kHG * hb < H) {                   // wave-uniform
+          floatx4v_t S = floatx4v_t{};
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          ps += lse2[i] > -__builtin_huge_valf() ? __builtin_amdgcn_exp2f(S[i] * sc2 - lse2[i]) : 0.0f;
-        ps += __shfl_xor(ps, 16, 64);
-        ps += __shfl_xor(ps, 32, 64);
-        if (g == 0) pw[16 * half + n] = ps;
+          for (int ks = 0; ks < NK; ++ks) {
+            S = mfma16x32(qa[hb][ks], *reinterpret_cast<const bf16x8_t*>(kr + 64 * ks), S);
+            // a fence every few k-steps keeps the key-row reads from all being hoisted
+            // (their registers would not fit beside two head blocks' q operands)
+            if (ks % 6 == 5) __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            ps += lse2[hb][i] > -__builtin_huge_valf() ? __builtin_amdgcn_exp2f(S[i] * sc2 - lse2[hb][i]) : 0.0f;
+        }
       }
-    } else if (L < kTK) {
-      pw[L] = 0.0f;
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      if (g == 0) pw[16 * half + n] = ps;
     }
   };
   int ixa = 0, ixb = 0;       // indices of sub-tiles of even / odd number
@@ -1294,20 +1303,18 @@ hipError_t launch_attn_teacher(const void* q, const void* kv, const int32_t* idx
     return hipGetLastError();
   }
   const dim3 grid(T), block(kTW * 64);
-  if (d_qk == 576) {
-    const size_t shm = teacher_lds_bytes<576>();
-    e = hipFuncSetAttribute((const void*)attn_teacher_bf16_kernel<576>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_teacher_bf16_kernel<576>), grid, block, shm, st, (const uint16_t*)q,
-                       (const uint16_t*)kv, idx, lse, H, topk, scale, teacher);
-  } else {
-    const size_t shm = teacher_lds_bytes<512>();
-    e = hipFuncSetAttribute((const void*)attn_teacher_bf16_kernel<512>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_teacher_bf16_kernel<512>), grid, block, shm, st, (const uint16_t*)q,
-                       (const uint16_t*)kv, idx, lse, H, topk, scale, teacher);
-  }
-  return hipGetLastError();
+  auto go = [&](auto kern, size_t shm) -> hipError_t {
+    hipError_t r = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (r != hipSuccess) return r;
+    hipLaunchKernelGGL(kern, grid, block, shm, st, (const uint16_t*)q, (const uint16_t*)kv, idx, lse, H, topk,
+                       scale, teacher);
+    return hipGetLastError();
+  };
+  if (d_qk == 576)
+    return H > 64 ? go(attn_teacher_bf16_kernel<576, kTW, 2>, teacher_lds_bytes<576>())
+                  : go(attn_teacher_bf16_kernel<576, kTW, 1>, teacher_lds_bytes<576>());
+  return H > 64 ? go(attn_teacher_bf16_kernel<512, kTW, 2>, teacher_lds_bytes<512>())
+                : go(attn_teacher_bf16_kernel<512, kTW, 1>, teacher_lds_bytes<512>());
 }
 
 }  // namespace sa

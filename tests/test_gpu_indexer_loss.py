@@ -36,7 +36,8 @@ def close(got, ref, atol, rtol, what):
     assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} out of tolerance, max err {err.max():.3g}"
 
 
-@pytest.mark.parametrize("H,k,d_qk", [(16, 127, 512), (8, 64, 576), (128, 300, 576), (80, 33, 576)])
+@pytest.mark.parametrize("H,k,d_qk", [(16, 127, 512), (8, 64, 576), (128, 300, 576), (80, 33, 576),
+                                      (96, 65, 512), (64, 40, 576)])
 def test_attn_teacher_shapes(sa, H, k, d_qk):
     T, S = 20, 600
     g = torch.Generator().manual_seed(H + k + d_qk)
