@@ -332,8 +332,8 @@ size_t grp_bwd_lds_bytes(int D, int G, int nblk, int maxlen) {
 template <int D>
 SA_DEVICE int gswz(int row) { return D == 128 ? 2 * (row & 7) : 2 * (row & 3); }
 
-template <int D, int MODE>
-__global__ __launch_bounds__(kGrpWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+template <int D, int MODE, int NWV>
+__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void block_gqa_bwd_group_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ blk, const int32_t* __restrict__ cu, int nseq, int T, int Hq, int Hkv,
@@ -345,7 +345,7 @@ void block_gqa_bwd_group_kernel(
   constexpr int CPR = D * 2 / 16;         // 16-byte chunks per row
   constexpr int KSB = D * 2 + 16;         // padded stage row bytes
   constexpr int RWB = D * 2;              // swizzled row bytes
-  constexpr int NT = kGrpWaves * 64;
+  constexpr int NT = NWV * 64;            // NWV waves own rows 16 w .. 16 w + 15
   constexpr int LDN = (2 * 32 * CPR + NT - 1) / NT;   // 16-byte loads per thread per sub-tile
   static_assert(MODE == 1 || MODE == 2, "D-only or dq-only");
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -900,21 +900,22 @@ hipError_t launch_grouped(const void* q, const void* k, const void* v, const int
   const int GT = grp_tokens(G);
   const size_t shm = grp_bwd_lds_bytes(D, G, nblk, maxlen);
   const int by_xcd = 8 % Hkv == 0;
-  const int64_t ngrp = ((int64_t)T + GT - 1) / GT;
-  const int64_t grid = by_xcd ? (ngrp + 8 / Hkv - 1) / (8 / Hkv) * 8 : ngrp * Hkv;
-  if (grid > INT32_MAX) return hipErrorInvalidValue;
   // D of every row (into the first four bytes of its dq row), then dk and dv key-major,
   // then dq
-  auto grouped = [&](auto kern) -> hipError_t {
+  // gt tokens per group (gt G <= 16 nwv rows), nwv waves per workgroup
+  auto grouped = [&](auto kern, int gt, int nwv) -> hipError_t {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kGrpWaves * 64), shm, st, (const uint16_t*)q,
-                       (const uint16_t*)k, (const uint16_t*)v, blk, cu, nseq, T, Hq, Hkv, B, nblk, GT,
-                       grp_words(maxlen, GT), scale, (const uint16_t*)dout, lse, (uint16_t*)dq, dk, dv,
+    const int64_t ng = ((int64_t)T + gt - 1) / gt;
+    const int64_t gr = by_xcd ? (ng + 8 / Hkv - 1) / (8 / Hkv) * 8 : ng * Hkv;
+    if (gr > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kern, dim3((unsigned)gr), dim3(nwv * 64), shm, st, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, blk, cu, nseq, T, Hq, Hkv, B, nblk, gt,
+                       grp_words(maxlen, gt), scale, (const uint16_t*)dout, lse, (uint16_t*)dq, dk, dv,
                        by_xcd);
     return hipGetLastError();
   };
-  hipError_t e = grouped(block_gqa_bwd_group_kernel<D, 1>);
+  hipError_t e = grouped(block_gqa_bwd_group_kernel<D, 1, kGrpWaves>, GT, kGrpWaves);
   if (e != hipSuccess) return e;
   const size_t shk = kmaj_lds_bytes<D>();
   e = hipFuncSetAttribute((const void*)block_gqa_bwd_kmaj_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shk);
@@ -927,7 +928,10 @@ hipError_t launch_grouped(const void* q, const void* k, const void* v, const int
                      (const uint16_t*)dout, lse, (const uint16_t*)dq, dk, dv);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return grouped(block_gqa_bwd_group_kernel<D, 2>);
+  // the dq pass in workgroups of four waves over 64-row groups: at 151 VGPRs three
+  // of them share a CU, where one of eight waves fit
+  const int GT4 = G >= 2 ? 64 / G : kGrpMaxTok;
+  return grouped(block_gqa_bwd_group_kernel<D, 2, 4>, GT4, 4);
 }
 
 }  // namespace
