@@ -70,7 +70,7 @@ def _run_mla_bwd(sa, q, kv, idx, dout, scale):
 
 @pytest.mark.parametrize("H,k,d_qk", [(16, 65, 512), (16, 127, 576), (8, 64, 576), (64, 33, 576),
                                       (64, 200, 512), (128, 96, 512), (128, 2051, 576), (80, 1, 576),
-                                      (32, 70, 576)])
+                                      (32, 70, 576), (128, 1, 576), (64, 17, 576)])
 def test_sparse_mla_bwd_shapes(sa, H, k, d_qk):
     """Head counts 8..128 (partial 16-head groups), widths 512/576, top-k from 1 to the
     GLM width 2051; -1 slots, a repeated index, an all-invalid row."""
