@@ -289,7 +289,9 @@ sa_status sa_sparse_mla_fwd(const void* q, const void* kv, const int32_t* idx, i
  *   [T,H] fp32 (the forward's). Outputs: dq [T,H,d_qk] (dtype); dkv
  *   [S,d_qk] fp32, which the call zeroes and then accumulates into with
  *   floating-point atomics, so dkv's low bits may differ from run to run (every
- *   other output is deterministic).
+ *   other output is deterministic). No output may overlap an input or another
+ *   output: with bf16 at 64 or 128 heads the call keeps each row's D = dout . out in
+ *   the first four bytes of that row of dq between its launches, then overwrites dq.
  * Sizes: d_qk in {512, 576}; d_v == 512; H in [1, 128]; topk >= 1 (at most 8192 for
  *   SA_F32). Pointers 16-byte aligned (lse and idx: 4-byte).
  */
@@ -391,7 +393,9 @@ sa_status sa_block_sparse_gqa_fwd(const void* q, const void* k, const void* v,
  * Inputs as the forward plus dout [T,Hq,Dv] (dtype) and the forward's lse [T,Hq] fp32.
  * Outputs: dq [T,Hq,D] (dtype); dk [T,Hkv,D] and dv [T,Hkv,Dv] fp32, which the call
  * zeroes and then accumulates into with floating-point atomics (their low bits may
- * differ from run to run; dq is deterministic). Limits as the forward.
+ * differ from run to run; dq is deterministic). No output may overlap an input or
+ * another output: in bf16 the call keeps each row's D in the first four bytes of that
+ * row of dq between its launches, then overwrites dq. Limits as the forward.
  */
 sa_status sa_block_sparse_gqa_bwd(const void* q, const void* k, const void* v, const int32_t* blk,
                                   const void* dout, const float* lse, int dtype, int32_t T,
