@@ -838,9 +838,10 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_bwd_dkv_kernel(
 // only as the A operands of S and dP (channel-contiguous), so a wave keeps its 16
 // heads' q and dout in VGPRs and its dq tiles (16 heads x d_qk) in AGPRs, and each
 // gathered 32-key sub-tile serves 64 heads (the 32-head kernel gathers every row once
-// per 32 heads). The token's slot indices are staged in LDS first, so the rows of
-// sub-tile s + 2 are requested while sub-tile s is computed (two register buffers,
-// the loop body written out twice). Per sub-tile each wave forms S and dP of its 16
+// per 32 heads). The token's slot indices are staged in LDS first, and the rows of
+// sub-tile s + 1 are requested while sub-tile s is computed (one register buffer: a
+// second one, for rows two sub-tiles ahead, took the registers the compiler uses to
+// read the LDS operands ahead, and was slower). Per sub-tile each wave forms S and dP of its 16
 // heads x 32 keys (16x16x32 MFMAs, key rows as B operands), dS into a wave-private LDS
 // block as [head][key], and dq += dS K over the 32 keys (K^T by transposing reads): no
 // exchange between waves, one barrier per sub-tile (two key stages).
@@ -920,7 +921,7 @@ void sparse_mla_bwd_dq64_kernel(const uint16_t* __restrict__ q, const uint16_t* 
       *reinterpret_cast<bf16x8_t*>(kt + r * KRB + 16 * p) = nx[m];
     }
     __syncthreads();                     // this stage is in place; the other one is free
-    if (sub + 2 < nsub) load(nx, sub + 2);
+    if (sub + 1 < nsub) load(nx, sub + 1);
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       const int key = 16 * kh + n;
@@ -957,13 +958,13 @@ void sparse_mla_bwd_dq64_kernel(const uint16_t* __restrict__ q, const uint16_t* 
     }
     __builtin_amdgcn_wave_barrier();      // the dS rows are read before the next sub-tile's writes
   };
-  bf16x8_t nxA[NLD], nxB[NLD];
-  load(nxA, 0);
-  if (nsub > 1) load(nxB, 1);
+  bf16x8_t nx[NLD];
+  load(nx, 0);
+  // two steps per iteration (the two key stages): this form measured faster than one
 #pragma unroll 1
   for (int sub = 0; sub < nsub; sub += 2) {
-    step(sub, nxA);
-    if (sub + 1 < nsub) step(sub + 1, nxB);
+    step(sub, nx);
+    if (sub + 1 < nsub) step(sub + 1, nx);
   }
   // lane (g, n) of tile ct: heads hw + 4 g + e, channel 16 ct + n
 #pragma unroll
