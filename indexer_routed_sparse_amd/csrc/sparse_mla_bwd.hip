@@ -1043,13 +1043,14 @@ __global__ __launch_bounds__(kNT) void sparse_mla_bwd_f32_kernel(
 // operands in registers, its rows of the forward's lse). Four waves of up to 32 heads
 // take one wave per SIMD and 76 KB of LDS, so two workgroups share a CU and two tokens'
 // gathers are in flight there (eight waves of 16 heads held one workgroup per CU).
-// The token's slots go in 32-key sub-tiles that the whole workgroup gathers once into
+// The token's slots go in 16-key sub-tiles that the whole workgroup gathers once into
 // LDS (double-buffered, the next sub-tile's rows in registers while the current one
 // is computed); every wave forms S = Q K^T for its heads (16x16x32 MFMAs, key rows as
 // B operands as stored) and sums exp(scale s - lse) over its 16 heads per key; the
 // per-wave sums meet in LDS and one plain store per slot writes p_j / H.
 constexpr int kTW = 4;            // waves of a teacher workgroup
-constexpr int kTK = 32;           // keys per teacher sub-tile
+constexpr int kTK = 16;           // keys per teacher sub-tile (32 measured 3-4 % slower:
+                                  // its row buffer took registers the LDS reads use)
 
 template <int DQK>
 constexpr size_t teacher_lds_bytes() {
@@ -1093,12 +1094,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       lse2[hb][i] = (hh < H ? lse[(int64_t)t * H + hh] : -__builtin_huge_valf()) * kLog2e;
     }
   }
-  // Slot indices of a sub-tile: lane l holds slot kTK sub + (l mod 32), clamped to the
+  // Slot indices of a sub-tile: lane l holds slot kTK sub + (l mod kTK), clamped to the
   // last slot. As in the backward: two registers take turns (the loop body is written
   // out twice), each reloaded two sub-tiles ahead after its last use, and the row loads
   // take their indices by lane shuffles, so no load waits for an index load.
   auto idx_of = [&](int sub) __attribute__((always_inline)) {
-    return irow[min(sub * kTK + (L & 31), topk - 1)];
+    return irow[min(sub * kTK + (L & (kTK - 1)), topk - 1)];
   };
   bf16x8_t nx[NLD];
   auto load = [&](int ix) __attribute__((always_inline)) {
@@ -1136,7 +1137,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     ixc = idx_of(sub + 2);
     float* pw = part + (sub & 1) * NW * kTK + w * kTK;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int half = 0; half < kTK / 16; ++half) {
       const char* kr = kt + (16 * half + n) * KRB + 16 * g;
       float ps = 0.0f;
 #pragma unroll
